@@ -1,0 +1,140 @@
+"""Seeded synthetic inputs and workload shapes.
+
+This module holds no arithmetic of the method: it only draws random numbers
+with numpy's PCG64 generator and lists matrix shapes.  Both the HIP path (via
+the tests and the benchmark) and the CPU oracle consume the arrays it returns.
+
+Recipes (all ``np.random.default_rng`` = PCG64, ``standard_normal`` drawn in
+float32):
+
+* single 896 x 896 GEMV: rng = default_rng(0); W = rng.standard_normal((896,
+  896), float32) * float32(0.02); then x = rng.standard_normal(896,
+  float32).astype(float16).
+* Qwen2.5-shaped sweeps: matrix i (in the order L0.q, L0.k, L0.v, L0.o,
+  L0.gate, L0.up, L0.down, L1.q, ..., lm_head) uses
+  W_i = default_rng((cfg, i)).standard_normal((N, K), float32) * 0.02 and
+  x_i = default_rng((cfg, 1000 + i)).standard_normal(K, float32) as float16,
+  with cfg = 2 for the 0.5B model and 5 for the 7B model.
+* binary sign GEMV (N, K): bits = default_rng((4, N, K)).integers(0, 2,
+  (N, K)); W = 1 - 2*bits as float32; x bits from default_rng((4, N, K, 1)).
+* prefill activations: X = default_rng((5, 10000)) standard normal [512, 3584]
+  float16 for gate/up and default_rng((5, 10001)) [512, 18944] for down.
+
+Shapes follow the Qwen2.5-0.5B (hidden 896, intermediate 4864, 24 layers,
+2 KV heads x 64 = 128, vocab 151936, tied head) and Qwen2.5-7B (hidden 3584,
+intermediate 18944, 28 layers, 4 KV heads x 128 = 512, vocab 152064)
+configurations; weights are random stand-ins for trained checkpoints, since
+the GEMV's time does not depend on the values.
+"""
+
+import numpy as np
+
+QWEN05B = dict(hidden=896, inter=4864, layers=24, kv=128, vocab=151936)
+QWEN7B = dict(hidden=3584, inter=18944, layers=28, kv=512, vocab=152064)
+SWEEP_CFG = {"qwen2.5-0.5b": 2, "qwen2.5-7b": 5}
+MODELS = {"qwen2.5-0.5b": QWEN05B, "qwen2.5-7b": QWEN7B}
+
+
+def sweep_shapes(model="qwen2.5-0.5b"):
+    """[(name, N, K)] of every linear layer read per decoded token, in order."""
+    m = MODELS[model]
+    h, f, kv = m["hidden"], m["inter"], m["kv"]
+    out = []
+    for layer in range(m["layers"]):
+        for name, n, k in (("q", h, h), ("k", kv, h), ("v", kv, h), ("o", h, h),
+                           ("gate", f, h), ("up", f, h), ("down", h, f)):
+            out.append(("L%d.%s" % (layer, name), n, k))
+    out.append(("lm_head", m["vocab"], h))
+    return out
+
+
+def single_gemv_896():
+    """(W fp32 [896,896], x fp16 [896]) for the single-GEMV case, seed 0."""
+    r = np.random.default_rng(0)
+    W = r.standard_normal((896, 896), dtype=np.float32) * np.float32(0.02)
+    x = r.standard_normal(896, dtype=np.float32).astype(np.float16)
+    return W, x
+
+
+def sweep_matrix(model, i, N, K):
+    """(W fp32 [N,K], x fp16 [K]) of matrix i of a sweep."""
+    cfg = SWEEP_CFG[model]
+    W = np.random.default_rng((cfg, i)).standard_normal((N, K), dtype=np.float32)
+    W *= np.float32(0.02)
+    x = np.random.default_rng((cfg, 1000 + i)).standard_normal(K, dtype=np.float32)
+    return W, x.astype(np.float16)
+
+
+def sweep_weight_rows(model, i, N, K, rows):
+    """Rows of W_i without materialising the whole matrix when it is large.
+
+    PCG64 draws standard normals row-major, so row r needs the first r*K
+    draws skipped; for simplicity this regenerates the matrix in chunks."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cfg = SWEEP_CFG[model]
+    r = np.random.default_rng((cfg, i))
+    out = np.empty((rows.size, K), dtype=np.float32)
+    order = np.argsort(rows)
+    srt = rows[order]
+    chunk = max(1, (64 << 20) // (4 * K))
+    pos = 0
+    j = 0
+    while pos < N and j < srt.size:
+        cnt = min(chunk, N - pos)
+        blk = r.standard_normal((cnt, K), dtype=np.float32)
+        while j < srt.size and srt[j] < pos + cnt:
+            out[order[j]] = blk[srt[j] - pos]
+            j += 1
+        pos += cnt
+    return out * np.float32(0.02)
+
+
+def sweep_x(model, i, K):
+    cfg = SWEEP_CFG[model]
+    return np.random.default_rng((cfg, 1000 + i)).standard_normal(K, dtype=np.float32).astype(np.float16)
+
+
+def binary_case(N, K):
+    """(W {-1,+1} fp32 [N,K], x {-1,+1} fp32 [K]) for the sign GEMV."""
+    bits = np.random.default_rng((4, N, K)).integers(0, 2, (N, K))
+    xb = np.random.default_rng((4, N, K, 1)).integers(0, 2, K)
+    return (1 - 2 * bits).astype(np.float32), (1 - 2 * xb).astype(np.float32)
+
+
+BINARY_SHAPES = [(n, k) for n in (896, 4864, 151936) for k in (896, 4864)]
+
+
+def prefill_shapes():
+    """[(name, N, K)] of the M=512 prefill GEMMs (Qwen2.5-7B layer 0 MLP)."""
+    m = QWEN7B
+    return [("gate", m["inter"], m["hidden"]), ("up", m["inter"], m["hidden"]),
+            ("down", m["hidden"], m["inter"])]
+
+
+PREFILL_M = 512
+
+
+def prefill_X(K, M=PREFILL_M):
+    """fp16 activations [M, K]: seed (5, 10000) for K = 3584, (5, 10001) else."""
+    seed = (5, 10000) if K == QWEN7B["hidden"] else (5, 10001)
+    return np.random.default_rng(seed).standard_normal((M, K), dtype=np.float32).astype(np.float16)
+
+
+def prefill_W(name):
+    """Layer-0 gate/up/down weights of the 7B sweep (matrix indices 4, 5, 6)."""
+    idx = {"gate": 4, "up": 5, "down": 6}[name]
+    shapes = sweep_shapes("qwen2.5-7b")
+    _, N, K = shapes[idx]
+    W = np.random.default_rng((SWEEP_CFG["qwen2.5-7b"], idx)).standard_normal((N, K), dtype=np.float32)
+    return W * np.float32(0.02)
+
+
+def normal_matrix(seed, N, K, std=0.02):
+    """Small seeded test matrix: N(0, std) float32."""
+    W = np.random.default_rng(seed).standard_normal((N, K), dtype=np.float32)
+    return W * np.float32(std)
+
+
+def normal_vector(seed, K):
+    """Small seeded fp16 activation vector ~ N(0, 1)."""
+    return np.random.default_rng(seed).standard_normal(K, dtype=np.float32).astype(np.float16)

@@ -1,0 +1,90 @@
+"""Packers and unpackers for the four code layouts (test infrastructure only).
+
+Layouts (the library's storage contract; Whetstone, "The .wstone format" says
+only that nibbles are stored in the order the GEMV's 128-bit load consumes
+them; the reading taken here is the natural little-endian order, which a
+16-byte load of a row consumes front to back):
+
+* int4 codes   uint32 [N][K/8]: element 8j+i of a row in bits [4i, 4i+4) of
+                word j.
+* int4 meta    uint32 [N][K/128]: fp16 scale bits in bits [0,16), fp16 zero
+                bits in bits [16,32) (a little-endian half2 {scale, zero}).
+* K5 codes     uint8 [N][K] (one byte per weight), fp16 scale [N][K/128].
+* ternary      uint32 [N][K/16]: element 16j+i in bits [2i, 2i+2) of word j,
+                code = t + 1; fp16 scale [N][K/128].
+* binary       uint32 [N][K/32]: element 32j+i in bit i of word j.
+
+Packers build words by multiply-and-add over slots; unpackers read a slot with
+shift-and-mask.  They are written independently from the layout text above.
+"""
+
+import numpy as np
+
+
+def _pack_fields(codes, bits):
+    codes = np.asarray(codes)
+    if codes.ndim != 2:
+        raise ValueError("codes must be 2-D")
+    per = 32 // bits
+    N, K = codes.shape
+    if K % per:
+        raise ValueError("K must be a multiple of %d" % per)
+    c = codes.astype(np.uint64).reshape(N, K // per, per)
+    if np.any(c >> np.uint64(bits)):
+        raise ValueError("code does not fit in %d bits" % bits)
+    weights = (np.uint64(1) << (np.uint64(bits) * np.arange(per, dtype=np.uint64)))
+    return (c * weights).sum(axis=2).astype(np.uint32)
+
+
+def _unpack_fields(words, K, bits):
+    words = np.asarray(words, dtype=np.uint32)
+    per = 32 // bits
+    N = words.shape[0]
+    out = np.empty((N, K), dtype=np.uint8)
+    mask = np.uint32((1 << bits) - 1)
+    for i in range(per):
+        out[:, i::per] = ((words[:, : K // per] >> np.uint32(bits * i)) & mask).astype(np.uint8)
+    return out
+
+
+def pack_int4(q):
+    """int4 codes [N,K] (0..15) -> uint32 [N,K/8], LSB-first nibbles."""
+    return _pack_fields(q, 4)
+
+
+def unpack_int4(words, K):
+    """uint32 [N,K/8] -> int4 codes uint8 [N,K]."""
+    return _unpack_fields(words, K, 4)
+
+
+def pack_int4_meta(scale16, zero16):
+    """fp16 scale and fp16 zero [N,K/128] -> uint32 half2 {scale lo, zero hi}."""
+    s = np.asarray(scale16, dtype=np.float16).view(np.uint16).astype(np.uint32)
+    z = np.asarray(zero16, dtype=np.float16).view(np.uint16).astype(np.uint32)
+    return s + z * np.uint32(65536)
+
+
+def unpack_int4_meta(meta):
+    """uint32 half2 [N,K/128] -> (scale fp16, zero fp16)."""
+    meta = np.asarray(meta, dtype=np.uint32)
+    s = (meta & np.uint32(0xFFFF)).astype(np.uint16).view(np.float16)
+    z = (meta >> np.uint32(16)).astype(np.uint16).view(np.float16)
+    return s, z
+
+
+def pack_tern(codes):
+    """ternary codes [N,K] (0..2) -> uint32 [N,K/16], LSB-first 2-bit fields."""
+    return _pack_fields(codes, 2)
+
+
+def unpack_tern(words, K):
+    return _unpack_fields(words, K, 2)
+
+
+def pack_bits(bits):
+    """sign bits [N,K] (0/1) -> uint32 [N,K/32], bit i of word j = element 32j+i."""
+    return _pack_fields(bits, 1)
+
+
+def unpack_bits(words, K):
+    return _unpack_fields(words, K, 1)
