@@ -1,0 +1,344 @@
+"""Benchmark of the low-bit GEMV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one decode-equivalent weight sweep: every linear layer a Qwen2.5
+model reads per token, y_i = dequant(W_i) . x_i for all i, as ONE grouped
+kernel launch.  Default workload: the Qwen2.5-0.5B sweep (169 GEMVs) in the
+int4-g128 coding.  The timed region is exactly K steps between two stream
+synchronisations; packed weights are resident in HBM and rotated over enough
+distinct copies (>= 1 GiB in total) that no step is served from the 256 MB
+Infinity Cache.  One JSON line goes to stdout.
+
+value = algorithmic bytes per step (packed codes + fp16 metadata + x + y, each
+once) / measured time per step, in TB/s.  The roofline object reports the
+same kernel against the 8 TB/s HBM peak; cpu_baseline times the numpy oracle
+on a bounded sample of the same workload on the host cores.
+
+Other workloads (for measurement; each prints its own line): single-896,
+0.5b-k5, 0.5b-tern, bin, 7b-int4, 7b-prefill, probe.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "int4-g128 GEMV achieved HBM TB/s (% of peak) + decode-equiv tok/s, batch 1"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores
+ROTATE_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- workloads --
+
+def _pack(tkq, fmt, Wd):
+    if fmt == "int4":
+        return tkq.pack_int4_g128(Wd)
+    if fmt == "k5":
+        return tkq.pack_k5(Wd)
+    if fmt == "tern":
+        return tkq.pack_tern_g128(Wd)
+    return tkq.pack_bin(Wd), None
+
+
+def build_sweep(torch, tkq, inputs, model, fmt):
+    """Pack every matrix of the model's sweep; returns (items, shapes)."""
+    shapes = inputs.sweep_shapes(model)
+    items = []
+    t0 = time.time()
+    for i, (_, N, K) in enumerate(shapes):
+        if model == "qwen2.5-7b":
+            Wd = inputs.device_normal_matrix(torch, 5000 + i, N, K)
+            x = inputs.sweep_x(model, i, K)
+        else:
+            W, x = inputs.sweep_matrix(model, i, N, K)
+            Wd = torch.from_numpy(W).cuda()
+        codes, meta = _pack(tkq, fmt, Wd)
+        del Wd
+        y = torch.empty(N, dtype=torch.float16, device="cuda")
+        items.append(dict(codes=codes, meta=meta, x=torch.from_numpy(x).cuda(), y=y, N=N, K=K))
+    torch.cuda.synchronize()
+    log("packed %s %s sweep: %d matrices in %.1f s" % (model, fmt, len(items), time.time() - t0))
+    return items, shapes
+
+
+def rotated_batches(torch, tkq, fmt, items, footprint):
+    """Distinct copies of the packed weights (>= 1 GiB total), one batch each."""
+    copies = max(1, math.ceil(ROTATE_BYTES / footprint))
+    batches = [tkq.GemvBatch(fmt, items)]
+    for _ in range(copies - 1):
+        clone = [dict(it, codes=it["codes"].clone(),
+                      meta=None if it["meta"] is None else it["meta"].clone()) for it in items]
+        batches.append(tkq.GemvBatch(fmt, clone))
+    torch.cuda.synchronize()
+    return batches
+
+
+def time_steps(torch, run_step, steps, warmup):
+    """Warm up, then time exactly `steps` steps between synchronisations with
+    HIP events recorded on the stream the kernels are launched on."""
+    for s in range(warmup):
+        run_step(s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(steps):
+        run_step(s)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per step
+
+
+# ------------------------------------------------------------- cpu baseline --
+
+def cpu_baseline_gemv(inputs, model, fmt, budget_s=12.0):
+    """Oracle (numpy, fp64) quantize-free path timed on the host: dequantize the
+    stored codes and run the fp64 matvec, on matrices of the sweep in order
+    until the time budget is spent.  Rate = algorithmic bytes / time."""
+    import numpy as np
+
+    from oracle import accounting, pack, quant, ref
+
+    shapes = inputs.sweep_shapes(model)
+    done_bytes, spent, done = 0, 0.0, []
+    for i, (name, N, K) in enumerate(shapes):
+        if spent > budget_s:
+            break
+        if model == "qwen2.5-7b":
+            W = inputs.normal_matrix((5000, i), N, K)
+            x = inputs.sweep_x(model, i, K)
+        else:
+            W, x = inputs.sweep_matrix(model, i, N, K)
+        if N > 32768:            # bounded sample of the head: its first 32768 rows
+            W, N = W[:32768], 32768
+        if fmt == "int4":
+            q, s, z = quant.quantize_int4_g128(W)
+            codes, meta = pack.pack_int4(q), pack.pack_int4_meta(s, z)
+            t0 = time.perf_counter()
+            y = ref.gemv(ref.dequant_int4(codes, meta, K), x)
+        elif fmt == "k5":
+            c, s = quant.quantize_k5(W)
+            t0 = time.perf_counter()
+            y = ref.gemv(ref.dequant_k5(c, s), x)
+        elif fmt == "tern":
+            c, s = quant.quantize_tern_g128(W)
+            codes = pack.pack_tern(c)
+            t0 = time.perf_counter()
+            y = ref.gemv(ref.dequant_tern(codes, s, K), x)
+        dt = time.perf_counter() - t0
+        assert np.all(np.isfinite(y))
+        spent += dt
+        done_bytes += accounting.gemv_bytes(fmt, N, K)
+        done.append(name if N == shapes[i][1] else "%s[:%d]" % (name, N))
+    return done_bytes / spent, spent, done
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        return 1
+
+
+# ------------------------------------------------------------------- runners --
+
+def run_sweep(args, torch, tkq, inputs, model, fmt):
+    from gemm_tkq_gemv_amd import inputs as _inp  # noqa: F401
+    items, shapes = build_sweep(torch, tkq, inputs, model, fmt)
+    fmt_bytes = _fmt_bytes(fmt)
+    step_bytes = sum(fmt_bytes(n, k) for _, n, k in shapes)
+    footprint = sum(it["codes"].numel() * it["codes"].element_size()
+                    + (0 if it["meta"] is None else it["meta"].numel() * it["meta"].element_size())
+                    for it in items)
+    batches = rotated_batches(torch, tkq, fmt, items, footprint)
+    ms = time_steps(torch, lambda s: batches[s % len(batches)].run(), args.steps, args.warmup)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    ceiling_tok_s = HBM_PEAK_GBS * 1e9 / step_bytes
+    out = {
+        "metric": METRIC if fmt == "int4" else "%s GEMV achieved HBM TB/s + decode-equiv tok/s, batch 1" % fmt,
+        "value": round(gbs / 1000.0, 4), "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic: seeded N(0,0.02) weights at the model's shapes, N(0,1) fp16 x",
+        "config": {"workload": "%s decode weight sweep, %s, %d GEMVs in one launch, batch 1"
+                               % (model, _fmt_name(fmt), len(shapes)),
+                   "bytes_per_step": step_bytes, "copies_rotated": len(batches),
+                   "weights": _fmt_name(fmt), "x": "fp16", "accumulate": "fp32", "y": "fp16"},
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "tok_s": round(1000.0 / ms, 1), "ceiling_tok_s": round(ceiling_tok_s, 1),
+        "frac_of_ceiling": round((1000.0 / ms) / ceiling_tok_s, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": args.traffic},
+        "kernel": "gemv_kernel<%d>" % tkq.FORMATS[fmt],
+    }
+    del items, batches
+    return out
+
+
+def _fmt_name(fmt):
+    return {"int4": "int4-g128", "k5": "K5-g128", "tern": "ternary-g128 (2-bit)", "bin": "binary"}[fmt]
+
+
+def _fmt_bytes(fmt):
+    # codes + metadata + x + y per GEMV (the same accounting as the oracle's)
+    return {
+        "int4": lambda n, k: n * k // 2 + n * (k // 128) * 4 + 2 * k + 2 * n,
+        "k5": lambda n, k: n * k + n * (k // 128) * 2 + 2 * k + 2 * n,
+        "tern": lambda n, k: n * k // 4 + n * (k // 128) * 2 + 2 * k + 2 * n,
+        "bin": lambda n, k: n * k // 8 + k // 8 + 4 * n,
+    }[fmt]
+
+
+def run_binary(args, torch, tkq, inputs):
+    items = []
+    for N, K in inputs.BINARY_SHAPES:
+        W, x = inputs.binary_case(N, K)
+        bits = tkq.pack_bin(torch.from_numpy(W).cuda())
+        xb = tkq.pack_bin(torch.from_numpy(x).cuda())
+        items.append(dict(codes=bits, meta=None, x=xb, y=torch.empty(N, dtype=torch.int32, device="cuda"),
+                          N=N, K=K))
+    step_bytes = sum(_fmt_bytes("bin")(n, k) for n, k in inputs.BINARY_SHAPES)
+    footprint = sum(it["codes"].numel() * 4 for it in items)
+    batches = rotated_batches(torch, tkq, "bin", items, footprint)
+    ms = time_steps(torch, lambda s: batches[s % len(batches)].run(), args.steps, args.warmup)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    return {"metric": "binary XOR-popcount GEMV achieved HBM TB/s", "value": round(gbs / 1000, 4),
+            "unit": "TB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "u32", "data": "synthetic Bernoulli(0.5) signs",
+            "config": {"workload": "binary sign GEMVs N in {896,4864,151936} x K in {896,4864}, one launch",
+                       "bytes_per_step": step_bytes, "copies_rotated": len(batches)},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+
+
+def run_single(args, torch, tkq, inputs):
+    W, x = inputs.single_gemv_896()
+    codes, meta = tkq.pack_int4_g128(torch.from_numpy(W).cuda())
+    y = torch.empty(896, dtype=torch.float16, device="cuda")
+    batch = tkq.GemvBatch("int4", [dict(codes=codes, meta=meta, x=torch.from_numpy(x).cuda(), y=y,
+                                        N=896, K=896)])
+    ms = time_steps(torch, lambda s: batch.run(), args.steps, args.warmup)
+    b = _fmt_bytes("int4")(896, 896)
+    return {"metric": "single int4-g128 896x896 GEMV latency", "value": round(ms * 1000, 3),
+            "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": False, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f16", "data": "synthetic, seed 0",
+            "config": {"workload": "single int4-g128 GEMV 896x896 (cache-resident, launch-bound)",
+                       "bytes_per_step": b}}
+
+
+def run_prefill(args, torch, tkq, inputs):
+    gemms = []
+    for name, N, K in inputs.prefill_shapes():
+        W = inputs.prefill_W(name)
+        codes, meta = tkq.pack_int4_g128(torch.from_numpy(W).cuda())
+        X = torch.from_numpy(inputs.prefill_X(K)).cuda()
+        Y = torch.empty((inputs.PREFILL_M, N), dtype=torch.float16, device="cuda")
+        gemms.append((codes, meta, X, Y, N))
+
+    def step(_s):
+        for codes, meta, X, Y, N in gemms:
+            tkq.gemm_prefill(codes, meta, X, N, Y)
+
+    ms = time_steps(torch, step, args.steps, args.warmup)
+    flops = sum(2 * inputs.PREFILL_M * n * k for _, n, k in inputs.prefill_shapes())
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"metric": "int4-g128 prefill GEMM (M=512) TFLOP/s", "value": round(tf, 2),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f16",
+            "data": "synthetic N(0,0.02) weights, N(0,1) fp16 activations",
+            "config": {"workload": "qwen2.5-7b MLP gate+up+down prefill GEMMs, M=512, int4-g128 weights",
+                       "flops_per_step": flops},
+            "tok_s": round(inputs.PREFILL_M * 1000.0 / ms, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": None}}
+
+
+def run_probe(args, torch, tkq, inputs):
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    buf.fill_(1)
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    ms = time_steps(torch, lambda s: tkq.read_probe(buf, out), args.steps, args.warmup)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"metric": "read-only stream probe HBM GB/s", "value": round(gbs, 1), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
+            "data": "4 GiB buffer", "config": {"workload": "16-byte non-temporal read of 4 GiB"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="0.5b-int4",
+                    choices=["0.5b-int4", "0.5b-k5", "0.5b-tern", "bin", "single-896", "7b-int4",
+                             "7b-prefill", "probe"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--traffic", type=float, default=None,
+                    help="HBM bytes per launch from rocprofv3 FETCH_SIZE+WRITE_SIZE (scaled)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the batch-1 GEMV needs no collectives, and "
+              "this build runs on a single MI355X.  Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gemm_tkq_gemv_amd import inputs, tkq
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    tkq.lib()
+
+    w = args.workload
+    if w in ("0.5b-int4", "0.5b-k5", "0.5b-tern", "7b-int4"):
+        model = "qwen2.5-7b" if w.startswith("7b") else "qwen2.5-0.5b"
+        fmt = w.split("-")[1]
+        out = run_sweep(args, torch, tkq, inputs, model, fmt)
+        torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            rate, spent, done = cpu_baseline_gemv(inputs, model, fmt, args.cpu_budget)
+            cores = len(os.sched_getaffinity(0))
+            out["cpu_baseline"] = {
+                "value": round(rate / 1e12, 8), "unit": "TB/s", "cores": blas_threads(),
+                "host_cores_available": cores, "kind": "oracle",
+                "sample": "numpy oracle dequantize + fp64 matvec over the first %d matrices of the "
+                          "sweep in order (%s), %.1f s of CPU work; quantization not timed"
+                          % (len(done), ", ".join(done[:3] + (["..."] if len(done) > 3 else [])
+                                                 + done[-1:]), spent)}
+    elif w == "bin":
+        out = run_binary(args, torch, tkq, inputs)
+    elif w == "single-896":
+        out = run_single(args, torch, tkq, inputs)
+    elif w == "7b-prefill":
+        out = run_prefill(args, torch, tkq, inputs)
+    else:
+        out = run_probe(args, torch, tkq, inputs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,399 @@
+// Grouped low-bit GEMV for gfx950: y_i = dequant(W_i) . x_i for many
+// independent matrices in one launch.
+//
+// Decode at batch 1 reads every weight once for one multiply-add, so the
+// product is bound by HBM bandwidth (Whetstone README, "The one fact that
+// shapes everything": tok/s ceiling = bandwidth / bytes per token).  The
+// kernel is therefore organised around the byte stream:
+//
+//  * Work unit.  One workgroup (4 wave64s) owns a tile of consecutive rows of
+//    one matrix; the grid is the concatenation of every matrix's tiles, and a
+//    workgroup finds its matrix by binary search over the descriptors'
+//    first-tile indices (scalar loads).
+//  * Lanes.  L = 2^lg lanes share a row; lane `sub` of the group reads the
+//    row's 16-byte chunks sub, sub+L, ... (J "passes"), so every load
+//    instruction of the wave reads whole rows front to back: contiguous,
+//    coalesced, non-temporal 128-bit buffer loads.  With S k-slices, S waves
+//    split one row's chunks and combine through LDS.
+//  * x stays in registers.  Each lane owns fixed chunk positions, so it loads
+//    its slice of x once per tile and keeps it, pre-permuted to the order in
+//    which codes are unpacked.
+//  * Unpack with fp16 "magic numbers": OR-ing a code field into the mantissa
+//    of fp16 1024.0 gives 1024 + m*code exactly (m = 1, 4, 16, 64 or 256 by
+//    the field's bit position), two weights per 32-bit register, ready for
+//    v_dot2_f32_f16 (fp16 products, fp32 accumulation).  The constant 1024*x
+//    part is removed per chunk by subtracting the same dot-product chain
+//    evaluated on zero-point codes, so groups whose codes all equal the zero
+//    point contribute exactly 0.
+//  * Per-group fp16 scale (and int4 zero) are applied once per chunk in fp32;
+//    the row sum is a DPP butterfly inside the lane group; fp16 y is rounded
+//    to nearest even.  The binary coding XORs code and x words and counts
+//    bits (v_bcnt_u32_b32): y = K - 2 * popcount (Whetstone README, "Measured
+//    hardware facts").
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace tkq {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kMaxTileRows = kGemvMaxTileRows;
+constexpr uint32_t kMagic = 0x64006400u;  // fp16 pair (1024.0, 1024.0)
+
+// ---------------------------------------------------------------- codecs --
+// Each codec states, for one 16-byte chunk of codes:
+//   WPC  weights per chunk
+//   XR   u32 registers of prepared x (pairs of fp16)
+//   XB   bytes of x the chunk consumes
+//   CPG  chunks per 128-weight group;  MB metadata bytes per group
+//   prep(raw, xr)      permute natural x pairs into the unpack order
+//   dot(codes, xr)     sum over the chunk of (1024 + m*code) * x, as fp32
+//   kZero              a code word whose every field is the zero-point code
+
+template <int FMT>
+struct Codec;
+
+// int4: word w holds nibbles q0..q7 of elements 8i..8i+7.  (w & 0x000F000F)
+// pairs (q0, q4); (w & 0x00F000F0) pairs (16 q1, 16 q5); the same on w >> 8
+// gives (q2, q6) and (16 q3, 16 q7).  Two accumulators keep the x16 fields
+// apart and are combined as lo + hi/16.
+template <>
+struct Codec<kFmtInt4> {
+  static constexpr int WPC = 32, XR = 16, XB = 64, CPG = 4, MB = 4;
+  static constexpr uint32_t kZero = 0u;
+  __device__ static void prep(const uint32_t* raw, uint32_t* xr) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a = raw[4 * w], b = raw[4 * w + 1], c = raw[4 * w + 2], d = raw[4 * w + 3];
+      xr[4 * w + 0] = __builtin_amdgcn_perm(c, a, 0x05040100u);  // (x0, x4)
+      xr[4 * w + 1] = __builtin_amdgcn_perm(c, a, 0x07060302u);  // (x1, x5)
+      xr[4 * w + 2] = __builtin_amdgcn_perm(d, b, 0x05040100u);  // (x2, x6)
+      xr[4 * w + 3] = __builtin_amdgcn_perm(d, b, 0x07060302u);  // (x3, x7)
+    }
+  }
+  __device__ static float dot(u32x4 q, const uint32_t* xr) {
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t v = q[w], t = v >> 8;
+      lo = __builtin_amdgcn_fdot2(as_h2((v & 0x000F000Fu) | kMagic), as_h2(xr[4 * w + 0]), lo, false);
+      hi = __builtin_amdgcn_fdot2(as_h2((v & 0x00F000F0u) | kMagic), as_h2(xr[4 * w + 1]), hi, false);
+      lo = __builtin_amdgcn_fdot2(as_h2((t & 0x000F000Fu) | kMagic), as_h2(xr[4 * w + 2]), lo, false);
+      hi = __builtin_amdgcn_fdot2(as_h2((t & 0x00F000F0u) | kMagic), as_h2(xr[4 * w + 3]), hi, false);
+    }
+    return fmaf(hi, 0.0625f, lo);
+  }
+};
+
+// K5: one byte per weight.  v_perm builds (1024 + c0, 1024 + c2) and
+// (1024 + c1, 1024 + c3) from a code word and the byte 0x64.
+template <>
+struct Codec<kFmtK5> {
+  static constexpr int WPC = 16, XR = 8, XB = 32, CPG = 8, MB = 2;
+  static constexpr uint32_t kZero = 0x79797979u;  // 121 = value 0
+  __device__ static void prep(const uint32_t* raw, uint32_t* xr) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a = raw[2 * w], b = raw[2 * w + 1];  // (x0,x1), (x2,x3)
+      xr[2 * w + 0] = __builtin_amdgcn_perm(b, a, 0x05040100u);  // (x0, x2)
+      xr[2 * w + 1] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // (x1, x3)
+    }
+  }
+  __device__ static float dot(u32x4 q, const uint32_t* xr) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t v = q[w];
+      acc = __builtin_amdgcn_fdot2(as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04020400u)),
+                                   as_h2(xr[2 * w + 0]), acc, false);
+      acc = __builtin_amdgcn_fdot2(as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04030401u)),
+                                   as_h2(xr[2 * w + 1]), acc, false);
+    }
+    return acc;
+  }
+};
+
+// Ternary: 2-bit fields, element 16i+s at bits 2s.  Masks 3 << 2s for
+// s = 0..4 (both halves) give (1024 + 4^s c_s, 1024 + 4^s c_{s+8}); the word
+// shifted right by 10 gives s = 5, 6, 7 with multipliers 1, 4, 16.
+template <>
+struct Codec<kFmtTern> {
+  static constexpr int WPC = 64, XR = 32, XB = 128, CPG = 2, MB = 2;
+  static constexpr uint32_t kZero = 0x55555555u;  // code 1 = value 0
+  __device__ static void prep(const uint32_t* raw, uint32_t* xr) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      // raw[8w + p] = (x_{2p}, x_{2p+1}) of word w's 16 elements
+      const uint32_t* r = raw + 8 * w;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const uint32_t lo = r[s >> 1], hi = r[4 + (s >> 1)];
+        xr[8 * w + s] = (s & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
+                                : __builtin_amdgcn_perm(hi, lo, 0x05040100u);  // (x_s, x_{s+8})
+      }
+    }
+  }
+  __device__ static float dot(u32x4 q, const uint32_t* xr) {
+    float a1 = 0.0f, a4 = 0.0f, a16 = 0.0f, a64 = 0.0f, a256 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t v = q[w], t = v >> 10;
+      const uint32_t* x = xr + 8 * w;
+      a1 = __builtin_amdgcn_fdot2(as_h2((v & 0x00030003u) | kMagic), as_h2(x[0]), a1, false);
+      a4 = __builtin_amdgcn_fdot2(as_h2((v & 0x000C000Cu) | kMagic), as_h2(x[1]), a4, false);
+      a16 = __builtin_amdgcn_fdot2(as_h2((v & 0x00300030u) | kMagic), as_h2(x[2]), a16, false);
+      a64 = __builtin_amdgcn_fdot2(as_h2((v & 0x00C000C0u) | kMagic), as_h2(x[3]), a64, false);
+      a256 = __builtin_amdgcn_fdot2(as_h2((v & 0x03000300u) | kMagic), as_h2(x[4]), a256, false);
+      a1 = __builtin_amdgcn_fdot2(as_h2((t & 0x00030003u) | kMagic), as_h2(x[5]), a1, false);
+      a4 = __builtin_amdgcn_fdot2(as_h2((t & 0x000C000Cu) | kMagic), as_h2(x[6]), a4, false);
+      a16 = __builtin_amdgcn_fdot2(as_h2((t & 0x00300030u) | kMagic), as_h2(x[7]), a16, false);
+    }
+    return fmaf(a256, 0.00390625f, fmaf(a64, 0.015625f, fmaf(a16, 0.0625f, fmaf(a4, 0.25f, a1))));
+  }
+};
+
+// Binary: 128 sign bits per chunk; x is kept as packed words.
+template <>
+struct Codec<kFmtBin> {
+  static constexpr int WPC = 128, XR = 4, XB = 16, CPG = 1, MB = 0;
+  __device__ static void prep(const uint32_t* raw, uint32_t* xr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr[i] = raw[i];
+  }
+  __device__ static int dot(u32x4 q, const uint32_t* xr) {
+    int acc = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc += __builtin_popcount(q[w] ^ xr[w]);
+    return acc;
+  }
+};
+
+template <int FMT>
+constexpr int max_passes() {
+  return FMT == kFmtBin ? 8 : (FMT == kFmtTern ? 3 : 4);
+}
+
+// ------------------------------------------------------------ tile runner --
+struct Tile {
+  __amdgpu_buffer_rsrc_t codes, meta, x, y;
+  uint32_t row_bytes;       // bytes of codes per row
+  uint32_t meta_row_bytes;  // bytes of metadata per row
+  int lg, sub, prow, P;     // lanes-per-row log2, lane in group, row in step, rows per step
+  int S, slice;             // k-slices, this wave's slice
+  int rbase, steps;         // first tile row of this wave, row steps
+  int Cs, C, K;             // chunks per slice, chunks per row, columns
+};
+
+constexpr uint32_t kFar = 0x80000000u;  // offset past any buffer, no wrap
+
+template <int FMT, int J, int U>
+__device__ __forceinline__ void run_tile(const Tile& t, uint32_t* part) {
+  using Cd = Codec<FMT>;
+  constexpr bool kBin = FMT == kFmtBin;
+  using Acc = typename std::conditional<kBin, int, float>::type;
+
+  // Fixed chunk positions of this lane, its slice of x, and the constants.
+  uint32_t cof[J], mof[J];
+  uint32_t xr[J][Cd::XR];
+  float bias[J], xsum[J];
+  const int L = 1 << t.lg;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int local = t.sub + L * j;
+    const int c = t.slice * t.Cs + local;
+    const bool ok = local < t.Cs && c < t.C;
+    cof[j] = ok ? (uint32_t)c * 16u : kFar;
+    mof[j] = ok ? (uint32_t)(c / Cd::CPG) * Cd::MB : kFar;
+    uint32_t raw[Cd::XR];
+#pragma unroll
+    for (int i = 0; i < Cd::XR / 4; ++i) {
+      const u32x4 v = load16(t.x, ok ? (uint32_t)c * Cd::XB + 16u * i : kFar);
+      raw[4 * i + 0] = v[0];
+      raw[4 * i + 1] = v[1];
+      raw[4 * i + 2] = v[2];
+      raw[4 * i + 3] = v[3];
+    }
+    Cd::prep(raw, xr[j]);
+    if constexpr (!kBin) {
+      const u32x4 zc = {Cd::kZero, Cd::kZero, Cd::kZero, Cd::kZero};
+      bias[j] = Cd::dot(zc, xr[j]);
+      float sx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < Cd::XR; ++i) sx = __builtin_amdgcn_fdot2(as_h2(xr[j][i]), as_h2(0x3C003C00u), sx, false);
+      xsum[j] = sx;
+    }
+  }
+
+  auto issue = [&](int st, u32x4 (&cw)[U][J], uint32_t (&mw)[U][J]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t r = (uint32_t)(t.rbase + (st + u) * t.P + t.prow);
+      const uint32_t rb = r * t.row_bytes, mb = r * t.meta_row_bytes;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        cw[u][j] = load16_nt(t.codes, rb + cof[j]);
+        if constexpr (Cd::MB == 4) mw[u][j] = load4(t.meta, mb + mof[j]);
+        else if constexpr (Cd::MB == 2) mw[u][j] = load2(t.meta, mb + mof[j]);
+        else mw[u][j] = 0;
+      }
+    }
+  };
+
+  u32x4 cw[U][J];
+  uint32_t mw[U][J];
+  issue(0, cw, mw);
+  for (int st = 0; st < t.steps; st += U) {
+    u32x4 nc[U][J];
+    uint32_t nm[U][J];
+    if (st + U < t.steps) issue(st + U, nc, nm);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      Acc res = 0;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        if constexpr (kBin) {
+          res += Cd::dot(cw[u][j], xr[j]);
+        } else if constexpr (FMT == kFmtInt4) {
+          const float d = Cd::dot(cw[u][j], xr[j]) - bias[j];
+          res = fmaf(half_lo(mw[u][j]), fmaf(-half_hi(mw[u][j]), xsum[j], d), res);
+        } else {
+          const float d = Cd::dot(cw[u][j], xr[j]) - bias[j];
+          res = fmaf(half_lo(mw[u][j]), d, res);
+        }
+      }
+      const Acc v = group_sum(res, t.lg);
+      const uint32_t r = (uint32_t)(t.rbase + (st + u) * t.P + t.prow);
+      if (t.sub == L - 1) {
+        if (t.S == 1) {
+          if constexpr (kBin) store4(t.y, r * 4u, (uint32_t)(t.K - 2 * v));
+          else store2(t.y, r * 2u, half_bits(v));
+        } else if (r < (uint32_t)kMaxTileRows) {
+          if constexpr (kBin) part[t.slice * kMaxTileRows + r] = (uint32_t)v;
+          else part[t.slice * kMaxTileRows + r] = u32(v);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        cw[u][j] = nc[u][j];
+        mw[u][j] = nm[u][j];
+      }
+  }
+}
+
+template <int FMT, int J>
+__device__ __forceinline__ void run_passes(const Tile& t, uint32_t* part) {
+  if constexpr (J <= max_passes<FMT>()) {
+    constexpr int U = J == 1 ? 4 : (J == 2 ? 2 : 1);
+    run_tile<FMT, J, U>(t, part);
+  }
+}
+
+// ------------------------------------------------------------------ kernel --
+template <int FMT>
+__global__ __launch_bounds__(256) void gemv_kernel(const tkq_gemv_desc* __restrict__ descs, int count) {
+  using Cd = Codec<FMT>;
+  constexpr bool kBin = FMT == kFmtBin;
+  __shared__ uint32_t part[kWaves * kMaxTileRows];
+
+  // The matrix this workgroup works on: last descriptor with work0 <= tile.
+  const int tile = blockIdx.x;
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (descs[mid].work0 <= tile) lo = mid;
+    else hi = mid - 1;
+  }
+  const tkq_gemv_desc* d = descs + lo;
+  const int N = d->N, K = d->K, rpt = d->rows_per_tile;
+  const GemvShape sh = unpack_shape(d->shape);
+
+  Tile t;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  t.lg = sh.lanes_log2;
+  t.P = 64 >> t.lg;
+  t.sub = lane & ((1 << t.lg) - 1);
+  t.prow = lane >> t.lg;
+  t.S = sh.kslices;
+  t.slice = wave & (t.S - 1);
+  const int rg = wave / t.S, rows_per_rg = rpt / (kWaves / t.S);
+  t.rbase = rg * rows_per_rg;
+  t.steps = rows_per_rg / t.P;
+  t.K = K;
+  t.C = K / Cd::WPC;
+  t.Cs = (t.C + t.S - 1) / t.S;
+  t.row_bytes = (uint32_t)t.C * 16u;
+  t.meta_row_bytes = (uint32_t)(K / 128) * Cd::MB;
+  const int row0 = (tile - d->work0) * rpt;
+  const int nrows = min(rpt, N - row0);
+  const char* codes = (const char*)d->codes + (size_t)row0 * t.row_bytes;
+  t.codes = make_rsrc(codes, (uint32_t)nrows * t.row_bytes);
+  if constexpr (Cd::MB > 0) {
+    const char* meta = (const char*)d->meta + (size_t)row0 * t.meta_row_bytes;
+    t.meta = make_rsrc(meta, (uint32_t)nrows * t.meta_row_bytes);
+  } else {
+    t.meta = make_rsrc(d->codes, 0u);
+  }
+  t.x = make_rsrc(d->x, kBin ? (uint32_t)(K / 8) : (uint32_t)K * 2u);
+  const uint32_t ybytes = kBin ? 4u : 2u;
+  t.y = make_rsrc((char*)d->y + (size_t)row0 * ybytes, (uint32_t)nrows * ybytes);
+
+  switch (sh.passes) {
+    case 1: run_passes<FMT, 1>(t, part); break;
+    case 2: run_passes<FMT, 2>(t, part); break;
+    case 3: run_passes<FMT, 3>(t, part); break;
+    case 4: run_passes<FMT, 4>(t, part); break;
+    case 5: run_passes<FMT, 5>(t, part); break;
+    case 6: run_passes<FMT, 6>(t, part); break;
+    case 7: run_passes<FMT, 7>(t, part); break;
+    case 8: run_passes<FMT, 8>(t, part); break;
+    default: break;
+  }
+
+  if (t.S > 1) {
+    __syncthreads();
+    for (int r = threadIdx.x; r < nrows && r < kMaxTileRows; r += 64 * kWaves) {
+      if constexpr (kBin) {
+        int v = 0;
+        for (int s = 0; s < t.S; ++s) v += (int)part[s * kMaxTileRows + r];
+        store4(t.y, (uint32_t)r * 4u, (uint32_t)(K - 2 * v));
+      } else {
+        float v = 0.0f;
+        for (int s = 0; s < t.S; ++s) v += f32(part[s * kMaxTileRows + r]);
+        store2(t.y, (uint32_t)r * 2u, half_bits(v));
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int gemv_max_passes(int fmt) {
+  switch (fmt) {
+    case kFmtInt4: return max_passes<kFmtInt4>();
+    case kFmtK5: return max_passes<kFmtK5>();
+    case kFmtTern: return max_passes<kFmtTern>();
+    case kFmtBin: return max_passes<kFmtBin>();
+  }
+  return 0;
+}
+
+hipError_t launch_gemv(int fmt, const tkq_gemv_desc* dev_descs, int count, int64_t tiles,
+                       hipStream_t stream) {
+  const dim3 grid((uint32_t)tiles), block(64 * kWaves);
+  switch (fmt) {
+    case kFmtInt4: hipLaunchKernelGGL(gemv_kernel<kFmtInt4>, grid, block, 0, stream, dev_descs, count); break;
+    case kFmtK5: hipLaunchKernelGGL(gemv_kernel<kFmtK5>, grid, block, 0, stream, dev_descs, count); break;
+    case kFmtTern: hipLaunchKernelGGL(gemv_kernel<kFmtTern>, grid, block, 0, stream, dev_descs, count); break;
+    case kFmtBin: hipLaunchKernelGGL(gemv_kernel<kFmtBin>, grid, block, 0, stream, dev_descs, count); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tkq

@@ -1,0 +1,54 @@
+// Internal launch interface between the C-ABI layer (tkq_api.hip) and the
+// kernel translation units.  Every launcher assumes arguments that the C-ABI
+// layer has already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tkq.h"
+
+namespace tkq {
+
+constexpr int kFmtInt4 = TKQ_FMT_INT4_G128;
+constexpr int kFmtK5 = TKQ_FMT_K5_G128;
+constexpr int kFmtTern = TKQ_FMT_TERN_G128;
+constexpr int kFmtBin = TKQ_FMT_BIN;
+
+// Work decomposition of one GEMV, packed into tkq_gemv_desc::shape.
+struct GemvShape {
+  int lanes_log2;  // lanes cooperating on one row (1..64)
+  int passes;      // 16-byte chunks each lane reads per row
+  int kslices;     // waves that split one row's K range (1, 2 or 4)
+};
+__host__ __device__ inline int pack_shape(GemvShape s) { return s.lanes_log2 | (s.passes << 4) | (s.kslices << 12); }
+__host__ __device__ inline GemvShape unpack_shape(int v) { return {v & 15, (v >> 4) & 255, (v >> 12) & 15}; }
+
+// Weights carried by one 16-byte chunk of codes, per coding.
+inline int weights_per_chunk(int fmt) {
+  switch (fmt) {
+    case kFmtInt4: return 32;
+    case kFmtK5: return 16;
+    case kFmtTern: return 64;
+    case kFmtBin: return 128;
+  }
+  return 0;
+}
+
+// Largest row tile of one GEMV workgroup (bounds the k-slice LDS buffer).
+constexpr int kGemvMaxTileRows = 1024;
+
+// Largest `passes` value each kernel variant supports (x stays in registers).
+int gemv_max_passes(int fmt);
+hipError_t launch_gemv(int fmt, const tkq_gemv_desc* dev_descs, int count, int64_t tiles,
+                       hipStream_t stream);
+
+hipError_t launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* codes, void* meta,
+                       hipStream_t stream);
+
+hipError_t launch_prefill(int64_t M, int64_t N, int64_t K, const uint32_t* codes,
+                          const uint32_t* meta, const uint16_t* X, uint16_t* Y, hipStream_t stream);
+
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream);
+
+}  // namespace tkq

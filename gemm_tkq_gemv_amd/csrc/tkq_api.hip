@@ -1,0 +1,203 @@
+// C-ABI entry points of libtkq: host-side validation, the GEMV work planner,
+// and the kernel launches.  Every check runs on the host before any HIP call;
+// on failure nothing is enqueued.
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+constexpr int32_t kPlanMagic = 0x746b7131;  // "tkq1"
+constexpr int64_t kMaxWeights = int64_t(1) << 39;
+// Bytes of codes one wave aims to stream per tile: large enough to amortise
+// the per-tile setup (descriptor search, x slice, constants), small enough
+// that the last workgroups of a launch finish close together.
+constexpr int64_t kTileTargetBytes = 12 * 1024;
+constexpr int kMaxTileRows = tkq::kGemvMaxTileRows;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return TKQ_OK;
+  g_last_hip_error = (int)e;
+  return TKQ_EHIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool known_fmt(int fmt) {
+  return fmt == TKQ_FMT_INT4_G128 || fmt == TKQ_FMT_K5_G128 || fmt == TKQ_FMT_TERN_G128 ||
+         fmt == TKQ_FMT_BIN;
+}
+
+// Largest K each GEMV variant handles with x resident in registers:
+// chunks per row <= 4 k-slices x 64 lanes x max passes.
+int64_t gemv_max_k(int fmt) {
+  return int64_t(4) * 64 * tkq::gemv_max_passes(fmt) * tkq::weights_per_chunk(fmt);
+}
+
+int check_matrix(const float* W, int64_t N, int64_t K, int64_t kunit) {
+  if (!W || N < 1 || K < 1) return TKQ_EINVAL;
+  if (K % kunit || K > TKQ_MAX_K || N > INT32_MAX || N * K > kMaxWeights) return TKQ_ESHAPE;
+  if (!aligned16(W)) return TKQ_EALIGN;
+  return TKQ_OK;
+}
+
+int pack_common(int fmt, const float* W, int64_t N, int64_t K, void* codes, void* meta,
+                bool need_meta, int64_t kunit, void* stream) {
+  int st = check_matrix(W, N, K, kunit);
+  if (st) return st;
+  if (!codes || (need_meta && !meta)) return TKQ_EINVAL;
+  if (!aligned16(codes) || (need_meta && !aligned16(meta))) return TKQ_EALIGN;
+  return hip_status(tkq::launch_pack(fmt, W, N, K, codes, meta, (hipStream_t)stream));
+}
+
+// Choose lanes-per-row, passes and k-slices for one GEMV: the decomposition
+// with the fewest idle lane-chunk slots (16-byte chunks per row over
+// k-slices x lanes x passes); ties go to fewer k-slices, then fewer passes.
+tkq::GemvShape choose_shape(int fmt, int K) {
+  const int C = K / tkq::weights_per_chunk(fmt);
+  const int jmax = tkq::gemv_max_passes(fmt);
+  tkq::GemvShape best = {6, 0, 0};
+  double best_util = -1.0;
+  for (int S : {1, 2, 4}) {
+    const int Cs = (C + S - 1) / S;
+    for (int lg = 6; lg >= 0; --lg) {
+      const int L = 1 << lg;
+      const int J = (Cs + L - 1) / L;
+      if (J > jmax) continue;
+      const double util = double(C) / double(S * L * J);
+      const bool better = util > best_util + 1e-12 ||
+                          (util > best_util - 1e-12 &&
+                           (S < best.kslices || (S == best.kslices && J < best.passes)));
+      if (better) {
+        best = {lg, J, S};
+        best_util = util;
+      }
+    }
+  }
+  return best;
+}
+
+int rows_per_tile(int fmt, int N, int K, tkq::GemvShape sh) {
+  const int C = K / tkq::weights_per_chunk(fmt);
+  const int Cs = (C + sh.kslices - 1) / sh.kslices;
+  const int P = 64 >> sh.lanes_log2;       // rows per wave step
+  const int RG = 4 / sh.kslices;           // row groups per workgroup
+  const int U = sh.passes == 1 ? 4 : (sh.passes == 2 ? 2 : 1);  // steps per iteration
+  const int64_t step_bytes = int64_t(P) * Cs * 16;
+  int64_t steps = (kTileTargetBytes + step_bytes - 1) / step_bytes;
+  const int64_t need = ((int64_t(N) + RG - 1) / RG + P - 1) / P;  // steps to cover N
+  if (steps > need) steps = need;
+  steps = ((steps + U - 1) / U) * U;
+  while (steps > U && int64_t(RG) * P * steps > kMaxTileRows) steps -= U;
+  return (int)(int64_t(RG) * P * steps);
+}
+
+}  // namespace
+
+extern "C" {
+
+int tkq_version(void) { return TKQ_VERSION; }
+
+const char* tkq_strerror(int status) {
+  switch (status) {
+    case TKQ_OK: return "success";
+    case TKQ_EINVAL: return "invalid argument (null pointer, non-positive size or count)";
+    case TKQ_ESHAPE: return "unsupported shape (K not a multiple of the format's unit, or too large)";
+    case TKQ_EALIGN: return "device pointer not 16-byte aligned";
+    case TKQ_EFORMAT: return "unknown or mixed weight format";
+    case TKQ_EHIP: return "HIP call failed (see tkq_last_hip_error)";
+    case TKQ_EPLAN: return "plan was not produced by tkq_gemv_prepare";
+  }
+  return "unknown status";
+}
+
+int tkq_last_hip_error(void) { return g_last_hip_error; }
+
+int tkq_pack_int4_g128(const float* W, int64_t N, int64_t K, uint32_t* codes, uint32_t* meta,
+                       void* stream) {
+  return pack_common(TKQ_FMT_INT4_G128, W, N, K, codes, meta, true, 128, stream);
+}
+
+int tkq_pack_k5(const float* W, int64_t N, int64_t K, uint8_t* codes, uint16_t* scale,
+                void* stream) {
+  return pack_common(TKQ_FMT_K5_G128, W, N, K, codes, scale, true, 128, stream);
+}
+
+int tkq_pack_tern_g128(const float* W, int64_t N, int64_t K, uint32_t* codes, uint16_t* scale,
+                       void* stream) {
+  return pack_common(TKQ_FMT_TERN_G128, W, N, K, codes, scale, true, 128, stream);
+}
+
+int tkq_pack_bin(const float* W, int64_t N, int64_t K, uint32_t* bits, void* stream) {
+  return pack_common(TKQ_FMT_BIN, W, N, K, bits, nullptr, false, 32, stream);
+}
+
+int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan) {
+  if (!descs || !plan || count < 1) return TKQ_EINVAL;
+  const int fmt = descs[0].fmt;
+  if (!known_fmt(fmt)) return TKQ_EFORMAT;
+  for (int32_t i = 0; i < count; ++i) {
+    const tkq_gemv_desc& d = descs[i];
+    if (d.fmt != fmt) return TKQ_EFORMAT;
+    if (d.N < 1 || d.K < 1 || !d.codes || !d.x || !d.y) return TKQ_EINVAL;
+    if (fmt != TKQ_FMT_BIN && !d.meta) return TKQ_EINVAL;
+    if (d.K % 128 || d.K > gemv_max_k(fmt) || int64_t(d.N) * d.K > kMaxWeights) return TKQ_ESHAPE;
+    if (!aligned16(d.codes) || !aligned16(d.x) || !aligned16(d.y) ||
+        (fmt != TKQ_FMT_BIN && !aligned16(d.meta)))
+      return TKQ_EALIGN;
+  }
+  int64_t work = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    tkq_gemv_desc& d = descs[i];
+    const tkq::GemvShape sh = choose_shape(fmt, d.K);
+    if (sh.passes < 1) return TKQ_ESHAPE;
+    const int rpt = rows_per_tile(fmt, d.N, d.K, sh);
+    const int64_t tiles = (int64_t(d.N) + rpt - 1) / rpt;
+    if (work + tiles > INT32_MAX) return TKQ_ESHAPE;
+    d.work0 = (int32_t)work;
+    d.tiles = (int32_t)tiles;
+    d.rows_per_tile = rpt;
+    d.shape = tkq::pack_shape(sh);
+    d.reserved = 0;
+    work += tiles;
+  }
+  plan->fmt = fmt;
+  plan->count = count;
+  plan->tiles = work;
+  plan->variant = fmt;
+  plan->magic = kPlanMagic;
+  plan->reserved = 0;
+  return TKQ_OK;
+}
+
+int tkq_gemv(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs, void* stream) {
+  if (!plan || !dev_descs) return TKQ_EINVAL;
+  if (plan->magic != kPlanMagic || !known_fmt(plan->fmt) || plan->count < 1 || plan->tiles < 1 ||
+      plan->tiles > INT32_MAX)
+    return TKQ_EPLAN;
+  if (!aligned16(dev_descs)) return TKQ_EALIGN;
+  return hip_status(tkq::launch_gemv(plan->fmt, dev_descs, plan->count, plan->tiles,
+                                     (hipStream_t)stream));
+}
+
+int tkq_gemm_prefill(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint32_t* codes,
+                     const uint32_t* meta, const uint16_t* X, uint16_t* Y, void* stream) {
+  if (fmt != TKQ_FMT_INT4_G128) return TKQ_EFORMAT;
+  if (!codes || !meta || !X || !Y || M < 1 || N < 1 || K < 1) return TKQ_EINVAL;
+  if (K % 128 || K > TKQ_MAX_K || M > INT32_MAX || N > INT32_MAX || N * K > kMaxWeights ||
+      M * K > kMaxWeights || M * N > kMaxWeights || (N + 127) / 128 > INT32_MAX ||
+      (M + 127) / 128 > 65535 || 128 * K * 2 > INT32_MAX)
+    return TKQ_ESHAPE;
+  if (!aligned16(codes) || !aligned16(meta) || !aligned16(X) || !aligned16(Y)) return TKQ_EALIGN;
+  return hip_status(tkq::launch_prefill(M, N, K, codes, meta, X, Y, (hipStream_t)stream));
+}
+
+int tkq_read_probe(const void* buf, int64_t bytes, uint32_t* out, void* stream) {
+  if (!buf || !out || bytes < 16) return TKQ_EINVAL;
+  if (bytes % 16) return TKQ_ESHAPE;
+  if (!aligned16(buf) || !aligned16(out)) return TKQ_EALIGN;
+  return hip_status(tkq::launch_read_probe(buf, bytes, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -14,9 +14,13 @@ float32):
   L0.gate, L0.up, L0.down, L1.q, ..., lm_head) uses
   W_i = default_rng((cfg, i)).standard_normal((N, K), float32) * 0.02 and
   x_i = default_rng((cfg, 1000 + i)).standard_normal(K, float32) as float16,
-  with cfg = 2 for the 0.5B model and 5 for the 7B model.
+  with cfg = 2 for the 0.5B model (x_i also for the 7B model, cfg = 5).
 * binary sign GEMV (N, K): bits = default_rng((4, N, K)).integers(0, 2,
   (N, K)); W = 1 - 2*bits as float32; x bits from default_rng((4, N, K, 1)).
+* Qwen2.5-7B sweep weights: drawn on the device, torch Philox seeded with
+  5000 + i, N(0, 0.02); x_i as above with cfg = 5.
+* prefill weights: default_rng((5, 4 | 5 | 6)) for gate / up / down,
+  N(0, 0.02) float32 of the 7B MLP shapes.
 * prefill activations: X = default_rng((5, 10000)) standard normal [512, 3584]
   float16 for gate/up and default_rng((5, 10001)) [512, 18944] for down.
 
@@ -121,12 +125,24 @@ def prefill_X(K, M=PREFILL_M):
 
 
 def prefill_W(name):
-    """Layer-0 gate/up/down weights of the 7B sweep (matrix indices 4, 5, 6)."""
+    """7B-shaped MLP weights for the prefill GEMMs: numpy seeds (5, 4), (5, 5)
+    and (5, 6) for gate, up and down (N(0, 0.02) float32)."""
     idx = {"gate": 4, "up": 5, "down": 6}[name]
     shapes = sweep_shapes("qwen2.5-7b")
     _, N, K = shapes[idx]
     W = np.random.default_rng((SWEEP_CFG["qwen2.5-7b"], idx)).standard_normal((N, K), dtype=np.float32)
     return W * np.float32(0.02)
+
+
+def device_normal_matrix(torch, seed, N, K, std=0.02):
+    """N(0, std) float32 [N, K] drawn on the GPU with torch's seeded Philox
+    generator (used for the 7B-shaped sweep, whose 7.07 G weights take minutes
+    to draw on the host).  `torch` is passed in so this module imports no GPU
+    framework."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(int(seed))
+    W = torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32)
+    return W.mul_(std)
 
 
 def normal_matrix(seed, N, K, std=0.02):

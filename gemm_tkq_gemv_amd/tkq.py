@@ -1,0 +1,242 @@
+"""ctypes binding of libtkq (include/tkq.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  The raw
+C entry points are exposed under their C names through :func:`lib`; the
+functions below take torch tensors, allocate outputs with torch, and call the
+entry point of the same name.
+
+Storage dtypes: packed 32-bit words are held in ``torch.int32`` tensors (the
+bits are the uint32 words of the layout), fp16 scales in ``torch.float16``.
+
+If ``libtkq.so`` has not been built this module raises on first use; there is
+no fallback path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtkq.so")
+
+FMT_INT4_G128 = 1
+FMT_K5_G128 = 2
+FMT_TERN_G128 = 3
+FMT_BIN = 4
+FORMATS = {"int4": FMT_INT4_G128, "k5": FMT_K5_G128, "tern": FMT_TERN_G128, "bin": FMT_BIN}
+
+OK, EINVAL, ESHAPE, EALIGN, EFORMAT, EHIP, EPLAN = 0, -1, -2, -3, -4, -5, -6
+
+
+class TkqError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        msg = "%s failed: %s (status %d)" % (what, strerror(status), status)
+        if status == EHIP:
+            msg += ", hipError_t %d" % lib().tkq_last_hip_error()
+        super().__init__(msg)
+
+
+class GemvDesc(ctypes.Structure):
+    """tkq_gemv_desc (64 bytes)."""
+    _fields_ = [("fmt", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("work0", ctypes.c_int32), ("tiles", ctypes.c_int32),
+                ("rows_per_tile", ctypes.c_int32), ("shape", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("codes", ctypes.c_void_p),
+                ("meta", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+class GemvPlan(ctypes.Structure):
+    """tkq_gemv_plan (32 bytes)."""
+    _fields_ = [("fmt", ctypes.c_int32), ("count", ctypes.c_int32), ("tiles", ctypes.c_int64),
+                ("variant", ctypes.c_int32), ("magic", ctypes.c_int32),
+                ("reserved", ctypes.c_int64)]
+
+
+_I64, _I32, _P = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+_SIGNATURES = {
+    "tkq_version": ([], ctypes.c_int),
+    "tkq_strerror": ([ctypes.c_int], ctypes.c_char_p),
+    "tkq_last_hip_error": ([], ctypes.c_int),
+    "tkq_pack_int4_g128": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "tkq_pack_k5": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "tkq_pack_tern_g128": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "tkq_pack_bin": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
+    "tkq_gemv_prepare": ([ctypes.POINTER(GemvDesc), _I32, ctypes.POINTER(GemvPlan)], ctypes.c_int),
+    "tkq_gemv": ([ctypes.POINTER(GemvPlan), _P, _P], ctypes.c_int),
+    "tkq_gemm_prefill": ([_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
+    "tkq_read_probe": ([_P, _I64, _P, _P], ctypes.c_int),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libtkq.so with argument types set (raises if not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libtkq.so is not built (python -m gemm_tkq_gemv_amd.build); "
+                               "there is no fallback path")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def strerror(status):
+    return lib().tkq_strerror(status).decode()
+
+
+def _call(name, *args):
+    st = getattr(lib(), name)(*args)
+    if st != OK:
+        raise TkqError(st, name)
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, dtype, name, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a CUDA (HIP) tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t
+
+
+# ---- quantize + pack ---------------------------------------------------------
+
+def pack_int4_g128(W, stream=None):
+    """W fp32 [N,K] -> (codes int32 [N,K/8], meta int32 [N,K/128] = half2 {s,z})."""
+    _need(W, torch.float32, "W")
+    N, K = W.shape
+    codes = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
+    meta = torch.empty((N, K // 128), dtype=torch.int32, device=W.device)
+    _call("tkq_pack_int4_g128", _ptr(W), N, K, _ptr(codes), _ptr(meta), _stream(stream))
+    return codes, meta
+
+
+def pack_k5(W, stream=None):
+    """W fp32 [N,K] -> (codes uint8 [N,K], scale fp16 [N,K/128])."""
+    _need(W, torch.float32, "W")
+    N, K = W.shape
+    codes = torch.empty((N, K), dtype=torch.uint8, device=W.device)
+    scale = torch.empty((N, K // 128), dtype=torch.float16, device=W.device)
+    _call("tkq_pack_k5", _ptr(W), N, K, _ptr(codes), _ptr(scale), _stream(stream))
+    return codes, scale
+
+
+def pack_tern_g128(W, stream=None):
+    """W fp32 [N,K] -> (codes int32 [N,K/16], scale fp16 [N,K/128])."""
+    _need(W, torch.float32, "W")
+    N, K = W.shape
+    codes = torch.empty((N, K // 16), dtype=torch.int32, device=W.device)
+    scale = torch.empty((N, K // 128), dtype=torch.float16, device=W.device)
+    _call("tkq_pack_tern_g128", _ptr(W), N, K, _ptr(codes), _ptr(scale), _stream(stream))
+    return codes, scale
+
+
+def pack_bin(W, stream=None):
+    """W fp32 [N,K] (or [K]) -> sign bits int32 [N,K/32] (or [K/32])."""
+    _need(W, torch.float32, "W")
+    vec = W.dim() == 1
+    W2 = W.view(1, -1) if vec else W
+    N, K = W2.shape
+    bits = torch.empty((N, K // 32), dtype=torch.int32, device=W.device)
+    _call("tkq_pack_bin", _ptr(W2), N, K, _ptr(bits), _stream(stream))
+    return bits.view(-1) if vec else bits
+
+
+PACKERS = {FMT_INT4_G128: pack_int4_g128, FMT_K5_G128: pack_k5,
+           FMT_TERN_G128: pack_tern_g128}
+
+
+# ---- grouped GEMV ------------------------------------------------------------
+
+class GemvBatch:
+    """A prepared grouped GEMV: many y_i = dequant(W_i) . x_i in one launch.
+
+    items: sequence of dicts with keys codes, meta (None for binary), x, y,
+    N, K (tensors already on the device).  The descriptor table is built,
+    planned by tkq_gemv_prepare and copied to the device once; run() launches
+    tkq_gemv on the current (or given) stream."""
+
+    def __init__(self, fmt, items, device=None):
+        fmt = FORMATS.get(fmt, fmt)
+        items = list(items)
+        if not items:
+            raise ValueError("empty GEMV batch")
+        n = len(items)
+        descs = (GemvDesc * n)()
+        self._keep = []
+        for d, it in zip(descs, items):
+            d.fmt, d.N, d.K = fmt, int(it["N"]), int(it["K"])
+            for key in ("codes", "meta", "x", "y"):
+                t = it.get(key)
+                if t is None:
+                    setattr(d, key, None)
+                    continue
+                if not t.is_cuda or not t.is_contiguous():
+                    raise ValueError("%s must be a contiguous device tensor" % key)
+                setattr(d, key, t.data_ptr())
+                self._keep.append(t)
+        self.plan = GemvPlan()
+        _call("tkq_gemv_prepare", descs, n, ctypes.byref(self.plan))
+        self.descs = descs
+        raw = bytes(ctypes.string_at(ctypes.addressof(descs), ctypes.sizeof(descs)))
+        dev = device if device is not None else self._keep[0].device
+        self.dev_descs = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(dev)
+        self.fmt, self.count, self.tiles = fmt, n, int(self.plan.tiles)
+
+    def run(self, stream=None):
+        _call("tkq_gemv", ctypes.byref(self.plan), _ptr(self.dev_descs), _stream(stream))
+
+
+def gemv(fmt, codes, meta, x, N, K, y=None, stream=None):
+    """Single GEMV y = dequant(W) . x (binary: K - 2 popcount(W ^ x), int32)."""
+    fmt = FORMATS.get(fmt, fmt)
+    if y is None:
+        dt = torch.int32 if fmt == FMT_BIN else torch.float16
+        y = torch.empty(N, dtype=dt, device=codes.device)
+    GemvBatch(fmt, [dict(codes=codes, meta=meta, x=x, y=y, N=N, K=K)]).run(stream)
+    return y
+
+
+# ---- prefill GEMM --------------------------------------------------------------
+
+def gemm_prefill(codes, meta, X, N, Y=None, stream=None):
+    """Y fp16 [M,N] = X fp16 [M,K] . dequant(W_int4_g128)^T."""
+    _need(X, torch.float16, "X")
+    M, K = X.shape
+    _need(codes, torch.int32, "codes", (N, K // 8))
+    _need(meta, torch.int32, "meta", (N, K // 128))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _need(Y, torch.float16, "Y", (M, N))
+    _call("tkq_gemm_prefill", FMT_INT4_G128, M, N, K, _ptr(codes), _ptr(meta), _ptr(X), _ptr(Y),
+          _stream(stream))
+    return Y
+
+
+def read_probe(buf, out=None, stream=None):
+    """Stream `buf` once with 16-byte non-temporal loads (bandwidth reference)."""
+    if out is None:
+        out = torch.zeros(4, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _call("tkq_read_probe", _ptr(buf), nbytes, _ptr(out), _stream(stream))
+    return out

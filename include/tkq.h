@@ -1,0 +1,211 @@
+/*
+ * tkq.h - C ABI of the MI355X (gfx950) low-bit weight GEMV library.
+ *
+ * The library computes the batch-1 decode product y = dequant(W_q) . x, in
+ * which every weight is read once and used for one multiply-add (Whetstone
+ * README, "The one fact that shapes everything"), for four weight codings,
+ * plus the quantize-and-pack step that produces them and the M >= 64 prefill
+ * GEMM over the int4 coding.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument named as a tensor (W, codes, meta, scale, bits, x,
+ *   y, X, Y, buf, out, dev_descs) is a DEVICE pointer owned by the caller
+ *   (e.g. a torch tensor's data_ptr()).  The library never allocates, frees or
+ *   retains device memory, and keeps no mutable global state apart from a
+ *   per-thread copy of the last HIP error code.  Host pointers are named
+ *   descs / plan and are read (and, for tkq_gemv_prepare, written) during the
+ *   call only.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Every device entry point only enqueues work on it and returns; results
+ *   are visible after the caller synchronises that stream.  Device faults
+ *   surface at that synchronisation, as usual in HIP.
+ * - Arguments are validated on the host BEFORE any HIP call.  A non-zero
+ *   return is a negative TKQ_E* status and nothing was enqueued (except for
+ *   TKQ_EHIP, which reports a failed launch; see tkq_last_hip_error()).
+ * - Tensors are dense, row-major and contiguous; "[N][K/8]" means N rows of
+ *   K/8 elements.  All device pointers must be 16-byte aligned.
+ * - The content of device buffers (codes, descriptors) is not validated:
+ *   codes that the packers never emit decode arithmetically (see each format),
+ *   and a descriptor table that does not match its plan is undefined
+ *   behaviour.
+ * - Non-finite weights passed to a packer are a precondition violation.
+ *
+ * Weight codings (storage layouts)
+ * --------------------------------
+ * TKQ_FMT_INT4_G128 (Whetstone README, "What the weights can actually
+ *   survive": group-128 round-to-nearest int4 with an f16 scale and an f16
+ *   zero per group, 4.25 bits/weight):
+ *     codes uint32 [N][K/8]  : element 8j+i of a row in bits [4i,4i+4) of word j
+ *     meta  uint32 [N][K/128]: fp16 scale in bits [0,16), fp16 zero in [16,32)
+ *     w = scale * (q - zero)
+ * TKQ_FMT_K5_G128 (TKintegers K5, "What is K5?": one byte per weight holding
+ *   five balanced trits, 243 values):
+ *     codes uint8 [N][K], scale fp16 [N][K/128]
+ *     w = scale * (c - 121); bytes 243..255 are never produced and decode as
+ *     c - 121 as well.
+ * TKQ_FMT_TERN_G128 (Whetstone README, bytes/token table, "ternary g128"):
+ *     codes uint32 [N][K/16]: element 16j+i in bits [2i,2i+2), code = t + 1
+ *     scale fp16 [N][K/128];  w = scale * (code - 1); code 3 is never produced
+ *     and decodes as +2.
+ * TKQ_FMT_BIN (Whetstone README, "Measured hardware facts": {-1,+1} packed as
+ *   bits {1,0}):
+ *     bits uint32 [N][K/32]  : element 32j+i in bit i of word j, 1 <=> -1
+ *     no metadata; x is packed the same way (uint32 [K/32]); y is int32.
+ */
+#ifndef TKQ_H
+#define TKQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TKQ_VERSION 10000 /* major*10000 + minor*100 + patch */
+
+/* ---- status codes ------------------------------------------------------ */
+#define TKQ_OK 0
+#define TKQ_EINVAL (-1)  /* null pointer, non-positive size, bad count     */
+#define TKQ_ESHAPE (-2)  /* K not a multiple of the format's unit, size
+                            beyond the supported range                     */
+#define TKQ_EALIGN (-3)  /* a device pointer is not 16-byte aligned        */
+#define TKQ_EFORMAT (-4) /* unknown format, or mixed formats in one call   */
+#define TKQ_EHIP (-5)    /* a HIP call failed: see tkq_last_hip_error()    */
+#define TKQ_EPLAN (-6)   /* plan not produced by tkq_gemv_prepare          */
+
+/* ---- weight codings ---------------------------------------------------- */
+#define TKQ_FMT_INT4_G128 1
+#define TKQ_FMT_K5_G128 2
+#define TKQ_FMT_TERN_G128 3
+#define TKQ_FMT_BIN 4
+
+/* Size limits: 1 <= N <= 2^31-1, 128 <= K <= 2^20 (K % 128 == 0 for the
+ * group-128 codings and for every GEMV; K % 32 == 0 is enough for
+ * tkq_pack_bin), and N*K <= 2^39 weights.  A GEMV additionally needs
+ * K <= 32768 (int4), 16384 (K5), 49152 (ternary) or 262144 (binary). */
+#define TKQ_MAX_K (1 << 20)
+
+/* Library version (TKQ_VERSION of the build). */
+int tkq_version(void);
+
+/* Static string describing a status code (never NULL). */
+const char* tkq_strerror(int status);
+
+/* hipError_t of the last failed HIP call made by this thread (0 if none). */
+int tkq_last_hip_error(void);
+
+/* ---- quantize + pack ----------------------------------------------------
+ * W is fp32 [N][K] on the device.  Each function writes every output element
+ * exactly once; the results are bit-identical to an IEEE fp32 evaluation of
+ * the formulas below (true division, rint = round half to even, fp32->fp16
+ * round to nearest even).  A scale that rounds to fp16 zero is stored as 1.0
+ * (Whetstone README, status list: the fp16 scale that underflowed to zero).
+ */
+
+/* int4 g128, asymmetric RTN (Whetstone README, "What the weights can
+ * actually survive").  Per row and 128-column group:
+ *   lo = min(min w, 0), hi = max(max w, 0), s = fp16((hi - lo) / 15),
+ *   z = clamp(rint(-lo / s), 0, 15), q = clamp(rint(w / s) + z, 0, 15).
+ * codes: uint32 [N][K/8]; meta: uint32 [N][K/128] = half2 {s, z}.
+ * K % 128 == 0. */
+int tkq_pack_int4_g128(const float* W, int64_t N, int64_t K, uint32_t* codes,
+                       uint32_t* meta, void* stream);
+
+/* K5 byte codes (TKintegers K5, "What is K5?"), symmetric absmax RTN per
+ * 128-column group: s = fp16(max|w| / 121), c = clamp(rint(w / s), -121,
+ * 121) + 121.  codes: uint8 [N][K]; scale: fp16 bits [N][K/128].
+ * K % 128 == 0. */
+int tkq_pack_k5(const float* W, int64_t N, int64_t K, uint8_t* codes,
+                uint16_t* scale, void* stream);
+
+/* Ternary g128 (Whetstone README, "ternary g128"), absmean RTN per group:
+ * s = fp16((|w_0| + |w_1| + ... + |w_127|) / 128) summed in k order in fp32,
+ * t = clamp(rint(w / s), -1, 1), code = t + 1.
+ * codes: uint32 [N][K/16]; scale: fp16 bits [N][K/128].  K % 128 == 0. */
+int tkq_pack_tern_g128(const float* W, int64_t N, int64_t K, uint32_t* codes,
+                       uint16_t* scale, void* stream);
+
+/* Sign bits (Whetstone README, "Measured hardware facts"): bit = 1 exactly
+ * when w < 0.  bits: uint32 [N][K/32].  K % 32 == 0.  Also packs x (N = 1). */
+int tkq_pack_bin(const float* W, int64_t N, int64_t K, uint32_t* bits,
+                 void* stream);
+
+/* ---- grouped GEMV -------------------------------------------------------
+ * One launch computes any number of independent GEMVs y_i = W_i . x_i that
+ * share one coding (e.g. every linear layer read for one decoded token).
+ *
+ * Float codings: y[n] = sum_k w[n,k] x[k], fp32 accumulation, fp16 output
+ * rounded to nearest even; |y - y_exact| <= 2e-3 * sum_k |w[n,k] x[k]|.
+ * Binary: y[n] = K - 2 * popcount(W[n] XOR x) (Whetstone README, "Measured
+ * hardware facts"), exact int32.
+ *
+ * Usage: fill fmt, N, K, codes, meta, x, y of each host descriptor; call
+ * tkq_gemv_prepare (fills the [prepare] fields and the plan); copy the
+ * descriptor array to device memory (16-byte aligned); call tkq_gemv with the
+ * plan and the device copy, as often as wanted.  Outputs must not overlap
+ * each other or any input.
+ */
+typedef struct tkq_gemv_desc {
+  int32_t fmt;           /* TKQ_FMT_*; identical in every descriptor        */
+  int32_t N;             /* rows = length of y, >= 1                        */
+  int32_t K;             /* columns = length of x, multiple of 128          */
+  int32_t work0;         /* [prepare] index of the first row tile           */
+  int32_t tiles;         /* [prepare] number of row tiles                   */
+  int32_t rows_per_tile; /* [prepare] rows handled by one workgroup         */
+  int32_t shape;         /* [prepare] lanes-per-row log2 | passes<<4 |
+                                      k-slices<<12                          */
+  int32_t reserved;      /* [prepare] zero                                  */
+  const void* codes;     /* packed codes (layout per fmt)                   */
+  const void* meta;      /* int4: uint32 half2 [N][K/128]; K5, ternary: fp16
+                            [N][K/128]; binary: ignored (may be NULL)       */
+  const void* x;         /* fp16 [K]; binary: uint32 [K/32]                 */
+  void* y;               /* fp16 [N]; binary: int32 [N]                     */
+} tkq_gemv_desc;         /* 64 bytes */
+
+typedef struct tkq_gemv_plan {
+  int32_t fmt;        /* common coding of the descriptors                   */
+  int32_t count;      /* number of descriptors                              */
+  int64_t tiles;      /* total row tiles = workgroups per launch            */
+  int32_t variant;    /* kernel variant chosen for the descriptors          */
+  int32_t magic;      /* set by tkq_gemv_prepare                            */
+  int64_t reserved;
+} tkq_gemv_plan;
+
+/* Host only.  Validates every descriptor (fmt, sizes, non-null and 16-byte
+ * aligned pointers, all fmt equal), chooses each GEMV's work decomposition,
+ * writes the [prepare] fields of descs[0..count) and fills *plan.
+ * Returns TKQ_OK or TKQ_EINVAL / TKQ_ESHAPE / TKQ_EALIGN / TKQ_EFORMAT. */
+int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan);
+
+/* Launches one kernel over plan->tiles workgroups on `stream`.
+ * dev_descs: device copy of the prepared descriptors (plan->count of them,
+ * 16-byte aligned).  Returns TKQ_OK, TKQ_EINVAL, TKQ_EALIGN, TKQ_EPLAN or
+ * TKQ_EHIP. */
+int tkq_gemv(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs,
+             void* stream);
+
+/* ---- prefill GEMM -------------------------------------------------------
+ * Y[m,n] = sum_k X[m,k] * w[n,k] with w the int4 g128 dequantized weights
+ * (TKintegers K5, "What is K5?": tiles of low-bit codes are expanded to fp16
+ * matrix-core operands with fp32 accumulation).  fp16 output rounded to
+ * nearest even; |Y - Y_exact| <= 2e-3 * sum_k |X[m,k] w[n,k]| entry-wise.
+ * fmt must be TKQ_FMT_INT4_G128.  X: fp16 bits [M][K]; Y: fp16 bits [M][N];
+ * codes, meta as produced by tkq_pack_int4_g128.  Any M >= 1; tuned for
+ * M >= 64 (decode, M = 1, belongs to tkq_gemv).  K % 128 == 0. */
+int tkq_gemm_prefill(int32_t fmt, int64_t M, int64_t N, int64_t K,
+                     const uint32_t* codes, const uint32_t* meta,
+                     const uint16_t* X, uint16_t* Y, void* stream);
+
+/* ---- bandwidth probe ----------------------------------------------------
+ * Reads `bytes` bytes of `buf` once with the same 16-byte non-temporal loads
+ * the GEMV uses and writes their XOR into out[0..3] (uint32 x 4), so that the
+ * read cannot be elided.  bytes % 16 == 0, bytes >= 16.  A reference for the
+ * achievable HBM read rate; not part of the GEMV. */
+int tkq_read_probe(const void* buf, int64_t bytes, uint32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TKQ_H */

@@ -1,0 +1,185 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/tkq.h declares, its structs have the declared layout, argument
+validation rejects bad calls before any HIP call, and the GEMV planner's
+host-side output is consistent."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gemm_tkq_gemv_amd import inputs, tkq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tkq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tkq.LIB_PATH), reason="libtkq.so not built")
+
+A = 0x7f0000000000  # fake, 16-byte aligned device addresses (never dereferenced)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tkq_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = _declared()
+    assert "tkq_gemv" in names and "tkq_gemm_prefill" in names
+    lib = tkq.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    # and the binding types every one of them
+    assert set(names) == set(tkq._SIGNATURES)
+
+
+def test_struct_layout():
+    assert ctypes.sizeof(tkq.GemvDesc) == 64
+    assert ctypes.sizeof(tkq.GemvPlan) == 32
+    assert tkq.GemvDesc.codes.offset == 32 and tkq.GemvDesc.y.offset == 56
+    text = open(HEADER).read()
+    assert "} tkq_gemv_desc;         /* 64 bytes */" in text
+
+
+def test_version_and_strings():
+    lib = tkq.lib()
+    assert lib.tkq_version() == 10000
+    for st in range(0, -7, -1):
+        assert tkq.strerror(st)
+    assert "unknown" in tkq.strerror(-99)
+
+
+@pytest.mark.parametrize("name", ["tkq_pack_int4_g128", "tkq_pack_k5", "tkq_pack_tern_g128"])
+def test_pack_validation(name):
+    f = getattr(tkq.lib(), name)
+    assert f(None, 4, 128, A, A, None) == tkq.EINVAL
+    assert f(A, 0, 128, A, A, None) == tkq.EINVAL
+    assert f(A, 4, 0, A, A, None) == tkq.EINVAL
+    assert f(A, 4, 100, A, A, None) == tkq.ESHAPE
+    assert f(A, 4, 96, A, A, None) == tkq.ESHAPE
+    assert f(A, 4, (1 << 20) + 128, A, A, None) == tkq.ESHAPE
+    assert f(A, 1 << 31, 128, A, A, None) == tkq.ESHAPE
+    assert f(A, 4, 128, None, A, None) == tkq.EINVAL
+    assert f(A, 4, 128, A, None, None) == tkq.EINVAL
+    assert f(A + 4, 4, 128, A, A, None) == tkq.EALIGN
+    assert f(A, 4, 128, A + 8, A, None) == tkq.EALIGN
+    assert f(A, 4, 128, A, A + 2, None) == tkq.EALIGN
+
+
+def test_pack_bin_validation():
+    f = tkq.lib().tkq_pack_bin
+    assert f(None, 1, 32, A, None) == tkq.EINVAL
+    assert f(A, 1, 48, A, None) == tkq.ESHAPE
+    assert f(A, 1, 32, None, None) == tkq.EINVAL
+    assert f(A, 1, 32, A + 4, None) == tkq.EALIGN
+
+
+def _descs(fmt, shapes):
+    arr = (tkq.GemvDesc * len(shapes))()
+    for i, (n, k) in enumerate(shapes):
+        d = arr[i]
+        d.fmt, d.N, d.K = fmt, n, k
+        d.codes, d.meta, d.x, d.y = A, A + 0x100000, A + 0x200000, A + 0x300000
+    return arr
+
+
+def _prepare(arr):
+    plan = tkq.GemvPlan()
+    st = tkq.lib().tkq_gemv_prepare(arr, len(arr), ctypes.byref(plan))
+    return st, plan
+
+
+def _shape(d):
+    return 1 << (d.shape & 15), (d.shape >> 4) & 255, (d.shape >> 12) & 15
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
+def test_prepare_tiles_cover_rows(fmt):
+    shapes = [(1, 128), (7, 896), (128, 896), (4864, 896), (896, 4864), (333, 4864), (151936, 896)]
+    arr = _descs(fmt, shapes)
+    st, plan = _prepare(arr)
+    assert st == tkq.OK
+    work = 0
+    for d, (n, k) in zip(arr, shapes):
+        assert d.work0 == work
+        assert d.tiles * d.rows_per_tile >= n > (d.tiles - 1) * d.rows_per_tile
+        L, J, S = _shape(d)
+        per_chunk = {1: 32, 2: 16, 3: 64, 4: 128}[fmt]
+        C = k // per_chunk
+        assert S in (1, 2, 4) and 1 <= J <= 8
+        assert S * L * J >= C                       # every chunk has a lane
+        P = 64 // L
+        assert d.rows_per_tile % ((4 // S) * P) == 0
+        assert d.rows_per_tile <= 1024
+        work += d.tiles
+    assert plan.tiles == work and plan.count == len(shapes) and plan.fmt == fmt
+
+
+def test_prepare_shapes_for_model_matrices():
+    arr = _descs(1, [(896, 896), (896, 4864), (3584, 3584), (3584, 18944)])
+    assert _prepare(arr)[0] == tkq.OK
+    assert _shape(arr[0]) == (32, 1, 1)   # 28 chunks: 32 lanes, one pass
+    assert _shape(arr[1]) == (64, 3, 1)   # 152 chunks: 64 lanes, three passes
+    assert _shape(arr[2]) == (64, 2, 1)   # 112 chunks
+    assert _shape(arr[3]) == (64, 3, 4)   # 592 chunks: four k-slices
+
+
+def test_prepare_sweep_counts():
+    shapes = [(n, k) for _, n, k in inputs.sweep_shapes("qwen2.5-0.5b")]
+    arr = _descs(1, shapes)
+    st, plan = _prepare(arr)
+    assert st == tkq.OK and plan.count == 169 and plan.tiles > 1024
+
+
+def test_prepare_validation():
+    arr = _descs(1, [(8, 128), (8, 256)])
+    arr[1].fmt = 2
+    assert _prepare(arr)[0] == tkq.EFORMAT
+    arr = _descs(7, [(8, 128)])
+    assert _prepare(arr)[0] == tkq.EFORMAT
+    arr = _descs(1, [(8, 200)])
+    assert _prepare(arr)[0] == tkq.ESHAPE
+    arr = _descs(1, [(8, 65536)])             # beyond the int4 GEMV's K
+    assert _prepare(arr)[0] == tkq.ESHAPE
+    arr = _descs(1, [(0, 128)])
+    assert _prepare(arr)[0] == tkq.EINVAL
+    arr = _descs(1, [(8, 128)])
+    arr[0].meta = None
+    assert _prepare(arr)[0] == tkq.EINVAL
+    arr = _descs(4, [(8, 128)])
+    arr[0].meta = None                        # binary needs no metadata
+    assert _prepare(arr)[0] == tkq.OK
+    arr = _descs(1, [(8, 128)])
+    arr[0].x = A + 2
+    assert _prepare(arr)[0] == tkq.EALIGN
+    plan = tkq.GemvPlan()
+    assert tkq.lib().tkq_gemv_prepare(arr, 0, ctypes.byref(plan)) == tkq.EINVAL
+
+
+def test_gemv_rejects_unprepared_plan():
+    plan = tkq.GemvPlan()
+    plan.fmt, plan.count, plan.tiles = 1, 1, 1
+    assert tkq.lib().tkq_gemv(ctypes.byref(plan), A, None) == tkq.EPLAN
+    arr = _descs(1, [(8, 128)])
+    st, plan = _prepare(arr)
+    assert tkq.lib().tkq_gemv(ctypes.byref(plan), None, None) == tkq.EINVAL
+    assert tkq.lib().tkq_gemv(ctypes.byref(plan), A + 8, None) == tkq.EALIGN
+
+
+def test_prefill_validation():
+    f = tkq.lib().tkq_gemm_prefill
+    assert f(2, 64, 128, 128, A, A, A, A, None) == tkq.EFORMAT
+    assert f(1, 0, 128, 128, A, A, A, A, None) == tkq.EINVAL
+    assert f(1, 64, 128, 100, A, A, A, A, None) == tkq.ESHAPE
+    assert f(1, 64, 128, 128, None, A, A, A, None) == tkq.EINVAL
+    assert f(1, 64, 128, 128, A, A, A + 2, A, None) == tkq.EALIGN
+
+
+def test_read_probe_validation():
+    f = tkq.lib().tkq_read_probe
+    assert f(None, 64, A, None) == tkq.EINVAL
+    assert f(A, 8, A, None) == tkq.EINVAL
+    assert f(A, 24, A, None) == tkq.ESHAPE
+    assert f(A + 4, 64, A, None) == tkq.EALIGN

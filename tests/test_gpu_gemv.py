@@ -1,0 +1,150 @@
+"""GPU grouped GEMV against the fp64 oracle: per-row bound for the float
+codings, bit-exact for binary; ragged shapes spanning several tiles, grouped
+launches of mixed shapes, and the special cases with exact answers."""
+
+import numpy as np
+import pytest
+
+from gemm_tkq_gemv_amd import inputs
+from helpers import (assert_codes_equal, check_gemv, device_codes_np, gpu_or_skip, oracle_pack,
+                     oracle_wdeq)
+from oracle import ref as oref
+
+pytestmark = pytest.mark.gpu
+
+MAXK = {"int4": 18944, "k5": 4864, "tern": 18944, "bin": 18944}
+
+
+def _shapes(fmt):
+    s = [(1, 128), (5, 256), (128, 896), (333, 896), (1000, 4864), (77, 1152), (2049, 384)]
+    s.append((300, MAXK[fmt]))
+    return s
+
+
+def _inputs(fmt, N, K, seed):
+    if fmt == "bin":
+        W = (1 - 2 * np.random.default_rng((seed, 1)).integers(0, 2, (N, K))).astype(np.float32)
+        x = (1 - 2 * np.random.default_rng((seed, 2)).integers(0, 2, K)).astype(np.float32)
+        return W, x
+    return inputs.normal_matrix((seed, N, K), N, K), inputs.normal_vector((seed, 9, K), K)
+
+
+def _device_pack(torch, tkq, fmt, Wd):
+    if fmt == "int4":
+        return tkq.pack_int4_g128(Wd)
+    if fmt == "k5":
+        return tkq.pack_k5(Wd)
+    if fmt == "tern":
+        return tkq.pack_tern_g128(Wd)
+    return tkq.pack_bin(Wd), None
+
+
+def _items(torch, tkq, fmt, mats):
+    items = []
+    for W, x in mats:
+        N, K = W.shape
+        codes, meta = _device_pack(torch, tkq, fmt, torch.from_numpy(W).cuda())
+        if fmt == "bin":
+            xd = tkq.pack_bin(torch.from_numpy(x).cuda())
+            y = torch.full((N,), -7, dtype=torch.int32, device="cuda")
+        else:
+            xd = torch.from_numpy(x).cuda()
+            y = torch.full((N,), float("nan"), dtype=torch.float16, device="cuda")
+        items.append(dict(codes=codes, meta=meta, x=xd, y=y, N=N, K=K))
+    return items
+
+
+def _check(fmt, W, x, y, codes, meta, what):
+    oc, om = oracle_pack(fmt, W)
+    assert_codes_equal(fmt, device_codes_np(fmt, codes, meta), (oc, om))
+    K = W.shape[1]
+    if fmt == "bin":
+        xb = oracle_pack("bin", x[None, :])[0][0]
+        want = oref.bin_gemv(oc, xb, K)
+        got = y.cpu().numpy()
+        assert np.array_equal(got, want), "%s: %d rows differ" % (what, int((got != want).sum()))
+        return
+    w_deq = oracle_wdeq(fmt, oc, om, K)
+    check_gemv(y.float().cpu().numpy(), w_deq, x, what)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin"])
+def test_gemv_single_shapes(fmt):
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    for i, (N, K) in enumerate(_shapes(fmt)):
+        W, x = _inputs(fmt, N, K, 100 + i)
+        (it,) = _items(torch, tkq, fmt, [(W, x)])
+        tkq.GemvBatch(fmt, [it]).run()
+        torch.cuda.synchronize()
+        _check(fmt, W, x, it["y"], it["codes"], it["meta"], "%s %dx%d" % (fmt, N, K))
+
+
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin"])
+def test_gemv_grouped_mixed_shapes(fmt):
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    mats = [_inputs(fmt, N, K, 200 + i) for i, (N, K) in enumerate(_shapes(fmt))]
+    items = _items(torch, tkq, fmt, mats)
+    batch = tkq.GemvBatch(fmt, items)
+    batch.run()
+    torch.cuda.synchronize()
+    first = [it["y"].clone() for it in items]
+    for (W, x), it in zip(mats, items):
+        _check(fmt, W, x, it["y"], it["codes"], it["meta"], "%s grouped %s" % (fmt, W.shape))
+    # a second launch gives bit-identical outputs (no races, no state)
+    for it in items:
+        it["y"].fill_(0)
+    batch.run()
+    torch.cuda.synchronize()
+    for a, it in zip(first, items):
+        assert torch.equal(a, it["y"])
+
+
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern"])
+def test_gemv_unit_vectors_bit_exact(fmt):
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    N, K = 300, 896
+    W = inputs.normal_matrix((301, N, K), N, K)
+    oc, om = oracle_pack(fmt, W)
+    w_deq = oracle_wdeq(fmt, oc, om, K)
+    codes, meta = _device_pack(torch, tkq, fmt, torch.from_numpy(W).cuda())
+    for k in (0, 1, 4, 5, 31, 32, 127, 128, 500, 895):
+        e = torch.zeros(K, dtype=torch.float16, device="cuda")
+        e[k] = 1
+        y = tkq.gemv(fmt, codes, meta, e, N, K)
+        torch.cuda.synchronize()
+        want = w_deq[:, k].astype(np.float16)
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), want.view(np.uint16)), (fmt, k)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern"])
+def test_gemv_exact_zeros(fmt):
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    N, K = 130, 896
+    W = inputs.normal_matrix((401, N, K), N, K)
+    W[7] = 0.0          # zero rows
+    W[64] = 0.0
+    W[100, :128] = 0.0  # one zero group inside a live row
+    codes, meta = _device_pack(torch, tkq, fmt, torch.from_numpy(W).cuda())
+    x = torch.from_numpy(inputs.normal_vector(402, K)).cuda()
+    y = tkq.gemv(fmt, codes, meta, x, N, K).float().cpu().numpy()
+    assert y[7] == 0 and y[64] == 0
+    oc, om = oracle_pack(fmt, W)
+    check_gemv(y, oracle_wdeq(fmt, oc, om, K), x.cpu().numpy(), fmt)
+    y0 = tkq.gemv(fmt, codes, meta, torch.zeros(K, dtype=torch.float16, device="cuda"), N, K)
+    torch.cuda.synchronize()
+    assert torch.all(y0 == 0)
+
+
+def test_gemv_bin_all_plus_x():
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    N, K = 257, 4864
+    W, _ = inputs.binary_case(N, K)
+    bits = tkq.pack_bin(torch.from_numpy(W).cuda())
+    xb = torch.zeros(K // 32, dtype=torch.int32, device="cuda")       # all +1
+    y = tkq.gemv("bin", bits, None, xb, N, K).cpu().numpy()
+    assert np.array_equal(y, K - 2 * (W < 0).sum(axis=1))

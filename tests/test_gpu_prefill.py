@@ -1,0 +1,58 @@
+"""GPU prefill GEMM (int4 g128 weights, fp16 MFMA) against the fp64 oracle:
+entry-wise bound over the k-sum, ragged shapes, the 7B-shaped M = 512
+gate/up/down GEMMs in full, and consistency with the GEMV row by row."""
+
+import numpy as np
+import pytest
+
+from gemm_tkq_gemv_amd import inputs
+from helpers import gpu_or_skip, oracle_pack, oracle_wdeq
+from oracle import ref as oref
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(torch, tkq, W, X):
+    codes, meta = tkq.pack_int4_g128(torch.from_numpy(W).cuda())
+    Y = tkq.gemm_prefill(codes, meta, torch.from_numpy(X).cuda(), W.shape[0])
+    torch.cuda.synchronize()
+    return codes, meta, Y
+
+
+def _check(Y, X, w_deq, what):
+    Yr = oref.gemm(X, w_deq)
+    ok, worst = oref.check_within(Y.float().cpu().numpy(), Yr, oref.gemm_bound(X, w_deq))
+    assert ok, "%s: worst |err|/bound = %g" % (what, worst)
+    return worst
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (64, 128, 256), (65, 200, 384),
+                                   (130, 333, 896), (512, 256, 1024), (257, 129, 4864)])
+def test_prefill_ragged(M, N, K):
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    W = inputs.normal_matrix((500, M, N, K), N, K)
+    X = np.random.default_rng((501, M, K)).standard_normal((M, K), dtype=np.float32).astype(np.float16)
+    _, _, Y = _run(torch, tkq, W, X)
+    oc, om = oracle_pack("int4", W)
+    _check(Y, X, oracle_wdeq("int4", oc, om, K), "%dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("name", ["gate", "up", "down"])
+def test_prefill_7b_mlp_full(name):
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    W = inputs.prefill_W(name)
+    N, K = W.shape
+    X = inputs.prefill_X(K)
+    codes, meta, Y = _run(torch, tkq, W, X)
+    oc, om = oracle_pack("int4", W)
+    worst = _check(Y, X, oracle_wdeq("int4", oc, om, K), name)
+    print("prefill %s worst |err|/bound %.3g" % (name, worst))
+    # row m of the GEMM equals the GEMV of X[m] within the same bound
+    xm = torch.from_numpy(X[7]).cuda()
+    y = tkq.gemv("int4", codes, meta, xm, N, K)
+    torch.cuda.synchronize()
+    diff = np.abs(y.float().cpu().numpy().astype(np.float64) - Y[7].float().cpu().numpy())
+    w_deq = oracle_wdeq("int4", oc, om, K)
+    assert np.all(diff <= 2 * oref.gemv_bound(w_deq, X[7].astype(np.float64)))
