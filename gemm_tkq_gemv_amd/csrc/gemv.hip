@@ -20,16 +20,18 @@
 //    which codes are unpacked.
 //  * Unpack with fp16 "magic numbers": OR-ing a code field into the mantissa
 //    of fp16 1024.0 gives 1024 + m*code exactly (m = 1, 4, 16, 64 or 256 by
-//    the field's bit position), two weights per 32-bit register, ready for
-//    v_dot2_f32_f16 (fp16 products, fp32 accumulation).  The constant 1024*x
-//    part is removed per chunk by subtracting the same dot-product chain
-//    evaluated on zero-point codes, so groups whose codes all equal the zero
-//    point contribute exactly 0.
+//    the field's bit position), two weights per 32-bit register, one
+//    v_and_or_b32 each, ready for v_dot2_f32_f16 (fp16 products, fp32
+//    accumulation).  The constant 1024*x part is removed per chunk by
+//    subtracting the same dot-product chain evaluated on zero-point codes, so
+//    groups whose codes all equal the zero point contribute exactly 0.
 //  * Per-group fp16 scale (and int4 zero) are applied once per chunk in fp32;
 //    the row sum is a DPP butterfly inside the lane group; fp16 y is rounded
 //    to nearest even.  The binary coding XORs code and x words and counts
 //    bits (v_bcnt_u32_b32): y = K - 2 * popcount (Whetstone README, "Measured
 //    hardware facts").
+//  * Loads of the next row step are issued before the current step is
+//    computed (two register buffers used alternately).
 #include <type_traits>
 
 #include "device_common.h"
@@ -43,15 +45,31 @@ constexpr int kWaves = 4;
 constexpr int kMaxTileRows = kGemvMaxTileRows;
 constexpr uint32_t kMagic = 0x64006400u;  // fp16 pair (1024.0, 1024.0)
 
+// Constants held in registers.  A gfx9 VOP3 instruction (v_and_or_b32,
+// v_perm_b32) can encode no literal and read at most one SGPR, so masks live
+// in SGPRs and the magic number in a VGPR; the opaque moves keep the compiler
+// from folding them back into literals.
+__device__ __forceinline__ uint32_t in_sgpr(uint32_t c) {
+  uint32_t r;
+  asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "i"(c));
+  return r;
+}
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
 // ---------------------------------------------------------------- codecs --
 // Each codec states, for one 16-byte chunk of codes:
 //   WPC  weights per chunk
 //   XR   u32 registers of prepared x (pairs of fp16)
 //   XB   bytes of x the chunk consumes
 //   CPG  chunks per 128-weight group;  MB metadata bytes per group
-//   prep(raw, xr)      permute natural x pairs into the unpack order
-//   dot(codes, xr)     sum over the chunk of (1024 + m*code) * x, as fp32
-//   kZero              a code word whose every field is the zero-point code
+//   Regs register-resident constants (make() once per tile)
+//   prep(raw, xr)       permute natural x pairs into the unpack order
+//   dot(codes, xr, R)   sum over the chunk of (1024 + m*code) * x, as fp32
+//   kZero               a code word whose every field is the zero-point code
 
 template <int FMT>
 struct Codec;
@@ -64,6 +82,10 @@ template <>
 struct Codec<kFmtInt4> {
   static constexpr int WPC = 32, XR = 16, XB = 64, CPG = 4, MB = 4;
   static constexpr uint32_t kZero = 0u;
+  struct Regs {
+    uint32_t m0, m1, magic;
+  };
+  __device__ static Regs make() { return {in_sgpr(0x000F000Fu), in_sgpr(0x00F000F0u), in_vgpr(kMagic)}; }
   __device__ static void prep(const uint32_t* raw, uint32_t* xr) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -74,15 +96,15 @@ struct Codec<kFmtInt4> {
       xr[4 * w + 3] = __builtin_amdgcn_perm(d, b, 0x07060302u);  // (x3, x7)
     }
   }
-  __device__ static float dot(u32x4 q, const uint32_t* xr) {
+  __device__ static float dot(u32x4 q, const uint32_t* xr, const Regs& R) {
     float lo = 0.0f, hi = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t v = q[w], t = v >> 8;
-      lo = __builtin_amdgcn_fdot2(as_h2((v & 0x000F000Fu) | kMagic), as_h2(xr[4 * w + 0]), lo, false);
-      hi = __builtin_amdgcn_fdot2(as_h2((v & 0x00F000F0u) | kMagic), as_h2(xr[4 * w + 1]), hi, false);
-      lo = __builtin_amdgcn_fdot2(as_h2((t & 0x000F000Fu) | kMagic), as_h2(xr[4 * w + 2]), lo, false);
-      hi = __builtin_amdgcn_fdot2(as_h2((t & 0x00F000F0u) | kMagic), as_h2(xr[4 * w + 3]), hi, false);
+      lo = __builtin_amdgcn_fdot2(as_h2((v & R.m0) | R.magic), as_h2(xr[4 * w + 0]), lo, false);
+      hi = __builtin_amdgcn_fdot2(as_h2((v & R.m1) | R.magic), as_h2(xr[4 * w + 1]), hi, false);
+      lo = __builtin_amdgcn_fdot2(as_h2((t & R.m0) | R.magic), as_h2(xr[4 * w + 2]), lo, false);
+      hi = __builtin_amdgcn_fdot2(as_h2((t & R.m1) | R.magic), as_h2(xr[4 * w + 3]), hi, false);
     }
     return fmaf(hi, 0.0625f, lo);
   }
@@ -94,6 +116,10 @@ template <>
 struct Codec<kFmtK5> {
   static constexpr int WPC = 16, XR = 8, XB = 32, CPG = 8, MB = 2;
   static constexpr uint32_t kZero = 0x79797979u;  // 121 = value 0
+  struct Regs {
+    uint32_t sel_a, sel_b, magic;
+  };
+  __device__ static Regs make() { return {in_sgpr(0x04020400u), in_sgpr(0x04030401u), in_vgpr(0x64646464u)}; }
   __device__ static void prep(const uint32_t* raw, uint32_t* xr) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -102,15 +128,15 @@ struct Codec<kFmtK5> {
       xr[2 * w + 1] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // (x1, x3)
     }
   }
-  __device__ static float dot(u32x4 q, const uint32_t* xr) {
+  __device__ static float dot(u32x4 q, const uint32_t* xr, const Regs& R) {
     float acc = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t v = q[w];
-      acc = __builtin_amdgcn_fdot2(as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04020400u)),
-                                   as_h2(xr[2 * w + 0]), acc, false);
-      acc = __builtin_amdgcn_fdot2(as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04030401u)),
-                                   as_h2(xr[2 * w + 1]), acc, false);
+      acc = __builtin_amdgcn_fdot2(as_h2(__builtin_amdgcn_perm(R.magic, v, R.sel_a)), as_h2(xr[2 * w + 0]),
+                                   acc, false);
+      acc = __builtin_amdgcn_fdot2(as_h2(__builtin_amdgcn_perm(R.magic, v, R.sel_b)), as_h2(xr[2 * w + 1]),
+                                   acc, false);
     }
     return acc;
   }
@@ -123,6 +149,14 @@ template <>
 struct Codec<kFmtTern> {
   static constexpr int WPC = 64, XR = 32, XB = 128, CPG = 2, MB = 2;
   static constexpr uint32_t kZero = 0x55555555u;  // code 1 = value 0
+  struct Regs {
+    uint32_t m[5], magic;
+  };
+  __device__ static Regs make() {
+    return {{in_sgpr(0x00030003u), in_sgpr(0x000C000Cu), in_sgpr(0x00300030u), in_sgpr(0x00C000C0u),
+             in_sgpr(0x03000300u)},
+            in_vgpr(kMagic)};
+  }
   __device__ static void prep(const uint32_t* raw, uint32_t* xr) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -136,20 +170,20 @@ struct Codec<kFmtTern> {
       }
     }
   }
-  __device__ static float dot(u32x4 q, const uint32_t* xr) {
+  __device__ static float dot(u32x4 q, const uint32_t* xr, const Regs& R) {
     float a1 = 0.0f, a4 = 0.0f, a16 = 0.0f, a64 = 0.0f, a256 = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t v = q[w], t = v >> 10;
       const uint32_t* x = xr + 8 * w;
-      a1 = __builtin_amdgcn_fdot2(as_h2((v & 0x00030003u) | kMagic), as_h2(x[0]), a1, false);
-      a4 = __builtin_amdgcn_fdot2(as_h2((v & 0x000C000Cu) | kMagic), as_h2(x[1]), a4, false);
-      a16 = __builtin_amdgcn_fdot2(as_h2((v & 0x00300030u) | kMagic), as_h2(x[2]), a16, false);
-      a64 = __builtin_amdgcn_fdot2(as_h2((v & 0x00C000C0u) | kMagic), as_h2(x[3]), a64, false);
-      a256 = __builtin_amdgcn_fdot2(as_h2((v & 0x03000300u) | kMagic), as_h2(x[4]), a256, false);
-      a1 = __builtin_amdgcn_fdot2(as_h2((t & 0x00030003u) | kMagic), as_h2(x[5]), a1, false);
-      a4 = __builtin_amdgcn_fdot2(as_h2((t & 0x000C000Cu) | kMagic), as_h2(x[6]), a4, false);
-      a16 = __builtin_amdgcn_fdot2(as_h2((t & 0x00300030u) | kMagic), as_h2(x[7]), a16, false);
+      a1 = __builtin_amdgcn_fdot2(as_h2((v & R.m[0]) | R.magic), as_h2(x[0]), a1, false);
+      a4 = __builtin_amdgcn_fdot2(as_h2((v & R.m[1]) | R.magic), as_h2(x[1]), a4, false);
+      a16 = __builtin_amdgcn_fdot2(as_h2((v & R.m[2]) | R.magic), as_h2(x[2]), a16, false);
+      a64 = __builtin_amdgcn_fdot2(as_h2((v & R.m[3]) | R.magic), as_h2(x[3]), a64, false);
+      a256 = __builtin_amdgcn_fdot2(as_h2((v & R.m[4]) | R.magic), as_h2(x[4]), a256, false);
+      a1 = __builtin_amdgcn_fdot2(as_h2((t & R.m[0]) | R.magic), as_h2(x[5]), a1, false);
+      a4 = __builtin_amdgcn_fdot2(as_h2((t & R.m[1]) | R.magic), as_h2(x[6]), a4, false);
+      a16 = __builtin_amdgcn_fdot2(as_h2((t & R.m[2]) | R.magic), as_h2(x[7]), a16, false);
     }
     return fmaf(a256, 0.00390625f, fmaf(a64, 0.015625f, fmaf(a16, 0.0625f, fmaf(a4, 0.25f, a1))));
   }
@@ -159,22 +193,19 @@ struct Codec<kFmtTern> {
 template <>
 struct Codec<kFmtBin> {
   static constexpr int WPC = 128, XR = 4, XB = 16, CPG = 1, MB = 0;
+  struct Regs {};
+  __device__ static Regs make() { return {}; }
   __device__ static void prep(const uint32_t* raw, uint32_t* xr) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) xr[i] = raw[i];
   }
-  __device__ static int dot(u32x4 q, const uint32_t* xr) {
+  __device__ static int dot(u32x4 q, const uint32_t* xr, const Regs&) {
     int acc = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) acc += __builtin_popcount(q[w] ^ xr[w]);
     return acc;
   }
 };
-
-template <int FMT>
-constexpr int max_passes() {
-  return FMT == kFmtBin ? 8 : (FMT == kFmtTern ? 3 : 4);
-}
 
 // ------------------------------------------------------------ tile runner --
 struct Tile {
@@ -190,82 +221,91 @@ struct Tile {
 constexpr uint32_t kFar = 0x80000000u;  // offset past any buffer, no wrap
 
 template <int FMT, int J, int U>
-__device__ __forceinline__ void run_tile(const Tile& t, uint32_t* part) {
+struct Runner {
   using Cd = Codec<FMT>;
-  constexpr bool kBin = FMT == kFmtBin;
+  static constexpr bool kBin = FMT == kFmtBin;
   using Acc = typename std::conditional<kBin, int, float>::type;
 
-  // Fixed chunk positions of this lane, its slice of x, and the constants.
+  struct Buf {
+    u32x4 c[U][J];
+    uint32_t m[U][J];
+  };
+
+  const Tile& t;
+  typename Cd::Regs R;
   uint32_t cof[J], mof[J];
   uint32_t xr[J][Cd::XR];
   float bias[J], xsum[J];
-  const int L = 1 << t.lg;
+
+  __device__ __forceinline__ Runner(const Tile& tile) : t(tile), R(Cd::make()) {
+    // Fixed chunk positions of this lane, its slice of x, and the constants.
+    const int L = 1 << t.lg;
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int local = t.sub + L * j;
-    const int c = t.slice * t.Cs + local;
-    const bool ok = local < t.Cs && c < t.C;
-    cof[j] = ok ? (uint32_t)c * 16u : kFar;
-    mof[j] = ok ? (uint32_t)(c / Cd::CPG) * Cd::MB : kFar;
-    uint32_t raw[Cd::XR];
+    for (int j = 0; j < J; ++j) {
+      const int local = t.sub + L * j;
+      const int c = t.slice * t.Cs + local;
+      const bool ok = local < t.Cs && c < t.C;
+      cof[j] = ok ? (uint32_t)c * 16u : kFar;
+      mof[j] = ok ? (uint32_t)(c / Cd::CPG) * Cd::MB : kFar;
+      uint32_t raw[Cd::XR];
 #pragma unroll
-    for (int i = 0; i < Cd::XR / 4; ++i) {
-      const u32x4 v = load16(t.x, ok ? (uint32_t)c * Cd::XB + 16u * i : kFar);
-      raw[4 * i + 0] = v[0];
-      raw[4 * i + 1] = v[1];
-      raw[4 * i + 2] = v[2];
-      raw[4 * i + 3] = v[3];
-    }
-    Cd::prep(raw, xr[j]);
-    if constexpr (!kBin) {
-      const u32x4 zc = {Cd::kZero, Cd::kZero, Cd::kZero, Cd::kZero};
-      bias[j] = Cd::dot(zc, xr[j]);
-      float sx = 0.0f;
+      for (int i = 0; i < Cd::XR / 4; ++i) {
+        const u32x4 v = load16(t.x, ok ? (uint32_t)c * Cd::XB + 16u * i : kFar);
+        raw[4 * i + 0] = v[0];
+        raw[4 * i + 1] = v[1];
+        raw[4 * i + 2] = v[2];
+        raw[4 * i + 3] = v[3];
+      }
+      Cd::prep(raw, xr[j]);
+      if constexpr (!kBin) {
+        const u32x4 zc = {Cd::kZero, Cd::kZero, Cd::kZero, Cd::kZero};
+        bias[j] = Cd::dot(zc, xr[j], R);
+        float sx = 0.0f;
 #pragma unroll
-      for (int i = 0; i < Cd::XR; ++i) sx = __builtin_amdgcn_fdot2(as_h2(xr[j][i]), as_h2(0x3C003C00u), sx, false);
-      xsum[j] = sx;
+        for (int i = 0; i < Cd::XR; ++i) sx = __builtin_amdgcn_fdot2(as_h2(xr[j][i]), as_h2(0x3C003C00u), sx, false);
+        xsum[j] = sx;
+      }
     }
   }
 
-  auto issue = [&](int st, u32x4 (&cw)[U][J], uint32_t (&mw)[U][J]) {
+  __device__ __forceinline__ uint32_t row(int st, int u) const {
+    return (uint32_t)(t.rbase + (st + u) * t.P + t.prow);
+  }
+
+  __device__ __forceinline__ void issue(int st, Buf& b) const {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t r = (uint32_t)(t.rbase + (st + u) * t.P + t.prow);
+      const uint32_t r = row(st, u);
       const uint32_t rb = r * t.row_bytes, mb = r * t.meta_row_bytes;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        cw[u][j] = load16_nt(t.codes, rb + cof[j]);
-        if constexpr (Cd::MB == 4) mw[u][j] = load4(t.meta, mb + mof[j]);
-        else if constexpr (Cd::MB == 2) mw[u][j] = load2(t.meta, mb + mof[j]);
-        else mw[u][j] = 0;
+        b.c[u][j] = load16_nt(t.codes, rb + cof[j]);
+        if constexpr (Cd::MB == 4) b.m[u][j] = load4(t.meta, mb + mof[j]);
+        else if constexpr (Cd::MB == 2) b.m[u][j] = load2(t.meta, mb + mof[j]);
+        else b.m[u][j] = 0;
       }
     }
-  };
+  }
 
-  u32x4 cw[U][J];
-  uint32_t mw[U][J];
-  issue(0, cw, mw);
-  for (int st = 0; st < t.steps; st += U) {
-    u32x4 nc[U][J];
-    uint32_t nm[U][J];
-    if (st + U < t.steps) issue(st + U, nc, nm);
+  __device__ __forceinline__ void compute(int st, const Buf& b, uint32_t* part) const {
+    const int L = 1 << t.lg;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       Acc res = 0;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         if constexpr (kBin) {
-          res += Cd::dot(cw[u][j], xr[j]);
+          res += Cd::dot(b.c[u][j], xr[j], R);
         } else if constexpr (FMT == kFmtInt4) {
-          const float d = Cd::dot(cw[u][j], xr[j]) - bias[j];
-          res = fmaf(half_lo(mw[u][j]), fmaf(-half_hi(mw[u][j]), xsum[j], d), res);
+          const float d = Cd::dot(b.c[u][j], xr[j], R) - bias[j];
+          res = fmaf(half_lo(b.m[u][j]), fmaf(-half_hi(b.m[u][j]), xsum[j], d), res);
         } else {
-          const float d = Cd::dot(cw[u][j], xr[j]) - bias[j];
-          res = fmaf(half_lo(mw[u][j]), d, res);
+          const float d = Cd::dot(b.c[u][j], xr[j], R) - bias[j];
+          res = fmaf(half_lo(b.m[u][j]), d, res);
         }
       }
       const Acc v = group_sum(res, t.lg);
-      const uint32_t r = (uint32_t)(t.rbase + (st + u) * t.P + t.prow);
+      const uint32_t r = row(st, u);
       if (t.sub == L - 1) {
         if (t.S == 1) {
           if constexpr (kBin) store4(t.y, r * 4u, (uint32_t)(t.K - 2 * v));
@@ -276,26 +316,40 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint32_t* part) {
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        cw[u][j] = nc[u][j];
-        mw[u][j] = nm[u][j];
-      }
   }
+
+  // Two buffers used alternately: the loads of step st + U are in flight
+  // while step st is computed.
+  __device__ __forceinline__ void run(uint32_t* part) {
+    Buf a, b;
+    issue(0, a);
+    for (int st = 0; st < t.steps; st += 2 * U) {
+      if (st + U < t.steps) issue(st + U, b);
+      compute(st, a, part);
+      if (st + U >= t.steps) break;
+      if (st + 2 * U < t.steps) issue(st + 2 * U, a);
+      compute(st + U, b, part);
+    }
+  }
+};
+
+// Row steps handled per loop iteration for J passes (keeps ~4 chunks per
+// lane in flight); must match the host planner's rounding.
+template <int J>
+constexpr int unroll_for() {
+  return J == 1 ? 4 : (J == 2 ? 2 : 1);
 }
 
 template <int FMT, int J>
 __device__ __forceinline__ void run_passes(const Tile& t, uint32_t* part) {
-  if constexpr (J <= max_passes<FMT>()) {
-    constexpr int U = J == 1 ? 4 : (J == 2 ? 2 : 1);
-    run_tile<FMT, J, U>(t, part);
-  }
+  Runner<FMT, J, unroll_for<J>()> r(t);
+  r.run(part);
 }
 
 // ------------------------------------------------------------------ kernel --
-template <int FMT>
+// JMAX: the largest pass count among the launch's descriptors; only the
+// cases up to it are instantiated, so registers match the workload.
+template <int FMT, int JMAX>
 __global__ __launch_bounds__(256) void gemv_kernel(const tkq_gemv_desc* __restrict__ descs, int count) {
   using Cd = Codec<FMT>;
   constexpr bool kBin = FMT == kFmtBin;
@@ -344,14 +398,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(const tkq_gemv_desc* __restri
   t.y = make_rsrc((char*)d->y + (size_t)row0 * ybytes, (uint32_t)nrows * ybytes);
 
   switch (sh.passes) {
-    case 1: run_passes<FMT, 1>(t, part); break;
-    case 2: run_passes<FMT, 2>(t, part); break;
-    case 3: run_passes<FMT, 3>(t, part); break;
-    case 4: run_passes<FMT, 4>(t, part); break;
-    case 5: run_passes<FMT, 5>(t, part); break;
-    case 6: run_passes<FMT, 6>(t, part); break;
-    case 7: run_passes<FMT, 7>(t, part); break;
-    case 8: run_passes<FMT, 8>(t, part); break;
+#define TKQ_CASE(J)                                         \
+  case J:                                                   \
+    if constexpr (J <= JMAX) run_passes<FMT, J>(t, part); \
+    break;
+    TKQ_CASE(1)
+    TKQ_CASE(2)
+    TKQ_CASE(3)
+    TKQ_CASE(4)
+    TKQ_CASE(5)
+    TKQ_CASE(6)
+    TKQ_CASE(7)
+    TKQ_CASE(8)
+#undef TKQ_CASE
     default: break;
   }
 
@@ -371,6 +430,25 @@ __global__ __launch_bounds__(256) void gemv_kernel(const tkq_gemv_desc* __restri
   }
 }
 
+template <int FMT>
+constexpr int max_passes() {
+  return FMT == kFmtBin ? 8 : (FMT == kFmtTern ? 3 : 4);
+}
+
+typedef void (*GemvFn)(const tkq_gemv_desc*, int);
+
+template <int FMT>
+GemvFn pick(int jmax) {
+  switch (jmax) {
+    case 1: return gemv_kernel<FMT, 1>;
+    case 2: return gemv_kernel<FMT, 2>;
+    case 3: return gemv_kernel<FMT, 3>;
+    case 4: return gemv_kernel<FMT, 4>;
+  }
+  if constexpr (max_passes<FMT>() > 4) return gemv_kernel<FMT, max_passes<FMT>()>;
+  return nullptr;
+}
+
 }  // namespace
 
 int gemv_max_passes(int fmt) {
@@ -383,16 +461,17 @@ int gemv_max_passes(int fmt) {
   return 0;
 }
 
-hipError_t launch_gemv(int fmt, const tkq_gemv_desc* dev_descs, int count, int64_t tiles,
+hipError_t launch_gemv(int fmt, int jmax, const tkq_gemv_desc* dev_descs, int count, int64_t tiles,
                        hipStream_t stream) {
-  const dim3 grid((uint32_t)tiles), block(64 * kWaves);
+  GemvFn fn = nullptr;
   switch (fmt) {
-    case kFmtInt4: hipLaunchKernelGGL(gemv_kernel<kFmtInt4>, grid, block, 0, stream, dev_descs, count); break;
-    case kFmtK5: hipLaunchKernelGGL(gemv_kernel<kFmtK5>, grid, block, 0, stream, dev_descs, count); break;
-    case kFmtTern: hipLaunchKernelGGL(gemv_kernel<kFmtTern>, grid, block, 0, stream, dev_descs, count); break;
-    case kFmtBin: hipLaunchKernelGGL(gemv_kernel<kFmtBin>, grid, block, 0, stream, dev_descs, count); break;
-    default: return hipErrorInvalidValue;
+    case kFmtInt4: fn = pick<kFmtInt4>(jmax); break;
+    case kFmtK5: fn = pick<kFmtK5>(jmax); break;
+    case kFmtTern: fn = pick<kFmtTern>(jmax); break;
+    case kFmtBin: fn = pick<kFmtBin>(jmax); break;
   }
+  if (!fn) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fn, dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream, dev_descs, count);
   return hipGetLastError();
 }
 

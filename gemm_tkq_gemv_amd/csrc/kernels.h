@@ -40,7 +40,8 @@ constexpr int kGemvMaxTileRows = 1024;
 
 // Largest `passes` value each kernel variant supports (x stays in registers).
 int gemv_max_passes(int fmt);
-hipError_t launch_gemv(int fmt, const tkq_gemv_desc* dev_descs, int count, int64_t tiles,
+// jmax: largest `passes` among the descriptors (selects the kernel variant).
+hipError_t launch_gemv(int fmt, int jmax, const tkq_gemv_desc* dev_descs, int count, int64_t tiles,
                        hipStream_t stream);
 
 hipError_t launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* codes, void* meta,

@@ -148,6 +148,7 @@ int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan) {
       return TKQ_EALIGN;
   }
   int64_t work = 0;
+  int jmax = 1;
   for (int32_t i = 0; i < count; ++i) {
     tkq_gemv_desc& d = descs[i];
     const tkq::GemvShape sh = choose_shape(fmt, d.K);
@@ -161,11 +162,12 @@ int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan) {
     d.shape = tkq::pack_shape(sh);
     d.reserved = 0;
     work += tiles;
+    if (sh.passes > jmax) jmax = sh.passes;
   }
   plan->fmt = fmt;
   plan->count = count;
   plan->tiles = work;
-  plan->variant = fmt;
+  plan->variant = jmax;
   plan->magic = kPlanMagic;
   plan->reserved = 0;
   return TKQ_OK;
@@ -174,10 +176,10 @@ int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan) {
 int tkq_gemv(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs, void* stream) {
   if (!plan || !dev_descs) return TKQ_EINVAL;
   if (plan->magic != kPlanMagic || !known_fmt(plan->fmt) || plan->count < 1 || plan->tiles < 1 ||
-      plan->tiles > INT32_MAX)
+      plan->tiles > INT32_MAX || plan->variant < 1 || plan->variant > tkq::gemv_max_passes(plan->fmt))
     return TKQ_EPLAN;
   if (!aligned16(dev_descs)) return TKQ_EALIGN;
-  return hip_status(tkq::launch_gemv(plan->fmt, dev_descs, plan->count, plan->tiles,
+  return hip_status(tkq::launch_gemv(plan->fmt, plan->variant, dev_descs, plan->count, plan->tiles,
                                      (hipStream_t)stream));
 }
 

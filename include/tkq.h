@@ -167,7 +167,7 @@ typedef struct tkq_gemv_plan {
   int32_t fmt;        /* common coding of the descriptors                   */
   int32_t count;      /* number of descriptors                              */
   int64_t tiles;      /* total row tiles = workgroups per launch            */
-  int32_t variant;    /* kernel variant chosen for the descriptors          */
+  int32_t variant;    /* largest pass count: selects the kernel variant     */
   int32_t magic;      /* set by tkq_gemv_prepare                            */
   int64_t reserved;
 } tkq_gemv_plan;
