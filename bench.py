@@ -85,19 +85,46 @@ def rotated_batches(torch, tkq, fmt, items, footprint):
     return batches
 
 
-def time_steps(torch, run_step, steps, warmup):
+def time_steps(torch, run_step, steps, warmup, graph="none", period=1):
     """Warm up, then time exactly `steps` steps between synchronisations with
-    HIP events recorded on the stream the kernels are launched on."""
+    HIP events recorded on the stream the kernels are launched on.
+
+    graph="step": each of the `period` distinct steps (rotation copies) is
+    captured once as a HIP graph and step s replays graph s % period;
+    graph="all": the `steps` timed steps are captured as one graph that is
+    replayed once inside the timed region (warm-up steps run eagerly)."""
     for s in range(warmup):
         run_step(s)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for s in range(steps):
-        run_step(s)
-    end.record(stream)
+    if graph == "none":
+        start.record(stream)
+        for s in range(steps):
+            run_step(s)
+        end.record(stream)
+    elif graph == "step":
+        graphs = []
+        for p in range(period):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_step(p)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for s in range(steps):
+            graphs[s % period].replay()
+        end.record(stream)
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in range(steps):
+                run_step(s)
+        torch.cuda.synchronize()
+        start.record(stream)
+        g.replay()
+        end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps  # ms per step
 
@@ -163,7 +190,8 @@ def run_sweep(args, torch, tkq, inputs, model, fmt):
                     + (0 if it["meta"] is None else it["meta"].numel() * it["meta"].element_size())
                     for it in items)
     batches = rotated_batches(torch, tkq, fmt, items, footprint)
-    ms = time_steps(torch, lambda s: batches[s % len(batches)].run(), args.steps, args.warmup)
+    ms = time_steps(torch, lambda s: batches[s % len(batches)].run(), args.steps, args.warmup,
+                    args.graph, len(batches))
     gbs = step_bytes / (ms * 1e-3) / 1e9
     ceiling_tok_s = HBM_PEAK_GBS * 1e9 / step_bytes
     out = {
@@ -175,7 +203,8 @@ def run_sweep(args, torch, tkq, inputs, model, fmt):
         "config": {"workload": "%s decode weight sweep, %s, %d GEMVs in one launch, batch 1"
                                % (model, _fmt_name(fmt), len(shapes)),
                    "bytes_per_step": step_bytes, "copies_rotated": len(batches),
-                   "weights": _fmt_name(fmt), "x": "fp16", "accumulate": "fp32", "y": "fp16"},
+                   "weights": _fmt_name(fmt), "x": "fp16", "accumulate": "fp32", "y": "fp16",
+                   "launch": "hip graph replay" if args.graph != "none" else "stream launch"},
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tok_s": round(1000.0 / ms, 1), "ceiling_tok_s": round(ceiling_tok_s, 1),
         "frac_of_ceiling": round((1000.0 / ms) / ceiling_tok_s, 4),
@@ -230,7 +259,7 @@ def run_single(args, torch, tkq, inputs):
     y = torch.empty(896, dtype=torch.float16, device="cuda")
     batch = tkq.GemvBatch("int4", [dict(codes=codes, meta=meta, x=torch.from_numpy(x).cuda(), y=y,
                                         N=896, K=896)])
-    ms = time_steps(torch, lambda s: batch.run(), args.steps, args.warmup)
+    ms = time_steps(torch, lambda s: batch.run(), args.steps, args.warmup, args.graph, 1)
     b = _fmt_bytes("int4")(896, 896)
     return {"metric": "single int4-g128 896x896 GEMV latency", "value": round(ms * 1000, 3),
             "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -292,8 +321,13 @@ def main():
     ap.add_argument("--workload", default="0.5b-int4",
                     choices=["0.5b-int4", "0.5b-k5", "0.5b-tern", "bin", "single-896", "7b-int4",
                              "7b-prefill", "probe"])
+    ap.add_argument("--graph", default="none", choices=["none", "step", "all"],
+                    help="launch steps as HIP graph replays (see time_steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before anything else, copy a MIB-sized device buffer once (a kernel of "
+                         "known traffic for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--traffic", type=float, default=None,
                     help="HBM bytes per launch from rocprofv3 FETCH_SIZE+WRITE_SIZE (scaled)")
     args = ap.parse_args()
@@ -310,6 +344,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     tkq.lib()
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration << 18, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     w = args.workload
     if w in ("0.5b-int4", "0.5b-k5", "0.5b-tern", "7b-int4"):

@@ -41,8 +41,16 @@ namespace tkq {
 
 namespace {
 
+#ifndef TKQ_GEMV_PINGPONG
+#define TKQ_GEMV_PINGPONG 0
+#endif
+#ifndef TKQ_GEMV_WPE
+#define TKQ_GEMV_WPE 1  // minimum waves per SIMD the register budget must allow
+#endif
+
 constexpr int kWaves = 4;
 constexpr int kMaxTileRows = kGemvMaxTileRows;
+static_assert(sizeof(tkq_gemv_desc) == 64, "descriptor layout");
 constexpr uint32_t kMagic = 0x64006400u;  // fp16 pair (1024.0, 1024.0)
 
 // Constants held in registers.  A gfx9 VOP3 instruction (v_and_or_b32,
@@ -238,7 +246,7 @@ struct Runner {
   float bias[J], xsum[J];
 
   __device__ __forceinline__ Runner(const Tile& tile) : t(tile), R(Cd::make()) {
-    // Fixed chunk positions of this lane, its slice of x, and the constants.
+    // Fixed chunk positions of this lane.
     const int L = 1 << t.lg;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -247,10 +255,18 @@ struct Runner {
       const bool ok = local < t.Cs && c < t.C;
       cof[j] = ok ? (uint32_t)c * 16u : kFar;
       mof[j] = ok ? (uint32_t)(c / Cd::CPG) * Cd::MB : kFar;
+    }
+  }
+
+  // This lane's slice of x, permuted for the unpack, and its constants.
+  __device__ __forceinline__ void load_x() {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint32_t xo = cof[j] == kFar ? kFar : (cof[j] / 16u) * (uint32_t)Cd::XB;
       uint32_t raw[Cd::XR];
 #pragma unroll
       for (int i = 0; i < Cd::XR / 4; ++i) {
-        const u32x4 v = load16(t.x, ok ? (uint32_t)c * Cd::XB + 16u * i : kFar);
+        const u32x4 v = load16(t.x, xo == kFar ? kFar : xo + 16u * i);
         raw[4 * i + 0] = v[0];
         raw[4 * i + 1] = v[1];
         raw[4 * i + 2] = v[2];
@@ -318,11 +334,13 @@ struct Runner {
     }
   }
 
-  // Two buffers used alternately: the loads of step st + U are in flight
-  // while step st is computed.
   __device__ __forceinline__ void run(uint32_t* part) {
+#if TKQ_GEMV_PINGPONG
+    // Two buffers used alternately: the loads of step st + U are in flight
+    // while step st is computed.
     Buf a, b;
-    issue(0, a);
+    issue(0, a);  // the first codes stream in while x is prepared
+    load_x();
     for (int st = 0; st < t.steps; st += 2 * U) {
       if (st + U < t.steps) issue(st + U, b);
       compute(st, a, part);
@@ -330,19 +348,23 @@ struct Runner {
       if (st + 2 * U < t.steps) issue(st + 2 * U, a);
       compute(st + U, b, part);
     }
+#else
+    // One buffer: U row steps are loaded, then computed; the other waves of
+    // the CU keep the memory system busy meanwhile.
+    Buf a;
+    issue(0, a);  // the first codes stream in while x is prepared
+    load_x();
+    for (int st = 0; st < t.steps; st += U) {
+      if (st > 0) issue(st, a);
+      compute(st, a, part);
+    }
+#endif
   }
 };
 
-// Row steps handled per loop iteration for J passes (keeps ~4 chunks per
-// lane in flight); must match the host planner's rounding.
-template <int J>
-constexpr int unroll_for() {
-  return J == 1 ? 4 : (J == 2 ? 2 : 1);
-}
-
 template <int FMT, int J>
 __device__ __forceinline__ void run_passes(const Tile& t, uint32_t* part) {
-  Runner<FMT, J, unroll_for<J>()> r(t);
+  Runner<FMT, J, gemv_unroll(J)> r(t);
   r.run(part);
 }
 
@@ -350,12 +372,13 @@ __device__ __forceinline__ void run_passes(const Tile& t, uint32_t* part) {
 // JMAX: the largest pass count among the launch's descriptors; only the
 // cases up to it are instantiated, so registers match the workload.
 template <int FMT, int JMAX>
-__global__ __launch_bounds__(256) void gemv_kernel(const tkq_gemv_desc* __restrict__ descs, int count) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WPE, 8))) void gemv_kernel(const tkq_gemv_desc* __restrict__ descs, int count) {
   using Cd = Codec<FMT>;
   constexpr bool kBin = FMT == kFmtBin;
   __shared__ uint32_t part[kWaves * kMaxTileRows];
 
-  // The matrix this workgroup works on: last descriptor with work0 <= tile.
+  // The matrix this workgroup works on: last descriptor with work0 <= tile
+  // (binary search; the loads hit the scalar cache after the first few).
   const int tile = blockIdx.x;
   int lo = 0, hi = count - 1;
   while (lo < hi) {

@@ -38,6 +38,22 @@ inline int weights_per_chunk(int fmt) {
 // Largest row tile of one GEMV workgroup (bounds the k-slice LDS buffer).
 constexpr int kGemvMaxTileRows = 1024;
 
+// Row steps a wave keeps in flight per loop iteration for J passes: deep
+// enough that every CU has ~100 KB of loads outstanding.  Used by the kernel
+// and by the planner (tile heights are multiples of it).
+#ifndef TKQ_GEMV_U1
+#define TKQ_GEMV_U1 4
+#endif
+#ifndef TKQ_GEMV_U2
+#define TKQ_GEMV_U2 2
+#endif
+#ifndef TKQ_GEMV_U3
+#define TKQ_GEMV_U3 1
+#endif
+__host__ __device__ constexpr int gemv_unroll(int passes) {
+  return passes == 1 ? TKQ_GEMV_U1 : (passes == 2 ? TKQ_GEMV_U2 : TKQ_GEMV_U3);
+}
+
 // Largest `passes` value each kernel variant supports (x stays in registers).
 int gemv_max_passes(int fmt);
 // jmax: largest `passes` among the descriptors (selects the kernel variant).

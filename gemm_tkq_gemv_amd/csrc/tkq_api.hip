@@ -13,7 +13,10 @@ constexpr int64_t kMaxWeights = int64_t(1) << 39;
 // Bytes of codes one wave aims to stream per tile: large enough to amortise
 // the per-tile setup (descriptor search, x slice, constants), small enough
 // that the last workgroups of a launch finish close together.
-constexpr int64_t kTileTargetBytes = 12 * 1024;
+#ifndef TKQ_TILE_BYTES
+#define TKQ_TILE_BYTES (24 * 1024)
+#endif
+constexpr int64_t kTileTargetBytes = TKQ_TILE_BYTES;
 constexpr int kMaxTileRows = tkq::kGemvMaxTileRows;
 
 int hip_status(hipError_t e) {
@@ -83,7 +86,7 @@ int rows_per_tile(int fmt, int N, int K, tkq::GemvShape sh) {
   const int Cs = (C + sh.kslices - 1) / sh.kslices;
   const int P = 64 >> sh.lanes_log2;       // rows per wave step
   const int RG = 4 / sh.kslices;           // row groups per workgroup
-  const int U = sh.passes == 1 ? 4 : (sh.passes == 2 ? 2 : 1);  // steps per iteration
+  const int U = tkq::gemv_unroll(sh.passes);  // steps per loop iteration
   const int64_t step_bytes = int64_t(P) * Cs * 16;
   int64_t steps = (kTileTargetBytes + step_bytes - 1) / step_bytes;
   const int64_t need = ((int64_t(N) + RG - 1) / RG + P - 1) / P;  // steps to cover N
