@@ -9,7 +9,10 @@
 //  * Work unit.  One workgroup (4 wave64s) owns a tile of consecutive rows of
 //    one matrix; the grid is the concatenation of every matrix's tiles, and a
 //    workgroup finds its matrix by binary search over the descriptors'
-//    first-tile indices (scalar loads).
+//    first-tile indices (scalar loads).  Tiles are large (~24 KB per wave,
+//    amortising the per-tile setup) except over the last stretch of the
+//    sweep, where small tiles let the final workgroups finish together
+//    instead of trailing one large tile's duration behind each other.
 //  * Lanes.  L = 2^lg lanes share a row; lane `sub` of the group reads the
 //    row's 16-byte chunks sub, sub+L, ... (J "passes"), so every load
 //    instruction of the wave reads whole rows front to back: contiguous,
@@ -387,7 +390,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WP
     else hi = mid - 1;
   }
   const tkq_gemv_desc* d = descs + lo;
-  const int N = d->N, K = d->K, rpt = d->rows_per_tile;
+  const int N = d->N, K = d->K;
+  // Large tiles first, then small tiles for the rest of the matrix.
+  const int local = tile - d->work0, nbig = d->big_tiles;
+  const int rpt = local < nbig ? d->rows_per_tile : d->small_rows;
+  const int row0 = local < nbig ? local * rpt : nbig * d->rows_per_tile + (local - nbig) * rpt;
   const GemvShape sh = unpack_shape(d->shape);
 
   Tile t;
@@ -406,7 +413,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WP
   t.Cs = (t.C + t.S - 1) / t.S;
   t.row_bytes = (uint32_t)t.C * 16u;
   t.meta_row_bytes = (uint32_t)(K / 128) * Cd::MB;
-  const int row0 = (tile - d->work0) * rpt;
   const int nrows = min(rpt, N - row0);
   const char* codes = (const char*)d->codes + (size_t)row0 * t.row_bytes;
   t.codes = make_rsrc(codes, (uint32_t)nrows * t.row_bytes);

@@ -16,7 +16,15 @@ constexpr int64_t kMaxWeights = int64_t(1) << 39;
 #ifndef TKQ_TILE_BYTES
 #define TKQ_TILE_BYTES (24 * 1024)
 #endif
-constexpr int64_t kTileTargetBytes = TKQ_TILE_BYTES;
+// The last TKQ_TAIL_BYTES of a sweep use tiles of TKQ_SMALL_TILE_BYTES per
+// wave: about two rounds of small tiles for every workgroup slot of a
+// 256-CU part, so the launch ends with short tiles.
+#ifndef TKQ_SMALL_TILE_BYTES
+#define TKQ_SMALL_TILE_BYTES (4 * 1024)
+#endif
+#ifndef TKQ_TAIL_BYTES
+#define TKQ_TAIL_BYTES (40 << 20)
+#endif
 constexpr int kMaxTileRows = tkq::kGemvMaxTileRows;
 
 int hip_status(hipError_t e) {
@@ -81,7 +89,7 @@ tkq::GemvShape choose_shape(int fmt, int K) {
   return best;
 }
 
-int rows_per_tile(int fmt, int N, int K, tkq::GemvShape sh) {
+int rows_per_tile(int fmt, int N, int K, tkq::GemvShape sh, int64_t kTileTargetBytes) {
   const int C = K / tkq::weights_per_chunk(fmt);
   const int Cs = (C + sh.kslices - 1) / sh.kslices;
   const int P = 64 >> sh.lanes_log2;       // rows per wave step
@@ -150,21 +158,36 @@ int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan) {
         (fmt != TKQ_FMT_BIN && !aligned16(d.meta)))
       return TKQ_EALIGN;
   }
-  int64_t work = 0;
+  // Sweep position where the small-tile tail begins.
+  int64_t total = 0;
+  for (int32_t i = 0; i < count; ++i)
+    total += int64_t(descs[i].N) * (descs[i].K / tkq::weights_per_chunk(fmt)) * 16;
+  const int64_t tail_start = total > TKQ_TAIL_BYTES ? total - TKQ_TAIL_BYTES : 0;
+
+  int64_t work = 0, pos = 0;
   int jmax = 1;
   for (int32_t i = 0; i < count; ++i) {
     tkq_gemv_desc& d = descs[i];
     const tkq::GemvShape sh = choose_shape(fmt, d.K);
     if (sh.passes < 1) return TKQ_ESHAPE;
-    const int rpt = rows_per_tile(fmt, d.N, d.K, sh);
-    const int64_t tiles = (int64_t(d.N) + rpt - 1) / rpt;
+    const int big = rows_per_tile(fmt, d.N, d.K, sh, TKQ_TILE_BYTES);
+    const int small = rows_per_tile(fmt, d.N, d.K, sh, TKQ_SMALL_TILE_BYTES);
+    const int64_t row_bytes = int64_t(d.K / tkq::weights_per_chunk(fmt)) * 16;
+    // rows above the tail start get large tiles
+    int64_t big_rows = 0;
+    if (pos + d.N * row_bytes <= tail_start) big_rows = d.N;
+    else if (pos < tail_start) big_rows = (tail_start - pos + row_bytes - 1) / row_bytes;
+    const int64_t nbig = (big_rows + big - 1) / big;
+    const int64_t rest = int64_t(d.N) - nbig * big;
+    const int64_t tiles = nbig + (rest > 0 ? (rest + small - 1) / small : 0);
     if (work + tiles > INT32_MAX) return TKQ_ESHAPE;
     d.work0 = (int32_t)work;
-    d.tiles = (int32_t)tiles;
-    d.rows_per_tile = rpt;
+    d.big_tiles = (int32_t)nbig;
+    d.rows_per_tile = big;
     d.shape = tkq::pack_shape(sh);
-    d.reserved = 0;
+    d.small_rows = small;
     work += tiles;
+    pos += d.N * row_bytes;
     if (sh.passes > jmax) jmax = sh.passes;
   }
   plan->fmt = fmt;

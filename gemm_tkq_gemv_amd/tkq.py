@@ -41,9 +41,9 @@ class TkqError(RuntimeError):
 class GemvDesc(ctypes.Structure):
     """tkq_gemv_desc (64 bytes)."""
     _fields_ = [("fmt", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
-                ("work0", ctypes.c_int32), ("tiles", ctypes.c_int32),
+                ("work0", ctypes.c_int32), ("big_tiles", ctypes.c_int32),
                 ("rows_per_tile", ctypes.c_int32), ("shape", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("codes", ctypes.c_void_p),
+                ("small_rows", ctypes.c_int32), ("codes", ctypes.c_void_p),
                 ("meta", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 

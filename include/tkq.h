@@ -151,11 +151,13 @@ typedef struct tkq_gemv_desc {
   int32_t N;             /* rows = length of y, >= 1                        */
   int32_t K;             /* columns = length of x, multiple of 128          */
   int32_t work0;         /* [prepare] index of the first row tile           */
-  int32_t tiles;         /* [prepare] number of row tiles                   */
-  int32_t rows_per_tile; /* [prepare] rows handled by one workgroup         */
+  int32_t big_tiles;     /* [prepare] number of large tiles (rows_per_tile
+                                      rows each) at the top of the matrix   */
+  int32_t rows_per_tile; /* [prepare] rows of a large tile                  */
   int32_t shape;         /* [prepare] lanes-per-row log2 | passes<<4 |
                                       k-slices<<12                          */
-  int32_t reserved;      /* [prepare] zero                                  */
+  int32_t small_rows;    /* [prepare] rows of a small tile; small tiles
+                                      cover the rows below the large ones   */
   const void* codes;     /* packed codes (layout per fmt)                   */
   const void* meta;      /* int4: uint32 half2 [N][K/128]; K5, ternary: fp16
                             [N][K/128]; binary: ignored (may be NULL)       */

@@ -95,6 +95,18 @@ def _shape(d):
     return 1 << (d.shape & 15), (d.shape >> 4) & 255, (d.shape >> 12) & 15
 
 
+def _tiles(d):
+    """Row ranges of a prepared descriptor's tiles: large, then small."""
+    out, r = [], 0
+    for _ in range(d.big_tiles):
+        out.append((r, d.rows_per_tile))
+        r += d.rows_per_tile
+    while r < d.N:
+        out.append((r, d.small_rows))
+        r += d.small_rows
+    return out
+
+
 @pytest.mark.parametrize("fmt", [1, 2, 3, 4])
 def test_prepare_tiles_cover_rows(fmt):
     shapes = [(1, 128), (7, 896), (128, 896), (4864, 896), (896, 4864), (333, 4864), (151936, 896)]
@@ -102,19 +114,27 @@ def test_prepare_tiles_cover_rows(fmt):
     st, plan = _prepare(arr)
     assert st == tkq.OK
     work = 0
+    per_chunk = {1: 32, 2: 16, 3: 64, 4: 128}[fmt]
     for d, (n, k) in zip(arr, shapes):
         assert d.work0 == work
-        assert d.tiles * d.rows_per_tile >= n > (d.tiles - 1) * d.rows_per_tile
+        tiles = _tiles(d)
+        # tiles are disjoint, in order, and cover rows 0..N-1 (the last may overhang)
+        assert tiles[0][0] == 0 and tiles[-1][0] < n <= tiles[-1][0] + tiles[-1][1]
+        for (r0, h0), (r1, _) in zip(tiles, tiles[1:]):
+            assert r1 == r0 + h0
         L, J, S = _shape(d)
-        per_chunk = {1: 32, 2: 16, 3: 64, 4: 128}[fmt]
         C = k // per_chunk
         assert S in (1, 2, 4) and 1 <= J <= 8
         assert S * L * J >= C                       # every chunk has a lane
         P = 64 // L
-        assert d.rows_per_tile % ((4 // S) * P) == 0
-        assert d.rows_per_tile <= 1024
-        work += d.tiles
+        for h in (d.rows_per_tile, d.small_rows):
+            assert h % ((4 // S) * P) == 0 and 0 < h <= 1024
+        assert d.small_rows <= d.rows_per_tile
+        work += len(tiles)
     assert plan.tiles == work and plan.count == len(shapes) and plan.fmt == fmt
+    # the last stretch of a long sweep is cut into small tiles
+    last = arr[len(shapes) - 1]
+    assert last.big_tiles * last.rows_per_tile < last.N
 
 
 def test_prepare_shapes_for_model_matrices():
