@@ -26,6 +26,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -293,29 +295,37 @@ def run_single(args, torch, tkq, inputs):
 
 
 def run_prefill(args, torch, tkq, inputs):
+    """gate and up share X, so they run as one GEMM over the row-concatenated
+    [gate; up] weights (N = 2 x 18944); down is a second GEMM.  A caller-owned
+    fp32 workspace lets the library split K where that fills the GPU better."""
+    Ws = {name: inputs.prefill_W(name) for name, _, _ in inputs.prefill_shapes()}
+    M = inputs.PREFILL_M
     gemms = []
-    for name, N, K in inputs.prefill_shapes():
-        W = inputs.prefill_W(name)
+    for W in (np.concatenate([Ws["gate"], Ws["up"]]), Ws["down"]):
+        N, K = W.shape
         codes, meta = tkq.pack_int4_g128(torch.from_numpy(W).cuda())
         X = torch.from_numpy(inputs.prefill_X(K)).cuda()
-        Y = torch.empty((inputs.PREFILL_M, N), dtype=torch.float16, device="cuda")
-        gemms.append((codes, meta, X, Y, N))
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        ws = torch.empty(8 * M * N, dtype=torch.float32, device="cuda")
+        gemms.append((codes, meta, X, Y, N, ws))
+    del Ws
 
     def step(_s):
-        for codes, meta, X, Y, N in gemms:
-            tkq.gemm_prefill(codes, meta, X, N, Y)
+        for codes, meta, X, Y, N, ws in gemms:
+            tkq.gemm_prefill(codes, meta, X, N, Y, workspace=ws)
 
-    ms = time_steps(torch, step, args.steps, args.warmup)
-    flops = sum(2 * inputs.PREFILL_M * n * k for _, n, k in inputs.prefill_shapes())
+    ms = time_steps(torch, step, args.steps, args.warmup, args.graph, 1)
+    flops = sum(2 * M * n * k for _, n, k in inputs.prefill_shapes())
     tf = flops / (ms * 1e-3) / 1e12
     return {"metric": "int4-g128 prefill GEMM (M=512) TFLOP/s", "value": round(tf, 2),
             "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "f16",
             "data": "synthetic N(0,0.02) weights, N(0,1) fp16 activations",
-            "config": {"workload": "qwen2.5-7b MLP gate+up+down prefill GEMMs, M=512, int4-g128 weights",
+            "config": {"workload": "qwen2.5-7b MLP prefill, M=512, int4-g128 weights: gate+up as one "
+                                   "GEMM (N=37888, K=3584) then down (N=3584, K=18944)",
                        "flops_per_step": flops},
-            "tok_s": round(inputs.PREFILL_M * 1000.0 / ms, 1),
+            "tok_s": round(M * 1000.0 / ms, 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("7b-prefill")}}

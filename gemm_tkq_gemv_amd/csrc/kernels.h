@@ -63,8 +63,9 @@ hipError_t launch_gemv(int fmt, int jmax, const tkq_gemv_desc* dev_descs, int co
 hipError_t launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* codes, void* meta,
                        hipStream_t stream);
 
-hipError_t launch_prefill(int64_t M, int64_t N, int64_t K, const uint32_t* codes,
-                          const uint32_t* meta, const uint16_t* X, uint16_t* Y, hipStream_t stream);
+hipError_t launch_prefill(int64_t M, int64_t N, int64_t K, const uint32_t* codes, const uint32_t* meta,
+                          const uint16_t* X, uint16_t* Y, float* workspace, int64_t workspace_bytes,
+                          hipStream_t stream);
 
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream);
 

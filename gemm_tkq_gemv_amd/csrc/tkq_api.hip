@@ -210,15 +210,21 @@ int tkq_gemv(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs, void* st
 }
 
 int tkq_gemm_prefill(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint32_t* codes,
-                     const uint32_t* meta, const uint16_t* X, uint16_t* Y, void* stream) {
+                     const uint32_t* meta, const uint16_t* X, uint16_t* Y, float* workspace,
+                     int64_t workspace_bytes, void* stream) {
   if (fmt != TKQ_FMT_INT4_G128) return TKQ_EFORMAT;
-  if (!codes || !meta || !X || !Y || M < 1 || N < 1 || K < 1) return TKQ_EINVAL;
+  if (!codes || !meta || !X || !Y || M < 1 || N < 1 || K < 1 || workspace_bytes < 0 ||
+      (workspace && workspace_bytes == 0))
+    return TKQ_EINVAL;
   if (K % 128 || K > TKQ_MAX_K || M > INT32_MAX || N > INT32_MAX || N * K > kMaxWeights ||
-      M * K > kMaxWeights || M * N > kMaxWeights || (N + 127) / 128 > INT32_MAX ||
-      (M + 127) / 128 > 65535 || 128 * K * 2 > INT32_MAX)
+      M * K > kMaxWeights || M * N > kMaxWeights || (N + 63) / 64 > INT32_MAX ||
+      (M + 63) / 64 > 65535 || 128 * K * 2 > INT32_MAX)
     return TKQ_ESHAPE;
-  if (!aligned16(codes) || !aligned16(meta) || !aligned16(X) || !aligned16(Y)) return TKQ_EALIGN;
-  return hip_status(tkq::launch_prefill(M, N, K, codes, meta, X, Y, (hipStream_t)stream));
+  if (!aligned16(codes) || !aligned16(meta) || !aligned16(X) || !aligned16(Y) ||
+      (workspace && !aligned16(workspace)))
+    return TKQ_EALIGN;
+  return hip_status(tkq::launch_prefill(M, N, K, codes, meta, X, Y, workspace,
+                                        workspace ? workspace_bytes : 0, (hipStream_t)stream));
 }
 
 int tkq_read_probe(const void* buf, int64_t bytes, uint32_t* out, void* stream) {

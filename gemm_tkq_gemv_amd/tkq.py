@@ -65,7 +65,7 @@ _SIGNATURES = {
     "tkq_pack_bin": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
     "tkq_gemv_prepare": ([ctypes.POINTER(GemvDesc), _I32, ctypes.POINTER(GemvPlan)], ctypes.c_int),
     "tkq_gemv": ([ctypes.POINTER(GemvPlan), _P, _P], ctypes.c_int),
-    "tkq_gemm_prefill": ([_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
+    "tkq_gemm_prefill": ([_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
     "tkq_read_probe": ([_P, _I64, _P, _P], ctypes.c_int),
 }
 
@@ -219,8 +219,11 @@ def gemv(fmt, codes, meta, x, N, K, y=None, stream=None):
 
 # ---- prefill GEMM --------------------------------------------------------------
 
-def gemm_prefill(codes, meta, X, N, Y=None, stream=None):
-    """Y fp16 [M,N] = X fp16 [M,K] . dequant(W_int4_g128)^T."""
+def gemm_prefill(codes, meta, X, N, Y=None, workspace=None, stream=None):
+    """Y fp16 [M,N] = X fp16 [M,K] . dequant(W_int4_g128)^T.
+
+    workspace: optional float32 device tensor; with >= 2*M*N elements the
+    library may split K and use it for fp32 partial products."""
     _need(X, torch.float16, "X")
     M, K = X.shape
     _need(codes, torch.int32, "codes", (N, K // 8))
@@ -228,8 +231,12 @@ def gemm_prefill(codes, meta, X, N, Y=None, stream=None):
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
     _need(Y, torch.float16, "Y", (M, N))
+    ws, wsb = None, 0
+    if workspace is not None:
+        _need(workspace, torch.float32, "workspace")
+        ws, wsb = _ptr(workspace), workspace.numel() * 4
     _call("tkq_gemm_prefill", FMT_INT4_G128, M, N, K, _ptr(codes), _ptr(meta), _ptr(X), _ptr(Y),
-          _stream(stream))
+          ws, wsb, _stream(stream))
     return Y
 
 

@@ -194,10 +194,17 @@ int tkq_gemv(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs,
  * nearest even; |Y - Y_exact| <= 2e-3 * sum_k |X[m,k] w[n,k]| entry-wise.
  * fmt must be TKQ_FMT_INT4_G128.  X: fp16 bits [M][K]; Y: fp16 bits [M][N];
  * codes, meta as produced by tkq_pack_int4_g128.  Any M >= 1; tuned for
- * M >= 64 (decode, M = 1, belongs to tkq_gemv).  K % 128 == 0. */
+ * M >= 64 (decode, M = 1, belongs to tkq_gemv).  K % 128 == 0.
+ * workspace (optional, may be NULL with workspace_bytes 0): caller-owned
+ * device memory, 16-byte aligned, not overlapping any other argument.  When
+ * it holds at least 2*M*N floats the library may split K over workgroups,
+ * writing fp32 partial products there and summing them in a second kernel
+ * on the same stream; its contents are undefined afterwards.  Calls that
+ * share one workspace must be ordered (same stream). */
 int tkq_gemm_prefill(int32_t fmt, int64_t M, int64_t N, int64_t K,
                      const uint32_t* codes, const uint32_t* meta,
-                     const uint16_t* X, uint16_t* Y, void* stream);
+                     const uint16_t* X, uint16_t* Y, float* workspace,
+                     int64_t workspace_bytes, void* stream);
 
 /* ---- bandwidth probe ----------------------------------------------------
  * Reads `bytes` bytes of `buf` once with the same 16-byte non-temporal loads

@@ -190,11 +190,14 @@ def test_gemv_rejects_unprepared_plan():
 
 def test_prefill_validation():
     f = tkq.lib().tkq_gemm_prefill
-    assert f(2, 64, 128, 128, A, A, A, A, None) == tkq.EFORMAT
-    assert f(1, 0, 128, 128, A, A, A, A, None) == tkq.EINVAL
-    assert f(1, 64, 128, 100, A, A, A, A, None) == tkq.ESHAPE
-    assert f(1, 64, 128, 128, None, A, A, A, None) == tkq.EINVAL
-    assert f(1, 64, 128, 128, A, A, A + 2, A, None) == tkq.EALIGN
+    assert f(2, 64, 128, 128, A, A, A, A, None, 0, None) == tkq.EFORMAT
+    assert f(1, 0, 128, 128, A, A, A, A, None, 0, None) == tkq.EINVAL
+    assert f(1, 64, 128, 100, A, A, A, A, None, 0, None) == tkq.ESHAPE
+    assert f(1, 64, 128, 128, None, A, A, A, None, 0, None) == tkq.EINVAL
+    assert f(1, 64, 128, 128, A, A, A + 2, A, None, 0, None) == tkq.EALIGN
+    assert f(1, 64, 128, 128, A, A, A, A, A, -4, None) == tkq.EINVAL
+    assert f(1, 64, 128, 128, A, A, A, A, A, 0, None) == tkq.EINVAL
+    assert f(1, 64, 128, 128, A, A, A, A, A + 4, 1 << 20, None) == tkq.EALIGN
 
 
 def test_read_probe_validation():

@@ -12,9 +12,12 @@ from oracle import ref as oref
 pytestmark = pytest.mark.gpu
 
 
-def _run(torch, tkq, W, X):
+def _run(torch, tkq, W, X, split=False):
     codes, meta = tkq.pack_int4_g128(torch.from_numpy(W).cuda())
-    Y = tkq.gemm_prefill(codes, meta, torch.from_numpy(X).cuda(), W.shape[0])
+    ws = None
+    if split:   # room for 8 partial products: lets the library split K
+        ws = torch.full((8 * X.shape[0] * W.shape[0],), float("nan"), dtype=torch.float32, device="cuda")
+    Y = tkq.gemm_prefill(codes, meta, torch.from_numpy(X).cuda(), W.shape[0], workspace=ws)
     torch.cuda.synchronize()
     return codes, meta, Y
 
@@ -26,14 +29,16 @@ def _check(Y, X, w_deq, what):
     return worst
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (64, 128, 256), (65, 200, 384),
-                                   (130, 333, 896), (512, 256, 1024), (257, 129, 4864)])
-def test_prefill_ragged(M, N, K):
+                                   (130, 333, 896), (512, 256, 1024), (257, 129, 4864),
+                                   (512, 96, 8192), (33, 1000, 640)])
+def test_prefill_ragged(M, N, K, split):
     torch = gpu_or_skip()
     from gemm_tkq_gemv_amd import tkq
     W = inputs.normal_matrix((500, M, N, K), N, K)
     X = np.random.default_rng((501, M, K)).standard_normal((M, K), dtype=np.float32).astype(np.float16)
-    _, _, Y = _run(torch, tkq, W, X)
+    _, _, Y = _run(torch, tkq, W, X, split)
     oc, om = oracle_pack("int4", W)
     _check(Y, X, oracle_wdeq("int4", oc, om, K), "%dx%dx%d" % (M, N, K))
 
@@ -45,7 +50,7 @@ def test_prefill_7b_mlp_full(name):
     W = inputs.prefill_W(name)
     N, K = W.shape
     X = inputs.prefill_X(K)
-    codes, meta, Y = _run(torch, tkq, W, X)
+    codes, meta, Y = _run(torch, tkq, W, X, split=(name == "down"))
     oc, om = oracle_pack("int4", W)
     worst = _check(Y, X, oracle_wdeq("int4", oc, om, K), name)
     print("prefill %s worst |err|/bound %.3g" % (name, worst))
