@@ -10,21 +10,25 @@ namespace {
 thread_local int g_last_hip_error = 0;
 constexpr int32_t kPlanMagic = 0x746b7131;  // "tkq1"
 constexpr int64_t kMaxWeights = int64_t(1) << 39;
-// Bytes of codes one wave aims to stream per tile: large enough to amortise
-// the per-tile setup (descriptor search, x slice, constants), small enough
-// that the last workgroups of a launch finish close together.
-#ifndef TKQ_TILE_BYTES
-#define TKQ_TILE_BYTES (24 * 1024)
-#endif
-// The last TKQ_TAIL_BYTES of a sweep use tiles of TKQ_SMALL_TILE_BYTES per
-// wave: about two rounds of small tiles for every workgroup slot of a
-// 256-CU part, so the launch ends with short tiles.
-#ifndef TKQ_SMALL_TILE_BYTES
-#define TKQ_SMALL_TILE_BYTES (4 * 1024)
-#endif
-#ifndef TKQ_TAIL_BYTES
-#define TKQ_TAIL_BYTES (40 << 20)
-#endif
+// Planner parameters per coding (measured on MI355X, interleaved runs):
+//  tile   bytes of codes one wave streams per large tile: large enough to
+//         amortise the per-tile setup (descriptor search, x slice,
+//         constants);
+//  small  bytes per wave of the small tiles used over the last `tail` bytes
+//         of a sweep, so the final workgroups finish close together (about
+//         two rounds of small tiles for every workgroup slot of a 256-CU
+//         part);
+//  prefer_passes  on equal lane utilisation, the pass count to prefer: more
+//         passes = more rows per wave step = fewer cross-lane reductions per
+//         row, at the cost of x registers.
+struct PlanParams {
+  int prefer_passes;
+  int64_t tile, small, tail;
+};
+PlanParams plan_params(int fmt) {
+  if (fmt == TKQ_FMT_INT4_G128) return {2, 48 << 10, 4 << 10, 40 << 20};
+  return {1, 24 << 10, 4 << 10, 40 << 20};
+}
 constexpr int kMaxTileRows = tkq::kGemvMaxTileRows;
 
 int hip_status(hipError_t e) {
@@ -64,8 +68,9 @@ int pack_common(int fmt, const float* W, int64_t N, int64_t K, void* codes, void
 
 // Choose lanes-per-row, passes and k-slices for one GEMV: the decomposition
 // with the fewest idle lane-chunk slots (16-byte chunks per row over
-// k-slices x lanes x passes); ties go to fewer k-slices, then fewer passes.
+// k-slices x lanes x passes).
 tkq::GemvShape choose_shape(int fmt, int K) {
+  const int prefer = plan_params(fmt).prefer_passes;
   const int C = K / tkq::weights_per_chunk(fmt);
   const int jmax = tkq::gemv_max_passes(fmt);
   tkq::GemvShape best = {6, 0, 0};
@@ -77,9 +82,12 @@ tkq::GemvShape choose_shape(int fmt, int K) {
       const int J = (Cs + L - 1) / L;
       if (J > jmax) continue;
       const double util = double(C) / double(S * L * J);
+      // Ties: fewer k-slices, then the pass count closest to the preferred one.
+      const int dj = J > prefer ? J - prefer : prefer - J;
+      const int db = best.passes > prefer ? best.passes - prefer : prefer - best.passes;
       const bool better = util > best_util + 1e-12 ||
                           (util > best_util - 1e-12 &&
-                           (S < best.kslices || (S == best.kslices && J < best.passes)));
+                           (S < best.kslices || (S == best.kslices && dj < db)));
       if (better) {
         best = {lg, J, S};
         best_util = util;
@@ -162,7 +170,8 @@ int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan) {
   int64_t total = 0;
   for (int32_t i = 0; i < count; ++i)
     total += int64_t(descs[i].N) * (descs[i].K / tkq::weights_per_chunk(fmt)) * 16;
-  const int64_t tail_start = total > TKQ_TAIL_BYTES ? total - TKQ_TAIL_BYTES : 0;
+  const PlanParams pp = plan_params(fmt);
+  const int64_t tail_start = total > pp.tail ? total - pp.tail : 0;
 
   int64_t work = 0, pos = 0;
   int jmax = 1;
@@ -170,8 +179,8 @@ int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan) {
     tkq_gemv_desc& d = descs[i];
     const tkq::GemvShape sh = choose_shape(fmt, d.K);
     if (sh.passes < 1) return TKQ_ESHAPE;
-    const int big = rows_per_tile(fmt, d.N, d.K, sh, TKQ_TILE_BYTES);
-    const int small = rows_per_tile(fmt, d.N, d.K, sh, TKQ_SMALL_TILE_BYTES);
+    const int big = rows_per_tile(fmt, d.N, d.K, sh, pp.tile);
+    const int small = rows_per_tile(fmt, d.N, d.K, sh, pp.small);
     const int64_t row_bytes = int64_t(d.K / tkq::weights_per_chunk(fmt)) * 16;
     // rows above the tail start get large tiles
     int64_t big_rows = 0;

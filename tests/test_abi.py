@@ -140,7 +140,9 @@ def test_prepare_tiles_cover_rows(fmt):
 def test_prepare_shapes_for_model_matrices():
     arr = _descs(1, [(896, 896), (896, 4864), (3584, 3584), (3584, 18944)])
     assert _prepare(arr)[0] == tkq.OK
-    assert _shape(arr[0]) == (32, 1, 1)   # 28 chunks: 32 lanes, one pass
+    # int4 prefers two passes on ties: 28 chunks -> 16 lanes x 2 passes
+    # (4 rows per wave step) rather than 32 lanes x 1 pass (same utilisation)
+    assert _shape(arr[0]) == (16, 2, 1)
     assert _shape(arr[1]) == (64, 3, 1)   # 152 chunks: 64 lanes, three passes
     assert _shape(arr[2]) == (64, 2, 1)   # 112 chunks
     assert _shape(arr[3]) == (64, 3, 4)   # 592 chunks: four k-slices
