@@ -44,9 +44,9 @@ ROTATE_BYTES = 1 << 30
 TRAFFIC_SOURCES = ["gemm_tkq_gemv_amd/csrc/gemv.hip", "gemm_tkq_gemv_amd/csrc/tkq_api.hip",
                    "gemm_tkq_gemv_amd/csrc/prefill.hip", "gemm_tkq_gemv_amd/csrc/device_common.h",
                    "gemm_tkq_gemv_amd/csrc/kernels.h"]
-TRAFFIC_HASH = "8088e9d17e380126"
-TRAFFIC_BYTES = {"0.5b-int4": 266714350, "0.5b-k5": 506994491, "0.5b-tern": 135532787,
-                 "bin": 128688705, "7b-int4": 3792337845, "7b-prefill": 230583342}
+TRAFFIC_HASH = "f726477761c734ec"
+TRAFFIC_BYTES = {"0.5b-int4": 268848641, "0.5b-k5": 506989859, "0.5b-tern": 135531392,
+                 "bin": 128618467, "7b-int4": 3790890882, "7b-prefill": 575672431}
 
 
 def measured_traffic(workload):
