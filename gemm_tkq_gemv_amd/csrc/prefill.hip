@@ -1,9 +1,10 @@
 // Prefill GEMM over int4 g128 weights for gfx950: Y = X . dequant(W)^T.
 //
 // With M >= 64 tokens per weight the product is a dense contraction (the
-// Whetstone README, "Prior art": the low-bit arithmetic paths only pay off in
-// prefill or speculative verification, where the regime is compute-bound),
-// so this is the one place the library uses the matrix cores.  As in
+// Whetstone README, "Prior art": fast low-bit arithmetic helps only where many
+// tokens share each weight, i.e. prefill and speculative verification, which
+// are compute-bound), so this is the one place the library uses the matrix
+// cores.  As in
 // TKintegers K5 ("What is K5?"), tiles of low-bit codes are expanded to fp16
 // operands and multiplied with fp32 accumulation:
 //

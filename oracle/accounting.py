@@ -1,7 +1,7 @@
 """Byte and roofline accounting (test infrastructure only).
 
 Whetstone, "The one fact that shapes everything":
-  * the roofline equation: tok/s ceiling = bandwidth / bytes read per token;
+  * the roofline equation: ceiling (tok/s) = bandwidth / bytes per token;
   * the parameter table: transformer blocks vs the tied lm_head, both read on
     every token;
   * the bytes/token table: bytes = params * bits_per_weight / 8 per format.
@@ -32,7 +32,7 @@ def bytes_per_token(params, bpw):
 
 
 def ceiling_tok_s(bandwidth_bytes_s, bytes_token):
-    """The roofline: tok/s ceiling = bandwidth / bytes read per token."""
+    """The roofline: ceiling (tok/s) = bandwidth / bytes per token."""
     return bandwidth_bytes_s / bytes_token
 
 

@@ -1,9 +1,9 @@
 """Packers and unpackers for the four code layouts (test infrastructure only).
 
-Layouts (the library's storage contract; Whetstone, "The .wstone format" says
-only that nibbles are stored in the order the GEMV's 128-bit load consumes
-them; the reading taken here is the natural little-endian order, which a
-16-byte load of a row consumes front to back):
+Layouts (the library's storage contract; Whetstone, "The .wstone format"
+fixes the nibble order only as the one the GEMV's 16-byte loads read; the
+reading taken here is the natural little-endian order, which a 16-byte load
+of a row reads front to back):
 
 * int4 codes   uint32 [N][K/8]: element 8j+i of a row in bits [4i, 4i+4) of
                 word j.

@@ -10,8 +10,8 @@ taken where they are silent:
 
 * Whetstone, "What the weights can actually survive" (quality table and the
   quantizer table): the group-128 int4 format is round-to-nearest with a
-  group size of 128, and an f16 scale plus an f16 zero per group costs
-  32/128 = 0.25 bits/weight.  Reading: asymmetric min/max RTN over the
+  group size of 128, with one fp16 scale and one fp16 zero-point for every
+  128 weights (32 metadata bits per group, 0.25 bits/weight).  Reading: asymmetric min/max RTN over the
   group's range widened to include 0, ``w ~ s * (q - z)``, q in 0..15, z an
   integer zero-point stored in fp16.
 * Whetstone, status list: a shared fp16 scale underflowing to zero packed

@@ -27,7 +27,7 @@ def _expand_groups(per_group, K):
 
 def dequant_int4(codes, meta, K):
     """w = s * (q - z) per 128-group (Whetstone, "What the weights can actually
-    survive": f16 scale plus f16 zero per group).  Exact in fp64."""
+    survive": one fp16 scale and one fp16 zero-point per group).  Exact in fp64."""
     q = _pack.unpack_int4(codes, K).astype(np.float64)
     s, z = _pack.unpack_int4_meta(meta)
     return _expand_groups(s, K) * (q - _expand_groups(z, K))
