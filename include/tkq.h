@@ -34,8 +34,8 @@
  * Weight codings (storage layouts)
  * --------------------------------
  * TKQ_FMT_INT4_G128 (Whetstone README, "What the weights can actually
- *   survive": group-128 round-to-nearest int4 with an f16 scale and an f16
- *   zero per group, 4.25 bits/weight):
+ *   survive": round-to-nearest int4 in groups of 128, each group with an
+ *   fp16 scale and an fp16 zero-point, 4.25 bits/weight):
  *     codes uint32 [N][K/8]  : element 8j+i of a row in bits [4i,4i+4) of word j
  *     meta  uint32 [N][K/128]: fp16 scale in bits [0,16), fp16 zero in [16,32)
  *     w = scale * (q - zero)

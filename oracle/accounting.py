@@ -5,8 +5,9 @@ Whetstone, "The one fact that shapes everything":
   * the parameter table: transformer blocks vs the tied lm_head, both read on
     every token;
   * the bytes/token table: bytes = params * bits_per_weight / 8 per format.
-Whetstone, "What the weights can actually survive": an f16 scale and an f16
-zero per group of G weights cost 32/G bits per weight.
+Whetstone, "What the weights can actually survive": per-group metadata of one
+fp16 scale and one fp16 zero-point amounts to 32/G bits per weight for groups
+of G weights.
 
 Shapes are passed in as (name, N, K) tuples; nothing here knows a model.
 """
@@ -42,7 +43,10 @@ def ceiling_tok_s(bandwidth_bytes_s, bytes_token):
 #   K5        : K code bytes   + 2 bytes (fp16 scale) per 128
 #   ternary   : K/4 code bytes + 2 bytes (fp16 scale) per 128
 #   binary    : K/8 code bytes, no metadata, x is K/8 bytes, y is int32
+#   int4-hier-g32: K/2 code bytes + 1 byte (two 4-bit indices) per 32
+#               + 4 bytes (fp16 pair) per row
 _FMT_BYTES = {
+    "hier": (lambda n, k: n * (k // 2) + n * (k // 32) + 4 * n, lambda k: 2 * k, lambda n: 2 * n),
     "int4": (lambda n, k: n * (k // 2) + n * (k // 128) * 4, lambda k: 2 * k, lambda n: 2 * n),
     "k5": (lambda n, k: n * k + n * (k // 128) * 2, lambda k: 2 * k, lambda n: 2 * n),
     "tern": (lambda n, k: n * (k // 4) + n * (k // 128) * 2, lambda k: 2 * k, lambda n: 2 * n),

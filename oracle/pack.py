@@ -13,6 +13,11 @@ of a row reads front to back):
 * ternary      uint32 [N][K/16]: element 16j+i in bits [2i, 2i+2) of word j,
                 code = t + 1; fp16 scale [N][K/128].
 * binary       uint32 [N][K/32]: element 32j+i in bit i of word j.
+* int4-hier-g32 codes as int4; one metadata block per matrix:
+                bytes [0, N*K/32): byte n*(K/32)+g = sc | (mi << 4) of group g
+                of row n; zero padding up to a multiple of 16 bytes (offset
+                R); then uint32 [N] at R: fp16 d in bits [0,16), fp16 dmin in
+                bits [16,32).
 
 Packers build words by multiply-and-add over slots; unpackers read a slot with
 shift-and-mask.  They are written independently from the layout text above.
@@ -88,3 +93,44 @@ def pack_bits(bits):
 
 def unpack_bits(words, K):
     return _unpack_fields(words, K, 1)
+
+
+def hier_row_offset(N, K):
+    """Byte offset R of the per-row fp16 pairs in an int4-hier-g32 metadata
+    block: the group bytes rounded up to a multiple of 16."""
+    gb = int(N) * (int(K) // 32)
+    return (gb + 15) // 16 * 16
+
+
+def hier_meta_bytes(N, K):
+    """Size of an int4-hier-g32 metadata block."""
+    return hier_row_offset(N, K) + 4 * int(N)
+
+
+def pack_hier_meta(sc, mi, d16, dmin16):
+    """(sc, mi uint8 [N,K/32] in 0..15; d16, dmin16 fp16 [N]) -> uint8 block."""
+    sc = np.asarray(sc, dtype=np.uint8)
+    mi = np.asarray(mi, dtype=np.uint8)
+    if np.any(sc > 15) or np.any(mi > 15):
+        raise ValueError("index does not fit in 4 bits")
+    N, ng = sc.shape
+    K = ng * 32
+    out = np.zeros(hier_meta_bytes(N, K), dtype=np.uint8)
+    out[: N * ng] = (sc.astype(np.uint32) + mi.astype(np.uint32) * 16).reshape(-1).astype(np.uint8)
+    R = hier_row_offset(N, K)
+    rows = pack_int4_meta(np.asarray(d16, dtype=np.float16).reshape(N, 1),
+                          np.asarray(dmin16, dtype=np.float16).reshape(N, 1)).reshape(N)
+    out[R:R + 4 * N] = rows.astype("<u4").view(np.uint8)
+    return out
+
+
+def unpack_hier_meta(block, N, K):
+    """uint8 block -> (sc uint8 [N,K/32], mi uint8 [N,K/32], d16 fp16 [N],
+    dmin16 fp16 [N])."""
+    block = np.asarray(block, dtype=np.uint8)
+    ng = int(K) // 32
+    g = block[: N * ng].reshape(N, ng)
+    R = hier_row_offset(N, K)
+    rows = block[R:R + 4 * N].copy().view("<u4")
+    d16, dmin16 = unpack_int4_meta(rows)
+    return g & np.uint8(15), g >> np.uint8(4), d16, dmin16

@@ -26,6 +26,13 @@ taken where they are silent:
   -1, 1); stored code t + 1.
 * Whetstone, "Measured hardware facts": {-1,+1} values packed as bits {1,0}.
   Reading: bit = 1 exactly when the value is negative.
+* Whetstone, bytes/token table ("int4 hier-g32", 4.28 bits/weight), the
+  quantizer table ("group 32 with hierarchical scale metadata") and "Prior
+  art" (the Q4_K comparison): int4 in groups of 32 whose scale and offset are
+  4-bit indices against one fp16 pair per row.  Reading, as in Q4_K: each
+  group has a scale index sc and a min index mi, the row has fp16 (d, dmin),
+  and w ~ d*sc*q - dmin*mi with q in 0..15; RTN at every level (the pages
+  print no fitting procedure).
 """
 
 import numpy as np
@@ -142,3 +149,52 @@ def sign_bits(W):
     """Binary sign code (Whetstone, "Measured hardware facts": {-1,+1} packed as
     bits {1,0}).  bit = 1 exactly when w < 0; -0.0 and +values give 0."""
     return (np.asarray(W, dtype=np.float32) < 0).astype(np.uint8)
+
+
+HIER_GROUP = 32
+
+
+def quantize_int4_hier_g32(W):
+    """int4 with group 32 and two-level scales (Whetstone, quantizer table:
+    "group 32 with hierarchical scale metadata"; "Prior art": like Q4_K's
+    sub-scales against a super-block fp16 pair, but the super-block is a whole
+    row and the indices have 4 bits).
+
+    Per row n, in fp32 (every division true division, every rint half-even):
+      per group g of 32:  lo = min(min_k w, 0); hi = max(max_k w, 0)
+                          s_g = (hi - lo) / 15      (wanted step)
+                          m_g = -lo                 (wanted offset, >= 0)
+      d16    = fp16_rne(max_g s_g / 15);  d16 := 1 if d16 == 0
+      dmin16 = fp16_rne(max_g m_g / 15);  dmin16 := 1 if dmin16 == 0
+               (Whetstone, status list: a shared fp16 row scale that
+               underflows to zero must not be stored)
+      sc_g = clip(rint(s_g / d16), 1, 15)     (never 0: a group keeps a step)
+      mi_g = clip(rint(m_g / dmin16), 0, 15)
+      step_g = d16 * sc_g;  off_g = dmin16 * mi_g    (exact in fp32)
+      q = clip(rint((w + off_g) / step_g), 0, 15)
+
+    Dequantized weight: d16 * sc_g * q - dmin16 * mi_g.
+
+    Returns (q uint8 [N,K], sc uint8 [N,K/32], mi uint8 [N,K/32],
+             d16 fp16 [N], dmin16 fp16 [N]).
+    """
+    W = np.asarray(W, dtype=np.float32)
+    if W.ndim != 2 or W.shape[1] % HIER_GROUP:
+        raise ValueError("W must be [N, K] with K a multiple of 32")
+    N, K = W.shape
+    G = W.reshape(N, K // HIER_GROUP, HIER_GROUP)
+    lo = np.minimum(G.min(axis=2), F32(0))
+    hi = np.maximum(G.max(axis=2), F32(0))
+    s = (hi - lo) / F32(15)
+    m = -lo
+    d16 = _guard_zero_scale(fp16_rne(s.max(axis=1) / F32(15)))
+    dmin16 = _guard_zero_scale(fp16_rne(m.max(axis=1) / F32(15)))
+    df = d16.astype(np.float32)[:, None]
+    mf = dmin16.astype(np.float32)[:, None]
+    sc = np.clip(np.rint(s / df), F32(1), F32(15))
+    mi = np.clip(np.rint(m / mf), F32(0), F32(15))
+    step = df * sc
+    off = mf * mi
+    q = np.clip(np.rint((G + off[:, :, None]) / step[:, :, None]), F32(0), F32(15))
+    return (q.astype(np.uint8).reshape(N, K), sc.astype(np.uint8), mi.astype(np.uint8),
+            d16, dmin16)

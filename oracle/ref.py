@@ -33,6 +33,17 @@ def dequant_int4(codes, meta, K):
     return _expand_groups(s, K) * (q - _expand_groups(z, K))
 
 
+def dequant_int4_hier(codes, meta, N, K):
+    """w = d * sc * q - dmin * mi per 32-group (Whetstone, quantizer table,
+    "group 32 with hierarchical scale metadata", read as Q4_K-style two-level
+    scales; see quant.quantize_int4_hier_g32).  Exact in fp64."""
+    q = _pack.unpack_int4(codes, K).astype(np.float64)
+    sc, mi, d16, dmin16 = _pack.unpack_hier_meta(meta, N, K)
+    step = d16.astype(np.float64)[:, None] * sc.astype(np.float64)
+    off = dmin16.astype(np.float64)[:, None] * mi.astype(np.float64)
+    return np.repeat(step, 32, axis=1) * q - np.repeat(off, 32, axis=1)
+
+
 def k5_trits(c):
     """Five balanced trits of a K5 byte (TKintegers K5, "What is K5?").
 
