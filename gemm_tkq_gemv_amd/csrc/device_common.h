@@ -35,6 +35,9 @@ __device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off
 __device__ __forceinline__ uint16_t load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
+__device__ __forceinline__ uint32_t load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
 __device__ __forceinline__ void store2(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t v) {
   __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
 }

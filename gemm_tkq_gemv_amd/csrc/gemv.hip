@@ -200,6 +200,14 @@ struct Codec<kFmtTern> {
   }
 };
 
+// int4-hier-g32: the int4 code layout, so the int4 unpack; a chunk is exactly
+// one 32-weight group, whose metadata is one byte (scale index | min index
+// << 4).  The row's fp16 pair (d, dmin) is applied once per row.
+template <>
+struct Codec<kFmtHier> : Codec<kFmtInt4> {
+  static constexpr int CPG = 1, MB = 1;
+};
+
 // Binary: 128 sign bits per chunk; x is kept as packed words.
 template <>
 struct Codec<kFmtBin> {
@@ -221,6 +229,7 @@ struct Codec<kFmtBin> {
 // ------------------------------------------------------------ tile runner --
 struct Tile {
   __amdgpu_buffer_rsrc_t codes, meta, x, y;
+  __amdgpu_buffer_rsrc_t rmeta;  // int4-hier-g32: the rows' fp16 (d, dmin) pairs
   uint32_t row_bytes;       // bytes of codes per row
   uint32_t meta_row_bytes;  // bytes of metadata per row
   int lg, sub, prow, P;     // lanes-per-row log2, lane in group, row in step, rows per step
@@ -240,6 +249,7 @@ struct Runner {
   struct Buf {
     u32x4 c[U][J];
     uint32_t m[U][J];
+    uint32_t rp[U];  // int4-hier-g32 row pair
   };
 
   const Tile& t;
@@ -301,8 +311,10 @@ struct Runner {
         b.c[u][j] = load16_nt(t.codes, rb + cof[j]);
         if constexpr (Cd::MB == 4) b.m[u][j] = load4(t.meta, mb + mof[j]);
         else if constexpr (Cd::MB == 2) b.m[u][j] = load2(t.meta, mb + mof[j]);
+        else if constexpr (Cd::MB == 1) b.m[u][j] = load1(t.meta, mb + mof[j]);
         else b.m[u][j] = 0;
       }
+      if constexpr (FMT == kFmtHier) b.rp[u] = load4(t.rmeta, r * 4u);
     }
   }
 
@@ -311,10 +323,16 @@ struct Runner {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       Acc res = 0;
+      float rs = 0.0f, rm = 0.0f;  // int4-hier-g32: sum of sc*dot, sum of mi*sum(x)
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         if constexpr (kBin) {
           res += Cd::dot(b.c[u][j], xr[j], R);
+        } else if constexpr (FMT == kFmtHier) {
+          const float d = Cd::dot(b.c[u][j], xr[j], R) - bias[j];
+          const uint32_t m = b.m[u][j];
+          rs = fmaf((float)(m & 15u), d, rs);
+          rm = fmaf((float)(m >> 4), xsum[j], rm);
         } else if constexpr (FMT == kFmtInt4) {
           const float d = Cd::dot(b.c[u][j], xr[j], R) - bias[j];
           res = fmaf(half_lo(b.m[u][j]), fmaf(-half_hi(b.m[u][j]), xsum[j], d), res);
@@ -323,6 +341,7 @@ struct Runner {
           res = fmaf(half_lo(b.m[u][j]), d, res);
         }
       }
+      if constexpr (FMT == kFmtHier) res = fmaf(half_lo(b.rp[u]), rs, -half_hi(b.rp[u]) * rm);
       const Acc v = group_sum(res, t.lg);
       const uint32_t r = row(st, u);
       if (t.sub == L - 1) {
@@ -412,7 +431,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WP
   t.C = K / Cd::WPC;
   t.Cs = (t.C + t.S - 1) / t.S;
   t.row_bytes = (uint32_t)t.C * 16u;
-  t.meta_row_bytes = (uint32_t)(K / 128) * Cd::MB;
+  t.meta_row_bytes = (uint32_t)(t.C / Cd::CPG) * Cd::MB;
   const int nrows = min(rpt, N - row0);
   const char* codes = (const char*)d->codes + (size_t)row0 * t.row_bytes;
   t.codes = make_rsrc(codes, (uint32_t)nrows * t.row_bytes);
@@ -421,6 +440,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WP
     t.meta = make_rsrc(meta, (uint32_t)nrows * t.meta_row_bytes);
   } else {
     t.meta = make_rsrc(d->codes, 0u);
+  }
+  if constexpr (FMT == kFmtHier) {
+    const char* rm = (const char*)d->meta + hier_row_offset(N, K) + (size_t)row0 * 4u;
+    t.rmeta = make_rsrc(rm, (uint32_t)nrows * 4u);
+  } else {
+    t.rmeta = t.meta;
   }
   t.x = make_rsrc(d->x, kBin ? (uint32_t)(K / 8) : (uint32_t)K * 2u);
   const uint32_t ybytes = kBin ? 4u : 2u;
@@ -461,7 +486,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WP
 
 template <int FMT>
 constexpr int max_passes() {
-  return FMT == kFmtBin ? 8 : (FMT == kFmtTern ? 3 : 4);
+  return FMT == kFmtBin ? 8 : (FMT == kFmtTern ? 3 : 4);  // int4, hier-g32, K5: 4
 }
 
 typedef void (*GemvFn)(const tkq_gemv_desc*, int);
@@ -483,6 +508,7 @@ GemvFn pick(int jmax) {
 int gemv_max_passes(int fmt) {
   switch (fmt) {
     case kFmtInt4: return max_passes<kFmtInt4>();
+    case kFmtHier: return max_passes<kFmtHier>();
     case kFmtK5: return max_passes<kFmtK5>();
     case kFmtTern: return max_passes<kFmtTern>();
     case kFmtBin: return max_passes<kFmtBin>();
@@ -495,6 +521,7 @@ hipError_t launch_gemv(int fmt, int jmax, const tkq_gemv_desc* dev_descs, int co
   GemvFn fn = nullptr;
   switch (fmt) {
     case kFmtInt4: fn = pick<kFmtInt4>(jmax); break;
+    case kFmtHier: fn = pick<kFmtHier>(jmax); break;
     case kFmtK5: fn = pick<kFmtK5>(jmax); break;
     case kFmtTern: fn = pick<kFmtTern>(jmax); break;
     case kFmtBin: fn = pick<kFmtBin>(jmax); break;

@@ -14,6 +14,7 @@ constexpr int kFmtInt4 = TKQ_FMT_INT4_G128;
 constexpr int kFmtK5 = TKQ_FMT_K5_G128;
 constexpr int kFmtTern = TKQ_FMT_TERN_G128;
 constexpr int kFmtBin = TKQ_FMT_BIN;
+constexpr int kFmtHier = TKQ_FMT_INT4_HIER_G32;
 
 // Work decomposition of one GEMV, packed into tkq_gemv_desc::shape.
 struct GemvShape {
@@ -28,6 +29,7 @@ __host__ __device__ inline GemvShape unpack_shape(int v) { return {v & 15, (v >>
 inline int weights_per_chunk(int fmt) {
   switch (fmt) {
     case kFmtInt4: return 32;
+    case kFmtHier: return 32;
     case kFmtK5: return 16;
     case kFmtTern: return 64;
     case kFmtBin: return 128;
@@ -62,6 +64,9 @@ hipError_t launch_gemv(int fmt, int jmax, const tkq_gemv_desc* dev_descs, int co
 
 hipError_t launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* codes, void* meta,
                        hipStream_t stream);
+
+// Byte offset of the per-row fp16 pairs in an int4-hier-g32 metadata block.
+__host__ __device__ inline int64_t hier_row_offset(int64_t N, int64_t K) { return (N * (K / 32) + 15) / 16 * 16; }
 
 hipError_t launch_prefill(int64_t M, int64_t N, int64_t K, const uint32_t* codes, const uint32_t* meta,
                           const uint16_t* X, uint16_t* Y, float* workspace, int64_t workspace_bytes,

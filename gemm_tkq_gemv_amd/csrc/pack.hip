@@ -14,6 +14,12 @@
 //               z = clamp(rint(-lo/s), 0, 15), q = clamp(rint(w/s) + z, 0, 15)
 //   K5        : s = fp16(max|w| / 121), c = clamp(rint(w/s), -121, 121) + 121
 //   ternary   : s = fp16(sequential-sum|w| / 128), code = clamp(rint(w/s),-1,1)+1
+//   int4 hier-g32 (Whetstone README, quantizer table "group 32 with
+//               hierarchical scale metadata"; "Prior art", the Q4_K
+//               comparison): per 32-group s_g = (hi-lo)/15, m_g = -lo; per
+//               row d = fp16(max s_g / 15), dmin = fp16(max m_g / 15);
+//               sc = clamp(rint(s_g/d), 1, 15), mi = clamp(rint(m_g/dmin), 0, 15),
+//               q = clamp(rint((w + dmin*mi) / (d*sc)), 0, 15)
 // A scale that rounds to fp16 zero is stored as 1.0 (Whetstone README, status
 // list: the underflowing fp16 row scale).
 #include "device_common.h"
@@ -116,6 +122,61 @@ __global__ __launch_bounds__(256) void pack_tern_kernel(const float* __restrict_
   if (lane == 0) scale[g] = sbits;
 }
 
+// Minimum / maximum over each 32-lane half of the wave (one 32-weight group).
+__device__ __forceinline__ float half_wave_min(float v) {
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) v = fminf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float half_wave_max(float v) {
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// int4 hier-g32: one wavefront per row (the row pair depends on every group
+// of the row).  Each iteration covers 64 consecutive weights = two groups,
+// one per half-wave; lane l reads weight 64i + l (coalesced).  Pass 1 finds
+// the row maxima of the wanted step and offset, pass 2 re-reads the row and
+// writes codes and indices.  Lanes past K (when K % 64 == 32) see w = 0,
+// which contributes s = m = 0 to the maxima and writes nothing.
+__global__ __launch_bounds__(256) void pack_hier_kernel(const float* __restrict__ W, int64_t N, int64_t K,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ meta, int64_t rbase) {
+  const int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const int lane = threadIdx.x & 63;
+  const float* w = W + row * K;
+  float smax = 0.0f, mmax = 0.0f;
+  for (int64_t base = 0; base < K; base += 64) {
+    const int64_t k = base + lane;
+    const float v = k < K ? w[k] : 0.0f;
+    const float lo = fminf(half_wave_min(v), 0.0f), hi = fmaxf(half_wave_max(v), 0.0f);
+    smax = fmaxf(smax, (hi - lo) / 15.0f);
+    mmax = fmaxf(mmax, -lo);
+  }
+  uint16_t dbits, mbits;
+  const float d = guard_scale(wave_max(smax) / 15.0f, &dbits);
+  const float dmin = guard_scale(wave_max(mmax) / 15.0f, &mbits);
+  const int64_t ng = K / 32;
+  for (int64_t base = 0; base < K; base += 64) {
+    const int64_t k = base + lane;
+    const bool ok = k < K;
+    const float v = ok ? w[k] : 0.0f;
+    const float lo = fminf(half_wave_min(v), 0.0f), hi = fmaxf(half_wave_max(v), 0.0f);
+    const float sc = fminf(fmaxf(rintf(((hi - lo) / 15.0f) / d), 1.0f), 15.0f);
+    const float mi = fminf(fmaxf(rintf(-lo / dmin), 0.0f), 15.0f);
+    const float step = d * sc, off = dmin * mi;  // both exact
+    const int q = (int)fminf(fmaxf(rintf((v + off) / step), 0.0f), 15.0f);
+    const int other = __shfl_xor(q, 1, 64);
+    if (ok && (lane & 1) == 0) codes[row * (K / 2) + (k >> 1)] = (uint8_t)(q | (other << 4));
+    if (ok && (lane & 31) == 0) meta[row * ng + (k >> 5)] = (uint8_t)((int)sc | ((int)mi << 4));
+  }
+  if (lane == 0) *reinterpret_cast<uint32_t*>(meta + rbase + row * 4) = (uint32_t)dbits | ((uint32_t)mbits << 16);
+  // zero padding between the group bytes and the row pairs
+  if (row == 0 && N * ng + lane < rbase) meta[N * ng + lane] = 0;
+}
+
 // One thread per output word: 32 consecutive weights -> 32 sign bits.
 __global__ __launch_bounds__(256) void pack_bin_kernel(const float* __restrict__ W, int64_t words,
                                                        uint32_t* __restrict__ bits) {
@@ -143,6 +204,12 @@ hipError_t launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* code
     const int64_t blocks = (words + 255) / 256;
     hipLaunchKernelGGL(pack_bin_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, W, words,
                        (uint32_t*)codes);
+    return hipGetLastError();
+  }
+  if (fmt == kFmtHier) {
+    const int64_t blocks = (N + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL(pack_hier_kernel, dim3((uint32_t)blocks), dim3(64 * kWavesPerBlock), 0, stream, W, N, K,
+                       (uint8_t*)codes, (uint8_t*)meta, hier_row_offset(N, K));
     return hipGetLastError();
   }
   const int64_t groups = N * (K / kGroup);

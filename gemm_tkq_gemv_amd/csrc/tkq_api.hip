@@ -26,7 +26,7 @@ struct PlanParams {
   int64_t tile, small, tail;
 };
 PlanParams plan_params(int fmt) {
-  if (fmt == TKQ_FMT_INT4_G128) return {2, 48 << 10, 4 << 10, 40 << 20};
+  if (fmt == TKQ_FMT_INT4_G128 || fmt == TKQ_FMT_INT4_HIER_G32) return {2, 48 << 10, 4 << 10, 40 << 20};
   return {1, 24 << 10, 4 << 10, 40 << 20};
 }
 constexpr int kMaxTileRows = tkq::kGemvMaxTileRows;
@@ -41,8 +41,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool known_fmt(int fmt) {
   return fmt == TKQ_FMT_INT4_G128 || fmt == TKQ_FMT_K5_G128 || fmt == TKQ_FMT_TERN_G128 ||
-         fmt == TKQ_FMT_BIN;
+         fmt == TKQ_FMT_BIN || fmt == TKQ_FMT_INT4_HIER_G32;
 }
+
+// Column unit of a coding's GEMV (its group size, or one code word).
+int k_unit(int fmt) { return fmt == TKQ_FMT_INT4_HIER_G32 ? 32 : 128; }
 
 // Largest K each GEMV variant handles with x resident in registers:
 // chunks per row <= 4 k-slices x 64 lanes x max passes.
@@ -152,6 +155,16 @@ int tkq_pack_bin(const float* W, int64_t N, int64_t K, uint32_t* bits, void* str
   return pack_common(TKQ_FMT_BIN, W, N, K, bits, nullptr, false, 32, stream);
 }
 
+int tkq_pack_int4_hier_g32(const float* W, int64_t N, int64_t K, uint32_t* codes, uint8_t* meta,
+                           void* stream) {
+  return pack_common(TKQ_FMT_INT4_HIER_G32, W, N, K, codes, meta, true, 32, stream);
+}
+
+int64_t tkq_hier_meta_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 32 || K % 32 || K > TKQ_MAX_K || N > INT32_MAX) return -1;
+  return tkq::hier_row_offset(N, K) + 4 * N;
+}
+
 int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan) {
   if (!descs || !plan || count < 1) return TKQ_EINVAL;
   const int fmt = descs[0].fmt;
@@ -161,7 +174,7 @@ int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan) {
     if (d.fmt != fmt) return TKQ_EFORMAT;
     if (d.N < 1 || d.K < 1 || !d.codes || !d.x || !d.y) return TKQ_EINVAL;
     if (fmt != TKQ_FMT_BIN && !d.meta) return TKQ_EINVAL;
-    if (d.K % 128 || d.K > gemv_max_k(fmt) || int64_t(d.N) * d.K > kMaxWeights) return TKQ_ESHAPE;
+    if (d.K % k_unit(fmt) || d.K > gemv_max_k(fmt) || int64_t(d.N) * d.K > kMaxWeights) return TKQ_ESHAPE;
     if (!aligned16(d.codes) || !aligned16(d.x) || !aligned16(d.y) ||
         (fmt != TKQ_FMT_BIN && !aligned16(d.meta)))
       return TKQ_EALIGN;

@@ -24,7 +24,9 @@ FMT_INT4_G128 = 1
 FMT_K5_G128 = 2
 FMT_TERN_G128 = 3
 FMT_BIN = 4
-FORMATS = {"int4": FMT_INT4_G128, "k5": FMT_K5_G128, "tern": FMT_TERN_G128, "bin": FMT_BIN}
+FMT_INT4_HIER_G32 = 5
+FORMATS = {"int4": FMT_INT4_G128, "k5": FMT_K5_G128, "tern": FMT_TERN_G128, "bin": FMT_BIN,
+           "hier": FMT_INT4_HIER_G32}
 
 OK, EINVAL, ESHAPE, EALIGN, EFORMAT, EHIP, EPLAN = 0, -1, -2, -3, -4, -5, -6
 
@@ -63,6 +65,8 @@ _SIGNATURES = {
     "tkq_pack_k5": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "tkq_pack_tern_g128": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "tkq_pack_bin": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
+    "tkq_pack_int4_hier_g32": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "tkq_hier_meta_bytes": ([_I64, _I64], ctypes.c_int64),
     "tkq_gemv_prepare": ([ctypes.POINTER(GemvDesc), _I32, ctypes.POINTER(GemvPlan)], ctypes.c_int),
     "tkq_gemv": ([ctypes.POINTER(GemvPlan), _P, _P], ctypes.c_int),
     "tkq_gemm_prefill": ([_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
@@ -162,8 +166,27 @@ def pack_bin(W, stream=None):
     return bits.view(-1) if vec else bits
 
 
+def hier_meta_bytes(N, K):
+    """Size of an int4-hier-g32 metadata block (tkq_hier_meta_bytes)."""
+    n = lib().tkq_hier_meta_bytes(N, K)
+    if n < 0:
+        raise TkqError(ESHAPE, "tkq_hier_meta_bytes")
+    return n
+
+
+def pack_int4_hier_g32(W, stream=None):
+    """W fp32 [N,K] -> (codes int32 [N,K/8], meta uint8 [hier_meta_bytes(N,K)]):
+    group bytes sc | mi << 4, zero padding, then half2 {d, dmin} per row."""
+    _need(W, torch.float32, "W")
+    N, K = W.shape
+    codes = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
+    meta = torch.empty(hier_meta_bytes(N, K), dtype=torch.uint8, device=W.device)
+    _call("tkq_pack_int4_hier_g32", _ptr(W), N, K, _ptr(codes), _ptr(meta), _stream(stream))
+    return codes, meta
+
+
 PACKERS = {FMT_INT4_G128: pack_int4_g128, FMT_K5_G128: pack_k5,
-           FMT_TERN_G128: pack_tern_g128}
+           FMT_TERN_G128: pack_tern_g128, FMT_INT4_HIER_G32: pack_int4_hier_g32}
 
 
 # ---- grouped GEMV ------------------------------------------------------------

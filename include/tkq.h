@@ -52,6 +52,18 @@
  *   bits {1,0}):
  *     bits uint32 [N][K/32]  : element 32j+i in bit i of word j, 1 <=> -1
  *     no metadata; x is packed the same way (uint32 [K/32]); y is int32.
+ * TKQ_FMT_INT4_HIER_G32 (Whetstone README, bytes/token table "int4 hier-g32"
+ *   at 4.28 bits/weight, quantizer table "group 32 with hierarchical scale
+ *   metadata", and "Prior art": Q4_K-like sub-scales against an fp16 pair,
+ *   with a whole row as the super-block and 4-bit indices):
+ *     codes uint32 [N][K/8]  : as TKQ_FMT_INT4_G128
+ *     meta  one block of tkq_hier_meta_bytes(N, K) bytes:
+ *           bytes [0, N*K/32): byte n*(K/32)+g = sc | mi << 4 for group g
+ *                              (columns 32g..32g+31) of row n;
+ *           zero bytes up to R = N*K/32 rounded up to a multiple of 16;
+ *           uint32 [N] at byte R: fp16 d in bits [0,16), fp16 dmin in
+ *                              bits [16,32) of row n.
+ *     w = d * sc * q - dmin * mi
  */
 #ifndef TKQ_H
 #define TKQ_H
@@ -79,11 +91,13 @@ extern "C" {
 #define TKQ_FMT_K5_G128 2
 #define TKQ_FMT_TERN_G128 3
 #define TKQ_FMT_BIN 4
+#define TKQ_FMT_INT4_HIER_G32 5
 
-/* Size limits: 1 <= N <= 2^31-1, 128 <= K <= 2^20 (K % 128 == 0 for the
- * group-128 codings and for every GEMV; K % 32 == 0 is enough for
- * tkq_pack_bin), and N*K <= 2^39 weights.  A GEMV additionally needs
- * K <= 32768 (int4), 16384 (K5), 49152 (ternary) or 262144 (binary). */
+/* Size limits: 1 <= N <= 2^31-1, 32 <= K <= 2^20 (K % 128 == 0 for the
+ * group-128 codings and for their GEMVs; K % 32 == 0 for tkq_pack_bin, the
+ * int4-hier-g32 coding and their GEMVs), and N*K <= 2^39 weights.  A GEMV
+ * additionally needs K <= 32768 (int4 g128 and hier-g32), 16384 (K5), 49152
+ * (ternary) or 262144 (binary). */
 #define TKQ_MAX_K (1 << 20)
 
 /* Library version (TKQ_VERSION of the build). */
@@ -131,6 +145,23 @@ int tkq_pack_tern_g128(const float* W, int64_t N, int64_t K, uint32_t* codes,
 int tkq_pack_bin(const float* W, int64_t N, int64_t K, uint32_t* bits,
                  void* stream);
 
+/* int4-hier-g32, RTN at both levels (the pages print no fitting procedure).
+ * Per row, for every 32-column group g:
+ *   lo = min(min w, 0), hi = max(max w, 0), s_g = (hi - lo) / 15, m_g = -lo;
+ * then per row
+ *   d = fp16(max_g s_g / 15), dmin = fp16(max_g m_g / 15)  (0 -> 1.0),
+ *   sc_g = clamp(rint(s_g / d), 1, 15), mi_g = clamp(rint(m_g / dmin), 0, 15),
+ *   q = clamp(rint((w + dmin * mi_g) / (d * sc_g)), 0, 15)
+ * (d * sc_g and dmin * mi_g are exact in fp32).  codes: uint32 [N][K/8];
+ * meta: tkq_hier_meta_bytes(N, K) bytes (layout above; the padding is
+ * written as zeros).  K % 32 == 0; codes and meta 16-byte aligned. */
+int tkq_pack_int4_hier_g32(const float* W, int64_t N, int64_t K,
+                           uint32_t* codes, uint8_t* meta, void* stream);
+
+/* Bytes of an int4-hier-g32 metadata block for an N x K matrix (host only;
+ * -1 if N < 1, K < 32 or K % 32 != 0). */
+int64_t tkq_hier_meta_bytes(int64_t N, int64_t K);
+
 /* ---- grouped GEMV -------------------------------------------------------
  * One launch computes any number of independent GEMVs y_i = W_i . x_i that
  * share one coding (e.g. every linear layer read for one decoded token).
@@ -149,7 +180,8 @@ int tkq_pack_bin(const float* W, int64_t N, int64_t K, uint32_t* bits,
 typedef struct tkq_gemv_desc {
   int32_t fmt;           /* TKQ_FMT_*; identical in every descriptor        */
   int32_t N;             /* rows = length of y, >= 1                        */
-  int32_t K;             /* columns = length of x, multiple of 128          */
+  int32_t K;             /* columns = length of x, multiple of 128 (of 32
+                            for TKQ_FMT_INT4_HIER_G32)                      */
   int32_t work0;         /* [prepare] index of the first row tile           */
   int32_t big_tiles;     /* [prepare] number of large tiles (rows_per_tile
                                       rows each) at the top of the matrix   */
@@ -160,7 +192,8 @@ typedef struct tkq_gemv_desc {
                                       cover the rows below the large ones   */
   const void* codes;     /* packed codes (layout per fmt)                   */
   const void* meta;      /* int4: uint32 half2 [N][K/128]; K5, ternary: fp16
-                            [N][K/128]; binary: ignored (may be NULL)       */
+                            [N][K/128]; hier-g32: its metadata block;
+                            binary: ignored (may be NULL)                   */
   const void* x;         /* fp16 [K]; binary: uint32 [K/32]                 */
   void* y;               /* fp16 [N]; binary: int32 [N]                     */
 } tkq_gemv_desc;         /* 64 bytes */

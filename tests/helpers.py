@@ -10,7 +10,7 @@ from oracle import pack as opack
 from oracle import quant as oquant
 from oracle import ref as oref
 
-FMTS = ("int4", "k5", "tern", "bin")
+FMTS = ("int4", "k5", "tern", "bin", "hier")
 
 
 def gpu_or_skip():
@@ -48,6 +48,9 @@ def oracle_pack(fmt, W):
         return opack.pack_tern(c), s
     if fmt == "bin":
         return opack.pack_bits(oquant.sign_bits(W)), None
+    if fmt == "hier":
+        q, sc, mi, d16, dmin16 = oquant.quantize_int4_hier_g32(W)
+        return opack.pack_int4(q), opack.pack_hier_meta(sc, mi, d16, dmin16)
     raise ValueError(fmt)
 
 
@@ -59,6 +62,8 @@ def oracle_wdeq(fmt, codes, meta, K):
         return oref.dequant_k5(codes, meta)
     if fmt == "tern":
         return oref.dequant_tern(codes, meta, K)
+    if fmt == "hier":
+        return oref.dequant_int4_hier(codes, meta, codes.shape[0], K)
     raise ValueError(fmt)
 
 
@@ -70,7 +75,26 @@ def device_codes_np(fmt, codes, meta):
         return codes.cpu().numpy(), meta.cpu().numpy()
     if fmt == "tern":
         return u32(codes), meta.cpu().numpy()
+    if fmt == "hier":
+        return u32(codes), meta.cpu().numpy()
     return u32(codes), None
+
+
+def hier_meta_rows(meta, N, K, rows):
+    """The metadata block of selected rows of an int4-hier-g32 matrix (from
+    the full block as a numpy uint8 array), re-laid out for those rows."""
+    sc, mi, d16, dmin16 = opack.unpack_hier_meta(meta, N, K)
+    return opack.pack_hier_meta(sc[rows], mi[rows], d16[rows], dmin16[rows])
+
+
+def device_rows_np(fmt, codes, meta, N, K, rows):
+    """Packed codes and metadata of selected rows, as device_codes_np would
+    give for a matrix of just those rows."""
+    import torch
+    rt = torch.from_numpy(np.asarray(rows)).to(codes.device)
+    if fmt == "hier":
+        return u32(codes[rt]), hier_meta_rows(meta.cpu().numpy(), N, K, rows)
+    return device_codes_np(fmt, codes[rt], None if meta is None else meta[rt])
 
 
 def assert_codes_equal(fmt, got, want):

@@ -51,14 +51,17 @@ def test_version_and_strings():
     assert "unknown" in tkq.strerror(-99)
 
 
-@pytest.mark.parametrize("name", ["tkq_pack_int4_g128", "tkq_pack_k5", "tkq_pack_tern_g128"])
+@pytest.mark.parametrize("name", ["tkq_pack_int4_g128", "tkq_pack_k5", "tkq_pack_tern_g128",
+                                  "tkq_pack_int4_hier_g32"])
 def test_pack_validation(name):
     f = getattr(tkq.lib(), name)
     assert f(None, 4, 128, A, A, None) == tkq.EINVAL
     assert f(A, 0, 128, A, A, None) == tkq.EINVAL
     assert f(A, 4, 0, A, A, None) == tkq.EINVAL
     assert f(A, 4, 100, A, A, None) == tkq.ESHAPE
-    assert f(A, 4, 96, A, A, None) == tkq.ESHAPE
+    if name != "tkq_pack_int4_hier_g32":
+        assert f(A, 4, 96, A, A, None) == tkq.ESHAPE   # group 128
+    assert f(A, 4, 48, A, A, None) == tkq.ESHAPE
     assert f(A, 4, (1 << 20) + 128, A, A, None) == tkq.ESHAPE
     assert f(A, 1 << 31, 128, A, A, None) == tkq.ESHAPE
     assert f(A, 4, 128, None, A, None) == tkq.EINVAL
@@ -66,6 +69,18 @@ def test_pack_validation(name):
     assert f(A + 4, 4, 128, A, A, None) == tkq.EALIGN
     assert f(A, 4, 128, A + 8, A, None) == tkq.EALIGN
     assert f(A, 4, 128, A, A + 2, None) == tkq.EALIGN
+
+
+def test_hier_meta_bytes():
+    f = tkq.lib().tkq_hier_meta_bytes
+    assert f(1, 32) == 16 + 4                      # one group byte, padded to 16
+    assert f(896, 896) == 896 * 28 + 4 * 896       # 25088 is a multiple of 16
+    assert f(3, 96) == 16 + 12
+    assert f(5, 160) == 32 + 20                    # 25 group bytes -> 32
+    assert f(0, 32) == -1 and f(4, 48) == -1 and f(4, 0) == -1
+    from oracle import pack as opack
+    for n, k in [(1, 32), (3, 96), (5, 160), (151936, 896), (3584, 18944)]:
+        assert f(n, k) == opack.hier_meta_bytes(n, k)
 
 
 def test_pack_bin_validation():
@@ -107,14 +122,16 @@ def _tiles(d):
     return out
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5])
 def test_prepare_tiles_cover_rows(fmt):
     shapes = [(1, 128), (7, 896), (128, 896), (4864, 896), (896, 4864), (333, 4864), (151936, 896)]
+    if fmt == 5:
+        shapes[1:1] = [(3, 32), (65, 96)]
     arr = _descs(fmt, shapes)
     st, plan = _prepare(arr)
     assert st == tkq.OK
     work = 0
-    per_chunk = {1: 32, 2: 16, 3: 64, 4: 128}[fmt]
+    per_chunk = {1: 32, 2: 16, 3: 64, 4: 128, 5: 32}[fmt]
     for d, (n, k) in zip(arr, shapes):
         assert d.work0 == work
         tiles = _tiles(d)
@@ -163,6 +180,14 @@ def test_prepare_validation():
     assert _prepare(arr)[0] == tkq.EFORMAT
     arr = _descs(1, [(8, 200)])
     assert _prepare(arr)[0] == tkq.ESHAPE
+    arr = _descs(1, [(8, 96)])                # int4 g128 needs K % 128
+    assert _prepare(arr)[0] == tkq.ESHAPE
+    arr = _descs(5, [(8, 96), (3, 32)])       # hier-g32 needs only K % 32
+    assert _prepare(arr)[0] == tkq.OK
+    arr = _descs(5, [(8, 112)])
+    assert _prepare(arr)[0] == tkq.ESHAPE
+    arr = _descs(5, [(8, 65536)])
+    assert _prepare(arr)[0] == tkq.ESHAPE
     arr = _descs(1, [(8, 65536)])             # beyond the int4 GEMV's K
     assert _prepare(arr)[0] == tkq.ESHAPE
     arr = _descs(1, [(0, 128)])
@@ -193,6 +218,7 @@ def test_gemv_rejects_unprepared_plan():
 def test_prefill_validation():
     f = tkq.lib().tkq_gemm_prefill
     assert f(2, 64, 128, 128, A, A, A, A, None, 0, None) == tkq.EFORMAT
+    assert f(5, 64, 128, 128, A, A, A, A, None, 0, None) == tkq.EFORMAT
     assert f(1, 0, 128, 128, A, A, A, A, None, 0, None) == tkq.EINVAL
     assert f(1, 64, 128, 100, A, A, A, A, None, 0, None) == tkq.ESHAPE
     assert f(1, 64, 128, 128, None, A, A, A, None, 0, None) == tkq.EINVAL

@@ -12,11 +12,14 @@ from oracle import ref as oref
 
 pytestmark = pytest.mark.gpu
 
-MAXK = {"int4": 18944, "k5": 4864, "tern": 18944, "bin": 18944}
+MAXK = {"int4": 18944, "k5": 4864, "tern": 18944, "bin": 18944, "hier": 18944}
+FLOAT_FMTS = ["int4", "k5", "tern", "hier"]
 
 
 def _shapes(fmt):
     s = [(1, 128), (5, 256), (128, 896), (333, 896), (1000, 4864), (77, 1152), (2049, 384)]
+    if fmt == "hier":                       # K % 32 == 0 suffices
+        s += [(3, 32), (70, 96), (129, 160), (40, 32 * 593)]
     s.append((300, MAXK[fmt]))
     return s
 
@@ -36,6 +39,8 @@ def _device_pack(torch, tkq, fmt, Wd):
         return tkq.pack_k5(Wd)
     if fmt == "tern":
         return tkq.pack_tern_g128(Wd)
+    if fmt == "hier":
+        return tkq.pack_int4_hier_g32(Wd)
     return tkq.pack_bin(Wd), None
 
 
@@ -68,7 +73,7 @@ def _check(fmt, W, x, y, codes, meta, what):
     check_gemv(y.float().cpu().numpy(), w_deq, x, what)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin"])
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin", "hier"])
 def test_gemv_single_shapes(fmt):
     torch = gpu_or_skip()
     from gemm_tkq_gemv_amd import tkq
@@ -80,7 +85,7 @@ def test_gemv_single_shapes(fmt):
         _check(fmt, W, x, it["y"], it["codes"], it["meta"], "%s %dx%d" % (fmt, N, K))
 
 
-@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin"])
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin", "hier"])
 def test_gemv_grouped_mixed_shapes(fmt):
     torch = gpu_or_skip()
     from gemm_tkq_gemv_amd import tkq
@@ -101,7 +106,7 @@ def test_gemv_grouped_mixed_shapes(fmt):
         assert torch.equal(a, it["y"])
 
 
-@pytest.mark.parametrize("fmt", ["int4", "k5", "tern"])
+@pytest.mark.parametrize("fmt", FLOAT_FMTS)
 def test_gemv_unit_vectors_bit_exact(fmt):
     torch = gpu_or_skip()
     from gemm_tkq_gemv_amd import tkq
@@ -119,7 +124,7 @@ def test_gemv_unit_vectors_bit_exact(fmt):
         assert np.array_equal(y.cpu().numpy().view(np.uint16), want.view(np.uint16)), (fmt, k)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "k5", "tern"])
+@pytest.mark.parametrize("fmt", FLOAT_FMTS)
 def test_gemv_exact_zeros(fmt):
     torch = gpu_or_skip()
     from gemm_tkq_gemv_amd import tkq

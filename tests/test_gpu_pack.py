@@ -21,13 +21,15 @@ def _pack_gpu(fmt, W):
         out = tkq.pack_k5(Wd)
     elif fmt == "tern":
         out = tkq.pack_tern_g128(Wd)
+    elif fmt == "hier":
+        out = tkq.pack_int4_hier_g32(Wd)
     else:
         out = (tkq.pack_bin(Wd), None)
     torch.cuda.synchronize()
     return device_codes_np(fmt, *out)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin"])
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin", "hier"])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_pack_bit_exact(fmt, shape):
     N, K = shape
@@ -59,7 +61,7 @@ def _degenerate_rows():
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin"])
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin", "hier"])
 def test_pack_degenerate_groups(fmt):
     W = _degenerate_rows()
     assert_codes_equal(fmt, _pack_gpu(fmt, W), oracle_pack(fmt, W))
@@ -75,3 +77,29 @@ def test_pack_bin_k_multiple_of_32(K):
     W, x = inputs.binary_case(5, K)
     assert_codes_equal("bin", _pack_gpu("bin", W), oracle_pack("bin", W))
     assert_codes_equal("bin", _pack_gpu("bin", x[None, :]), oracle_pack("bin", x[None, :]))
+
+
+@pytest.mark.parametrize("shape", [(1, 32), (5, 96), (3, 160), (65, 224), (2, 32 * 593)])
+def test_pack_hier_k_multiple_of_32(shape):
+    """int4-hier-g32 needs only K % 32 == 0: K % 64 == 32 leaves the last
+    half-wave of the packer idle; the block padding is written as zeros."""
+    N, K = shape
+    W = inputs.normal_matrix((78, N, K), N, K)
+    W[0, :32] *= np.float32(1e-7)                 # a tiny group beside normal ones
+    assert_codes_equal("hier", _pack_gpu("hier", W), oracle_pack("hier", W))
+
+
+def test_pack_hier_row_scale_guard():
+    """Rows whose fp16 row scale underflows (Whetstone, status list): the
+    stored d / dmin are 1.0, bit-exact with the oracle, beside normal rows."""
+    W = inputs.normal_matrix((79, 6, 256), 6, 256)
+    W[1] = 1e-9
+    W[2] = -3e-9
+    W[3, :] = 0.0
+    W[4] *= np.float32(1e-5)
+    got = _pack_gpu("hier", W)
+    want = oracle_pack("hier", W)
+    assert_codes_equal("hier", got, want)
+    from oracle import pack as opack
+    _, _, d16, dmin16 = opack.unpack_hier_meta(got[1], 6, 256)
+    assert np.all(d16[1:4] == 1.0) and np.all(dmin16 != 0)

@@ -1,6 +1,6 @@
 """Full-size workloads in the launch configuration the benchmark times: the
 single 896x896 GEMV, the Qwen2.5-0.5B sweep (169 GEMVs in one launch) in the
-int4, K5 and ternary codings, the binary sign GEMVs, and the Qwen2.5-7B int4
+int4, K5, ternary and int4-hier-g32 codings, the binary sign GEMVs, and the Qwen2.5-7B int4
 sweep (197 GEMVs).  Codes of sampled rows are bit-exact against the oracle's
 quantization of the same rows; sampled outputs are within the per-row bound
 (binary: every output exact)."""
@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 from gemm_tkq_gemv_amd import inputs
-from helpers import assert_codes_equal, check_gemv, device_codes_np, gpu_or_skip, oracle_pack, oracle_wdeq
+from helpers import (assert_codes_equal, check_gemv, device_codes_np, device_rows_np, gpu_or_skip, oracle_pack,
+                     oracle_wdeq)
 from oracle import ref as oref
 
 pytestmark = pytest.mark.gpu
@@ -34,11 +35,11 @@ def test_single_gemv_896():
 
 @pytest.fixture(scope="module")
 def sweep05b():
-    """Qwen2.5-0.5B sweep packed in int4, K5 and ternary, with sampled rows."""
+    """Qwen2.5-0.5B sweep packed in every float coding, with sampled rows."""
     torch = gpu_or_skip()
     from gemm_tkq_gemv_amd import tkq
     shapes = inputs.sweep_shapes("qwen2.5-0.5b")
-    packed = {f: [] for f in ("int4", "k5", "tern")}
+    packed = {f: [] for f in ("int4", "k5", "tern", "hier")}
     samples = []
     for i, (_, N, K) in enumerate(shapes):
         W, x = inputs.sweep_matrix("qwen2.5-0.5b", i, N, K)
@@ -46,7 +47,8 @@ def sweep05b():
         samples.append((rows, W[rows].copy(), x))
         Wd = torch.from_numpy(W).cuda()
         xd = torch.from_numpy(x).cuda()
-        for f, fn in (("int4", tkq.pack_int4_g128), ("k5", tkq.pack_k5), ("tern", tkq.pack_tern_g128)):
+        for f, fn in (("int4", tkq.pack_int4_g128), ("k5", tkq.pack_k5), ("tern", tkq.pack_tern_g128),
+                      ("hier", tkq.pack_int4_hier_g32)):
             codes, meta = fn(Wd)
             y = torch.full((N,), float("nan"), dtype=torch.float16, device="cuda")
             packed[f].append(dict(codes=codes, meta=meta, x=xd, y=y, N=N, K=K))
@@ -55,7 +57,7 @@ def sweep05b():
     return packed, samples
 
 
-@pytest.mark.parametrize("fmt", ["int4", "k5", "tern"])
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "hier"])
 def test_sweep_05b(sweep05b, fmt):
     torch = gpu_or_skip()
     from gemm_tkq_gemv_amd import tkq
@@ -69,8 +71,7 @@ def test_sweep_05b(sweep05b, fmt):
         y = it["y"].float().cpu().numpy()
         assert np.all(np.isfinite(y))
         oc, om = oracle_pack(fmt, Wr)
-        rt = torch.from_numpy(rows).cuda()
-        got = device_codes_np(fmt, it["codes"][rt], it["meta"][rt])
+        got = device_rows_np(fmt, it["codes"], it["meta"], it["N"], it["K"], rows)
         assert_codes_equal(fmt, got, (oc, om))
         worst = max(worst, check_gemv(y[rows], oracle_wdeq(fmt, oc, om, it["K"]), x,
                                       "%s N=%d K=%d" % (fmt, it["N"], it["K"])))
