@@ -13,6 +13,8 @@ of a row reads front to back):
 * ternary      uint32 [N][K/16]: element 16j+i in bits [2i, 2i+2) of word j,
                 code = t + 1; fp16 scale [N][K/128].
 * binary       uint32 [N][K/32]: element 32j+i in bit i of word j.
+* int2         uint32 [N][K/16]: element 16j+i in bits [2i, 2i+2) of word j
+                (the ternary field layout), meta as int4 (half2 {scale, zero}).
 * int4-hier-g32 codes as int4; one metadata block per matrix:
                 bytes [0, N*K/32): byte n*(K/32)+g = sc | (mi << 4) of group g
                 of row n; zero padding up to a multiple of 16 bytes (offset
@@ -83,6 +85,15 @@ def pack_tern(codes):
 
 
 def unpack_tern(words, K):
+    return _unpack_fields(words, K, 2)
+
+
+def pack_int2(q):
+    """int2 codes [N,K] (0..3) -> uint32 [N,K/16], LSB-first 2-bit fields."""
+    return _pack_fields(q, 2)
+
+
+def unpack_int2(words, K):
     return _unpack_fields(words, K, 2)
 
 

@@ -112,3 +112,13 @@ def test_sweep_bytes_other_codings():
 def test_prefill_flops():
     tot = sum(acc.gemm_flops(512, n, k) for _, n, k in inputs.prefill_shapes())
     assert tot == 208_574_349_312
+
+
+def test_int2_bytes_match_page_row():
+    # Whetstone bytes/token table: int2 g128 at 2.25 bits/weight, 138.9 MB
+    vals, fmts = _read("whetstone_roofline.txt")
+    shapes = inputs.sweep_shapes("qwen2.5-0.5b")
+    total = sum(acc.weight_bytes("int2", n, k) for _, n, k in shapes)
+    bpw, mb, _ = fmts["int2_g128"]
+    assert 8.0 * total / acc.linear_params(shapes) == bpw
+    assert abs(total / 1e6 - mb) <= 0.05 + 1e-9

@@ -135,3 +135,71 @@ def test_relative_error_sanity():
     assert 0.08 < rel(d4) < 0.12
     assert 0.45 < rel(dt) < 0.56
     assert rel(dk) < 0.01
+
+
+# ---- int2 g128 (Whetstone, "int2 g128": 2-bit codes, int4-style metadata) ----
+
+def _int2_roundtrip(W):
+    q, s, z = quant.quantize_int2_g128(W)
+    return q, s, z, ref.dequant_int2(pack.pack_int2(q), pack.pack_int4_meta(s, z), W.shape[1])
+
+
+def test_int2_lossless_on_grid():
+    # weights on the 1/4 grid spanning [-0.5, 0.25]: hi - lo = 3/4, s = 1/4
+    # exactly, z = 2 and q = 4 w + 2
+    k = np.tile(np.arange(4), 32)
+    W = ((k.astype(np.float32) - 2) / np.float32(4))[None, :]
+    q, s, z, w = _int2_roundtrip(W)
+    assert s[0, 0] == np.float16(0.25) and z[0, 0] == 2
+    assert np.array_equal(q[0].astype(int), k)
+    assert np.array_equal(w.astype(np.float32), W)
+
+
+def test_int2_rounding_half_even():
+    W = np.zeros((1, 128), np.float32)
+    W[0, 0], W[0, 1] = -0.5, 0.25          # s = 0.25, z = 2
+    W[0, 2] = 0.125                        # w/s = 0.5 -> 0 (half even) -> q = 2
+    W[0, 3] = -0.375                       # -1.5 -> -2 -> q = 0
+    W[0, 4] = -0.125                       # -0.5 -> -0 -> q = 2
+    q, s, z, w = _int2_roundtrip(W)
+    assert q[0, :5].tolist() == [0, 3, 2, 0, 2]
+
+
+def test_int2_codes_are_nearest_level():
+    """Brute force: each code is the nearest of the four levels s*(q - z)
+    (ties excluded), and the dequantized weight is within half a step of every
+    weight inside the group's range."""
+    rng = np.random.default_rng(21)
+    W = (rng.standard_normal((5, 256)) * 0.02).astype(np.float32)
+    q, s, z, w = _int2_roundtrip(W)
+    for n in range(5):
+        for g in range(2):
+            sf, zf = float(s[n, g]), float(z[n, g])
+            levels = sf * (np.arange(4) - zf)
+            for k in range(128 * g, 128 * g + 128):
+                err = np.abs(float(W[n, k]) - levels)
+                o = np.argsort(err)
+                if err[o[1]] - err[o[0]] > 1e-9:
+                    assert q[n, k] == o[0]
+
+
+@pytest.mark.parametrize("val", [0.0, 1e-9, -0.3, 0.7])
+def test_int2_degenerate_groups(val):
+    # constant groups: the range [min(v,0), max(v,0)] puts v on a level (up
+    # to the fp16 rounding of s); a scale that underflows is stored as 1 and
+    # the group dequantizes to 0
+    W = np.full((1, 128), val, np.float32)
+    q, s, z, w = _int2_roundtrip(W)
+    assert s[0, 0] != 0
+    if abs(val) < 1e-6:
+        assert s[0, 0] == 1 and np.all(w == 0)
+    else:
+        assert np.max(np.abs(w - W)) <= 3 * 2.0 ** -11 * abs(val)
+
+
+def test_int2_pack_layout():
+    q = np.zeros((1, 32), np.uint8)
+    q[0, 17] = 3                           # word 1, field 1 -> bits 2..3
+    words = pack.pack_int2(q)
+    assert words.tolist() == [[0, 3 << 2]]
+    assert np.array_equal(pack.unpack_int2(words, 32), q)
