@@ -208,6 +208,14 @@ struct Codec<kFmtHier> : Codec<kFmtInt4> {
   static constexpr int CPG = 1, MB = 1;
 };
 
+// int2 g128: the ternary field layout (so the ternary unpack, with code 0 as
+// the bias reference) and the int4 metadata (fp16 scale and zero-point).
+template <>
+struct Codec<kFmtInt2> : Codec<kFmtTern> {
+  static constexpr uint32_t kZero = 0u;
+  static constexpr int CPG = 2, MB = 4;
+};
+
 // Binary: 128 sign bits per chunk; x is kept as packed words.
 template <>
 struct Codec<kFmtBin> {
@@ -333,7 +341,7 @@ struct Runner {
           const uint32_t m = b.m[u][j];
           rs = fmaf((float)(m & 15u), d, rs);
           rm = fmaf((float)(m >> 4), xsum[j], rm);
-        } else if constexpr (FMT == kFmtInt4) {
+        } else if constexpr (FMT == kFmtInt4 || FMT == kFmtInt2) {
           const float d = Cd::dot(b.c[u][j], xr[j], R) - bias[j];
           res = fmaf(half_lo(b.m[u][j]), fmaf(-half_hi(b.m[u][j]), xsum[j], d), res);
         } else {
@@ -486,7 +494,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WP
 
 template <int FMT>
 constexpr int max_passes() {
-  return FMT == kFmtBin ? 8 : (FMT == kFmtTern ? 3 : 4);  // int4, hier-g32, K5: 4
+  return FMT == kFmtBin ? 8 : ((FMT == kFmtTern || FMT == kFmtInt2) ? 3 : 4);  // int4, hier-g32, K5: 4
 }
 
 typedef void (*GemvFn)(const tkq_gemv_desc*, int);
@@ -509,6 +517,7 @@ int gemv_max_passes(int fmt) {
   switch (fmt) {
     case kFmtInt4: return max_passes<kFmtInt4>();
     case kFmtHier: return max_passes<kFmtHier>();
+    case kFmtInt2: return max_passes<kFmtInt2>();
     case kFmtK5: return max_passes<kFmtK5>();
     case kFmtTern: return max_passes<kFmtTern>();
     case kFmtBin: return max_passes<kFmtBin>();
@@ -522,6 +531,7 @@ hipError_t launch_gemv(int fmt, int jmax, const tkq_gemv_desc* dev_descs, int co
   switch (fmt) {
     case kFmtInt4: fn = pick<kFmtInt4>(jmax); break;
     case kFmtHier: fn = pick<kFmtHier>(jmax); break;
+    case kFmtInt2: fn = pick<kFmtInt2>(jmax); break;
     case kFmtK5: fn = pick<kFmtK5>(jmax); break;
     case kFmtTern: fn = pick<kFmtTern>(jmax); break;
     case kFmtBin: fn = pick<kFmtBin>(jmax); break;

@@ -15,6 +15,7 @@ constexpr int kFmtK5 = TKQ_FMT_K5_G128;
 constexpr int kFmtTern = TKQ_FMT_TERN_G128;
 constexpr int kFmtBin = TKQ_FMT_BIN;
 constexpr int kFmtHier = TKQ_FMT_INT4_HIER_G32;
+constexpr int kFmtInt2 = TKQ_FMT_INT2_G128;
 
 // Work decomposition of one GEMV, packed into tkq_gemv_desc::shape.
 struct GemvShape {
@@ -32,6 +33,7 @@ inline int weights_per_chunk(int fmt) {
     case kFmtHier: return 32;
     case kFmtK5: return 16;
     case kFmtTern: return 64;
+    case kFmtInt2: return 64;
     case kFmtBin: return 128;
   }
   return 0;

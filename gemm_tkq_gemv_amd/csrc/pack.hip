@@ -14,6 +14,7 @@
 //               z = clamp(rint(-lo/s), 0, 15), q = clamp(rint(w/s) + z, 0, 15)
 //   K5        : s = fp16(max|w| / 121), c = clamp(rint(w/s), -121, 121) + 121
 //   ternary   : s = fp16(sequential-sum|w| / 128), code = clamp(rint(w/s),-1,1)+1
+//   int2 g128 : as int4 with 4 levels: s = fp16((hi-lo)/3), z, q in 0..3
 //   int4 hier-g32 (Whetstone README, quantizer table "group 32 with
 //               hierarchical scale metadata"; "Prior art", the Q4_K
 //               comparison): per 32-group s_g = (hi-lo)/15, m_g = -lo; per
@@ -64,6 +65,30 @@ __global__ __launch_bounds__(256) void pack_int4_kernel(const float* __restrict_
   // elements 2*lane, 2*lane+1 are nibbles (2*lane)%8, +1 of word (2*lane)/8:
   // little-endian, so byte `lane` of the row's group block.
   codes[row * (K / 2) + col / 2 + lane] = (uint8_t)(q0 | (q1 << 4));
+  if (lane == 0) meta[g] = (uint32_t)sbits | ((uint32_t)half_bits(zf) << 16);
+}
+
+__global__ __launch_bounds__(256) void pack_int2_kernel(const float* __restrict__ W, int64_t K,
+                                                        int64_t groups, uint8_t* __restrict__ codes,
+                                                        uint32_t* __restrict__ meta) {
+  int64_t g;
+  if (!group_of_wave(groups, &g)) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t gpr = K / kGroup;
+  const int64_t row = g / gpr, col = (g - row * gpr) * kGroup;
+  const float2 w = *reinterpret_cast<const float2*>(W + row * K + col + 2 * lane);
+  const float lo = fminf(wave_min(fminf(w.x, w.y)), 0.0f);
+  const float hi = fmaxf(wave_max(fmaxf(w.x, w.y)), 0.0f);
+  uint16_t sbits;
+  const float s = guard_scale((hi - lo) / 3.0f, &sbits);
+  const float zf = (float)(int)fminf(fmaxf(rintf(-lo / s), 0.0f), 3.0f);
+  const int q0 = (int)fminf(fmaxf(rintf(w.x / s) + zf, 0.0f), 3.0f);
+  const int q1 = (int)fminf(fmaxf(rintf(w.y / s) + zf, 0.0f), 3.0f);
+  // 2-bit fields: elements 2*lane, 2*lane+1 form nibble `lane` of the group's
+  // 32 bytes; lanes 2m and 2m+1 share byte m.
+  const int nib = q0 | (q1 << 2);
+  const int other = __shfl_xor(nib, 1, 64);
+  if ((lane & 1) == 0) codes[row * (K / 4) + col / 4 + (lane >> 1)] = (uint8_t)(nib | (other << 4));
   if (lane == 0) meta[g] = (uint32_t)sbits | ((uint32_t)half_bits(zf) << 16);
 }
 
@@ -218,6 +243,10 @@ hipError_t launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* code
   switch (fmt) {
     case kFmtInt4:
       hipLaunchKernelGGL(pack_int4_kernel, grid, block, 0, stream, W, K, groups, (uint8_t*)codes,
+                         (uint32_t*)meta);
+      break;
+    case kFmtInt2:
+      hipLaunchKernelGGL(pack_int2_kernel, grid, block, 0, stream, W, K, groups, (uint8_t*)codes,
                          (uint32_t*)meta);
       break;
     case kFmtK5:

@@ -41,7 +41,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool known_fmt(int fmt) {
   return fmt == TKQ_FMT_INT4_G128 || fmt == TKQ_FMT_K5_G128 || fmt == TKQ_FMT_TERN_G128 ||
-         fmt == TKQ_FMT_BIN || fmt == TKQ_FMT_INT4_HIER_G32;
+         fmt == TKQ_FMT_BIN || fmt == TKQ_FMT_INT4_HIER_G32 || fmt == TKQ_FMT_INT2_G128;
 }
 
 // Column unit of a coding's GEMV (its group size, or one code word).
@@ -153,6 +153,11 @@ int tkq_pack_tern_g128(const float* W, int64_t N, int64_t K, uint32_t* codes, ui
 
 int tkq_pack_bin(const float* W, int64_t N, int64_t K, uint32_t* bits, void* stream) {
   return pack_common(TKQ_FMT_BIN, W, N, K, bits, nullptr, false, 32, stream);
+}
+
+int tkq_pack_int2_g128(const float* W, int64_t N, int64_t K, uint32_t* codes, uint32_t* meta,
+                       void* stream) {
+  return pack_common(TKQ_FMT_INT2_G128, W, N, K, codes, meta, true, 128, stream);
 }
 
 int tkq_pack_int4_hier_g32(const float* W, int64_t N, int64_t K, uint32_t* codes, uint8_t* meta,

@@ -52,6 +52,10 @@
  *   bits {1,0}):
  *     bits uint32 [N][K/32]  : element 32j+i in bit i of word j, 1 <=> -1
  *     no metadata; x is packed the same way (uint32 [K/32]); y is int32.
+ * TKQ_FMT_INT2_G128 (Whetstone README, bytes/token and quality tables, "int2
+ *   g128" at 2.25 bits/weight):
+ *     codes uint32 [N][K/16] : element 16j+i in bits [2i,2i+2) of word j
+ *     meta  uint32 [N][K/128]: as TKQ_FMT_INT4_G128;  w = scale * (q - zero)
  * TKQ_FMT_INT4_HIER_G32 (Whetstone README, bytes/token table "int4 hier-g32"
  *   at 4.28 bits/weight, quantizer table "group 32 with hierarchical scale
  *   metadata", and "Prior art": Q4_K-like sub-scales against an fp16 pair,
@@ -92,12 +96,13 @@ extern "C" {
 #define TKQ_FMT_TERN_G128 3
 #define TKQ_FMT_BIN 4
 #define TKQ_FMT_INT4_HIER_G32 5
+#define TKQ_FMT_INT2_G128 6
 
 /* Size limits: 1 <= N <= 2^31-1, 32 <= K <= 2^20 (K % 128 == 0 for the
  * group-128 codings and for their GEMVs; K % 32 == 0 for tkq_pack_bin, the
  * int4-hier-g32 coding and their GEMVs), and N*K <= 2^39 weights.  A GEMV
  * additionally needs K <= 32768 (int4 g128 and hier-g32), 16384 (K5), 49152
- * (ternary) or 262144 (binary). */
+ * (ternary, int2) or 262144 (binary). */
 #define TKQ_MAX_K (1 << 20)
 
 /* Library version (TKQ_VERSION of the build). */
@@ -139,6 +144,13 @@ int tkq_pack_k5(const float* W, int64_t N, int64_t K, uint8_t* codes,
  * codes: uint32 [N][K/16]; scale: fp16 bits [N][K/128].  K % 128 == 0. */
 int tkq_pack_tern_g128(const float* W, int64_t N, int64_t K, uint32_t* codes,
                        uint16_t* scale, void* stream);
+
+/* int2 g128, asymmetric RTN (Whetstone README, "int2 g128"): the int4 g128
+ * quantizer with four levels: s = fp16((hi - lo) / 3), z = clamp(rint(-lo /
+ * s), 0, 3), q = clamp(rint(w / s) + z, 0, 3).  codes: uint32 [N][K/16];
+ * meta: uint32 [N][K/128] = half2 {s, z}.  K % 128 == 0. */
+int tkq_pack_int2_g128(const float* W, int64_t N, int64_t K, uint32_t* codes,
+                       uint32_t* meta, void* stream);
 
 /* Sign bits (Whetstone README, "Measured hardware facts"): bit = 1 exactly
  * when w < 0.  bits: uint32 [N][K/32].  K % 32 == 0.  Also packs x (N = 1). */
@@ -191,7 +203,7 @@ typedef struct tkq_gemv_desc {
   int32_t small_rows;    /* [prepare] rows of a small tile; small tiles
                                       cover the rows below the large ones   */
   const void* codes;     /* packed codes (layout per fmt)                   */
-  const void* meta;      /* int4: uint32 half2 [N][K/128]; K5, ternary: fp16
+  const void* meta;      /* int4, int2: uint32 half2 [N][K/128]; K5, ternary: fp16
                             [N][K/128]; hier-g32: its metadata block;
                             binary: ignored (may be NULL)                   */
   const void* x;         /* fp16 [K]; binary: uint32 [K/32]                 */
