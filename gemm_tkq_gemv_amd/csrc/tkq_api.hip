@@ -3,6 +3,8 @@
 // on failure nothing is enqueued.
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace {
@@ -21,13 +23,20 @@ constexpr int64_t kMaxWeights = int64_t(1) << 39;
 //  prefer_passes  on equal lane utilisation, the pass count to prefer: more
 //         passes = more rows per wave step = fewer cross-lane reductions per
 //         row, at the cost of x registers.
+//  max_passes  cap on passes: the launch's kernel variant is sized for the
+//         largest pass count of its matrices, so one long-K matrix would set
+//         the register budget (and occupancy) of the whole sweep.
+#ifndef TKQ_TERN_JMAX
+#define TKQ_TERN_JMAX 2
+#endif
 struct PlanParams {
-  int prefer_passes;
+  int prefer_passes, max_passes;
   int64_t tile, small, tail;
 };
 PlanParams plan_params(int fmt) {
-  if (fmt == TKQ_FMT_INT4_G128 || fmt == TKQ_FMT_INT4_HIER_G32) return {2, 48 << 10, 4 << 10, 40 << 20};
-  return {1, 24 << 10, 4 << 10, 40 << 20};
+  if (fmt == TKQ_FMT_INT4_G128 || fmt == TKQ_FMT_INT4_HIER_G32) return {2, 4, 48 << 10, 4 << 10, 40 << 20};
+  if (fmt == TKQ_FMT_TERN_G128 || fmt == TKQ_FMT_INT2_G128) return {1, TKQ_TERN_JMAX, 24 << 10, 4 << 10, 40 << 20};
+  return {1, 8, 24 << 10, 4 << 10, 40 << 20};
 }
 constexpr int kMaxTileRows = tkq::kGemvMaxTileRows;
 
@@ -75,7 +84,7 @@ int pack_common(int fmt, const float* W, int64_t N, int64_t K, void* codes, void
 tkq::GemvShape choose_shape(int fmt, int K) {
   const int prefer = plan_params(fmt).prefer_passes;
   const int C = K / tkq::weights_per_chunk(fmt);
-  const int jmax = tkq::gemv_max_passes(fmt);
+  const int jmax = std::min(tkq::gemv_max_passes(fmt), plan_params(fmt).max_passes);
   tkq::GemvShape best = {6, 0, 0};
   double best_util = -1.0;
   for (int S : {1, 2, 4}) {
