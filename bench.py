@@ -233,8 +233,9 @@ def blas_threads():
 
 # ------------------------------------------------------------------- runners --
 
-def run_sweep(args, torch, tkq, inputs, model, fmt):
-    from gemm_tkq_gemv_amd import inputs as _inp  # noqa: F401
+def run_sweep(args, torch, tkq, inputs, model, fmt, greedy=False):
+    """greedy: the launch also selects the largest output of the last GEMV
+    (the output projection) into a device token (tkq_gemv_argmax)."""
     items, shapes = build_sweep(torch, tkq, inputs, model, fmt)
     fmt_bytes = _fmt_bytes(fmt)
     step_bytes = sum(fmt_bytes(n, k) for _, n, k in shapes)
@@ -242,8 +243,14 @@ def run_sweep(args, torch, tkq, inputs, model, fmt):
                     + (0 if it["meta"] is None else it["meta"].numel() * it["meta"].element_size())
                     for it in items)
     batches = rotated_batches(torch, tkq, fmt, items, footprint)
-    ms = time_steps(torch, lambda s: batches[s % len(batches)].run(), args.steps, args.warmup,
-                    args.graph, len(batches))
+    if greedy:
+        token = torch.zeros(1, dtype=torch.int32, device="cuda")
+        scratch = batches[0].greedy_scratch()
+        last = len(items) - 1
+        step = lambda s: batches[s % len(batches)].run_argmax(last, token, scratch)  # noqa: E731
+    else:
+        step = lambda s: batches[s % len(batches)].run()  # noqa: E731
+    ms = time_steps(torch, step, args.steps, args.warmup, args.graph, len(batches))
     gbs = step_bytes / (ms * 1e-3) / 1e9
     ceiling_tok_s = HBM_PEAK_GBS * 1e9 / step_bytes
     out = {
@@ -252,8 +259,9 @@ def run_sweep(args, torch, tkq, inputs, model, fmt):
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic: seeded N(0,0.02) weights at the model's shapes, N(0,1) fp16 x",
-        "config": {"workload": "%s decode weight sweep, %s, %d GEMVs in one launch, batch 1"
-                               % (model, _fmt_name(fmt), len(shapes)),
+        "config": {"workload": "%s decode weight sweep, %s, %d GEMVs in one launch, batch 1%s"
+                               % (model, _fmt_name(fmt), len(shapes),
+                                  ", greedy token selected on the GPU in the same launch" if greedy else ""),
                    "bytes_per_step": step_bytes, "copies_rotated": len(batches),
                    "weights": _fmt_name(fmt), "x": "fp16", "accumulate": "fp32", "y": "fp16",
                    "launch": "hip graph replay" if args.graph != "none" else "stream launch"},
@@ -385,7 +393,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="0.5b-int4",
-                    choices=["0.5b-int4", "0.5b-k5", "0.5b-tern", "0.5b-hier", "0.5b-int2", "bin", "single-896",
+                    choices=["0.5b-int4", "0.5b-int4-greedy", "0.5b-k5", "0.5b-tern", "0.5b-hier",
+                             "0.5b-int2", "bin", "single-896",
                              "7b-int4", "7b-hier", "7b-prefill", "probe"])
     ap.add_argument("--graph", default="none", choices=["none", "step", "all"],
                     help="launch steps as HIP graph replays (see time_steps)")
@@ -419,10 +428,11 @@ def main():
         del src, dst
 
     w = args.workload
-    if w in ("0.5b-int4", "0.5b-k5", "0.5b-tern", "0.5b-hier", "0.5b-int2", "7b-int4", "7b-hier"):
+    if w in ("0.5b-int4", "0.5b-int4-greedy", "0.5b-k5", "0.5b-tern", "0.5b-hier", "0.5b-int2",
+             "7b-int4", "7b-hier"):
         model = "qwen2.5-7b" if w.startswith("7b") else "qwen2.5-0.5b"
         fmt = w.split("-")[1]
-        out = run_sweep(args, torch, tkq, inputs, model, fmt)
+        out = run_sweep(args, torch, tkq, inputs, model, fmt, greedy=w.endswith("greedy"))
         torch.cuda.empty_cache()
         if not args.no_cpu_baseline:
             rate, spent, done, passes = cpu_baseline_gemv(inputs, model, fmt, args.cpu_budget)

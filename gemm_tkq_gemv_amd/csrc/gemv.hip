@@ -33,8 +33,15 @@
 //    to nearest even.  The binary coding XORs code and x words and counts
 //    bits (v_bcnt_u32_b32): y = K - 2 * popcount (Whetstone README, "Measured
 //    hardware facts").
-//  * Loads of the next row step are issued before the current step is
-//    computed (two register buffers used alternately).
+//  * Greedy selection (a separate kernel variant): the workgroups of one
+//    chosen matrix also reduce their outputs, in registers, to the largest
+//    (value, smallest row) as a 64-bit order-preserving key and store it to
+//    their own slot of a caller scratch array; a one-workgroup kernel then
+//    reduces the slots to the winning row, so the index of the largest logit
+//    never goes through the host and the logits are not read back (Whetstone
+//    README, status list: the greedy path stays on the GPU).  Slots instead
+//    of atomics: the output projection's tiles finish together at the end of
+//    a sweep, and thousands of device-scope atomics on one address serialise.
 #include <type_traits>
 
 #include "device_common.h"
@@ -244,11 +251,36 @@ struct Tile {
   int S, slice;             // k-slices, this wave's slice
   int rbase, steps;         // first tile row of this wave, row steps
   int Cs, C, K;             // chunks per slice, chunks per row, columns
+  int row0, nrows;          // first matrix row of the tile, rows in the tile
+  bool track;               // greedy selection over this matrix
 };
+
+// Order-preserving key of an output: larger value -> larger key, and among
+// equal values the smaller row -> larger key.  fp16: -0 counts as +0 (NaN
+// patterns order beyond the infinities); int32 (binary): two's complement.
+__device__ __forceinline__ uint64_t greedy_key_f16(uint32_t bits, uint32_t row) {
+  bits &= 0xFFFFu;
+  if (bits == 0x8000u) bits = 0u;
+  const uint32_t ord = (bits & 0x8000u) ? (~bits & 0xFFFFu) : (bits | 0x8000u);
+  return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - row);
+}
+__device__ __forceinline__ uint64_t greedy_key_i32(uint32_t v, uint32_t row) {
+  return ((uint64_t)(v ^ 0x80000000u) << 32) | (uint64_t)(0xFFFFFFFFu - row);
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
+    v = max_u64(v, ((uint64_t)hi << 32) | lo);
+  }
+  return v;
+}
 
 constexpr uint32_t kFar = 0x80000000u;  // offset past any buffer, no wrap
 
-template <int FMT, int J, int U>
+template <int FMT, int J, int U, bool GREEDY>
 struct Runner {
   using Cd = Codec<FMT>;
   static constexpr bool kBin = FMT == kFmtBin;
@@ -265,6 +297,7 @@ struct Runner {
   uint32_t cof[J], mof[J];
   uint32_t xr[J][Cd::XR];
   float bias[J], xsum[J];
+  mutable uint64_t best = 0;  // greedy variant: best key of this lane's rows
 
   __device__ __forceinline__ Runner(const Tile& tile) : t(tile), R(Cd::make()) {
     // Fixed chunk positions of this lane.
@@ -354,8 +387,15 @@ struct Runner {
       const uint32_t r = row(st, u);
       if (t.sub == L - 1) {
         if (t.S == 1) {
-          if constexpr (kBin) store4(t.y, r * 4u, (uint32_t)(t.K - 2 * v));
-          else store2(t.y, r * 2u, half_bits(v));
+          if constexpr (kBin) {
+            const uint32_t o = (uint32_t)(t.K - 2 * v);
+            store4(t.y, r * 4u, o);
+            if (GREEDY && t.track && r < (uint32_t)t.nrows) best = max_u64(best, greedy_key_i32(o, t.row0 + r));
+          } else {
+            const uint16_t h = half_bits(v);
+            store2(t.y, r * 2u, h);
+            if (GREEDY && t.track && r < (uint32_t)t.nrows) best = max_u64(best, greedy_key_f16(h, t.row0 + r));
+          }
         } else if (r < (uint32_t)kMaxTileRows) {
           if constexpr (kBin) part[t.slice * kMaxTileRows + r] = (uint32_t)v;
           else part[t.slice * kMaxTileRows + r] = u32(v);
@@ -392,20 +432,29 @@ struct Runner {
   }
 };
 
-template <int FMT, int J>
-__device__ __forceinline__ void run_passes(const Tile& t, uint32_t* part) {
-  Runner<FMT, J, gemv_unroll(J)> r(t);
+template <int FMT, int J, bool GREEDY>
+__device__ __forceinline__ uint64_t run_passes(const Tile& t, uint32_t* part) {
+  Runner<FMT, J, gemv_unroll(J), GREEDY> r(t);
   r.run(part);
+  return r.best;
 }
 
 // ------------------------------------------------------------------ kernel --
 // JMAX: the largest pass count among the launch's descriptors; only the
 // cases up to it are instantiated, so registers match the workload.
-template <int FMT, int JMAX>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WPE, 8))) void gemv_kernel(const tkq_gemv_desc* __restrict__ descs, int count) {
+// Greedy variant arguments: the target descriptor and the slot array (one
+// key per tile of the target).
+struct Greedy {
+  int target;
+  uint64_t* slots;
+};
+
+template <int FMT, int JMAX, bool GREEDY>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WPE, 8))) void gemv_kernel(const tkq_gemv_desc* __restrict__ descs, int count, Greedy g) {
   using Cd = Codec<FMT>;
   constexpr bool kBin = FMT == kFmtBin;
   __shared__ uint32_t part[kWaves * kMaxTileRows];
+  __shared__ unsigned long long wave_best[kWaves];
 
   // The matrix this workgroup works on: last descriptor with work0 <= tile
   // (binary search; the loads hit the scalar cache after the first few).
@@ -441,6 +490,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WP
   t.row_bytes = (uint32_t)t.C * 16u;
   t.meta_row_bytes = (uint32_t)(t.C / Cd::CPG) * Cd::MB;
   const int nrows = min(rpt, N - row0);
+  t.row0 = row0;
+  t.nrows = nrows;
+  t.track = GREEDY && lo == g.target;
   const char* codes = (const char*)d->codes + (size_t)row0 * t.row_bytes;
   t.codes = make_rsrc(codes, (uint32_t)nrows * t.row_bytes);
   if constexpr (Cd::MB > 0) {
@@ -459,10 +511,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WP
   const uint32_t ybytes = kBin ? 4u : 2u;
   t.y = make_rsrc((char*)d->y + (size_t)row0 * ybytes, (uint32_t)nrows * ybytes);
 
+  uint64_t best = 0;
   switch (sh.passes) {
-#define TKQ_CASE(J)                                         \
-  case J:                                                   \
-    if constexpr (J <= JMAX) run_passes<FMT, J>(t, part); \
+#define TKQ_CASE(J)                                                \
+  case J:                                                          \
+    if constexpr (J <= JMAX) best = run_passes<FMT, J, GREEDY>(t, part); \
     break;
     TKQ_CASE(1)
     TKQ_CASE(2)
@@ -482,13 +535,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WP
       if constexpr (kBin) {
         int v = 0;
         for (int s = 0; s < t.S; ++s) v += (int)part[s * kMaxTileRows + r];
-        store4(t.y, (uint32_t)r * 4u, (uint32_t)(K - 2 * v));
+        const uint32_t o = (uint32_t)(K - 2 * v);
+        store4(t.y, (uint32_t)r * 4u, o);
+        if (GREEDY && t.track) best = max_u64(best, greedy_key_i32(o, (uint32_t)(row0 + r)));
       } else {
         float v = 0.0f;
         for (int s = 0; s < t.S; ++s) v += f32(part[s * kMaxTileRows + r]);
-        store2(t.y, (uint32_t)r * 2u, half_bits(v));
+        const uint16_t h = half_bits(v);
+        store2(t.y, (uint32_t)r * 2u, h);
+        if (GREEDY && t.track) best = max_u64(best, greedy_key_f16(h, (uint32_t)(row0 + r)));
       }
     }
+  }
+
+  if constexpr (GREEDY) {
+    if (t.track) {  // uniform over the workgroup
+      best = wave_max_u64(best);
+      if (lane == 0) wave_best[wave] = best;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        uint64_t b = wave_best[0];
+        for (int w = 1; w < kWaves; ++w) b = max_u64(b, wave_best[w]);
+        g.slots[tile - d->work0] = b;
+      }
+    }
+  }
+}
+
+// One workgroup: the largest key over the target's tile slots -> its row.
+__global__ __launch_bounds__(256) void greedy_finish_kernel(const tkq_gemv_desc* __restrict__ descs, int count,
+                                                            int target, int tiles,
+                                                            const uint64_t* __restrict__ slots,
+                                                            int32_t* __restrict__ token) {
+  __shared__ unsigned long long wave_best[kWaves];
+  const int first = descs[target].work0;
+  const int n = (target + 1 < count ? descs[target + 1].work0 : tiles) - first;
+  uint64_t best = 0;
+  for (int i = threadIdx.x; i < n; i += 64 * kWaves) best = max_u64(best, slots[i]);
+  best = wave_max_u64(best);
+  if ((threadIdx.x & 63) == 0) wave_best[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t b = wave_best[0];
+    for (int w = 1; w < kWaves; ++w) b = max_u64(b, wave_best[w]);
+    *token = (int32_t)(0xFFFFFFFFu - (uint32_t)b);
   }
 }
 
@@ -497,18 +587,23 @@ constexpr int max_passes() {
   return FMT == kFmtBin ? 8 : ((FMT == kFmtTern || FMT == kFmtInt2) ? 3 : 4);  // int4, hier-g32, K5: 4
 }
 
-typedef void (*GemvFn)(const tkq_gemv_desc*, int);
+typedef void (*GemvFn)(const tkq_gemv_desc*, int, Greedy);
+
+template <int FMT, bool GREEDY>
+GemvFn pick_variant(int jmax) {
+  switch (jmax) {
+    case 1: return gemv_kernel<FMT, 1, GREEDY>;
+    case 2: return gemv_kernel<FMT, 2, GREEDY>;
+    case 3: return gemv_kernel<FMT, 3, GREEDY>;
+    case 4: return gemv_kernel<FMT, 4, GREEDY>;
+  }
+  if constexpr (max_passes<FMT>() > 4) return gemv_kernel<FMT, max_passes<FMT>(), GREEDY>;
+  return nullptr;
+}
 
 template <int FMT>
-GemvFn pick(int jmax) {
-  switch (jmax) {
-    case 1: return gemv_kernel<FMT, 1>;
-    case 2: return gemv_kernel<FMT, 2>;
-    case 3: return gemv_kernel<FMT, 3>;
-    case 4: return gemv_kernel<FMT, 4>;
-  }
-  if constexpr (max_passes<FMT>() > 4) return gemv_kernel<FMT, max_passes<FMT>()>;
-  return nullptr;
+GemvFn pick(int jmax, bool greedy) {
+  return greedy ? pick_variant<FMT, true>(jmax) : pick_variant<FMT, false>(jmax);
 }
 
 }  // namespace
@@ -526,18 +621,26 @@ int gemv_max_passes(int fmt) {
 }
 
 hipError_t launch_gemv(int fmt, int jmax, const tkq_gemv_desc* dev_descs, int count, int64_t tiles,
-                       hipStream_t stream) {
+                       int target, int32_t* token, uint64_t* slots, hipStream_t stream) {
+  const bool greedy = target >= 0;
   GemvFn fn = nullptr;
   switch (fmt) {
-    case kFmtInt4: fn = pick<kFmtInt4>(jmax); break;
-    case kFmtHier: fn = pick<kFmtHier>(jmax); break;
-    case kFmtInt2: fn = pick<kFmtInt2>(jmax); break;
-    case kFmtK5: fn = pick<kFmtK5>(jmax); break;
-    case kFmtTern: fn = pick<kFmtTern>(jmax); break;
-    case kFmtBin: fn = pick<kFmtBin>(jmax); break;
+    case kFmtInt4: fn = pick<kFmtInt4>(jmax, greedy); break;
+    case kFmtHier: fn = pick<kFmtHier>(jmax, greedy); break;
+    case kFmtInt2: fn = pick<kFmtInt2>(jmax, greedy); break;
+    case kFmtK5: fn = pick<kFmtK5>(jmax, greedy); break;
+    case kFmtTern: fn = pick<kFmtTern>(jmax, greedy); break;
+    case kFmtBin: fn = pick<kFmtBin>(jmax, greedy); break;
   }
   if (!fn) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(fn, dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream, dev_descs, count);
+  const Greedy g = {target, slots};
+  hipLaunchKernelGGL(fn, dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream, dev_descs, count, g);
+  if (greedy) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(greedy_finish_kernel, dim3(1), dim3(64 * kWaves), 0, stream, dev_descs, count, target,
+                       (int)tiles, (const uint64_t*)slots, token);
+  }
   return hipGetLastError();
 }
 

@@ -61,8 +61,10 @@ __host__ __device__ constexpr int gemv_unroll(int passes) {
 // Largest `passes` value each kernel variant supports (x stays in registers).
 int gemv_max_passes(int fmt);
 // jmax: largest `passes` among the descriptors (selects the kernel variant).
+// target >= 0: also select the largest output of descriptor `target` into
+// *token (slots: scratch of one uint64 per tile of the launch).
 hipError_t launch_gemv(int fmt, int jmax, const tkq_gemv_desc* dev_descs, int count, int64_t tiles,
-                       hipStream_t stream);
+                       int target, int32_t* token, uint64_t* slots, hipStream_t stream);
 
 hipError_t launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* codes, void* meta,
                        hipStream_t stream);

@@ -235,14 +235,31 @@ int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan) {
   return TKQ_OK;
 }
 
-int tkq_gemv(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs, void* stream) {
+static int check_plan(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs) {
   if (!plan || !dev_descs) return TKQ_EINVAL;
   if (plan->magic != kPlanMagic || !known_fmt(plan->fmt) || plan->count < 1 || plan->tiles < 1 ||
       plan->tiles > INT32_MAX || plan->variant < 1 || plan->variant > tkq::gemv_max_passes(plan->fmt))
     return TKQ_EPLAN;
   if (!aligned16(dev_descs)) return TKQ_EALIGN;
+  return TKQ_OK;
+}
+
+int tkq_gemv(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs, void* stream) {
+  const int st = check_plan(plan, dev_descs);
+  if (st) return st;
+  return hip_status(tkq::launch_gemv(plan->fmt, plan->variant, dev_descs, plan->count, plan->tiles, -1,
+                                     nullptr, nullptr, (hipStream_t)stream));
+}
+
+int tkq_gemv_argmax(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs, int32_t target,
+                    int32_t* token, uint64_t* scratch, int64_t scratch_bytes, void* stream) {
+  const int st = check_plan(plan, dev_descs);
+  if (st) return st;
+  if (!token || !scratch || target < 0 || target >= plan->count) return TKQ_EINVAL;
+  if (scratch_bytes < 8 * plan->tiles) return TKQ_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(token) & 3u) || !aligned16(scratch)) return TKQ_EALIGN;
   return hip_status(tkq::launch_gemv(plan->fmt, plan->variant, dev_descs, plan->count, plan->tiles,
-                                     (hipStream_t)stream));
+                                     target, token, scratch, (hipStream_t)stream));
 }
 
 int tkq_gemm_prefill(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint32_t* codes,

@@ -71,6 +71,7 @@ _SIGNATURES = {
     "tkq_hier_meta_bytes": ([_I64, _I64], ctypes.c_int64),
     "tkq_gemv_prepare": ([ctypes.POINTER(GemvDesc), _I32, ctypes.POINTER(GemvPlan)], ctypes.c_int),
     "tkq_gemv": ([ctypes.POINTER(GemvPlan), _P, _P], ctypes.c_int),
+    "tkq_gemv_argmax": ([ctypes.POINTER(GemvPlan), _P, _I32, _P, _P, _I64, _P], ctypes.c_int),
     "tkq_gemm_prefill": ([_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
     "tkq_read_probe": ([_P, _I64, _P, _P], ctypes.c_int),
 }
@@ -241,6 +242,18 @@ class GemvBatch:
 
     def run(self, stream=None):
         _call("tkq_gemv", ctypes.byref(self.plan), _ptr(self.dev_descs), _stream(stream))
+
+    def greedy_scratch(self):
+        """Scratch for run_argmax: one int64 per tile of the launch."""
+        return torch.empty(self.tiles, dtype=torch.int64, device=self.dev_descs.device)
+
+    def run_argmax(self, target, token, scratch, stream=None):
+        """run() plus the index of the largest output of item `target` into
+        token (int32 device tensor, 1 element); scratch: greedy_scratch()."""
+        _need(token, torch.int32, "token")
+        _need(scratch, torch.int64, "scratch")
+        _call("tkq_gemv_argmax", ctypes.byref(self.plan), _ptr(self.dev_descs), int(target),
+              _ptr(token), _ptr(scratch), scratch.numel() * 8, _stream(stream))
 
 
 def gemv(fmt, codes, meta, x, N, K, y=None, stream=None):

@@ -232,6 +232,26 @@ int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan);
 int tkq_gemv(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs,
              void* stream);
 
+/* Grouped GEMV plus greedy selection (Whetstone README, status list: the
+ * greedy decode path never leaves the GPU; the output projection is the
+ * last GEMV of a token).  Computes exactly what tkq_gemv computes, and the
+ * index of the largest output of descriptor `target` (0 <= target < count),
+ * written to *token (device int32).  The workgroups of the target reduce
+ * their outputs in registers as they store them; a second, one-workgroup
+ * kernel on the same stream combines the per-tile results.  The comparison
+ * is on the stored outputs (fp16 bits for the float codings, -0 equal to +0;
+ * int32 for binary); on equal values the smallest index wins; NaN outputs
+ * order above +inf.
+ * scratch: caller-owned device memory of scratch_bytes >= 8 * plan->tiles,
+ * 16-byte aligned, any contents (overwritten).  Calls that share a scratch
+ * buffer or token must not run concurrently.
+ * Returns as tkq_gemv, plus TKQ_EINVAL (target out of range, null token or
+ * scratch, scratch too small) and TKQ_EALIGN (token not 4-byte or scratch
+ * not 16-byte aligned). */
+int tkq_gemv_argmax(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs,
+                    int32_t target, int32_t* token, uint64_t* scratch,
+                    int64_t scratch_bytes, void* stream);
+
 /* ---- prefill GEMM -------------------------------------------------------
  * Y[m,n] = sum_k X[m,k] * w[n,k] with w the int4 g128 dequantized weights
  * (TKintegers K5, "What is K5?": tiles of low-bit codes are expanded to fp16

@@ -136,3 +136,19 @@ def bin_gemv(w_words, x_words, K):
     x = np.asarray(x_words, dtype=np.uint32)
     pc = np.bitwise_count(w ^ x[None, :]).astype(np.int64).sum(axis=1)
     return (np.int64(K) - 2 * pc).astype(np.int32)
+
+
+def greedy_token(y):
+    """Greedy decoding's choice from one vector of logits (Whetstone README,
+    status list: greedy selection stays on the GPU): the index of the largest
+    value, the first such index on ties, with -0 and +0 equal.  A plain scan.
+    The comparison is on the values as given (the stored fp16 logits of the
+    GEMV, or the int32 outputs of the binary coding)."""
+    vals = np.asarray(y).astype(np.float64).ravel()
+    if vals.size == 0:
+        raise ValueError("empty vector")
+    best = 0
+    for i in range(1, vals.size):
+        if vals[i] > vals[best]:
+            best = i
+    return best

@@ -215,6 +215,25 @@ def test_gemv_rejects_unprepared_plan():
     assert tkq.lib().tkq_gemv(ctypes.byref(plan), A + 8, None) == tkq.EALIGN
 
 
+def test_gemv_argmax_validation():
+    f = tkq.lib().tkq_gemv_argmax
+    plan = tkq.GemvPlan()
+    plan.fmt, plan.count, plan.tiles = 1, 1, 1
+    assert f(ctypes.byref(plan), A, 0, A, A, 1 << 20, None) == tkq.EPLAN
+    arr = _descs(1, [(8, 128), (16, 256)])
+    st, plan = _prepare(arr)
+    assert st == tkq.OK
+    sb = 8 * plan.tiles
+    assert f(ctypes.byref(plan), A, -1, A, A, sb, None) == tkq.EINVAL
+    assert f(ctypes.byref(plan), A, 2, A, A, sb, None) == tkq.EINVAL
+    assert f(ctypes.byref(plan), A, 1, None, A, sb, None) == tkq.EINVAL
+    assert f(ctypes.byref(plan), A, 1, A, None, sb, None) == tkq.EINVAL
+    assert f(ctypes.byref(plan), A, 1, A, A, sb - 8, None) == tkq.EINVAL
+    assert f(ctypes.byref(plan), A, 1, A + 2, A, sb, None) == tkq.EALIGN
+    assert f(ctypes.byref(plan), A, 1, A, A + 8, sb, None) == tkq.EALIGN
+    assert f(ctypes.byref(plan), A + 8, 1, A, A, sb, None) == tkq.EALIGN
+
+
 def test_prefill_validation():
     f = tkq.lib().tkq_gemm_prefill
     assert f(2, 64, 128, 128, A, A, A, A, None, 0, None) == tkq.EFORMAT
