@@ -277,6 +277,44 @@ def run_sweep(args, torch, tkq, inputs, model, fmt, greedy=False):
     return out
 
 
+def run_small(args, torch, tkq, inputs, model, M):
+    """Multi-token GEMV: the model's whole sweep for M tokens at once
+    (speculative verification of M draft tokens), int4 g128, one launch."""
+    items, shapes = build_sweep(torch, tkq, inputs, model, "int4")
+    for i, it in enumerate(items):
+        K, N = it["K"], it["N"]
+        X = np.stack([inputs.normal_vector((6, i, m), K) for m in range(M)])
+        it["x"] = torch.from_numpy(X).cuda()
+        it["y"] = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    weight_bytes = sum(it["codes"].numel() * 4 + it["meta"].numel() * 4 for it in items)
+    step_bytes = weight_bytes + sum(M * (2 * k + 2 * n) for _, n, k in shapes)
+    flops = sum(2 * M * n * k for _, n, k in shapes)
+    copies = max(1, math.ceil(ROTATE_BYTES / weight_bytes))
+    batches = [tkq.GemvBatch("int4", items, tokens=M)]
+    for _ in range(copies - 1):
+        clone = [dict(it, codes=it["codes"].clone(), meta=it["meta"].clone()) for it in items]
+        batches.append(tkq.GemvBatch("int4", clone, tokens=M))
+    torch.cuda.synchronize()
+    ms = time_steps(torch, lambda s: batches[s % len(batches)].run(), args.steps, args.warmup, args.graph,
+                    len(batches))
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    return {"metric": "int4-g128 multi-token GEMV (M=%d) achieved HBM TB/s" % M,
+            "value": round(gbs / 1000.0, 4), "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f16",
+            "data": "synthetic: seeded N(0,0.02) weights at the model's shapes, N(0,1) fp16 tokens",
+            "config": {"workload": "%s weight sweep for %d tokens at once (int4-g128, %d matrices, one launch)"
+                                   % (model, M, len(shapes)),
+                       "tokens": M, "bytes_per_step": step_bytes, "flops_per_step": flops,
+                       "copies_rotated": len(batches)},
+            "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "tok_s": round(M * 1000.0 / ms, 1),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+            "kernel": "small_m_kernel"}
+
+
 def _fmt_name(fmt):
     return {"int4": "int4-g128", "k5": "K5-g128", "tern": "ternary-g128 (2-bit)", "bin": "binary",
             "hier": "int4-hier-g32", "int2": "int2-g128"}[fmt]
@@ -394,7 +432,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="0.5b-int4",
                     choices=["0.5b-int4", "0.5b-int4-greedy", "0.5b-k5", "0.5b-tern", "0.5b-hier",
-                             "0.5b-int2", "bin", "single-896",
+                             "0.5b-int2", "0.5b-int4-m2", "0.5b-int4-m4", "0.5b-int4-m8", "0.5b-int4-m16",
+                             "7b-int4-m16", "bin", "single-896",
                              "7b-int4", "7b-hier", "7b-prefill", "probe"])
     ap.add_argument("--graph", default="none", choices=["none", "step", "all"],
                     help="launch steps as HIP graph replays (see time_steps)")
@@ -444,6 +483,9 @@ def main():
                           "matrices of the sweep (%s), %.1f s of CPU work; quantization not timed"
                           % (passes, len(done), ", ".join(done[:3] + (["..."] if len(done) > 3 else [])
                                                           + done[-1:]), spent)}
+    elif "-m" in w:
+        model = "qwen2.5-7b" if w.startswith("7b") else "qwen2.5-0.5b"
+        out = run_small(args, torch, tkq, inputs, model, int(w.split("-m")[1]))
     elif w == "bin":
         out = run_binary(args, torch, tkq, inputs)
     elif w == "single-896":

@@ -1,0 +1,157 @@
+// Multi-token GEMV over int4 g128 weights for gfx950: Y[m, n] = sum_k X[m, k]
+// * w[n, k] for M = 1..16 tokens at once (speculative verification, short
+// prefill: Whetstone README, "Prior art", where several tokens share every
+// weight read; the timing table's 16-token pass).
+//
+// Every weight is still read from HBM once, but it is used M times, so at
+// M = 16 the arithmetic (~60 flop per byte of int4) is beyond the vector ALUs
+// at full bandwidth; the products run on the matrix cores:
+//
+//  * One wave owns 16 weight rows; a workgroup (4 waves) owns 64 rows of one
+//    matrix, and a grouped launch concatenates the tiles of many matrices
+//    (a scalar binary search finds a workgroup's matrix, as in the GEMV).
+//  * Per 128-column quantization group, lane l loads one 16-byte chunk: row
+//    l % 16, columns 32 (l / 16) .. +31 of the group.  These are exactly the
+//    A operands of four v_mfma_f32_16x16x32_f16 (lane l supplies row l % 16
+//    and the k-block l / 16), so the weights go from HBM to the matrix cores
+//    through registers only.  The chunk is unpacked with the fp16 magic
+//    number (1024 + m * code), shifted by the zero point (exact small
+//    integers) and scaled (one fp16 rounding of s * (q - z)).
+//  * The tokens' x slices are staged through LDS, 512 columns per round, in
+//    the k order the unpack produces (0, 4, 1, 5, 2, 6, 3, 7 within each 8),
+//    and read as the B operands (lane l: token l % 16, k-block l / 16).
+//    Lanes of tokens >= M contribute zeros.
+//  * fp32 accumulation; Y rounded to fp16 (nearest even) on store.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace tkq {
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 hv2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kTileRows = 16 * kWaves;
+constexpr int KC = 512;          // columns of X staged per round (4 groups)
+constexpr int kLdsRow = KC + 8;  // halves per staged token row (16 bytes of padding)
+constexpr uint32_t kMagic = 0x64006400u;
+
+__device__ __forceinline__ uint32_t in_sgpr(uint32_t c) {
+  uint32_t r;
+  asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "i"(c));
+  return r;
+}
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+__device__ __forceinline__ hv2 h2(uint32_t u) { return __builtin_bit_cast(hv2, u); }
+__device__ __forceinline__ uint32_t u32h(hv2 h) { return __builtin_bit_cast(uint32_t, h); }
+
+// One code word (8 nibbles, natural order) -> 8 fp16 weights s * (q - z) in
+// the order (0, 4, 1, 5, 2, 6, 3, 7).
+__device__ __forceinline__ half8 dequant_word(uint32_t w, uint32_t m0, uint32_t m1, uint32_t magic, hv2 nz1,
+                                              hv2 nz16, hv2 s) {
+  const hv2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const uint32_t t = w >> 8;
+  const hv2 a = (h2((w & m0) | magic) + nz1) * s;                    // (q0, q4)
+  const hv2 b = (h2((w & m1) | magic) * sixteenth + nz16) * s;       // (q1, q5)
+  const hv2 c = (h2((t & m0) | magic) + nz1) * s;                    // (q2, q6)
+  const hv2 d = (h2((t & m1) | magic) * sixteenth + nz16) * s;       // (q3, q7)
+  u32x4 v = {u32h(a), u32h(b), u32h(c), u32h(d)};
+  return __builtin_bit_cast(half8, v);
+}
+
+__global__ __launch_bounds__(256) void small_m_kernel(const tkq_gemv_desc* __restrict__ descs, int count, int M) {
+  __shared__ __attribute__((aligned(16))) _Float16 xs[16 * kLdsRow];
+
+  const int tile = blockIdx.x;
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (descs[mid].work0 <= tile) lo = mid;
+    else hi = mid - 1;
+  }
+  const tkq_gemv_desc* d = descs + lo;
+  const int N = d->N, K = d->K;
+  const int row0 = (tile - d->work0) * kTileRows;
+  const int nrows = min(kTileRows, N - row0);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, c = lane >> 4;
+  const uint32_t lrow = (uint32_t)(wave * 16 + r);
+  const uint32_t row_bytes = (uint32_t)K / 2u, meta_row = (uint32_t)(K / 128) * 4u;
+  const __amdgpu_buffer_rsrc_t codes =
+      make_rsrc((const char*)d->codes + (size_t)row0 * row_bytes, (uint32_t)nrows * row_bytes);
+  const __amdgpu_buffer_rsrc_t meta =
+      make_rsrc((const char*)d->meta + (size_t)row0 * meta_row, (uint32_t)nrows * meta_row);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(d->x, (uint32_t)M * (uint32_t)K * 2u);
+  const uint32_t m0 = in_sgpr(0x000F000Fu), m1 = in_sgpr(0x00F000F0u), magic = in_vgpr(kMagic);
+  const bool live_token = r < M;
+
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int kc = 0; kc < K; kc += KC) {
+    const int ng = min(KC, K - kc) / 128;  // groups this round (1..4)
+    // This round's codes and metadata are in flight while x is staged.
+    u32x4 q[4];
+    uint32_t mt[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (g < ng) {
+        q[g] = load16_nt(codes, lrow * row_bytes + (uint32_t)(kc + 128 * g) / 2u + 16u * c);
+        mt[g] = load4(meta, lrow * meta_row + (uint32_t)((kc / 128 + g) * 4));
+      }
+    }
+    __syncthreads();  // the previous round's reads of xs are done
+    const int units = ng * 16;  // 8-column units per token row
+    for (int u = threadIdx.x; u < M * units; u += 64 * kWaves) {
+      const int m = u / units, e = u - m * units;
+      const u32x4 v = load16(xr, (uint32_t)(m * K + kc + 8 * e) * 2u);
+      u32x4 p;
+      p[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);  // (x0, x4)
+      p[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);  // (x1, x5)
+      p[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);  // (x2, x6)
+      p[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);  // (x3, x7)
+      *reinterpret_cast<u32x4*>(&xs[m * kLdsRow + 8 * e]) = p;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (g < ng) {
+        const hv2 s = {h2(mt[g])[0], h2(mt[g])[0]};
+        const _Float16 z = h2(mt[g])[1];
+        const hv2 nz1 = {(_Float16)(-1024.0f) - z, (_Float16)(-1024.0f) - z};
+        const hv2 nz16 = {(_Float16)(-64.0f) - z, (_Float16)(-64.0f) - z};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const half8 a = dequant_word(q[g][j], m0, m1, magic, nz1, nz16, s);
+          half8 b = {};
+          if (live_token) b = *reinterpret_cast<const half8*>(&xs[r * kLdsRow + 128 * g + 32 * c + 8 * j]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // lane l holds Y rows 4 (l / 16) + i of the wave's block for token l % 16
+  if (live_token) {
+    const __amdgpu_buffer_rsrc_t y = make_rsrc(d->y, (uint32_t)M * (uint32_t)N * 2u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = row0 + wave * 16 + 4 * c + i;
+      if (n < N) store2(y, (uint32_t)(r * N + n) * 2u, half_bits(acc[i]));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_small_m(const tkq_gemv_desc* dev_descs, int count, int64_t tiles, int M, hipStream_t stream) {
+  hipLaunchKernelGGL(small_m_kernel, dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream, dev_descs, count, M);
+  return hipGetLastError();
+}
+
+}  // namespace tkq

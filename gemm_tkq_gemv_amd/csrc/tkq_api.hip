@@ -10,7 +10,8 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
-constexpr int32_t kPlanMagic = 0x746b7131;  // "tkq1"
+constexpr int32_t kPlanMagic = 0x746b7131;   // "tkq1": tkq_gemv_prepare
+constexpr int32_t kSmallMagic = 0x746b7132;  // "tkq2": tkq_gemm_small_prepare
 constexpr int64_t kMaxWeights = int64_t(1) << 39;
 // Planner parameters per coding (measured on MI355X, interleaved runs):
 //  tile   bytes of codes one wave streams per large tile: large enough to
@@ -260,6 +261,45 @@ int tkq_gemv_argmax(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs, i
   if ((reinterpret_cast<uintptr_t>(token) & 3u) || !aligned16(scratch)) return TKQ_EALIGN;
   return hip_status(tkq::launch_gemv(plan->fmt, plan->variant, dev_descs, plan->count, plan->tiles,
                                      target, token, scratch, (hipStream_t)stream));
+}
+
+int tkq_gemm_small_prepare(tkq_gemv_desc* descs, int32_t count, int32_t M, tkq_gemv_plan* plan) {
+  if (!descs || !plan || count < 1 || M < 1) return TKQ_EINVAL;
+  if (M > tkq::kSmallMaxM) return TKQ_ESHAPE;
+  int64_t work = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    tkq_gemv_desc& d = descs[i];
+    if (d.fmt != TKQ_FMT_INT4_G128) return TKQ_EFORMAT;
+    if (d.N < 1 || d.K < 1 || !d.codes || !d.meta || !d.x || !d.y) return TKQ_EINVAL;
+    if (d.K % 128 || d.K > TKQ_MAX_K || int64_t(d.N) * d.K > kMaxWeights ||
+        int64_t(M) * d.K * 2 > INT32_MAX || int64_t(M) * d.N * 2 > INT32_MAX)
+      return TKQ_ESHAPE;
+    if (!aligned16(d.codes) || !aligned16(d.meta) || !aligned16(d.x) || !aligned16(d.y)) return TKQ_EALIGN;
+    const int64_t tiles = (int64_t(d.N) + tkq::kSmallTileRows - 1) / tkq::kSmallTileRows;
+    if (work + tiles > INT32_MAX) return TKQ_ESHAPE;
+    d.work0 = (int32_t)work;
+    d.big_tiles = (int32_t)tiles;
+    d.rows_per_tile = tkq::kSmallTileRows;
+    d.shape = 0;
+    d.small_rows = tkq::kSmallTileRows;
+    work += tiles;
+  }
+  plan->fmt = TKQ_FMT_INT4_G128;
+  plan->count = count;
+  plan->tiles = work;
+  plan->variant = M;
+  plan->magic = kSmallMagic;
+  plan->reserved = 0;
+  return TKQ_OK;
+}
+
+int tkq_gemm_small(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs, void* stream) {
+  if (!plan || !dev_descs) return TKQ_EINVAL;
+  if (plan->magic != kSmallMagic || plan->fmt != TKQ_FMT_INT4_G128 || plan->count < 1 || plan->tiles < 1 ||
+      plan->tiles > INT32_MAX || plan->variant < 1 || plan->variant > tkq::kSmallMaxM)
+    return TKQ_EPLAN;
+  if (!aligned16(dev_descs)) return TKQ_EALIGN;
+  return hip_status(tkq::launch_small_m(dev_descs, plan->count, plan->tiles, plan->variant, (hipStream_t)stream));
 }
 
 int tkq_gemm_prefill(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint32_t* codes,

@@ -72,6 +72,9 @@ _SIGNATURES = {
     "tkq_gemv_prepare": ([ctypes.POINTER(GemvDesc), _I32, ctypes.POINTER(GemvPlan)], ctypes.c_int),
     "tkq_gemv": ([ctypes.POINTER(GemvPlan), _P, _P], ctypes.c_int),
     "tkq_gemv_argmax": ([ctypes.POINTER(GemvPlan), _P, _I32, _P, _P, _I64, _P], ctypes.c_int),
+    "tkq_gemm_small_prepare": ([ctypes.POINTER(GemvDesc), _I32, _I32, ctypes.POINTER(GemvPlan)],
+                               ctypes.c_int),
+    "tkq_gemm_small": ([ctypes.POINTER(GemvPlan), _P, _P], ctypes.c_int),
     "tkq_gemm_prefill": ([_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
     "tkq_read_probe": ([_P, _I64, _P, _P], ctypes.c_int),
 }
@@ -213,7 +216,9 @@ class GemvBatch:
     planned by tkq_gemv_prepare and copied to the device once; run() launches
     tkq_gemv on the current (or given) stream."""
 
-    def __init__(self, fmt, items, device=None):
+    def __init__(self, fmt, items, device=None, tokens=None):
+        """tokens: None for the batch-1 GEMV (x [K], y [N]); M in 1..16 for
+        the multi-token GEMV (x [M, K], y [M, N]; int4 g128 only)."""
         fmt = FORMATS.get(fmt, fmt)
         items = list(items)
         if not items:
@@ -233,7 +238,11 @@ class GemvBatch:
                 setattr(d, key, t.data_ptr())
                 self._keep.append(t)
         self.plan = GemvPlan()
-        _call("tkq_gemv_prepare", descs, n, ctypes.byref(self.plan))
+        self.tokens = tokens
+        if tokens is None:
+            _call("tkq_gemv_prepare", descs, n, ctypes.byref(self.plan))
+        else:
+            _call("tkq_gemm_small_prepare", descs, n, int(tokens), ctypes.byref(self.plan))
         self.descs = descs
         raw = bytes(ctypes.string_at(ctypes.addressof(descs), ctypes.sizeof(descs)))
         dev = device if device is not None else self._keep[0].device
@@ -241,7 +250,10 @@ class GemvBatch:
         self.fmt, self.count, self.tiles = fmt, n, int(self.plan.tiles)
 
     def run(self, stream=None):
-        _call("tkq_gemv", ctypes.byref(self.plan), _ptr(self.dev_descs), _stream(stream))
+        if self.tokens is None:
+            _call("tkq_gemv", ctypes.byref(self.plan), _ptr(self.dev_descs), _stream(stream))
+        else:
+            _call("tkq_gemm_small", ctypes.byref(self.plan), _ptr(self.dev_descs), _stream(stream))
 
     def greedy_scratch(self):
         """Scratch for run_argmax: one int64 per tile of the launch."""

@@ -252,6 +252,32 @@ int tkq_gemv_argmax(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs,
                     int32_t target, int32_t* token, uint64_t* scratch,
                     int64_t scratch_bytes, void* stream);
 
+/* ---- multi-token GEMV (M = 1..16) ----------------------------------------
+ * Y_i[m, n] = sum_k X_i[m, k] * w_i[n, k] for M tokens at once over many
+ * int4 g128 matrices in one launch: the regime between batch-1 decode and
+ * prefill (Whetstone README, "Prior art": speculative verification and
+ * prefill, where several tokens share each weight read).  Each weight is
+ * read from HBM once and used M times; the products run on the matrix cores
+ * from fp16 weights s * (q - z) (one rounding) with fp32 accumulation;
+ * fp16 output rounded to nearest even;
+ * |Y - Y_exact| <= 2e-3 * sum_k |X[m,k] w[n,k]| entry-wise.
+ *
+ * Descriptors as for tkq_gemv with fmt = TKQ_FMT_INT4_G128, except
+ *   x: fp16 [M][K] (token-major), y: fp16 [M][N] (token-major).
+ * tkq_gemm_small_prepare (host only) validates them (K % 128 == 0, M*K and
+ * M*N below 2^30), fills the [prepare] fields and *plan for this M; a plan
+ * from tkq_gemv_prepare is not accepted here, nor the reverse.
+ * Returns TKQ_OK, TKQ_EINVAL (null pointers, count or M < 1), TKQ_ESHAPE
+ * (M > 16 or sizes), TKQ_EFORMAT (not int4 g128) or TKQ_EALIGN. */
+int tkq_gemm_small_prepare(tkq_gemv_desc* descs, int32_t count, int32_t M,
+                           tkq_gemv_plan* plan);
+
+/* Launches the prepared multi-token GEMV on `stream` (dev_descs: device copy
+ * of the prepared descriptors, 16-byte aligned).  Returns TKQ_OK,
+ * TKQ_EINVAL, TKQ_EALIGN, TKQ_EPLAN or TKQ_EHIP. */
+int tkq_gemm_small(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs,
+                   void* stream);
+
 /* ---- prefill GEMM -------------------------------------------------------
  * Y[m,n] = sum_k X[m,k] * w[n,k] with w the int4 g128 dequantized weights
  * (TKintegers K5, "What is K5?": tiles of low-bit codes are expanded to fp16

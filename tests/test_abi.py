@@ -234,6 +234,28 @@ def test_gemv_argmax_validation():
     assert f(ctypes.byref(plan), A + 8, 1, A, A, sb, None) == tkq.EALIGN
 
 
+def test_gemm_small_prepare():
+    f = tkq.lib().tkq_gemm_small_prepare
+    arr = _descs(1, [(1, 128), (64, 896), (65, 896), (151936, 896)])
+    plan = tkq.GemvPlan()
+    assert f(arr, 4, 16, ctypes.byref(plan)) == tkq.OK
+    assert [d.work0 for d in arr] == [0, 1, 2, 4]
+    assert plan.tiles == 4 + 151936 // 64 and plan.variant == 16
+    assert f(arr, 4, 17, ctypes.byref(plan)) == tkq.ESHAPE
+    assert f(arr, 4, 0, ctypes.byref(plan)) == tkq.EINVAL
+    bad = _descs(2, [(8, 128)])
+    assert f(bad, 1, 4, ctypes.byref(plan)) == tkq.EFORMAT
+    bad = _descs(1, [(8, 96)])
+    assert f(bad, 1, 4, ctypes.byref(plan)) == tkq.ESHAPE
+    # plans are not interchangeable between the batch-1 and multi-token entry points
+    g = tkq.lib().tkq_gemm_small
+    st, p1 = _prepare(_descs(1, [(8, 128)]))
+    assert g(ctypes.byref(p1), A, None) == tkq.EPLAN
+    assert f(arr, 4, 3, ctypes.byref(plan)) == tkq.OK
+    assert tkq.lib().tkq_gemv(ctypes.byref(plan), A, None) == tkq.EPLAN
+    assert g(ctypes.byref(plan), A + 8, None) == tkq.EALIGN
+
+
 def test_prefill_validation():
     f = tkq.lib().tkq_gemm_prefill
     assert f(2, 64, 128, 128, A, A, A, A, None, 0, None) == tkq.EFORMAT
