@@ -17,10 +17,13 @@
 //    through registers only.  The chunk is unpacked with the fp16 magic
 //    number (1024 + m * code), shifted by the zero point (exact small
 //    integers) and scaled (one fp16 rounding of s * (q - z)).
-//  * The tokens' x slices are staged through LDS, 512 columns per round, in
+//  * The tokens' x slices are staged through LDS, KC columns per round, in
 //    the k order the unpack produces (0, 4, 1, 5, 2, 6, 3, 7 within each 8),
 //    and read as the B operands (lane l: token l % 16, k-block l / 16).
 //    Lanes of tokens >= M contribute zeros.
+//  * The codes of round i + 1 are loaded into a second register buffer
+//    while round i is computed, so every wave keeps its next KC / 2 bytes
+//    per row in flight.
 //  * fp32 accumulation; Y rounded to fp16 (nearest even) on store.
 #include "device_common.h"
 #include "kernels.h"
@@ -34,9 +37,17 @@ typedef _Float16 hv2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
-constexpr int kTileRows = 16 * kWaves;
-constexpr int KC = 512;          // columns of X staged per round (4 groups)
-constexpr int kLdsRow = KC + 8;  // halves per staged token row (16 bytes of padding)
+constexpr int kTileRows = kSmallTileRows;  // 16 rows per wave
+#ifndef TKQ_SMALL_KC
+#define TKQ_SMALL_KC 1024
+#endif
+constexpr int KC = TKQ_SMALL_KC;  // columns of X staged per round
+constexpr int GR = KC / 128;      // quantization groups per round
+constexpr int kLdsRow = KC + 8;   // halves per staged token row (16 bytes of padding)
+#ifndef TKQ_SMALL_ACC
+#define TKQ_SMALL_ACC 1
+#endif
+constexpr int NACC = TKQ_SMALL_ACC;  // independent accumulators (MFMA dependency chains)
 constexpr uint32_t kMagic = 0x64006400u;
 
 __device__ __forceinline__ uint32_t in_sgpr(uint32_t c) {
@@ -66,6 +77,65 @@ __device__ __forceinline__ half8 dequant_word(uint32_t w, uint32_t m0, uint32_t 
   return __builtin_bit_cast(half8, v);
 }
 
+struct CodeBuf {
+  u32x4 q[GR];
+  uint32_t m[GR];
+};
+
+struct SmallTile {
+  __amdgpu_buffer_rsrc_t codes, meta, x;
+  uint32_t lrow, row_bytes, meta_row;
+  int K, M, c, r;
+};
+
+__device__ __forceinline__ void load_round(const SmallTile& t, int kc, CodeBuf& b) {
+  const int ng = min(KC, t.K - kc) / 128;
+#pragma unroll
+  for (int g = 0; g < GR; ++g) {
+    if (g < ng) {
+      b.q[g] = load16_nt(t.codes, t.lrow * t.row_bytes + (uint32_t)(kc + 128 * g) / 2u + 16u * t.c);
+      b.m[g] = load4(t.meta, t.lrow * t.meta_row + (uint32_t)((kc / 128 + g) * 4));
+    }
+  }
+}
+
+// Stage X[0..M)[kc, kc + KC) into LDS in the unpack's k order.
+__device__ __forceinline__ void stage_x(const SmallTile& t, int kc, _Float16* xs) {
+  const int units = min(KC, t.K - kc) / 8;  // 8-column units per token row
+  for (int u = threadIdx.x; u < t.M * units; u += 64 * kWaves) {
+    const int m = u / units, e = u - m * units;
+    const u32x4 v = load16(t.x, (uint32_t)(m * t.K + kc + 8 * e) * 2u);
+    u32x4 p;
+    p[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);  // (x0, x4)
+    p[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);  // (x1, x5)
+    p[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);  // (x2, x6)
+    p[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);  // (x3, x7)
+    *reinterpret_cast<u32x4*>(&xs[m * kLdsRow + 8 * e]) = p;
+  }
+}
+
+__device__ __forceinline__ void compute_round(const SmallTile& t, int kc, const CodeBuf& b, const _Float16* xs,
+                                              uint32_t m0, uint32_t m1, uint32_t magic, f32x4 (&acc)[NACC]) {
+  const int ng = min(KC, t.K - kc) / 128;
+  const bool live_token = t.r < t.M;
+#pragma unroll
+  for (int g = 0; g < GR; ++g) {
+    if (g < ng) {
+      const hv2 s = {h2(b.m[g])[0], h2(b.m[g])[0]};
+      const _Float16 z = h2(b.m[g])[1];
+      const hv2 nz1 = {(_Float16)(-1024.0f) - z, (_Float16)(-1024.0f) - z};
+      const hv2 nz16 = {(_Float16)(-64.0f) - z, (_Float16)(-64.0f) - z};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const half8 a = dequant_word(b.q[g][j], m0, m1, magic, nz1, nz16, s);
+        half8 xb = {};
+        if (live_token) xb = *reinterpret_cast<const half8*>(&xs[t.r * kLdsRow + 128 * g + 32 * t.c + 8 * j]);
+        acc[j % NACC] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, xb, acc[j % NACC], 0, 0, 0);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void small_m_kernel(const tkq_gemv_desc* __restrict__ descs, int count, int M) {
   __shared__ __attribute__((aligned(16))) _Float16 xs[16 * kLdsRow];
 
@@ -81,68 +151,47 @@ __global__ __launch_bounds__(256) void small_m_kernel(const tkq_gemv_desc* __res
   const int row0 = (tile - d->work0) * kTileRows;
   const int nrows = min(kTileRows, N - row0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = lane & 15, c = lane >> 4;
-  const uint32_t lrow = (uint32_t)(wave * 16 + r);
-  const uint32_t row_bytes = (uint32_t)K / 2u, meta_row = (uint32_t)(K / 128) * 4u;
-  const __amdgpu_buffer_rsrc_t codes =
-      make_rsrc((const char*)d->codes + (size_t)row0 * row_bytes, (uint32_t)nrows * row_bytes);
-  const __amdgpu_buffer_rsrc_t meta =
-      make_rsrc((const char*)d->meta + (size_t)row0 * meta_row, (uint32_t)nrows * meta_row);
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(d->x, (uint32_t)M * (uint32_t)K * 2u);
+  SmallTile t;
+  t.r = lane & 15;
+  t.c = lane >> 4;
+  t.K = K;
+  t.M = M;
+  t.lrow = (uint32_t)(wave * 16 + t.r);
+  t.row_bytes = (uint32_t)K / 2u;
+  t.meta_row = (uint32_t)(K / 128) * 4u;
+  t.codes = make_rsrc((const char*)d->codes + (size_t)row0 * t.row_bytes, (uint32_t)nrows * t.row_bytes);
+  t.meta = make_rsrc((const char*)d->meta + (size_t)row0 * t.meta_row, (uint32_t)nrows * t.meta_row);
+  t.x = make_rsrc(d->x, (uint32_t)M * (uint32_t)K * 2u);
   const uint32_t m0 = in_sgpr(0x000F000Fu), m1 = in_sgpr(0x00F000F0u), magic = in_vgpr(kMagic);
-  const bool live_token = r < M;
 
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int kc = 0; kc < K; kc += KC) {
-    const int ng = min(KC, K - kc) / 128;  // groups this round (1..4)
-    // This round's codes and metadata are in flight while x is staged.
-    u32x4 q[4];
-    uint32_t mt[4];
+  f32x4 acc[NACC];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (g < ng) {
-        q[g] = load16_nt(codes, lrow * row_bytes + (uint32_t)(kc + 128 * g) / 2u + 16u * c);
-        mt[g] = load4(meta, lrow * meta_row + (uint32_t)((kc / 128 + g) * 4));
-      }
-    }
+  for (int i = 0; i < NACC; ++i) acc[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  CodeBuf a, b;
+  load_round(t, 0, a);
+  for (int kc = 0; kc < K; kc += 2 * KC) {
     __syncthreads();  // the previous round's reads of xs are done
-    const int units = ng * 16;  // 8-column units per token row
-    for (int u = threadIdx.x; u < M * units; u += 64 * kWaves) {
-      const int m = u / units, e = u - m * units;
-      const u32x4 v = load16(xr, (uint32_t)(m * K + kc + 8 * e) * 2u);
-      u32x4 p;
-      p[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);  // (x0, x4)
-      p[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);  // (x1, x5)
-      p[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);  // (x2, x6)
-      p[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);  // (x3, x7)
-      *reinterpret_cast<u32x4*>(&xs[m * kLdsRow + 8 * e]) = p;
-    }
+    stage_x(t, kc, xs);
     __syncthreads();
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (g < ng) {
-        const hv2 s = {h2(mt[g])[0], h2(mt[g])[0]};
-        const _Float16 z = h2(mt[g])[1];
-        const hv2 nz1 = {(_Float16)(-1024.0f) - z, (_Float16)(-1024.0f) - z};
-        const hv2 nz16 = {(_Float16)(-64.0f) - z, (_Float16)(-64.0f) - z};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const half8 a = dequant_word(q[g][j], m0, m1, magic, nz1, nz16, s);
-          half8 b = {};
-          if (live_token) b = *reinterpret_cast<const half8*>(&xs[r * kLdsRow + 128 * g + 32 * c + 8 * j]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
-        }
-      }
-    }
+    if (kc + KC < K) load_round(t, kc + KC, b);
+    compute_round(t, kc, a, xs, m0, m1, magic, acc);
+    if (kc + KC >= K) break;
+    __syncthreads();
+    stage_x(t, kc + KC, xs);
+    __syncthreads();
+    if (kc + 2 * KC < K) load_round(t, kc + 2 * KC, a);
+    compute_round(t, kc + KC, b, xs, m0, m1, magic, acc);
   }
 
   // lane l holds Y rows 4 (l / 16) + i of the wave's block for token l % 16
-  if (live_token) {
+#pragma unroll
+  for (int i = 1; i < NACC; ++i) acc[0] += acc[i];
+  if (t.r < M) {
     const __amdgpu_buffer_rsrc_t y = make_rsrc(d->y, (uint32_t)M * (uint32_t)N * 2u);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int n = row0 + wave * 16 + 4 * c + i;
-      if (n < N) store2(y, (uint32_t)(r * N + n) * 2u, half_bits(acc[i]));
+      const int n = row0 + wave * 16 + 4 * t.c + i;
+      if (n < N) store2(y, (uint32_t)(t.r * N + n) * 2u, half_bits(acc[0][i]));
     }
   }
 }

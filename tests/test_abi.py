@@ -239,8 +239,11 @@ def test_gemm_small_prepare():
     arr = _descs(1, [(1, 128), (64, 896), (65, 896), (151936, 896)])
     plan = tkq.GemvPlan()
     assert f(arr, 4, 16, ctypes.byref(plan)) == tkq.OK
-    assert [d.work0 for d in arr] == [0, 1, 2, 4]
-    assert plan.tiles == 4 + 151936 // 64 and plan.variant == 16
+    rows = arr[0].rows_per_tile                    # one workgroup per tile of rows
+    assert rows % 64 == 0 and all(d.rows_per_tile == rows for d in arr)
+    tiles = [-(-n // rows) for n in (1, 64, 65, 151936)]
+    assert [d.work0 for d in arr] == [0, tiles[0], sum(tiles[:2]), sum(tiles[:3])]
+    assert plan.tiles == sum(tiles) and plan.variant == 16
     assert f(arr, 4, 17, ctypes.byref(plan)) == tkq.ESHAPE
     assert f(arr, 4, 0, ctypes.byref(plan)) == tkq.EINVAL
     bad = _descs(2, [(8, 128)])
