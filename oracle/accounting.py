@@ -43,10 +43,12 @@ def ceiling_tok_s(bandwidth_bytes_s, bytes_token):
 #   K5        : K code bytes   + 2 bytes (fp16 scale) per 128
 #   ternary   : K/4 code bytes + 2 bytes (fp16 scale) per 128
 #   binary    : K/8 code bytes, no metadata, x is K/8 bytes, y is int32
+#   int3 g128 : 3K/8 code bytes + 4 bytes (fp16 scale, fp16 zero) per 128
 #   int2 g128 : K/4 code bytes + 4 bytes (fp16 scale, fp16 zero) per 128
 #   int4-hier-g32: K/2 code bytes + 1 byte (two 4-bit indices) per 32
 #               + 4 bytes (fp16 pair) per row
 _FMT_BYTES = {
+    "int3": (lambda n, k: n * (3 * k // 8) + n * (k // 128) * 4, lambda k: 2 * k, lambda n: 2 * n),
     "int2": (lambda n, k: n * (k // 4) + n * (k // 128) * 4, lambda k: 2 * k, lambda n: 2 * n),
     "hier": (lambda n, k: n * (k // 2) + n * (k // 32) + 4 * n, lambda k: 2 * k, lambda n: 2 * n),
     "int4": (lambda n, k: n * (k // 2) + n * (k // 128) * 4, lambda k: 2 * k, lambda n: 2 * n),

@@ -15,6 +15,16 @@ of a row reads front to back):
 * binary       uint32 [N][K/32]: element 32j+i in bit i of word j.
 * int2         uint32 [N][K/16]: element 16j+i in bits [2i, 2i+2) of word j
                 (the ternary field layout), meta as int4 (half2 {scale, zero}).
+* int3         3 bits per weight, K*3/8 bytes per row, meta as int4.  The
+                pages fix only the density (3.25 bits/weight with the g128
+                metadata); the layout is chosen for the GEMV's 16-byte loads:
+                within a 128-group, block b (codes 32b..32b+31) is three
+                32-bit words W0, W1, W2; word Wj holds code 10j+f in bits
+                [3f, 3f+3) and code 10j+5+f in bits [16+3f, 16+3f+3) for
+                f = 0..4, and bit j of code 30 in bit 15, bit j of code 31 in
+                bit 31.  The group's 12 words (b0W0, b0W1, b0W2, b1W0, ...)
+                form three 16-byte planes (words 0-3, 4-7, 8-11); plane p of
+                group g sits at byte p*K/8 + 16*g of the row.
 * int4-hier-g32 codes as int4; one metadata block per matrix:
                 bytes [0, N*K/32): byte n*(K/32)+g = sc | (mi << 4) of group g
                 of row n; zero padding up to a multiple of 16 bytes (offset
@@ -86,6 +96,53 @@ def pack_tern(codes):
 
 def unpack_tern(words, K):
     return _unpack_fields(words, K, 2)
+
+
+def _int3_block_words(c):
+    """32 codes (uint64 array [..., 32]) -> the block's 3 words [..., 3]."""
+    words = []
+    for j in range(3):
+        w = np.zeros(c.shape[:-1], dtype=np.uint64)
+        for f in range(5):
+            w = w + c[..., 10 * j + f] * np.uint64(1 << (3 * f))
+            w = w + c[..., 10 * j + 5 + f] * np.uint64(1 << (16 + 3 * f))
+        w = w + ((c[..., 30] >> np.uint64(j)) & np.uint64(1)) * np.uint64(1 << 15)
+        w = w + ((c[..., 31] >> np.uint64(j)) & np.uint64(1)) * np.uint64(1 << 31)
+        words.append(w)
+    return np.stack(words, axis=-1)
+
+
+def pack_int3(q):
+    """int3 codes [N,K] (0..7) -> uint32 [N, 3K/32] in the plane layout."""
+    q = np.asarray(q)
+    N, K = q.shape
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    c = q.astype(np.uint64)
+    if np.any(c > 7):
+        raise ValueError("code does not fit in 3 bits")
+    ng = K // 128
+    blocks = c.reshape(N, ng, 4, 32)
+    words = _int3_block_words(blocks).reshape(N, ng, 12)          # b0W0 b0W1 b0W2 b1W0 ...
+    planes = words.reshape(N, ng, 3, 4).transpose(0, 2, 1, 3)      # [N][plane][group][4]
+    return planes.reshape(N, 3 * ng * 4).astype(np.uint32)
+
+
+def unpack_int3(words, K):
+    """uint32 [N, 3K/32] -> int3 codes uint8 [N,K] (shift-and-mask reads)."""
+    words = np.asarray(words, dtype=np.uint32).astype(np.uint64)
+    N = words.shape[0]
+    ng = K // 128
+    w = words.reshape(N, 3, ng, 4).transpose(0, 2, 1, 3).reshape(N, ng, 4, 3)
+    out = np.zeros((N, ng, 4, 32), dtype=np.uint8)
+    for j in range(3):
+        wj = w[..., j]
+        for f in range(5):
+            out[..., 10 * j + f] = (wj >> np.uint64(3 * f)) & np.uint64(7)
+            out[..., 10 * j + 5 + f] = (wj >> np.uint64(16 + 3 * f)) & np.uint64(7)
+        out[..., 30] |= (((wj >> np.uint64(15)) & np.uint64(1)) << np.uint64(j)).astype(np.uint8)
+        out[..., 31] |= (((wj >> np.uint64(31)) & np.uint64(1)) << np.uint64(j)).astype(np.uint8)
+    return out.reshape(N, K)
 
 
 def pack_int2(q):

@@ -118,6 +118,32 @@ def quantize_int2_g128(W):
     return q.reshape(N, ng * GROUP), s16, z.astype(np.float16)
 
 
+def quantize_int3_g128(W):
+    """int3, group 128, asymmetric round-to-nearest (Whetstone, bytes/token
+    and quality tables: "int3 g128" at 3.25 bits/weight = 3-bit codes plus
+    the same 32 metadata bits per 128 as int4 g128).  Reading: the int4 g128
+    quantizer with eight levels.
+
+    Per row n and group g, in fp32:
+      lo = min(min_k w, 0); hi = max(max_k w, 0)
+      s  = (hi - lo) / 7;  s16 = fp16_rne(s); s16 := 1 if s16 == 0
+      z  = clip(rint(-lo / s16), 0, 7)             (integer, stored as fp16)
+      q  = clip(rint(w / s16) + z, 0, 7)
+
+    Returns (q uint8 [N,K], scale fp16 [N,K/128], zero fp16 [N,K/128]).
+    """
+    G = _groups(W)
+    N, ng, _ = G.shape
+    lo = np.minimum(G.min(axis=2), F32(0))
+    hi = np.maximum(G.max(axis=2), F32(0))
+    s16 = _guard_zero_scale(fp16_rne((hi - lo) / F32(7)))
+    sf = s16.astype(np.float32)
+    z = np.clip(np.rint(-lo / sf), F32(0), F32(7)).astype(np.int32)
+    q = np.rint(G / sf[:, :, None]) + z[:, :, None].astype(np.float32)
+    q = np.clip(q, F32(0), F32(7)).astype(np.uint8)
+    return q.reshape(N, ng * GROUP), s16, z.astype(np.float16)
+
+
 def quantize_k5(W):
     """K5 byte codes, fp16 scale per 128 weights (TKintegers K5, "What is K5?").
 

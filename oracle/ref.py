@@ -41,6 +41,14 @@ def dequant_int2(codes, meta, K):
     return _expand_groups(s, K) * (q - _expand_groups(z, K))
 
 
+def dequant_int3(codes, meta, K):
+    """w = s * (q - z) per 128-group, q in 0..7 (Whetstone, "int3 g128": the
+    int4 g128 metadata with 3-bit codes).  Exact in fp64."""
+    q = _pack.unpack_int3(codes, K).astype(np.float64)
+    s, z = _pack.unpack_int4_meta(meta)
+    return _expand_groups(s, K) * (q - _expand_groups(z, K))
+
+
 def dequant_int4_hier(codes, meta, N, K):
     """w = d * sc * q - dmin * mi per 32-group (Whetstone, quantizer table,
     "group 32 with hierarchical scale metadata", read as Q4_K-style two-level

@@ -122,3 +122,13 @@ def test_int2_bytes_match_page_row():
     bpw, mb, _ = fmts["int2_g128"]
     assert 8.0 * total / acc.linear_params(shapes) == bpw
     assert abs(total / 1e6 - mb) <= 0.05 + 1e-9
+
+
+def test_int3_bytes_match_page_row():
+    # Whetstone bytes/token table: int3 g128 at 3.25 bits/weight, 200.7 MB
+    vals, fmts = _read("whetstone_roofline.txt")
+    shapes = inputs.sweep_shapes("qwen2.5-0.5b")
+    total = sum(acc.weight_bytes("int3", n, k) for _, n, k in shapes)
+    bpw, mb, _ = fmts["int3_g128"]
+    assert 8.0 * total / acc.linear_params(shapes) == bpw
+    assert abs(total / 1e6 - mb) <= 0.05 + 1e-9

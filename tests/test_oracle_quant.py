@@ -203,3 +203,71 @@ def test_int2_pack_layout():
     words = pack.pack_int2(q)
     assert words.tolist() == [[0, 3 << 2]]
     assert np.array_equal(pack.unpack_int2(words, 32), q)
+
+
+# ---- int3 g128 (Whetstone, "int3 g128": 3-bit codes, int4-style metadata) ----
+
+def _int3_roundtrip(W):
+    q, s, z = quant.quantize_int3_g128(W)
+    codes = pack.pack_int3(q)
+    return q, s, z, codes, ref.dequant_int3(codes, pack.pack_int4_meta(s, z), W.shape[1])
+
+
+def test_int3_lossless_on_grid():
+    # weights on the 1/8 grid spanning [-0.5, 0.375]: hi - lo = 7/8, s = 1/8,
+    # z = 4 and q = 8 w + 4
+    k = np.tile(np.arange(8), 16)
+    W = ((k.astype(np.float32) - 4) / np.float32(8))[None, :]
+    q, s, z, codes, w = _int3_roundtrip(W)
+    assert s[0, 0] == np.float16(0.125) and z[0, 0] == 4
+    assert np.array_equal(q[0].astype(int), k)
+    assert np.array_equal(w.astype(np.float32), W)
+
+
+def test_int3_codes_are_nearest_level():
+    rng = np.random.default_rng(31)
+    W = (rng.standard_normal((4, 256)) * 0.02).astype(np.float32)
+    q, s, z, codes, w = _int3_roundtrip(W)
+    for n in range(4):
+        for g in range(2):
+            levels = float(s[n, g]) * (np.arange(8) - float(z[n, g]))
+            for k in range(128 * g, 128 * g + 128):
+                err = np.abs(float(W[n, k]) - levels)
+                o = np.argsort(err)
+                if err[o[1]] - err[o[0]] > 1e-9:
+                    assert q[n, k] == o[0]
+
+
+def test_int3_layout_one_hot():
+    """Each code position lands where the layout text puts it."""
+    K = 256
+    for pos, val in [(0, 7), (4, 5), (5, 3), (9, 7), (10, 1), (27, 6), (29, 7), (30, 5), (31, 6),
+                     (128 + 32 * 3 + 31, 7), (128 + 64 + 17, 2)]:
+        q = np.zeros((1, K), np.uint8)
+        q[0, pos] = val
+        words = pack.pack_int3(q)
+        assert words.shape == (1, 3 * K // 32)
+        g, e = divmod(pos, 128)
+        b, t = divmod(e, 32)
+        widx = 3 * b                           # index of W0 of the block in the group's 12 words
+        nz = np.flatnonzero(words[0])
+        expect = {}
+        if t < 30:
+            j, f = divmod(t, 10)
+            shift = 3 * f if f < 5 else 16 + 3 * (f - 5)
+            i = widx + j
+            expect[(i // 4) * (K // 128) * 4 + 4 * g + i % 4] = val << shift
+        else:
+            for j in range(3):
+                if (val >> j) & 1:
+                    i = widx + j
+                    expect[(i // 4) * (K // 128) * 4 + 4 * g + i % 4] = 1 << (15 if t == 30 else 31)
+        assert sorted(nz.tolist()) == sorted(expect), pos
+        for idx, v in expect.items():
+            assert int(words[0, idx]) == v, pos
+        assert np.array_equal(pack.unpack_int3(words, K), q)
+
+
+def test_int3_roundtrip_random_codes():
+    q = np.random.default_rng(32).integers(0, 8, (5, 384)).astype(np.uint8)
+    assert np.array_equal(pack.unpack_int3(pack.pack_int3(q), 384), q)
