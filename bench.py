@@ -75,6 +75,8 @@ def _pack(tkq, fmt, Wd):
         return tkq.pack_int4_hier_g32(Wd)
     if fmt == "int2":
         return tkq.pack_int2_g128(Wd)
+    if fmt == "int3":
+        return tkq.pack_int3_g128(Wd)
     return tkq.pack_bin(Wd), None
 
 
@@ -188,6 +190,9 @@ def cpu_baseline_gemv(inputs, model, fmt, budget_s=10.0):
         elif fmt == "int2":
             q, s, z = quant.quantize_int2_g128(W)
             prepared.append((fmt, (pack.pack_int2(q), pack.pack_int4_meta(s, z)), x, N, K))
+        elif fmt == "int3":
+            q, s, z = quant.quantize_int3_g128(W)
+            prepared.append((fmt, (pack.pack_int3(q), pack.pack_int4_meta(s, z)), x, N, K))
         elif fmt == "hier":
             q, sc, mi, d16, dmin16 = quant.quantize_int4_hier_g32(W)
             prepared.append((fmt, (pack.pack_int4(q), pack.pack_hier_meta(sc, mi, d16, dmin16)), x, N, K))
@@ -207,6 +212,8 @@ def cpu_baseline_gemv(inputs, model, fmt, budget_s=10.0):
             y = ref.gemv(ref.dequant_int4_hier(c, m, N, K), x)
         elif f == "int2":
             y = ref.gemv(ref.dequant_int2(c, m, K), x)
+        elif f == "int3":
+            y = ref.gemv(ref.dequant_int3(c, m, K), x)
         else:
             y = ref.gemv(ref.dequant_tern(c, m, K), x)
         assert np.all(np.isfinite(y))
@@ -317,7 +324,7 @@ def run_small(args, torch, tkq, inputs, model, M):
 
 def _fmt_name(fmt):
     return {"int4": "int4-g128", "k5": "K5-g128", "tern": "ternary-g128 (2-bit)", "bin": "binary",
-            "hier": "int4-hier-g32", "int2": "int2-g128"}[fmt]
+            "hier": "int4-hier-g32", "int2": "int2-g128", "int3": "int3-g128"}[fmt]
 
 
 def _fmt_bytes(fmt):
@@ -329,6 +336,7 @@ def _fmt_bytes(fmt):
         "bin": lambda n, k: n * k // 8 + k // 8 + 4 * n,
         "hier": lambda n, k: n * k // 2 + n * (k // 32) + 4 * n + 2 * k + 2 * n,
         "int2": lambda n, k: n * k // 4 + n * (k // 128) * 4 + 2 * k + 2 * n,
+        "int3": lambda n, k: 3 * n * k // 8 + n * (k // 128) * 4 + 2 * k + 2 * n,
     }[fmt]
 
 
@@ -432,7 +440,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="0.5b-int4",
                     choices=["0.5b-int4", "0.5b-int4-greedy", "0.5b-k5", "0.5b-tern", "0.5b-hier",
-                             "0.5b-int2", "0.5b-int4-m2", "0.5b-int4-m4", "0.5b-int4-m8", "0.5b-int4-m16",
+                             "0.5b-int2", "0.5b-int3", "0.5b-int4-m2", "0.5b-int4-m4", "0.5b-int4-m8", "0.5b-int4-m16",
                              "7b-int4-m16", "bin", "single-896",
                              "7b-int4", "7b-hier", "7b-prefill", "probe"])
     ap.add_argument("--graph", default="none", choices=["none", "step", "all"],
@@ -468,7 +476,7 @@ def main():
 
     w = args.workload
     if w in ("0.5b-int4", "0.5b-int4-greedy", "0.5b-k5", "0.5b-tern", "0.5b-hier", "0.5b-int2",
-             "7b-int4", "7b-hier"):
+             "0.5b-int3", "7b-int4", "7b-hier"):
         model = "qwen2.5-7b" if w.startswith("7b") else "qwen2.5-0.5b"
         fmt = w.split("-")[1]
         out = run_sweep(args, torch, tkq, inputs, model, fmt, greedy=w.endswith("greedy"))

@@ -81,6 +81,7 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
 // ---------------------------------------------------------------- codecs --
 // Each codec states, for one 16-byte chunk of codes:
 //   WPC  weights per chunk
+//   PLANES  16-byte loads per chunk (one per plane of the row)
 //   XR   u32 registers of prepared x (pairs of fp16)
 //   XB   bytes of x the chunk consumes
 //   CPG  chunks per 128-weight group;  MB metadata bytes per group
@@ -98,7 +99,7 @@ struct Codec;
 // apart and are combined as lo + hi/16.
 template <>
 struct Codec<kFmtInt4> {
-  static constexpr int WPC = 32, XR = 16, XB = 64, CPG = 4, MB = 4;
+  static constexpr int WPC = 32, XR = 16, XB = 64, CPG = 4, MB = 4, PLANES = 1;
   static constexpr uint32_t kZero = 0u;
   struct Regs {
     uint32_t m0, m1, magic;
@@ -132,7 +133,7 @@ struct Codec<kFmtInt4> {
 // (1024 + c1, 1024 + c3) from a code word and the byte 0x64.
 template <>
 struct Codec<kFmtK5> {
-  static constexpr int WPC = 16, XR = 8, XB = 32, CPG = 8, MB = 2;
+  static constexpr int WPC = 16, XR = 8, XB = 32, CPG = 8, MB = 2, PLANES = 1;
   static constexpr uint32_t kZero = 0x79797979u;  // 121 = value 0
   struct Regs {
     uint32_t sel_a, sel_b, magic;
@@ -165,7 +166,7 @@ struct Codec<kFmtK5> {
 // shifted right by 10 gives s = 5, 6, 7 with multipliers 1, 4, 16.
 template <>
 struct Codec<kFmtTern> {
-  static constexpr int WPC = 64, XR = 32, XB = 128, CPG = 2, MB = 2;
+  static constexpr int WPC = 64, XR = 32, XB = 128, CPG = 2, MB = 2, PLANES = 1;
   static constexpr uint32_t kZero = 0x55555555u;  // code 1 = value 0
   struct Regs {
     uint32_t m[5], magic;
@@ -223,10 +224,78 @@ struct Codec<kFmtInt2> : Codec<kFmtTern> {
   static constexpr int CPG = 2, MB = 4;
 };
 
+// int3 g128: a chunk is one 128-group = three 16-byte planes (12 words, four
+// 32-weight blocks of three words).  Word j of a block holds codes 10j..10j+4
+// at bits 3f and 10j+5..10j+9 at bits 16+3f, so masks 7<<3f on both halves
+// give (1024 + 8^f c, 1024 + 8^f c') for f = 0, 1, 2 and the word shifted
+// right by 9 gives f = 3, 4 with multipliers 1, 8.  Codes 30 and 31 are
+// spread over bits 15 and 31 of the three words (bit j in word j) and are
+// gathered into one pair with three shift + and_or steps.  Metadata as int4.
+struct Planes3 {
+  u32x4 p[3];
+};
+
+template <>
+struct Codec<kFmtInt3> {
+  static constexpr int WPC = 128, XR = 64, XB = 256, CPG = 1, MB = 4, PLANES = 3;
+  static constexpr uint32_t kZero = 0u;
+  struct Regs {
+    uint32_t m0, m1, m2, s0, s1, s2, magic;
+  };
+  __device__ static Regs make() {
+    return {in_sgpr(0x00070007u), in_sgpr(0x00380038u), in_sgpr(0x01C001C0u), in_sgpr(0x00010001u),
+            in_sgpr(0x00020002u), in_sgpr(0x00040004u), in_vgpr(kMagic)};
+  }
+  // pair (e1, e2) of a block's x values; raw[i] = (x_2i, x_2i+1)
+  __device__ static uint32_t xpair(const uint32_t* raw, int e1, int e2) {
+    const uint32_t lo = (e1 & 1) ? 0x0302u : 0x0100u, hi = (e2 & 1) ? 0x0706u : 0x0504u;
+    return __builtin_amdgcn_perm(raw[e2 >> 1], raw[e1 >> 1], (hi << 16) | lo);
+  }
+  __device__ static void prep(const uint32_t* raw, uint32_t* xr) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t* r = raw + 16 * b;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+#pragma unroll
+        for (int f = 0; f < 5; ++f) xr[16 * b + 5 * j + f] = xpair(r, 10 * j + f, 10 * j + 5 + f);
+      }
+      xr[16 * b + 15] = xpair(r, 30, 31);
+    }
+  }
+  __device__ static float dot(const Planes3& q, const uint32_t* xr, const Regs& R) {
+    float a1 = 0.0f, a8 = 0.0f, a64 = 0.0f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      uint32_t w[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int n = 3 * b + j;
+        w[j] = q.p[n >> 2][n & 3];
+      }
+      const uint32_t* x = xr + 16 * b;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const uint32_t v = w[j], t = v >> 9;
+        a1 = __builtin_amdgcn_fdot2(as_h2((v & R.m0) | R.magic), as_h2(x[5 * j + 0]), a1, false);
+        a8 = __builtin_amdgcn_fdot2(as_h2((v & R.m1) | R.magic), as_h2(x[5 * j + 1]), a8, false);
+        a64 = __builtin_amdgcn_fdot2(as_h2((v & R.m2) | R.magic), as_h2(x[5 * j + 2]), a64, false);
+        a1 = __builtin_amdgcn_fdot2(as_h2((t & R.m0) | R.magic), as_h2(x[5 * j + 3]), a1, false);
+        a8 = __builtin_amdgcn_fdot2(as_h2((t & R.m1) | R.magic), as_h2(x[5 * j + 4]), a8, false);
+      }
+      uint32_t p = ((w[0] >> 15) & R.s0) | R.magic;
+      p = ((w[1] >> 14) & R.s1) | p;
+      p = ((w[2] >> 13) & R.s2) | p;
+      a1 = __builtin_amdgcn_fdot2(as_h2(p), as_h2(x[15]), a1, false);
+    }
+    return fmaf(a64, 0.015625f, fmaf(a8, 0.125f, a1));
+  }
+};
+
 // Binary: 128 sign bits per chunk; x is kept as packed words.
 template <>
 struct Codec<kFmtBin> {
-  static constexpr int WPC = 128, XR = 4, XB = 16, CPG = 1, MB = 0;
+  static constexpr int WPC = 128, XR = 4, XB = 16, CPG = 1, MB = 0, PLANES = 1;
   struct Regs {};
   __device__ static Regs make() { return {}; }
   __device__ static void prep(const uint32_t* raw, uint32_t* xr) {
@@ -246,6 +315,7 @@ struct Tile {
   __amdgpu_buffer_rsrc_t codes, meta, x, y;
   __amdgpu_buffer_rsrc_t rmeta;  // int4-hier-g32: the rows' fp16 (d, dmin) pairs
   uint32_t row_bytes;       // bytes of codes per row
+  uint32_t plane_bytes;     // bytes of one plane of a row (PLANES > 1)
   uint32_t meta_row_bytes;  // bytes of metadata per row
   int lg, sub, prow, P;     // lanes-per-row log2, lane in group, row in step, rows per step
   int S, slice;             // k-slices, this wave's slice
@@ -286,8 +356,9 @@ struct Runner {
   static constexpr bool kBin = FMT == kFmtBin;
   using Acc = typename std::conditional<kBin, int, float>::type;
 
+  using Chunk = typename std::conditional<Cd::PLANES == 3, Planes3, u32x4>::type;
   struct Buf {
-    u32x4 c[U][J];
+    Chunk c[U][J];
     uint32_t m[U][J];
     uint32_t rp[U];  // int4-hier-g32 row pair
   };
@@ -328,7 +399,13 @@ struct Runner {
       }
       Cd::prep(raw, xr[j]);
       if constexpr (!kBin) {
-        const u32x4 zc = {Cd::kZero, Cd::kZero, Cd::kZero, Cd::kZero};
+        Chunk zc;
+        if constexpr (Cd::PLANES == 3) {
+#pragma unroll
+          for (int p = 0; p < 3; ++p) zc.p[p] = (u32x4){Cd::kZero, Cd::kZero, Cd::kZero, Cd::kZero};
+        } else {
+          zc = (u32x4){Cd::kZero, Cd::kZero, Cd::kZero, Cd::kZero};
+        }
         bias[j] = Cd::dot(zc, xr[j], R);
         float sx = 0.0f;
 #pragma unroll
@@ -349,7 +426,12 @@ struct Runner {
       const uint32_t rb = r * t.row_bytes, mb = r * t.meta_row_bytes;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        b.c[u][j] = load16_nt(t.codes, rb + cof[j]);
+        if constexpr (Cd::PLANES == 3) {
+#pragma unroll
+          for (int p = 0; p < 3; ++p) b.c[u][j].p[p] = load16_nt(t.codes, rb + (uint32_t)p * t.plane_bytes + cof[j]);
+        } else {
+          b.c[u][j] = load16_nt(t.codes, rb + cof[j]);
+        }
         if constexpr (Cd::MB == 4) b.m[u][j] = load4(t.meta, mb + mof[j]);
         else if constexpr (Cd::MB == 2) b.m[u][j] = load2(t.meta, mb + mof[j]);
         else if constexpr (Cd::MB == 1) b.m[u][j] = load1(t.meta, mb + mof[j]);
@@ -374,7 +456,7 @@ struct Runner {
           const uint32_t m = b.m[u][j];
           rs = fmaf((float)(m & 15u), d, rs);
           rm = fmaf((float)(m >> 4), xsum[j], rm);
-        } else if constexpr (FMT == kFmtInt4 || FMT == kFmtInt2) {
+        } else if constexpr (FMT == kFmtInt4 || FMT == kFmtInt2 || FMT == kFmtInt3) {
           const float d = Cd::dot(b.c[u][j], xr[j], R) - bias[j];
           res = fmaf(half_lo(b.m[u][j]), fmaf(-half_hi(b.m[u][j]), xsum[j], d), res);
         } else {
@@ -432,9 +514,19 @@ struct Runner {
   }
 };
 
+// Row steps per loop iteration: the planner's unroll, or for the 48-byte
+// int3 chunks a divisor of it (tile heights stay multiples).
+#ifndef TKQ_INT3_U
+#define TKQ_INT3_U 2
+#endif
+template <int FMT, int J>
+constexpr int runner_unroll() {
+  return Codec<FMT>::PLANES == 3 ? (gemv_unroll(J) % TKQ_INT3_U == 0 ? TKQ_INT3_U : 1) : gemv_unroll(J);
+}
+
 template <int FMT, int J, bool GREEDY>
 __device__ __forceinline__ uint64_t run_passes(const Tile& t, uint32_t* part) {
-  Runner<FMT, J, gemv_unroll(J), GREEDY> r(t);
+  Runner<FMT, J, runner_unroll<FMT, J>(), GREEDY> r(t);
   r.run(part);
   return r.best;
 }
@@ -487,7 +579,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WP
   t.K = K;
   t.C = K / Cd::WPC;
   t.Cs = (t.C + t.S - 1) / t.S;
-  t.row_bytes = (uint32_t)t.C * 16u;
+  t.plane_bytes = (uint32_t)t.C * 16u;
+  t.row_bytes = t.plane_bytes * (uint32_t)Cd::PLANES;
   t.meta_row_bytes = (uint32_t)(t.C / Cd::CPG) * Cd::MB;
   const int nrows = min(rpt, N - row0);
   t.row0 = row0;
@@ -584,7 +677,7 @@ __global__ __launch_bounds__(256) void greedy_finish_kernel(const tkq_gemv_desc*
 
 template <int FMT>
 constexpr int max_passes() {
-  return FMT == kFmtBin ? 8 : ((FMT == kFmtTern || FMT == kFmtInt2) ? 3 : 4);  // int4, hier-g32, K5: 4
+  return FMT == kFmtBin ? 8 : ((FMT == kFmtTern || FMT == kFmtInt2) ? 3 : (FMT == kFmtInt3 ? 2 : 4));
 }
 
 typedef void (*GemvFn)(const tkq_gemv_desc*, int, Greedy);
@@ -613,6 +706,7 @@ int gemv_max_passes(int fmt) {
     case kFmtInt4: return max_passes<kFmtInt4>();
     case kFmtHier: return max_passes<kFmtHier>();
     case kFmtInt2: return max_passes<kFmtInt2>();
+    case kFmtInt3: return max_passes<kFmtInt3>();
     case kFmtK5: return max_passes<kFmtK5>();
     case kFmtTern: return max_passes<kFmtTern>();
     case kFmtBin: return max_passes<kFmtBin>();
@@ -628,6 +722,7 @@ hipError_t launch_gemv(int fmt, int jmax, const tkq_gemv_desc* dev_descs, int co
     case kFmtInt4: fn = pick<kFmtInt4>(jmax, greedy); break;
     case kFmtHier: fn = pick<kFmtHier>(jmax, greedy); break;
     case kFmtInt2: fn = pick<kFmtInt2>(jmax, greedy); break;
+    case kFmtInt3: fn = pick<kFmtInt3>(jmax, greedy); break;
     case kFmtK5: fn = pick<kFmtK5>(jmax, greedy); break;
     case kFmtTern: fn = pick<kFmtTern>(jmax, greedy); break;
     case kFmtBin: fn = pick<kFmtBin>(jmax, greedy); break;

@@ -16,6 +16,7 @@ constexpr int kFmtTern = TKQ_FMT_TERN_G128;
 constexpr int kFmtBin = TKQ_FMT_BIN;
 constexpr int kFmtHier = TKQ_FMT_INT4_HIER_G32;
 constexpr int kFmtInt2 = TKQ_FMT_INT2_G128;
+constexpr int kFmtInt3 = TKQ_FMT_INT3_G128;
 
 // Work decomposition of one GEMV, packed into tkq_gemv_desc::shape.
 struct GemvShape {
@@ -34,10 +35,15 @@ inline int weights_per_chunk(int fmt) {
     case kFmtK5: return 16;
     case kFmtTern: return 64;
     case kFmtInt2: return 64;
+    case kFmtInt3: return 128;
     case kFmtBin: return 128;
   }
   return 0;
 }
+
+// Bytes of codes per chunk (one lane's unit of a row): 16, or 48 for int3
+// (three 16-byte planes).
+inline int chunk_bytes(int fmt) { return fmt == kFmtInt3 ? 48 : 16; }
 
 // Largest row tile of one GEMV workgroup (bounds the k-slice LDS buffer).
 constexpr int kGemvMaxTileRows = 1024;

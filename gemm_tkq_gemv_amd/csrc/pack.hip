@@ -15,6 +15,8 @@
 //   K5        : s = fp16(max|w| / 121), c = clamp(rint(w/s), -121, 121) + 121
 //   ternary   : s = fp16(sequential-sum|w| / 128), code = clamp(rint(w/s),-1,1)+1
 //   int2 g128 : as int4 with 4 levels: s = fp16((hi-lo)/3), z, q in 0..3
+//   int3 g128 : as int4 with 8 levels: s = fp16((hi-lo)/7), z, q in 0..7,
+//               stored in the GEMV's plane layout (see tkq.h)
 //   int4 hier-g32 (Whetstone README, quantizer table "group 32 with
 //               hierarchical scale metadata"; "Prior art", the Q4_K
 //               comparison): per 32-group s_g = (hi-lo)/15, m_g = -lo; per
@@ -89,6 +91,43 @@ __global__ __launch_bounds__(256) void pack_int2_kernel(const float* __restrict_
   const int nib = q0 | (q1 << 2);
   const int other = __shfl_xor(nib, 1, 64);
   if ((lane & 1) == 0) codes[row * (K / 4) + col / 4 + (lane >> 1)] = (uint8_t)(nib | (other << 4));
+  if (lane == 0) meta[g] = (uint32_t)sbits | ((uint32_t)half_bits(zf) << 16);
+}
+
+// int3: the wave's 128 codes go through LDS; lanes 0..11 each build one of
+// the group's 12 words and store it into its plane.
+__global__ __launch_bounds__(256) void pack_int3_kernel(const float* __restrict__ W, int64_t K, int64_t groups,
+                                                        uint32_t* __restrict__ codes, uint32_t* __restrict__ meta) {
+  __shared__ uint8_t cs[kWavesPerBlock][kGroup];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  int64_t g;
+  const bool live = group_of_wave(groups, &g);
+  const int64_t gpr = K / kGroup;
+  const int64_t row = live ? g / gpr : 0, grp = live ? g - row * gpr : 0;
+  float2 w = make_float2(0.0f, 0.0f);
+  if (live) w = *reinterpret_cast<const float2*>(W + row * K + grp * kGroup + 2 * lane);
+  const float lo = fminf(wave_min(fminf(w.x, w.y)), 0.0f);
+  const float hi = fmaxf(wave_max(fmaxf(w.x, w.y)), 0.0f);
+  uint16_t sbits;
+  const float s = guard_scale((hi - lo) / 7.0f, &sbits);
+  const float zf = (float)(int)fminf(fmaxf(rintf(-lo / s), 0.0f), 7.0f);
+  cs[wave][2 * lane] = (uint8_t)(int)fminf(fmaxf(rintf(w.x / s) + zf, 0.0f), 7.0f);
+  cs[wave][2 * lane + 1] = (uint8_t)(int)fminf(fmaxf(rintf(w.y / s) + zf, 0.0f), 7.0f);
+  __syncthreads();
+  if (!live) return;
+  if (lane < 12) {
+    const int b = lane / 3, j = lane - 3 * b;
+    const uint8_t* c = cs[wave] + 32 * b;
+    uint32_t word = 0;
+#pragma unroll
+    for (int f = 0; f < 5; ++f) word |= ((uint32_t)c[10 * j + f] << (3 * f)) | ((uint32_t)c[10 * j + 5 + f] << (16 + 3 * f));
+    word |= ((uint32_t)(c[30] >> j) & 1u) << 15;
+    word |= ((uint32_t)(c[31] >> j) & 1u) << 31;
+    // plane lane / 4, word lane % 4 of this group's 16 bytes in that plane
+    const int64_t plane_words = K / 32;  // K/8 bytes per plane
+    codes[row * (3 * K / 32) + (lane >> 2) * plane_words + 4 * grp + (lane & 3)] = word;
+  }
   if (lane == 0) meta[g] = (uint32_t)sbits | ((uint32_t)half_bits(zf) << 16);
 }
 
@@ -243,6 +282,10 @@ hipError_t launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* code
   switch (fmt) {
     case kFmtInt4:
       hipLaunchKernelGGL(pack_int4_kernel, grid, block, 0, stream, W, K, groups, (uint8_t*)codes,
+                         (uint32_t*)meta);
+      break;
+    case kFmtInt3:
+      hipLaunchKernelGGL(pack_int3_kernel, grid, block, 0, stream, W, K, groups, (uint32_t*)codes,
                          (uint32_t*)meta);
       break;
     case kFmtInt2:

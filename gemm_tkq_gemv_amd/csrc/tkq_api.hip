@@ -37,6 +37,7 @@ struct PlanParams {
 PlanParams plan_params(int fmt) {
   if (fmt == TKQ_FMT_INT4_G128 || fmt == TKQ_FMT_INT4_HIER_G32) return {2, 4, 48 << 10, 4 << 10, 40 << 20};
   if (fmt == TKQ_FMT_TERN_G128 || fmt == TKQ_FMT_INT2_G128) return {1, TKQ_TERN_JMAX, 24 << 10, 4 << 10, 40 << 20};
+  if (fmt == TKQ_FMT_INT3_G128) return {1, 1, 24 << 10, 4 << 10, 40 << 20};
   return {1, 8, 24 << 10, 4 << 10, 40 << 20};
 }
 constexpr int kMaxTileRows = tkq::kGemvMaxTileRows;
@@ -51,16 +52,18 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool known_fmt(int fmt) {
   return fmt == TKQ_FMT_INT4_G128 || fmt == TKQ_FMT_K5_G128 || fmt == TKQ_FMT_TERN_G128 ||
-         fmt == TKQ_FMT_BIN || fmt == TKQ_FMT_INT4_HIER_G32 || fmt == TKQ_FMT_INT2_G128;
+         fmt == TKQ_FMT_BIN || fmt == TKQ_FMT_INT4_HIER_G32 || fmt == TKQ_FMT_INT2_G128 ||
+         fmt == TKQ_FMT_INT3_G128;
 }
 
 // Column unit of a coding's GEMV (its group size, or one code word).
 int k_unit(int fmt) { return fmt == TKQ_FMT_INT4_HIER_G32 ? 32 : 128; }
 
-// Largest K each GEMV variant handles with x resident in registers:
-// chunks per row <= 4 k-slices x 64 lanes x max passes.
+// Largest K each GEMV handles with x resident in registers: chunks per row
+// <= 4 k-slices x 64 lanes x the planner's pass cap.
 int64_t gemv_max_k(int fmt) {
-  return int64_t(4) * 64 * tkq::gemv_max_passes(fmt) * tkq::weights_per_chunk(fmt);
+  return int64_t(4) * 64 * std::min(tkq::gemv_max_passes(fmt), plan_params(fmt).max_passes) *
+         tkq::weights_per_chunk(fmt);
 }
 
 int check_matrix(const float* W, int64_t N, int64_t K, int64_t kunit) {
@@ -116,7 +119,7 @@ int rows_per_tile(int fmt, int N, int K, tkq::GemvShape sh, int64_t kTileTargetB
   const int P = 64 >> sh.lanes_log2;       // rows per wave step
   const int RG = 4 / sh.kslices;           // row groups per workgroup
   const int U = tkq::gemv_unroll(sh.passes);  // steps per loop iteration
-  const int64_t step_bytes = int64_t(P) * Cs * 16;
+  const int64_t step_bytes = int64_t(P) * Cs * tkq::chunk_bytes(fmt);
   int64_t steps = (kTileTargetBytes + step_bytes - 1) / step_bytes;
   const int64_t need = ((int64_t(N) + RG - 1) / RG + P - 1) / P;  // steps to cover N
   if (steps > need) steps = need;
@@ -170,6 +173,11 @@ int tkq_pack_int2_g128(const float* W, int64_t N, int64_t K, uint32_t* codes, ui
   return pack_common(TKQ_FMT_INT2_G128, W, N, K, codes, meta, true, 128, stream);
 }
 
+int tkq_pack_int3_g128(const float* W, int64_t N, int64_t K, uint32_t* codes, uint32_t* meta,
+                       void* stream) {
+  return pack_common(TKQ_FMT_INT3_G128, W, N, K, codes, meta, true, 128, stream);
+}
+
 int tkq_pack_int4_hier_g32(const float* W, int64_t N, int64_t K, uint32_t* codes, uint8_t* meta,
                            void* stream) {
   return pack_common(TKQ_FMT_INT4_HIER_G32, W, N, K, codes, meta, true, 32, stream);
@@ -197,7 +205,7 @@ int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan) {
   // Sweep position where the small-tile tail begins.
   int64_t total = 0;
   for (int32_t i = 0; i < count; ++i)
-    total += int64_t(descs[i].N) * (descs[i].K / tkq::weights_per_chunk(fmt)) * 16;
+    total += int64_t(descs[i].N) * (descs[i].K / tkq::weights_per_chunk(fmt)) * tkq::chunk_bytes(fmt);
   const PlanParams pp = plan_params(fmt);
   const int64_t tail_start = total > pp.tail ? total - pp.tail : 0;
 
@@ -209,7 +217,7 @@ int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan) {
     if (sh.passes < 1) return TKQ_ESHAPE;
     const int big = rows_per_tile(fmt, d.N, d.K, sh, pp.tile);
     const int small = rows_per_tile(fmt, d.N, d.K, sh, pp.small);
-    const int64_t row_bytes = int64_t(d.K / tkq::weights_per_chunk(fmt)) * 16;
+    const int64_t row_bytes = int64_t(d.K / tkq::weights_per_chunk(fmt)) * tkq::chunk_bytes(fmt);
     // rows above the tail start get large tiles
     int64_t big_rows = 0;
     if (pos + d.N * row_bytes <= tail_start) big_rows = d.N;

@@ -26,8 +26,9 @@ FMT_TERN_G128 = 3
 FMT_BIN = 4
 FMT_INT4_HIER_G32 = 5
 FMT_INT2_G128 = 6
+FMT_INT3_G128 = 7
 FORMATS = {"int4": FMT_INT4_G128, "k5": FMT_K5_G128, "tern": FMT_TERN_G128, "bin": FMT_BIN,
-           "hier": FMT_INT4_HIER_G32, "int2": FMT_INT2_G128}
+           "hier": FMT_INT4_HIER_G32, "int2": FMT_INT2_G128, "int3": FMT_INT3_G128}
 
 OK, EINVAL, ESHAPE, EALIGN, EFORMAT, EHIP, EPLAN = 0, -1, -2, -3, -4, -5, -6
 
@@ -68,6 +69,7 @@ _SIGNATURES = {
     "tkq_pack_bin": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
     "tkq_pack_int4_hier_g32": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "tkq_pack_int2_g128": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "tkq_pack_int3_g128": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "tkq_hier_meta_bytes": ([_I64, _I64], ctypes.c_int64),
     "tkq_gemv_prepare": ([ctypes.POINTER(GemvDesc), _I32, ctypes.POINTER(GemvPlan)], ctypes.c_int),
     "tkq_gemv": ([ctypes.POINTER(GemvPlan), _P, _P], ctypes.c_int),
@@ -182,6 +184,16 @@ def pack_int2_g128(W, stream=None):
     return codes, meta
 
 
+def pack_int3_g128(W, stream=None):
+    """W fp32 [N,K] -> (codes int32 [N,3K/32] (plane layout), meta int32 [N,K/128])."""
+    _need(W, torch.float32, "W")
+    N, K = W.shape
+    codes = torch.empty((N, 3 * K // 32), dtype=torch.int32, device=W.device)
+    meta = torch.empty((N, K // 128), dtype=torch.int32, device=W.device)
+    _call("tkq_pack_int3_g128", _ptr(W), N, K, _ptr(codes), _ptr(meta), _stream(stream))
+    return codes, meta
+
+
 def hier_meta_bytes(N, K):
     """Size of an int4-hier-g32 metadata block (tkq_hier_meta_bytes)."""
     n = lib().tkq_hier_meta_bytes(N, K)
@@ -203,7 +215,7 @@ def pack_int4_hier_g32(W, stream=None):
 
 PACKERS = {FMT_INT4_G128: pack_int4_g128, FMT_K5_G128: pack_k5,
            FMT_TERN_G128: pack_tern_g128, FMT_INT4_HIER_G32: pack_int4_hier_g32,
-           FMT_INT2_G128: pack_int2_g128}
+           FMT_INT2_G128: pack_int2_g128, FMT_INT3_G128: pack_int3_g128}
 
 
 # ---- grouped GEMV ------------------------------------------------------------

@@ -56,6 +56,16 @@
  *   g128" at 2.25 bits/weight):
  *     codes uint32 [N][K/16] : element 16j+i in bits [2i,2i+2) of word j
  *     meta  uint32 [N][K/128]: as TKQ_FMT_INT4_G128;  w = scale * (q - zero)
+ * TKQ_FMT_INT3_G128 (Whetstone README, bytes/token and quality tables, "int3
+ *   g128" at 3.25 bits/weight):
+ *     codes uint32 [N][3K/32]: per 128-group g, block b (codes 32b..32b+31)
+ *           is three words W0..W2; Wj holds code 10j+f in bits [3f,3f+3) and
+ *           code 10j+5+f in bits [16+3f,16+3f+3) (f = 0..4), bit j of code 30
+ *           in bit 15 and bit j of code 31 in bit 31.  The group's 12 words
+ *           (b0W0, b0W1, b0W2, b1W0, ...) form three 16-byte planes (words
+ *           0-3, 4-7, 8-11); plane p of group g is at byte p*K/8 + 16g of the
+ *           row (rows are 3K/8 bytes).
+ *     meta  uint32 [N][K/128]: as TKQ_FMT_INT4_G128;  w = scale * (q - zero)
  * TKQ_FMT_INT4_HIER_G32 (Whetstone README, bytes/token table "int4 hier-g32"
  *   at 4.28 bits/weight, quantizer table "group 32 with hierarchical scale
  *   metadata", and "Prior art": Q4_K-like sub-scales against an fp16 pair,
@@ -97,12 +107,13 @@ extern "C" {
 #define TKQ_FMT_BIN 4
 #define TKQ_FMT_INT4_HIER_G32 5
 #define TKQ_FMT_INT2_G128 6
+#define TKQ_FMT_INT3_G128 7
 
 /* Size limits: 1 <= N <= 2^31-1, 32 <= K <= 2^20 (K % 128 == 0 for the
  * group-128 codings and for their GEMVs; K % 32 == 0 for tkq_pack_bin, the
  * int4-hier-g32 coding and their GEMVs), and N*K <= 2^39 weights.  A GEMV
- * additionally needs K <= 32768 (int4 g128 and hier-g32), 16384 (K5), 49152
- * (ternary, int2) or 262144 (binary). */
+ * additionally needs K <= 32768 (int4 g128, hier-g32, ternary, int2, int3),
+ * 16384 (K5) or 262144 (binary). */
 #define TKQ_MAX_K (1 << 20)
 
 /* Library version (TKQ_VERSION of the build). */
@@ -150,6 +161,14 @@ int tkq_pack_tern_g128(const float* W, int64_t N, int64_t K, uint32_t* codes,
  * s), 0, 3), q = clamp(rint(w / s) + z, 0, 3).  codes: uint32 [N][K/16];
  * meta: uint32 [N][K/128] = half2 {s, z}.  K % 128 == 0. */
 int tkq_pack_int2_g128(const float* W, int64_t N, int64_t K, uint32_t* codes,
+                       uint32_t* meta, void* stream);
+
+/* int3 g128, asymmetric RTN (Whetstone README, "int3 g128"): the int4 g128
+ * quantizer with eight levels: s = fp16((hi - lo) / 7), z = clamp(rint(-lo /
+ * s), 0, 7), q = clamp(rint(w / s) + z, 0, 7).  codes: uint32 [N][3K/32] in
+ * the plane layout above; meta: uint32 [N][K/128] = half2 {s, z}.
+ * K % 128 == 0. */
+int tkq_pack_int3_g128(const float* W, int64_t N, int64_t K, uint32_t* codes,
                        uint32_t* meta, void* stream);
 
 /* Sign bits (Whetstone README, "Measured hardware facts"): bit = 1 exactly
@@ -203,7 +222,7 @@ typedef struct tkq_gemv_desc {
   int32_t small_rows;    /* [prepare] rows of a small tile; small tiles
                                       cover the rows below the large ones   */
   const void* codes;     /* packed codes (layout per fmt)                   */
-  const void* meta;      /* int4, int2: uint32 half2 [N][K/128]; K5, ternary: fp16
+  const void* meta;      /* int4, int3, int2: uint32 half2 [N][K/128]; K5, ternary: fp16
                             [N][K/128]; hier-g32: its metadata block;
                             binary: ignored (may be NULL)                   */
   const void* x;         /* fp16 [K]; binary: uint32 [K/32]                 */

@@ -10,7 +10,7 @@ from oracle import pack as opack
 from oracle import quant as oquant
 from oracle import ref as oref
 
-FMTS = ("int4", "k5", "tern", "bin", "hier", "int2")
+FMTS = ("int4", "k5", "tern", "bin", "hier", "int2", "int3")
 
 
 def gpu_or_skip():
@@ -51,6 +51,9 @@ def oracle_pack(fmt, W):
     if fmt == "int2":
         q, s, z = oquant.quantize_int2_g128(W)
         return opack.pack_int2(q), opack.pack_int4_meta(s, z)
+    if fmt == "int3":
+        q, s, z = oquant.quantize_int3_g128(W)
+        return opack.pack_int3(q), opack.pack_int4_meta(s, z)
     if fmt == "hier":
         q, sc, mi, d16, dmin16 = oquant.quantize_int4_hier_g32(W)
         return opack.pack_int4(q), opack.pack_hier_meta(sc, mi, d16, dmin16)
@@ -69,12 +72,14 @@ def oracle_wdeq(fmt, codes, meta, K):
         return oref.dequant_int4_hier(codes, meta, codes.shape[0], K)
     if fmt == "int2":
         return oref.dequant_int2(codes, meta, K)
+    if fmt == "int3":
+        return oref.dequant_int3(codes, meta, K)
     raise ValueError(fmt)
 
 
 def device_codes_np(fmt, codes, meta):
     """Device packed tensors -> numpy arrays in the oracle's dtypes."""
-    if fmt in ("int4", "int2"):
+    if fmt in ("int4", "int2", "int3"):
         return u32(codes), u32(meta)
     if fmt == "k5":
         return codes.cpu().numpy(), meta.cpu().numpy()

@@ -52,7 +52,7 @@ def test_version_and_strings():
 
 
 @pytest.mark.parametrize("name", ["tkq_pack_int4_g128", "tkq_pack_k5", "tkq_pack_tern_g128",
-                                  "tkq_pack_int4_hier_g32", "tkq_pack_int2_g128"])
+                                  "tkq_pack_int4_hier_g32", "tkq_pack_int2_g128", "tkq_pack_int3_g128"])
 def test_pack_validation(name):
     f = getattr(tkq.lib(), name)
     assert f(None, 4, 128, A, A, None) == tkq.EINVAL
@@ -122,7 +122,7 @@ def _tiles(d):
     return out
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5, 6, 7])
 def test_prepare_tiles_cover_rows(fmt):
     shapes = [(1, 128), (7, 896), (128, 896), (4864, 896), (896, 4864), (333, 4864), (151936, 896)]
     if fmt == 5:
@@ -131,7 +131,7 @@ def test_prepare_tiles_cover_rows(fmt):
     st, plan = _prepare(arr)
     assert st == tkq.OK
     work = 0
-    per_chunk = {1: 32, 2: 16, 3: 64, 4: 128, 5: 32, 6: 64}[fmt]
+    per_chunk = {1: 32, 2: 16, 3: 64, 4: 128, 5: 32, 6: 64, 7: 128}[fmt]
     for d, (n, k) in zip(arr, shapes):
         assert d.work0 == work
         tiles = _tiles(d)
@@ -176,7 +176,7 @@ def test_prepare_validation():
     arr = _descs(1, [(8, 128), (8, 256)])
     arr[1].fmt = 2
     assert _prepare(arr)[0] == tkq.EFORMAT
-    arr = _descs(7, [(8, 128)])
+    arr = _descs(99, [(8, 128)])
     assert _prepare(arr)[0] == tkq.EFORMAT
     arr = _descs(1, [(8, 200)])
     assert _prepare(arr)[0] == tkq.ESHAPE

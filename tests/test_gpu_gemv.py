@@ -12,8 +12,9 @@ from oracle import ref as oref
 
 pytestmark = pytest.mark.gpu
 
-MAXK = {"int4": 18944, "k5": 4864, "tern": 18944, "bin": 18944, "hier": 18944, "int2": 18944}
-FLOAT_FMTS = ["int4", "k5", "tern", "hier", "int2"]
+MAXK = {"int4": 18944, "k5": 4864, "tern": 18944, "bin": 18944, "hier": 18944, "int2": 18944,
+        "int3": 18944}
+FLOAT_FMTS = ["int4", "k5", "tern", "hier", "int2", "int3"]
 
 
 def _shapes(fmt):
@@ -43,6 +44,8 @@ def _device_pack(torch, tkq, fmt, Wd):
         return tkq.pack_int4_hier_g32(Wd)
     if fmt == "int2":
         return tkq.pack_int2_g128(Wd)
+    if fmt == "int3":
+        return tkq.pack_int3_g128(Wd)
     return tkq.pack_bin(Wd), None
 
 
@@ -75,7 +78,7 @@ def _check(fmt, W, x, y, codes, meta, what):
     check_gemv(y.float().cpu().numpy(), w_deq, x, what)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin", "hier", "int2"])
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin", "hier", "int2", "int3"])
 def test_gemv_single_shapes(fmt):
     torch = gpu_or_skip()
     from gemm_tkq_gemv_amd import tkq
@@ -87,7 +90,7 @@ def test_gemv_single_shapes(fmt):
         _check(fmt, W, x, it["y"], it["codes"], it["meta"], "%s %dx%d" % (fmt, N, K))
 
 
-@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin", "hier", "int2"])
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin", "hier", "int2", "int3"])
 def test_gemv_grouped_mixed_shapes(fmt):
     torch = gpu_or_skip()
     from gemm_tkq_gemv_amd import tkq

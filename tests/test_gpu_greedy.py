@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 def _pack(tkq, fmt, Wd):
     return {"int4": tkq.pack_int4_g128, "k5": tkq.pack_k5, "tern": tkq.pack_tern_g128,
-            "hier": tkq.pack_int4_hier_g32, "int2": tkq.pack_int2_g128}[fmt](Wd)
+            "hier": tkq.pack_int4_hier_g32, "int2": tkq.pack_int2_g128, "int3": tkq.pack_int3_g128}[fmt](Wd)
 
 
 def _run(torch, tkq, fmt, mats, target, calls=1):
@@ -64,7 +64,7 @@ def test_greedy_lm_head_shape(fmt):
     _check_choice(fmt, W, x, items[0]["y"], toks[0])
 
 
-@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "int2"])
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "int2", "int3"])
 def test_greedy_target_inside_group(fmt):
     """A grouped launch of mixed shapes; the target is the first, a middle and
     the last descriptor in turn; other matrices' outputs are unaffected."""

@@ -25,13 +25,15 @@ def _pack_gpu(fmt, W):
         out = tkq.pack_int4_hier_g32(Wd)
     elif fmt == "int2":
         out = tkq.pack_int2_g128(Wd)
+    elif fmt == "int3":
+        out = tkq.pack_int3_g128(Wd)
     else:
         out = (tkq.pack_bin(Wd), None)
     torch.cuda.synchronize()
     return device_codes_np(fmt, *out)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin", "hier", "int2"])
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin", "hier", "int2", "int3"])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_pack_bit_exact(fmt, shape):
     N, K = shape
@@ -63,7 +65,7 @@ def _degenerate_rows():
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin", "hier", "int2"])
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin", "hier", "int2", "int3"])
 def test_pack_degenerate_groups(fmt):
     W = _degenerate_rows()
     assert_codes_equal(fmt, _pack_gpu(fmt, W), oracle_pack(fmt, W))

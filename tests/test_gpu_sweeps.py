@@ -1,6 +1,6 @@
 """Full-size workloads in the launch configuration the benchmark times: the
 single 896x896 GEMV, the Qwen2.5-0.5B sweep (169 GEMVs in one launch) in the
-int4, K5, ternary, int4-hier-g32 and int2 codings, the binary sign GEMVs, and the Qwen2.5-7B int4
+int4, K5, ternary, int4-hier-g32, int2 and int3 codings, the binary sign GEMVs, and the Qwen2.5-7B int4
 sweep (197 GEMVs).  Codes of sampled rows are bit-exact against the oracle's
 quantization of the same rows; sampled outputs are within the per-row bound
 (binary: every output exact)."""
@@ -39,7 +39,7 @@ def sweep05b():
     torch = gpu_or_skip()
     from gemm_tkq_gemv_amd import tkq
     shapes = inputs.sweep_shapes("qwen2.5-0.5b")
-    packed = {f: [] for f in ("int4", "k5", "tern", "hier", "int2")}
+    packed = {f: [] for f in ("int4", "k5", "tern", "hier", "int2", "int3")}
     samples = []
     for i, (_, N, K) in enumerate(shapes):
         W, x = inputs.sweep_matrix("qwen2.5-0.5b", i, N, K)
@@ -48,7 +48,8 @@ def sweep05b():
         Wd = torch.from_numpy(W).cuda()
         xd = torch.from_numpy(x).cuda()
         for f, fn in (("int4", tkq.pack_int4_g128), ("k5", tkq.pack_k5), ("tern", tkq.pack_tern_g128),
-                      ("hier", tkq.pack_int4_hier_g32), ("int2", tkq.pack_int2_g128)):
+                      ("hier", tkq.pack_int4_hier_g32), ("int2", tkq.pack_int2_g128),
+                      ("int3", tkq.pack_int3_g128)):
             codes, meta = fn(Wd)
             y = torch.full((N,), float("nan"), dtype=torch.float16, device="cuda")
             packed[f].append(dict(codes=codes, meta=meta, x=xd, y=y, N=N, K=K))
@@ -57,7 +58,7 @@ def sweep05b():
     return packed, samples
 
 
-@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "hier", "int2"])
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "hier", "int2", "int3"])
 def test_sweep_05b(sweep05b, fmt):
     torch = gpu_or_skip()
     from gemm_tkq_gemv_amd import tkq
