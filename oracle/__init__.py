@@ -17,10 +17,13 @@ ref         dequantization and the fp64 GEMV / GEMM definitions, the per-row
             tolerance bound, and the XOR-popcount binary GEMV.
 accounting  parameter counts, bits/weight, bytes per token and the
             bandwidth / bytes roofline ceiling.
+kv          the paged 4-bit KV cache (K per channel, V per token, pages of
+            128 tokens) and single-query decode attention in fp64, with its
+            derived tolerance.
 
 Every function cites the page passage it follows.  Pages are cited by title
 and section: "Whetstone" (the Whetstone README), "TKintegers K5" (the
-TKintegers K5 news digest) and "BitDecoding".
+TKintegers K5 news digest) and "BitDecoding" (the BitDecoding README).
 
 Pins: each function is checked by the ``-m "not gpu"`` tests against values
 the pages print, closed forms, exhaustive enumeration on tiny inputs, or

@@ -1,0 +1,158 @@
+"""Low-bit KV cache for decode attention (test infrastructure only).
+
+BitDecoding (the BitDecoding README, usage example): the KV cache of a
+long-context decode is stored with 4-bit codes in groups of 128, K quantized
+per channel ("k-channel": one scale/zero per channel for every 128 tokens)
+and V per token (one scale/zero per token for every 128 channels), head
+dimension 128; one decode step attends a single query token over the whole
+cache:  out[h] = softmax(scale * q[h] . K^T) . V  with the query head h
+reading the KV head h // (H / H_k).
+
+Readings taken where the page is silent:
+* The 4-bit quantizer is the same asymmetric round-to-nearest as the int4
+  g128 weights (oracle.quant.quantize_int4_g128): per group lo = min(min, 0),
+  hi = max(max, 0), s = fp16((hi - lo) / 15), integer zero-point z; a K group
+  is one channel over the 128 tokens of a page, a V group is one token over
+  its 128 channels.
+* Storage is paged: the cache of one (batch, KV head) is a sequence of
+  pages of 128 tokens, each page PAGE_BYTES long:
+    K codes  uint32 [128 tokens][16]   nibble c of token t: word t*16 + c//8,
+                                       bits 4*(c%8)            (8192 bytes)
+    V codes  uint32 [128 channels][16] nibble t of channel c: word c*16 + t//8,
+                                       bits 4*(t%8)            (8192 bytes)
+    K meta   uint32 [128 channels]     half2 {scale, zero} per channel (512)
+    V meta   uint32 [128 tokens]       half2 {scale, zero} per token   (512)
+  and the cache tensor is [B][H_k][pages][PAGE_BYTES].  V codes are stored
+  channel-major so that the value product, like the scores, reads whole
+  rows front to back.
+* The cache length is a multiple of 128 (whole pages).
+
+The attention itself is the plain definition in fp64 from the dequantized
+cache.  Its tolerance (attention_bound) is derived from the fp16 roundings a
+kernel makes when it folds the scales into the query and the probabilities;
+see that function.
+"""
+
+import numpy as np
+
+from . import pack as _pack
+from . import quant as _quant
+
+D = 128            # head dimension
+PAGE = 128         # tokens per page
+PAGE_WORDS = (8192 + 8192 + 512 + 512) // 4
+PAGE_BYTES = PAGE_WORDS * 4
+_KC, _VC, _KM, _VM = 0, 2048, 4096, 4224   # word offsets of the four parts
+
+
+def quantize_page(Kp, Vp):
+    """One page: Kp, Vp fp16/fp32 [128 tokens][128 channels] ->
+    (k_codes [t][c] uint8, k_s fp16 [c], k_z fp16 [c],
+     v_codes [t][c] uint8, v_s fp16 [t], v_z fp16 [t]).
+    K groups are channels (rows of Kp^T), V groups are tokens (rows of Vp)."""
+    Kp = np.asarray(Kp, dtype=np.float32)
+    Vp = np.asarray(Vp, dtype=np.float32)
+    if Kp.shape != (PAGE, D) or Vp.shape != (PAGE, D):
+        raise ValueError("a page is [128 tokens][128 channels]")
+    kq, ks, kz = _quant.quantize_int4_g128(np.ascontiguousarray(Kp.T))   # [c][t], per channel
+    vq, vs, vz = _quant.quantize_int4_g128(Vp)                           # [t][c], per token
+    return kq.T.copy(), ks[:, 0], kz[:, 0], vq, vs[:, 0], vz[:, 0]
+
+
+def pack_page(k_codes, k_s, k_z, v_codes, v_s, v_z):
+    """Quantized page -> uint32 [PAGE_WORDS] in the layout above."""
+    out = np.zeros(PAGE_WORDS, dtype=np.uint32)
+    out[_KC:_KC + 2048] = _pack.pack_int4(np.asarray(k_codes)).reshape(-1)        # rows = tokens
+    out[_VC:_VC + 2048] = _pack.pack_int4(np.asarray(v_codes).T).reshape(-1)      # rows = channels
+    out[_KM:_KM + 128] = _pack.pack_int4_meta(np.asarray(k_s)[:, None], np.asarray(k_z)[:, None])[:, 0]
+    out[_VM:_VM + 128] = _pack.pack_int4_meta(np.asarray(v_s)[:, None], np.asarray(v_z)[:, None])[:, 0]
+    return out
+
+
+def unpack_page(words):
+    """uint32 [PAGE_WORDS] -> dequantized (K [t][c], V [t][c]) in fp64."""
+    words = np.asarray(words, dtype=np.uint32)
+    kq = _pack.unpack_int4(words[_KC:_KC + 2048].reshape(PAGE, 16), D).astype(np.float64)      # [t][c]
+    vq = _pack.unpack_int4(words[_VC:_VC + 2048].reshape(D, 16), PAGE).astype(np.float64).T    # [t][c]
+    ks, kz = _pack.unpack_int4_meta(words[_KM:_KM + 128])
+    vs, vz = _pack.unpack_int4_meta(words[_VM:_VM + 128])
+    K = (kq - kz.astype(np.float64)[None, :]) * ks.astype(np.float64)[None, :]
+    V = (vq - vz.astype(np.float64)[:, None]) * vs.astype(np.float64)[:, None]
+    return K, V
+
+
+def pack_cache(K, V):
+    """K, V [B][T][H_k][128] (token-major, as a decoder writes them) ->
+    cache uint32 [B][H_k][T/128][PAGE_WORDS]."""
+    K = np.asarray(K)
+    V = np.asarray(V)
+    B, T, Hk, d = K.shape
+    if d != D or T % PAGE:
+        raise ValueError("head dimension 128 and whole pages of 128 tokens")
+    out = np.zeros((B, Hk, T // PAGE, PAGE_WORDS), dtype=np.uint32)
+    for b in range(B):
+        for h in range(Hk):
+            for p in range(T // PAGE):
+                sl = slice(PAGE * p, PAGE * (p + 1))
+                out[b, h, p] = pack_page(*quantize_page(K[b, sl, h], V[b, sl, h]))
+    return out
+
+
+def dequant_cache(cache):
+    """cache uint32 [B][H_k][P][PAGE_WORDS] -> (K, V) fp64 [B][H_k][T][128]."""
+    cache = np.asarray(cache, dtype=np.uint32)
+    B, Hk, P, _ = cache.shape
+    K = np.zeros((B, Hk, P * PAGE, D))
+    V = np.zeros((B, Hk, P * PAGE, D))
+    for b in range(B):
+        for h in range(Hk):
+            for p in range(P):
+                K[b, h, PAGE * p:PAGE * (p + 1)], V[b, h, PAGE * p:PAGE * (p + 1)] = unpack_page(cache[b, h, p])
+    return K, V
+
+
+def attention_decode(q, K, V, sm_scale):
+    """One decode step: q [B][H][128], K, V [B][H_k][T][128] (fp64 values)
+    -> (out [B][H][128], p [B][H][T]) in fp64: softmax(sm_scale q.K^T) V,
+    query head h reading KV head h // (H / H_k)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, _ = q.shape
+    Hk = K.shape[1]
+    if H % Hk:
+        raise ValueError("query heads must be a multiple of KV heads")
+    G = H // Hk
+    out = np.zeros((B, H, D))
+    probs = np.zeros((B, H, K.shape[2]))
+    for b in range(B):
+        for h in range(H):
+            s = sm_scale * (K[b, h // G] @ q[b, h])
+            e = np.exp(s - s.max())
+            p = e / e.sum()
+            probs[b, h] = p
+            out[b, h] = p @ V[b, h // G]
+    return out, probs
+
+
+def attention_bound(q, K, V, sm_scale):
+    """Per output element tolerance of a kernel that (a) rounds q_c * s_c (the
+    K channel scale) to fp16, (b) rounds p_t * s_t (the V token scale) to
+    fp16, (c) accumulates in fp32 and (d) stores fp16:
+      score error  |ds_t| <= u * A_t,  A_t = sm_scale * sum_c |q_c K_tc|
+      (u = 2^-11, the fp16 unit roundoff, from (a));
+      probabilities then move by a relative 2 max_t |ds_t| at most (to first
+      order), (b) and (d) add u each, (c) is far below;
+    so |out_c - ref_c| <= (4 u max_t A_t + 3 u) * sum_t p_t |V_tc| + 1e-6,
+    with the factor 2 of the first term doubled for the second-order terms
+    of the exponential.  Returns an array [B][H][128]."""
+    u = 2.0 ** -11
+    q = np.asarray(q, dtype=np.float64)
+    B, H, _ = q.shape
+    Hk = K.shape[1]
+    G = H // Hk
+    out, probs = attention_decode(q, K, V, sm_scale)
+    bound = np.zeros((B, H, D))
+    for b in range(B):
+        for h in range(H):
+            A = sm_scale * (np.abs(K[b, h // G]) @ np.abs(q[b, h]))
+            bound[b, h] = (4 * u * A.max() + 3 * u) * (probs[b, h] @ np.abs(V[b, h // G])) + 1e-6
+    return bound
