@@ -322,6 +322,43 @@ def run_small(args, torch, tkq, inputs, model, M):
             "kernel": "small_m_kernel"}
 
 
+def run_kv(args, torch, tkq, B, H, Hk, T):
+    """Single-query decode attention over a 4-bit paged KV cache (BitDecoding's
+    shape: head dimension 128, group 128, K per channel, V per token)."""
+    r = np.random.default_rng((9, B, H, Hk, T))
+    caches = []
+    for i in range(1):
+        K = torch.from_numpy(r.standard_normal((B, T, Hk, 128)).astype(np.float16)).cuda()
+        V = torch.from_numpy(r.standard_normal((B, T, Hk, 128)).astype(np.float16)).cuda()
+        caches.append(tkq.kv_pack(K, V))
+        del K, V
+    cache_bytes = caches[0].numel()
+    copies = max(1, math.ceil(ROTATE_BYTES / cache_bytes))
+    for _ in range(copies - 1):
+        caches.append(caches[0].clone())
+    q = torch.from_numpy(r.standard_normal((B, H, 128)).astype(np.float16)).cuda()
+    out = torch.empty_like(q)
+    ws = torch.empty((tkq.lib().tkq_kv_decode_workspace_bytes(B, H, Hk, T) + 3) // 4, dtype=torch.float32,
+                     device="cuda")
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(128)
+    ms = time_steps(torch, lambda s: tkq.kv_decode(q, caches[s % len(caches)], T, scale, out, ws), args.steps,
+                    args.warmup, args.graph, len(caches))
+    step_bytes = cache_bytes + 2 * 2 * B * H * 128
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    return {"metric": "4-bit KV-cache decode attention achieved HBM TB/s", "value": round(gbs / 1000.0, 4),
+            "unit": "TB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+            "data": "synthetic N(0,1) fp16 K, V, q",
+            "config": {"workload": "decode attention, batch %d, %d query / %d KV heads, head dim 128, %d cached "
+                                   "tokens, 4-bit KV (K per channel, V per token, group 128)" % (B, H, Hk, T),
+                       "bytes_per_step": step_bytes, "copies_rotated": len(caches)},
+            "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+            "kernel": "kv_decode_kernel + kv_merge_kernel"}
+
+
 def _fmt_name(fmt):
     return {"int4": "int4-g128", "k5": "K5-g128", "tern": "ternary-g128 (2-bit)", "bin": "binary",
             "hier": "int4-hier-g32", "int2": "int2-g128", "int3": "int3-g128"}[fmt]
@@ -441,7 +478,7 @@ def main():
     ap.add_argument("--workload", default="0.5b-int4",
                     choices=["0.5b-int4", "0.5b-int4-greedy", "0.5b-k5", "0.5b-tern", "0.5b-hier",
                              "0.5b-int2", "0.5b-int3", "0.5b-int4-m2", "0.5b-int4-m4", "0.5b-int4-m8", "0.5b-int4-m16",
-                             "7b-int4-m16", "bin", "single-896",
+                             "7b-int4-m16", "kv-32k", "kv-32k-gqa", "kv-4k", "bin", "single-896",
                              "7b-int4", "7b-hier", "7b-prefill", "probe"])
     ap.add_argument("--graph", default="none", choices=["none", "step", "all"],
                     help="launch steps as HIP graph replays (see time_steps)")
@@ -491,6 +528,10 @@ def main():
                           "matrices of the sweep (%s), %.1f s of CPU work; quantization not timed"
                           % (passes, len(done), ", ".join(done[:3] + (["..."] if len(done) > 3 else [])
                                                           + done[-1:]), spent)}
+    elif w.startswith("kv-"):
+        T = 4096 if w == "kv-4k" else 32768
+        Hk = 8 if w.endswith("gqa") else 32
+        out = run_kv(args, torch, tkq, 1, 32, Hk, T)
     elif "-m" in w:
         model = "qwen2.5-7b" if w.startswith("7b") else "qwen2.5-0.5b"
         out = run_small(args, torch, tkq, inputs, model, int(w.split("-m")[1]))

@@ -78,6 +78,14 @@ constexpr int kSmallTileRows = 64;
 constexpr int kSmallMaxM = 16;
 hipError_t launch_small_m(const tkq_gemv_desc* dev_descs, int count, int64_t tiles, int M, hipStream_t stream);
 
+// Low-bit KV cache (pages of 128 tokens, head dimension 128) and decode.
+constexpr int kKvPage = 128, kKvDim = 128, kKvPageBytes = 17408, kKvWaves = 4, kKvMaxGroup = 8;
+hipError_t launch_kv_pack(const uint16_t* K, const uint16_t* V, int B, int T, int Hk, uint32_t* cache,
+                          hipStream_t stream);
+int kv_splits(int B, int H, int Hk, int T, int cus, int* pages_per_split);
+hipError_t launch_kv_decode(const uint16_t* q, const uint32_t* cache, int B, int H, int Hk, int T, float sm_scale,
+                            uint16_t* out, float* ws, int splits, int pages_per_split, hipStream_t stream);
+
 hipError_t launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* codes, void* meta,
                        hipStream_t stream);
 

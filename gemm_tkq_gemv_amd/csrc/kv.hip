@@ -1,0 +1,436 @@
+// Low-bit KV cache and single-query decode attention for gfx950 (the
+// BitDecoding README: 4-bit KV codes in groups of 128, K quantized per channel
+// and V per token, head dimension 128; one decode step attends one query over
+// a long cache, which makes it another HBM-bound stream like the weight GEMV).
+//
+// Storage (one (batch, KV head) = a sequence of 128-token pages):
+//   K codes  uint32 [128 tokens][16]   4-bit, channel c of token t at
+//                                      word 16t + c/8, bits 4(c%8)
+//   V codes  uint32 [128 channels][16] 4-bit, token t of channel c at
+//                                      word 2048 + 16c + t/8, bits 4(t%8)
+//   K meta   uint32 [128]              half2 {scale, zero} per channel
+//   V meta   uint32 [128]              half2 {scale, zero} per token
+// V is channel-major so that the value product, like the scores, reads whole
+// rows front to back with 16-byte loads.
+//
+// Decode (one workgroup = a split of the pages of one KV head for up to four
+// query heads; wave w takes pages w, w + 4, ...):
+//  * Scores are a GEMV over the page's tokens: with per-channel scales,
+//    s_t = sum_c q_c sK_c (k_tc - zK_c) = sum_c q'_c k_tc - sum_c q'_c zK_c,
+//    q' = q * sK rounded to fp16 once per page; 4 lanes per token (32
+//    channels each), 16 tokens per wave step, the int4 magic-number unpack
+//    and v_dot2_f32_f16.
+//  * Online softmax over pages in fp32 (exp2 of log2-scaled scores).
+//  * The value product is a GEMV over the page's channels: with per-token
+//    scales, o_c = sum_t p_t sV_t (v_ct - zV_t) = sum_t p'_t v_ct - sum_t
+//    p'_t zV_t, p' = p * sV rounded to fp16 (in LDS, read back in the unpack
+//    order); 4 lanes per channel (32 tokens each).
+//  * The constant parts of the magic-number products (1024 or 64 per code
+//    position) and the zero points are removed per lane chunk in fp32.
+//  * Each workgroup writes (m, l, o[128]) per query head to a workspace; a
+//    second kernel merges the splits (log-sum-exp) and stores fp16.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace tkq {
+
+namespace {
+
+constexpr int kD = 128, kPage = 128;
+constexpr int kPageWords = 4352;  // (8192 + 8192 + 512 + 512) / 4
+constexpr int kKC = 0, kVC = 2048, kKM = 4096, kVM = 4224;
+constexpr int kWaves = 4;
+constexpr uint32_t kMagic = 0x64006400u;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ uint32_t in_sgpr(uint32_t c) {
+  uint32_t r;
+  asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "i"(c));
+  return r;
+}
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
+// ------------------------------------------------------------------ pack --
+// Same arithmetic as the int4 g128 weight packer: lo = min(min, 0),
+// hi = max(max, 0), s = fp16((hi - lo) / 15) (0 -> 1), z = clamp(rint(-lo / s),
+// 0, 15), q = clamp(rint(x / s) + z, 0, 15).
+__device__ __forceinline__ uint32_t quant_group(const float* v, int stride, uint8_t* q, int qstride) {
+  float lo = 0.0f, hi = 0.0f;
+  for (int i = 0; i < 128; ++i) {
+    lo = fminf(lo, v[i * stride]);
+    hi = fmaxf(hi, v[i * stride]);
+  }
+  _Float16 h = (_Float16)((hi - lo) / 15.0f);
+  if (h == (_Float16)0.0f) h = (_Float16)1.0f;
+  const float s = (float)h;
+  const float z = fminf(fmaxf(rintf(-lo / s), 0.0f), 15.0f);
+  for (int i = 0; i < 128; ++i) q[i * qstride] = (uint8_t)(int)fminf(fmaxf(rintf(v[i * stride] / s) + z, 0.0f), 15.0f);
+  return (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)half_bits(z) << 16);
+}
+
+// One workgroup (256 threads) per page; K and V are fp16 [B][T][Hk][128].
+__global__ __launch_bounds__(256) void kv_pack_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                                      int T, int Hk, uint32_t* __restrict__ cache) {
+  __shared__ float tile[kPage * (kD + 1)];
+  __shared__ uint8_t codes[kPage * kD];
+  const int p = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int P = T / kPage;
+  uint32_t* page = cache + (((size_t)b * Hk + hk) * P + p) * kPageWords;
+  for (int part = 0; part < 2; ++part) {
+    const uint16_t* src = part == 0 ? K : V;
+    // tile[t][c] = value of token 128p + t, channel c
+    for (int i = threadIdx.x; i < kPage * kD; i += 256) {
+      const int t = i / kD, c = i - t * kD;
+      const uint16_t bits = src[(((size_t)b * T + (size_t)kPage * p + t) * Hk + hk) * kD + c];
+      tile[t * (kD + 1) + c] = (float)__builtin_bit_cast(_Float16, bits);
+    }
+    __syncthreads();
+    if (threadIdx.x < 128) {
+      const int g = threadIdx.x;
+      if (part == 0)  // K: group = channel g over the tokens; codes[t][c]
+        page[kKM + g] = quant_group(tile + g, kD + 1, codes + g, kD);
+      else            // V: group = token g over the channels; codes[t][c]
+        page[kVM + g] = quant_group(tile + g * (kD + 1), 1, codes + g * kD, 1);
+    }
+    __syncthreads();
+    for (int w = threadIdx.x; w < 2048; w += 256) {
+      uint32_t word = 0;
+      if (part == 0) {  // token-major: word 16t + j holds channels 8j..8j+7 of token t
+        const int t = w >> 4, j = w & 15;
+        for (int i = 0; i < 8; ++i) word |= (uint32_t)codes[t * kD + 8 * j + i] << (4 * i);
+        page[kKC + w] = word;
+      } else {          // channel-major: word 16c + j holds tokens 8j..8j+7 of channel c
+        const int c = w >> 4, j = w & 15;
+        for (int i = 0; i < 8; ++i) word |= (uint32_t)codes[(8 * j + i) * kD + c] << (4 * i);
+        page[kVC + w] = word;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- decode --
+struct Regs {
+  uint32_t m0, m1, magic;
+};
+
+// sum over one 16-byte chunk (32 codes, natural nibble order) of
+// (1024 + m code) * x with the GEMV's pairing (0,4),(1,5),(2,6),(3,7) and
+// x16 fields rescaled: = sum_k code_k x_k + sum_k c_k x_k, c_k = 1024 for
+// even k, 64 for odd k.
+__device__ __forceinline__ float chunk_dot(u32x4 q, const uint32_t* xr, const Regs& R) {
+  float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t v = q[w], t = v >> 8;
+    lo = __builtin_amdgcn_fdot2(as_h2((v & R.m0) | R.magic), as_h2(xr[4 * w + 0]), lo, false);
+    hi = __builtin_amdgcn_fdot2(as_h2((v & R.m1) | R.magic), as_h2(xr[4 * w + 1]), hi, false);
+    lo = __builtin_amdgcn_fdot2(as_h2((t & R.m0) | R.magic), as_h2(xr[4 * w + 2]), lo, false);
+    hi = __builtin_amdgcn_fdot2(as_h2((t & R.m1) | R.magic), as_h2(xr[4 * w + 3]), hi, false);
+  }
+  return fmaf(hi, 0.0625f, lo);
+}
+
+// 32 natural-order fp16 values (16 words, 2 per word) -> the pairing order.
+__device__ __forceinline__ void pair_order(const uint32_t* raw, uint32_t* xr) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t a = raw[4 * w], b = raw[4 * w + 1], c = raw[4 * w + 2], d = raw[4 * w + 3];
+    xr[4 * w + 0] = __builtin_amdgcn_perm(c, a, 0x05040100u);  // (x0, x4)
+    xr[4 * w + 1] = __builtin_amdgcn_perm(c, a, 0x07060302u);  // (x1, x5)
+    xr[4 * w + 2] = __builtin_amdgcn_perm(d, b, 0x05040100u);  // (x2, x6)
+    xr[4 * w + 3] = __builtin_amdgcn_perm(d, b, 0x07060302u);  // (x3, x7)
+  }
+}
+
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+struct WaveLds {
+  uint32_t meta[256];           // K meta [128 channels] then V meta [128 tokens]
+  uint32_t qv[kKvMaxGroup][kD / 2];  // query heads, fp16 pairs in natural order
+  uint32_t pv[1][kPage / 2];    // p' of the current head, fp16 pairs in natural order
+  float o[kKvMaxGroup][kD];     // unnormalised outputs per head (in LDS: registers stay
+                                // independent of the number of heads)
+};
+
+// G: query heads per workgroup (1..8, all reading the same KV head).  Workspace per (b, head, split):
+// {m, l, o[128]} with o unnormalised relative to m (base-2 exponent).
+template <int G>
+__global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restrict__ q,
+                                                        const uint32_t* __restrict__ cache, int H, int Hk, int P,
+                                                        int pages_per_split, float scale_log2,
+                                                        float* __restrict__ ws, int splits) {
+  __shared__ WaveLds lds[kWaves];
+  __shared__ float merge[kWaves][G][kD + 2];
+  const int split = blockIdx.x, hsub = blockIdx.y, b = blockIdx.z;
+  const int gq = H / Hk;                        // query heads per KV head
+  const int hk = (hsub * G) / gq;               // this workgroup's KV head
+  const int h0 = hsub * G;                      // first query head
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int quad = lane >> 2, sub = lane & 3;
+  WaveLds& L = lds[wave];
+  const Regs R = {in_sgpr(0x000F000Fu), in_sgpr(0x00F000F0u), in_vgpr(kMagic)};
+
+  // query heads -> LDS (fp16 pairs)
+  for (int i = lane; i < G * kD / 2; i += 64) {
+    const int g = i / (kD / 2), w = i - g * (kD / 2);
+    L.qv[g][w] = reinterpret_cast<const uint32_t*>(q + ((size_t)b * H + h0 + g) * kD)[w];
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+  float m[G], l[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.0f;
+  }
+  for (int i = lane; i < G * kD; i += 64) L.o[i / kD][i % kD] = 0.0f;
+
+  const int p0 = split * pages_per_split, p1 = min(P, p0 + pages_per_split);
+  const uint32_t* base = cache + ((size_t)b * Hk + hk) * (size_t)P * kPageWords;
+  for (int p = p0 + wave; p < p1; p += kWaves) {
+    const __amdgpu_buffer_rsrc_t pg = make_rsrc(base + (size_t)p * kPageWords, kPageWords * 4u);
+    // page metadata -> LDS (one 16-byte load per lane covers all 256 words)
+    *reinterpret_cast<u32x4*>(&L.meta[4 * lane]) = load16(pg, (uint32_t)(kKM + 4 * lane) * 4u);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // The query heads one after another: the page comes from HBM for the
+    // first and from the caches for the others.
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      // ---- scores: lane chunk = channels 32 sub .. 32 sub + 31 of token 16 st + quad
+      float sc[8];
+      {
+        uint32_t qp[16];
+        {
+          uint32_t raw[16], sp[16], qr[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {  // (s_2i, s_2i+1) of the chunk's channels, and the query
+            raw[i] = __builtin_amdgcn_perm(L.meta[32 * sub + 2 * i + 1], L.meta[32 * sub + 2 * i], 0x05040100u);
+            qr[i] = L.qv[g][16 * sub + i];
+          }
+          pair_order(raw, sp);
+          pair_order(qr, qp);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) qp[i] = __builtin_bit_cast(uint32_t, as_h2(qp[i]) * as_h2(sp[i]));
+        }
+        // constant part of this lane's chunk: sum_c q'_c (zK_c + (c even ? 1024 : 64))
+        float cst = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const h2 pr = as_h2(qp[4 * w + i]);  // channels (8w + i, 8w + i + 4) of the chunk
+            const int ch = 32 * sub + 8 * w + i;
+            const float k0 = (i & 1) ? 64.0f : 1024.0f;
+            cst = fmaf((float)pr[0], half_hi(L.meta[ch]) + k0, cst);
+            cst = fmaf((float)pr[1], half_hi(L.meta[ch + 4]) + k0, cst);
+          }
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          u32x4 kc[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            kc[i] = load16_nt(pg, (uint32_t)(kKC + 16 * (16 * (4 * half + i) + quad) + 4 * sub) * 4u);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[4 * half + i] = quad_sum(chunk_dot(kc[i], qp, R) - cst) * scale_log2;
+        }
+      }
+
+      // ---- online softmax (base 2), p' = p * sV to LDS, constant part of V
+      float vconst, valpha;
+      {
+        float pm = sc[0];
+#pragma unroll
+        for (int st = 1; st < 8; ++st) pm = fmaxf(pm, sc[st]);
+        pm = wave_max_f(pm);
+        const float mn = fmaxf(m[g], pm);
+        const float alpha = exp2f(m[g] - mn);  // 0 on the first page (m = -inf)
+        m[g] = mn;
+        float ps = 0.0f, cs = 0.0f;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const int t = 16 * st + quad;
+          const float pt = exp2f(sc[st] - mn);
+          const uint32_t vm = L.meta[128 + t];
+          const _Float16 pp = (_Float16)(pt * half_lo(vm));  // p' = p * sV
+          // token t sits at position t % 8 of its word: even -> 1024, odd -> 64
+          const float k0 = (t & 1) ? 64.0f : 1024.0f;
+          if (sub == 0) {
+            ps += pt;
+            cs = fmaf((float)pp, half_hi(vm) + k0, cs);
+            reinterpret_cast<_Float16*>(L.pv[0])[t] = pp;
+          }
+        }
+        l[g] = l[g] * alpha + wave_sum_f(ps);
+        vconst = wave_sum_f(cs);
+        valpha = alpha;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+      // ---- value product: lane chunk = tokens 32 sub .. 32 sub + 31 of channel 16 st + quad
+      {
+        uint32_t pp[16];
+        {
+          uint32_t praw[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) praw[i] = L.pv[0][16 * sub + i];
+          pair_order(praw, pp);
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          u32x4 vc[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vc[i] = load16_nt(pg, (uint32_t)(kVC + 16 * (16 * (4 * half + i) + quad) + 4 * sub) * 4u);
+          // the constant part is common to every channel of the page
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float d = quad_sum(chunk_dot(vc[i], pp, R)) - vconst;
+            if (sub == 0) {
+              float& oc = L.o[g][16 * (4 * half + i) + quad];
+              oc = fmaf(oc, valpha, d);
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_sched_barrier(0);  // heads one after another: no overlap of their working sets
+    }
+  }
+
+  // ---- merge the four waves, then write this split's partial result
+  for (int i = lane; i < G * kD; i += 64) merge[wave][i / kD][i % kD] = L.o[i / kD][i % kD];
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      merge[wave][g][kD] = m[g];
+      merge[wave][g][kD + 1] = l[g];
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * kD; i += 256) {
+    const int g = i / kD, c = i - g * kD;
+    float M = -INFINITY;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, merge[w][g][kD]);
+    float Lsum = 0.0f, O = 0.0f;
+    for (int w = 0; w < kWaves; ++w) {
+      const float a = merge[w][g][kD] == -INFINITY ? 0.0f : exp2f(merge[w][g][kD] - M);
+      Lsum += merge[w][g][kD + 1] * a;
+      O += merge[w][g][c] * a;
+    }
+    float* out = ws + (((size_t)b * H + h0 + g) * splits + split) * (kD + 2);
+    out[c] = O;
+    if (c == 0) {
+      out[kD] = M;
+      out[kD + 1] = Lsum;
+    }
+  }
+}
+
+// One workgroup per (b, head): merge the splits, normalise, store fp16.
+__global__ __launch_bounds__(128) void kv_merge_kernel(const float* __restrict__ ws, int splits,
+                                                       uint16_t* __restrict__ out) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  const float* w = ws + (size_t)bh * splits * (kD + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, w[s * (kD + 2) + kD]);
+  float Lsum = 0.0f, O = 0.0f;
+  for (int s = 0; s < splits; ++s) {
+    const float ms = w[s * (kD + 2) + kD];
+    const float a = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+    Lsum += w[s * (kD + 2) + kD + 1] * a;
+    O += w[s * (kD + 2) + c] * a;
+  }
+  out[(size_t)bh * kD + c] = half_bits(O / Lsum);
+}
+
+}  // namespace
+
+hipError_t launch_kv_pack(const uint16_t* K, const uint16_t* V, int B, int T, int Hk, uint32_t* cache,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL(kv_pack_kernel, dim3((uint32_t)(T / kPage), (uint32_t)Hk, (uint32_t)B), dim3(256), 0, stream, K,
+                     V, T, Hk, cache);
+  return hipGetLastError();
+}
+
+// Query heads per workgroup: the whole group if it has at most 8 heads, else
+// its largest divisor up to 8.
+int kv_heads_per_wg(int H, int Hk) {
+  const int G = H / Hk;
+  for (int gb = G < kKvMaxGroup ? G : kKvMaxGroup; gb > 1; --gb)
+    if (G % gb == 0) return gb;
+  return 1;
+}
+
+int kv_splits(int B, int H, int Hk, int T, int cus, int* pages_per_split) {
+  const int P = T / kPage;
+  const int gb = kv_heads_per_wg(H, Hk);
+  const int64_t groups = (int64_t)B * (H / gb);
+  // enough workgroups for TKQ_KV_WG_PER_CU per CU (every wave streams its
+  // own pages; the merge of more splits costs little), at least one page per wave
+#ifndef TKQ_KV_WG_PER_CU
+#define TKQ_KV_WG_PER_CU 4
+#endif
+  int64_t want = ((int64_t)TKQ_KV_WG_PER_CU * cus + groups - 1) / groups;
+  int64_t max_splits = (P + kWaves - 1) / kWaves;
+  if (want > max_splits) want = max_splits;
+  if (want < 1) want = 1;
+  const int pps = (int)((P + want - 1) / want);
+  *pages_per_split = pps;
+  return (P + pps - 1) / pps;
+}
+
+hipError_t launch_kv_decode(const uint16_t* q, const uint32_t* cache, int B, int H, int Hk, int T, float sm_scale,
+                            uint16_t* out, float* ws, int splits, int pages_per_split, hipStream_t stream) {
+  const int P = T / kPage;
+  const int gb = kv_heads_per_wg(H, Hk);
+  const dim3 grid((uint32_t)splits, (uint32_t)(H / gb), (uint32_t)B);
+  const float sl2 = sm_scale * kLog2e;
+  switch (gb) {
+#define TKQ_KV_CASE(G)                                                                                          \
+  case G:                                                                                                      \
+    hipLaunchKernelGGL(kv_decode_kernel<G>, grid, dim3(256), 0, stream, q, cache, H, Hk, P, pages_per_split, sl2, \
+                       ws, splits);                                                                            \
+    break;
+    TKQ_KV_CASE(1)
+    TKQ_KV_CASE(2)
+    TKQ_KV_CASE(3)
+    TKQ_KV_CASE(4)
+    TKQ_KV_CASE(5)
+    TKQ_KV_CASE(6)
+    TKQ_KV_CASE(7)
+    TKQ_KV_CASE(8)
+#undef TKQ_KV_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kv_merge_kernel, dim3((uint32_t)(B * H)), dim3(128), 0, stream, ws, splits, out);
+  return hipGetLastError();
+}
+
+}  // namespace tkq

@@ -310,6 +310,54 @@ int tkq_gemm_small(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs, vo
   return hip_status(tkq::launch_small_m(dev_descs, plan->count, plan->tiles, plan->variant, (hipStream_t)stream));
 }
 
+static int check_kv(int64_t B, int64_t H, int64_t Hk, int64_t T, int64_t D) {
+  if (B < 1 || H < 1 || Hk < 1 || T < 1) return TKQ_EINVAL;
+  if (D != tkq::kKvDim || T % tkq::kKvPage || H % Hk || B > 65535 || T > (int64_t(1) << 24) ||
+      B * Hk * (T / tkq::kKvPage) * tkq::kKvPageBytes > (int64_t(1) << 40))
+    return TKQ_ESHAPE;
+  return TKQ_OK;
+}
+
+int64_t tkq_kv_cache_bytes(int32_t B, int32_t Hk, int32_t T) {
+  if (check_kv(B, Hk, Hk, T, tkq::kKvDim)) return -1;
+  return int64_t(B) * Hk * (T / tkq::kKvPage) * tkq::kKvPageBytes;
+}
+
+int64_t tkq_kv_decode_workspace_bytes(int32_t B, int32_t H, int32_t Hk, int32_t T) {
+  if (check_kv(B, H, Hk, T, tkq::kKvDim)) return -1;
+  const int64_t max_splits = (T / tkq::kKvPage + tkq::kKvWaves - 1) / tkq::kKvWaves;
+  return int64_t(B) * H * max_splits * (tkq::kKvDim + 2) * 4;
+}
+
+int tkq_kv_pack(const uint16_t* K, const uint16_t* V, int32_t B, int32_t T, int32_t Hk, int32_t D, uint32_t* cache,
+                void* stream) {
+  if (!K || !V || !cache) return TKQ_EINVAL;
+  const int st = check_kv(B, Hk, Hk, T, D);
+  if (st) return st;
+  if (!aligned16(K) || !aligned16(V) || !aligned16(cache)) return TKQ_EALIGN;
+  return hip_status(tkq::launch_kv_pack(K, V, B, T, Hk, cache, (hipStream_t)stream));
+}
+
+int tkq_kv_decode(const uint16_t* q, const uint32_t* cache, int32_t B, int32_t H, int32_t Hk, int32_t T, int32_t D,
+                  float sm_scale, uint16_t* out, float* workspace, int64_t workspace_bytes, void* stream) {
+  if (!q || !cache || !out || !workspace) return TKQ_EINVAL;
+  const int st = check_kv(B, H, Hk, T, D);
+  if (st) return st;
+  if (!(sm_scale > 0.0f) || !(sm_scale < 1e30f)) return TKQ_EINVAL;
+  if (workspace_bytes < tkq_kv_decode_workspace_bytes(B, H, Hk, T)) return TKQ_EINVAL;
+  if (!aligned16(q) || !aligned16(cache) || !aligned16(out) || !aligned16(workspace)) return TKQ_EALIGN;
+  int device = 0;
+  hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &device) : hipGetDevice(&device);
+  if (e != hipSuccess) return hip_status(e);
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return hip_status(e);
+  int pps = 1;
+  const int splits = tkq::kv_splits(B, H, Hk, T, cus, &pps);
+  return hip_status(tkq::launch_kv_decode(q, cache, B, H, Hk, T, sm_scale, out, workspace, splits, pps,
+                                          (hipStream_t)stream));
+}
+
 int tkq_gemm_prefill(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint32_t* codes,
                      const uint32_t* meta, const uint16_t* X, uint16_t* Y, float* workspace,
                      int64_t workspace_bytes, void* stream) {

@@ -77,6 +77,10 @@ _SIGNATURES = {
     "tkq_gemm_small_prepare": ([ctypes.POINTER(GemvDesc), _I32, _I32, ctypes.POINTER(GemvPlan)],
                                ctypes.c_int),
     "tkq_gemm_small": ([ctypes.POINTER(GemvPlan), _P, _P], ctypes.c_int),
+    "tkq_kv_cache_bytes": ([_I32, _I32, _I32], ctypes.c_int64),
+    "tkq_kv_decode_workspace_bytes": ([_I32, _I32, _I32, _I32], ctypes.c_int64),
+    "tkq_kv_pack": ([_P, _P, _I32, _I32, _I32, _I32, _P, _P], ctypes.c_int),
+    "tkq_kv_decode": ([_P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, _I64, _P], ctypes.c_int),
     "tkq_gemm_prefill": ([_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
     "tkq_read_probe": ([_P, _I64, _P, _P], ctypes.c_int),
 }
@@ -319,4 +323,39 @@ def read_probe(buf, out=None, stream=None):
         out = torch.zeros(4, dtype=torch.int32, device=buf.device)
     nbytes = buf.numel() * buf.element_size()
     _call("tkq_read_probe", _ptr(buf), nbytes, _ptr(out), _stream(stream))
+    return out
+
+
+# ---- low-bit KV cache decode attention ------------------------------------------
+
+def kv_pack(K, V, stream=None):
+    """K, V fp16 [B, T, Hk, 128] -> paged 4-bit cache (uint8 tensor of
+    tkq_kv_cache_bytes bytes, viewed as [B, Hk, T/128, 17408])."""
+    _need(K, torch.float16, "K")
+    _need(V, torch.float16, "V", K.shape)
+    B, T, Hk, D = K.shape
+    n = lib().tkq_kv_cache_bytes(B, Hk, T)
+    if n < 0 or D != 128:
+        raise TkqError(ESHAPE, "tkq_kv_cache_bytes")
+    cache = torch.empty(n, dtype=torch.uint8, device=K.device)
+    _call("tkq_kv_pack", _ptr(K), _ptr(V), B, T, Hk, D, _ptr(cache), _stream(stream))
+    return cache.view(B, Hk, T // 128, 17408)
+
+
+def kv_decode(q, cache, T, sm_scale, out=None, workspace=None, stream=None):
+    """q fp16 [B, H, 128] -> out fp16 [B, H, 128] over a cache from kv_pack."""
+    _need(q, torch.float16, "q")
+    B, H, D = q.shape
+    Hk = cache.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, torch.float16, "out", q.shape)
+    nws = lib().tkq_kv_decode_workspace_bytes(B, H, Hk, T)
+    if nws < 0:
+        raise TkqError(ESHAPE, "tkq_kv_decode_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty((nws + 3) // 4, dtype=torch.float32, device=q.device)
+    _need(workspace, torch.float32, "workspace")
+    _call("tkq_kv_decode", _ptr(q), _ptr(cache), B, H, Hk, T, D, float(sm_scale), _ptr(out), _ptr(workspace),
+          workspace.numel() * 4, _stream(stream))
     return out

@@ -297,6 +297,53 @@ int tkq_gemm_small_prepare(tkq_gemv_desc* descs, int32_t count, int32_t M,
 int tkq_gemm_small(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs,
                    void* stream);
 
+/* ---- low-bit KV cache and decode attention ------------------------------
+ * (BitDecoding README: 4-bit KV cache codes in groups of 128, K quantized per
+ * channel and V per token, head dimension 128, single-query decode.)
+ * The cache of one (batch, KV head) is a sequence of pages of 128 tokens,
+ * 17408 bytes each:
+ *   words [0, 2048)     K codes: token t, channel c in word 16t + c/8,
+ *                       bits [4(c%8), 4(c%8)+4)
+ *   words [2048, 4096)  V codes: token t, channel c in word 2048 + 16c + t/8,
+ *                       bits [4(t%8), 4(t%8)+4)
+ *   words [4096, 4224)  K half2 {scale, zero} of channel c (over the page)
+ *   words [4224, 4352)  V half2 {scale, zero} of token t (over its channels)
+ * value = scale * (code - zero); the quantizer is the int4 g128 one above
+ * (lo = min(min, 0), hi = max(max, 0), s = fp16((hi - lo) / 15), integer z).
+ * The cache tensor is [B][Hk][T/128][17408 bytes].
+ * Shapes: head dimension D = 128, T % 128 == 0, H % Hk == 0; query head h
+ * reads KV head h / (H / Hk). */
+
+/* Bytes of a cache for B x Hk x T tokens (host only; -1 if invalid). */
+int64_t tkq_kv_cache_bytes(int32_t B, int32_t Hk, int32_t T);
+
+/* Quantize and page a whole cache.  K, V: fp16 bits [B][T][Hk][D]
+ * (token-major), cache: tkq_kv_cache_bytes bytes; all 16-byte aligned.
+ * Bit-identical to an IEEE fp32 evaluation of the quantizer.
+ * Returns TKQ_OK, TKQ_EINVAL, TKQ_ESHAPE, TKQ_EALIGN or TKQ_EHIP. */
+int tkq_kv_pack(const uint16_t* K, const uint16_t* V, int32_t B, int32_t T,
+                int32_t Hk, int32_t D, uint32_t* cache, void* stream);
+
+/* Workspace bytes tkq_kv_decode needs (host only; -1 if invalid). */
+int64_t tkq_kv_decode_workspace_bytes(int32_t B, int32_t H, int32_t Hk,
+                                      int32_t T);
+
+/* One decode step: out[b,h,:] = softmax(sm_scale * q[b,h,:] . K^T) . V over
+ * the T cached tokens of KV head h / (H / Hk), with K and V the dequantized
+ * cache.  q, out: fp16 bits [B][H][D]; workspace: caller-owned device
+ * memory of at least tkq_kv_decode_workspace_bytes (any contents).
+ * Accuracy: the query times the K channel scale and the probability times
+ * the V token scale are rounded to fp16, accumulation is fp32, out is
+ * rounded to fp16; per element |out - exact| <= (4u max_t A_t + 3u) *
+ * sum_t p_t |V_t,c| + 1e-6, u = 2^-11, A_t = sm_scale sum_c |q_c K_t,c|.
+ * Two kernels on `stream` (the split decode, then the merge).  Returns
+ * TKQ_OK, TKQ_EINVAL (null pointers, sm_scale not positive and finite,
+ * workspace too small), TKQ_ESHAPE, TKQ_EALIGN or TKQ_EHIP. */
+int tkq_kv_decode(const uint16_t* q, const uint32_t* cache, int32_t B,
+                  int32_t H, int32_t Hk, int32_t T, int32_t D, float sm_scale,
+                  uint16_t* out, float* workspace, int64_t workspace_bytes,
+                  void* stream);
+
 /* ---- prefill GEMM -------------------------------------------------------
  * Y[m,n] = sum_k X[m,k] * w[n,k] with w the int4 g128 dequantized weights
  * (TKintegers K5, "What is K5?": tiles of low-bit codes are expanded to fp16

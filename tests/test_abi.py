@@ -259,6 +259,28 @@ def test_gemm_small_prepare():
     assert g(ctypes.byref(plan), A + 8, None) == tkq.EALIGN
 
 
+def test_kv_validation():
+    L = tkq.lib()
+    assert L.tkq_kv_cache_bytes(1, 32, 4096) == 32 * 32 * 17408
+    assert L.tkq_kv_cache_bytes(1, 32, 100) == -1
+    assert L.tkq_kv_decode_workspace_bytes(1, 32, 32, 4096) == 32 * 8 * 130 * 4
+    assert L.tkq_kv_decode_workspace_bytes(1, 28, 4, 128) == 28 * 1 * 130 * 4   # 7 per KV head
+    assert L.tkq_kv_decode_workspace_bytes(1, 8, 3, 128) == -1      # H % Hk != 0
+    pk = L.tkq_kv_pack
+    assert pk(None, A, 1, 128, 1, 128, A, None) == tkq.EINVAL
+    assert pk(A, A, 1, 128, 1, 64, A, None) == tkq.ESHAPE             # D must be 128
+    assert pk(A, A, 1, 200, 1, 128, A, None) == tkq.ESHAPE            # whole pages
+    assert pk(A, A, 1, 128, 1, 128, A + 4, None) == tkq.EALIGN
+    dec = L.tkq_kv_decode
+    ws = L.tkq_kv_decode_workspace_bytes(1, 4, 2, 256)
+    assert dec(A, A, 1, 4, 2, 256, 128, 0.1, A, A, ws - 4, None) == tkq.EINVAL
+    assert dec(A, A, 1, 4, 2, 256, 128, 0.0, A, A, ws, None) == tkq.EINVAL
+    assert dec(A, A, 1, 4, 2, 256, 128, float("nan"), A, A, ws, None) == tkq.EINVAL
+    assert dec(A, A, 1, 4, 3, 256, 128, 0.1, A, A, ws, None) == tkq.ESHAPE
+    assert dec(A, None, 1, 4, 2, 256, 128, 0.1, A, A, ws, None) == tkq.EINVAL
+    assert dec(A + 2, A, 1, 4, 2, 256, 128, 0.1, A, A, ws, None) == tkq.EALIGN
+
+
 def test_prefill_validation():
     f = tkq.lib().tkq_gemm_prefill
     assert f(2, 64, 128, 128, A, A, A, A, None, 0, None) == tkq.EFORMAT
