@@ -43,10 +43,13 @@ ROTATE_BYTES = 1 << 30
 # measured on: reported while the sources hash to TRAFFIC_HASH, else null.
 TRAFFIC_SOURCES = ["gemm_tkq_gemv_amd/csrc/gemv.hip", "gemm_tkq_gemv_amd/csrc/tkq_api.hip",
                    "gemm_tkq_gemv_amd/csrc/prefill.hip", "gemm_tkq_gemv_amd/csrc/device_common.h",
-                   "gemm_tkq_gemv_amd/csrc/kernels.h"]
-TRAFFIC_HASH = "f726477761c734ec"
-TRAFFIC_BYTES = {"0.5b-int4": 268848641, "0.5b-k5": 506989859, "0.5b-tern": 135531392,
-                 "bin": 128618467, "7b-int4": 3790890882, "7b-prefill": 575672431}
+                   "gemm_tkq_gemv_amd/csrc/kernels.h", "gemm_tkq_gemv_amd/csrc/small_m.hip",
+                   "gemm_tkq_gemv_amd/csrc/kv.hip"]
+TRAFFIC_HASH = "23ea0f8fb056439d"
+TRAFFIC_BYTES = {"0.5b-int4": 268831687, "0.5b-k5": 506979171, "0.5b-tern": 135443486, "bin": 128936040,
+                 "7b-int4": 3790845678, "7b-prefill": 572156335, "0.5b-hier": 268507113,
+                 "0.5b-int2": 143178110, "0.5b-int3": 214389520, "0.5b-int4-greedy": 266668711,
+                 "0.5b-int4-m16": 366618905, "kv-32k": 143389716}
 
 
 def measured_traffic(workload):
@@ -318,7 +321,7 @@ def run_small(args, torch, tkq, inputs, model, M):
             "tok_s": round(M * 1000.0 / ms, 1),
             "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload)},
             "kernel": "small_m_kernel"}
 
 
@@ -355,7 +358,7 @@ def run_kv(args, torch, tkq, B, H, Hk, T):
                        "bytes_per_step": step_bytes, "copies_rotated": len(caches)},
             "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload)},
             "kernel": "kv_decode_kernel + kv_merge_kernel"}
 
 
