@@ -345,8 +345,8 @@ def run_kv(args, torch, tkq, B, H, Hk, T):
                      device="cuda")
     torch.cuda.synchronize()
     scale = 1 / math.sqrt(128)
-    ms = time_steps(torch, lambda s: tkq.kv_decode(q, caches[s % len(caches)], T, scale, out, ws), args.steps,
-                    args.warmup, args.graph, len(caches))
+    decs = [tkq.KvDecoder(q, c, T, scale, out, ws) for c in caches]
+    ms = time_steps(torch, lambda s: decs[s % len(decs)].run(), args.steps, args.warmup, args.graph, len(decs))
     step_bytes = cache_bytes + 2 * 2 * B * H * 128
     gbs = step_bytes / (ms * 1e-3) / 1e9
     return {"metric": "4-bit KV-cache decode attention achieved HBM TB/s", "value": round(gbs / 1000.0, 4),
@@ -481,7 +481,7 @@ def main():
     ap.add_argument("--workload", default="0.5b-int4",
                     choices=["0.5b-int4", "0.5b-int4-greedy", "0.5b-k5", "0.5b-tern", "0.5b-hier",
                              "0.5b-int2", "0.5b-int3", "0.5b-int4-m2", "0.5b-int4-m4", "0.5b-int4-m8", "0.5b-int4-m16",
-                             "7b-int4-m16", "kv-32k", "kv-32k-gqa", "kv-4k", "bin", "single-896",
+                             "7b-int4-m16", "kv-32k", "kv-32k-gqa", "kv-4k", "kv-128k-gqa", "bin", "single-896",
                              "7b-int4", "7b-hier", "7b-prefill", "probe"])
     ap.add_argument("--graph", default="none", choices=["none", "step", "all"],
                     help="launch steps as HIP graph replays (see time_steps)")
@@ -532,7 +532,7 @@ def main():
                           % (passes, len(done), ", ".join(done[:3] + (["..."] if len(done) > 3 else [])
                                                           + done[-1:]), spent)}
     elif w.startswith("kv-"):
-        T = 4096 if w == "kv-4k" else 32768
+        T = {"4k": 4096, "32k": 32768, "128k": 131072}[w.split("-")[1]]
         Hk = 8 if w.endswith("gqa") else 32
         out = run_kv(args, torch, tkq, 1, 32, Hk, T)
     elif "-m" in w:

@@ -350,21 +350,262 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
   }
 }
 
+// ------------------------------------------------- decode, grouped queries --
+// With several query heads per KV head the two products are small GEMMs
+// (16 tokens x 128 channels x up to 16 heads per MFMA block), so they run on
+// the matrix cores and the work per page no longer grows with the group:
+//  * scores: A = K codes (lane l: token l % 16 of a 16-token block, channels
+//    32 (l / 16) .. +31 = one 16-byte chunk), unpacked with multiplier 1 only
+//    (four shifts per word) into (1024 + k) fp16 pairs; B = q' = q * sK
+//    (lane l: head l % 16, the same 32 channels), in the unpack's k order.
+//    D[token][head] - sum_c q'_c (1024 + zK_c) is the score.
+//  * softmax per head in the lanes of that head's column (l % 16), online
+//    over pages; p' = p * sV goes through LDS, head-major.
+//  * value product: A = V codes (lane l: channel l % 16 of a 16-channel
+//    block, tokens 32 (l / 16) .. +31), B = p' (lane l: head l % 16);
+//    D[channel][head] - sum_t p'_t (1024 + zV_t) is the page's output, and
+//    each lane keeps its head's 32 output values in registers.
+//  * each wave writes its own partial (m, l, o) per head; the merge kernel
+//    combines them with the other waves' and splits'.
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One code word (8 nibbles, natural order) -> (1024 + c) fp16 values in the
+// order (0, 4, 1, 5, 2, 6, 3, 7).
+__device__ __forceinline__ half8 unpack_plain(uint32_t w, uint32_t m, uint32_t magic) {
+  u32x4 v = {(w & m) | magic, ((w >> 4) & m) | magic, ((w >> 8) & m) | magic, ((w >> 12) & m) | magic};
+  return __builtin_bit_cast(half8, v);
+}
+__device__ __forceinline__ half8 as_half8(const uint32_t* p) {
+  u32x4 v = {p[0], p[1], p[2], p[3]};
+  return __builtin_bit_cast(half8, v);
+}
+
+#ifndef TKQ_KV_MFMA_WPE
+#define TKQ_KV_MFMA_WPE 3  // minimum waves per SIMD the register budget must allow
+#endif
+#ifndef TKQ_KV_VPREFETCH
+#define TKQ_KV_VPREFETCH 1  // load the first V codes before the softmax (more registers)
+#endif
+
+// NG: query heads of this workgroup (1..16, padded to 16 MFMA columns).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA_WPE, 8))) void kv_decode_mfma_kernel(const uint16_t* __restrict__ q,
+                                                             const uint32_t* __restrict__ cache, int H, int Hk,
+                                                             int P, int pages_per_split, float scale_log2,
+                                                             float* __restrict__ ws, int splits, int NG) {
+  __shared__ uint32_t qv[16][kD / 2];               // query heads, fp16 pairs (zero past NG)
+  __shared__ uint32_t metas[kWaves][256];           // K meta then V meta of the wave's page
+  __shared__ __attribute__((aligned(16))) _Float16 pvs[kWaves][16][kPage];  // p' per head
+  const int split = blockIdx.x, hsub = blockIdx.y, b = blockIdx.z;
+  const int gq = H / Hk;
+  const int h0 = hsub * NG, hk = h0 / gq;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, blk = lane >> 4;
+  const uint32_t M4 = in_sgpr(0x000F000Fu), magic = in_vgpr(kMagic);
+  for (int i = threadIdx.x; i < 16 * (kD / 2); i += 256) {
+    const int g = i / (kD / 2), w = i - g * (kD / 2);
+    qv[g][w] = g < NG ? reinterpret_cast<const uint32_t*>(q + ((size_t)b * H + h0 + g) * kD)[w] : 0u;
+  }
+  __syncthreads();
+  uint32_t* meta = metas[wave];
+  _Float16* pv = pvs[wave][col];
+
+  float m = -INFINITY, l = 0.0f;  // this lane's head (col)
+  f32x4 o[8];                      // channels 16 cb + 4 blk + r of head col
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int p0 = split * pages_per_split, p1 = min(P, p0 + pages_per_split);
+  const uint32_t* base = cache + ((size_t)b * Hk + hk) * (size_t)P * kPageWords;
+  for (int p = p0 + wave; p < p1; p += kWaves) {
+    const __amdgpu_buffer_rsrc_t pg = make_rsrc(base + (size_t)p * kPageWords, kPageWords * 4u);
+    *reinterpret_cast<u32x4*>(&meta[4 * lane]) = load16(pg, (uint32_t)(kKM + 4 * lane) * 4u);
+    u32x4 kc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kc[i] = load16_nt(pg, (uint32_t)(kKC + 16 * (16 * i + col) + 4 * blk) * 4u);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+    // ---- q' = q * sK for head col, channels 32 blk .. +31, and the score constant
+    uint32_t qb[16];
+    float cst = 0.0f;
+    {
+      uint32_t sraw[16], qraw[16], sp[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sraw[i] = __builtin_amdgcn_perm(meta[32 * blk + 2 * i + 1], meta[32 * blk + 2 * i], 0x05040100u);
+        qraw[i] = qv[col][16 * blk + i];
+      }
+      pair_order(sraw, sp);
+      pair_order(qraw, qb);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qb[i] = __builtin_bit_cast(uint32_t, as_h2(qb[i]) * as_h2(sp[i]));
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const h2 pr = as_h2(qb[4 * w + i]);  // channels (8w + i, 8w + i + 4) of the chunk
+          const int ch = 32 * blk + 8 * w + i;
+          cst = fmaf((float)pr[0], half_hi(meta[ch]) + 1024.0f, cst);
+          cst = fmaf((float)pr[1], half_hi(meta[ch + 4]) + 1024.0f, cst);
+        }
+      }
+      cst += __shfl_xor(cst, 16, 64);
+      cst += __shfl_xor(cst, 32, 64);
+    }
+
+    // ---- scores: 8 blocks of 16 tokens; lane holds tokens 16 tb + 4 blk + r of head col
+    float sc[8][4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (half == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kc[i] = load16_nt(pg, (uint32_t)(kKC + 16 * (16 * (4 + i) + col) + 4 * blk) * 4u);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_plain(kc[i][j], M4, magic), as_half8(qb + 4 * j), d, 0,
+                                                     0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[4 * half + i][r] = (d[r] - cst) * scale_log2;
+      }
+    }
+#if TKQ_KV_VPREFETCH
+    u32x4 vc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vc[i] = load16_nt(pg, (uint32_t)(kVC + 16 * (16 * i + col) + 4 * blk) * 4u);
+#endif
+
+    // ---- online softmax for head col
+    float pm = sc[0][0];
+#pragma unroll
+    for (int tb = 0; tb < 8; ++tb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pm = fmaxf(pm, sc[tb][r]);
+    }
+    pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
+    pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+    const float mn = fmaxf(m, pm);
+    const float alpha = exp2f(m - mn);  // 0 on the first page (m = -inf)
+    m = mn;
+    float ps = 0.0f, vcst = 0.0f;
+#pragma unroll
+    for (int tb = 0; tb < 8; ++tb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tb + 4 * blk + r;
+        const float pt = exp2f(sc[tb][r] - mn);
+        const uint32_t vm = meta[128 + t];
+        const _Float16 pp = (_Float16)(pt * half_lo(vm));  // p' = p * sV
+        pv[t] = pp;
+        ps += pt;
+        vcst = fmaf((float)pp, half_hi(vm) + 1024.0f, vcst);
+      }
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    vcst += __shfl_xor(vcst, 16, 64);
+    vcst += __shfl_xor(vcst, 32, 64);
+    l = l * alpha + ps;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+    // ---- value product: B = p' of head col, tokens 32 blk .. +31
+    uint32_t pb[16];
+    {
+      uint32_t praw[16];
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(pv) + 16 * blk;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) praw[i] = src[i];
+      pair_order(praw, pb);
+    }
+#if !TKQ_KV_VPREFETCH
+    u32x4 vc[4];
+#endif
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (half == 1 || !TKQ_KV_VPREFETCH) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          vc[i] = load16_nt(pg, (uint32_t)(kVC + 16 * (16 * (4 * half + i) + col) + 4 * blk) * 4u);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_plain(vc[i][j], M4, magic), as_half8(pb + 4 * j), d, 0,
+                                                     0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[4 * half + i][r] = fmaf(o[4 * half + i][r], alpha, d[r] - vcst);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  }
+
+  // ---- this wave's partial result for its heads: part = split * kWaves + wave
+  if (col < NG) {
+    float* out = ws + (((size_t)b * H + h0 + col) * ((size_t)splits * kWaves) + (size_t)split * kWaves + wave) *
+                          (kD + 2);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[16 * cb + 4 * blk + r] = o[cb][r];
+    }
+    if (blk == 0) {
+      out[kD] = m;
+      out[kD + 1] = l;
+    }
+  }
+}
+
 // One workgroup per (b, head): merge the splits, normalise, store fp16.
+// Threads take the splits 128 at a time (weights exp2(m_s - M) in LDS), and
+// each channel's sum over them keeps several independent loads in flight.
 __global__ __launch_bounds__(128) void kv_merge_kernel(const float* __restrict__ ws, int splits,
                                                        uint16_t* __restrict__ out) {
-  const int bh = blockIdx.x, c = threadIdx.x;
+  __shared__ float red[128];
+  __shared__ float wgt[128];
+  const int bh = blockIdx.x, tid = threadIdx.x;
   const float* w = ws + (size_t)bh * splits * (kD + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, w[s * (kD + 2) + kD]);
-  float Lsum = 0.0f, O = 0.0f;
-  for (int s = 0; s < splits; ++s) {
-    const float ms = w[s * (kD + 2) + kD];
-    const float a = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-    Lsum += w[s * (kD + 2) + kD + 1] * a;
-    O += w[s * (kD + 2) + c] * a;
+  float mloc = -INFINITY;
+  for (int s = tid; s < splits; s += 128) mloc = fmaxf(mloc, w[s * (kD + 2) + kD]);
+  red[tid] = mloc;
+  __syncthreads();
+  for (int o = 64; o >= 1; o >>= 1) {
+    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+    __syncthreads();
   }
-  out[(size_t)bh * kD + c] = half_bits(O / Lsum);
+  const float M = red[0];
+  float O = 0.0f, lloc = 0.0f;
+  for (int base = 0; base < splits; base += 128) {
+    const int s = base + tid;
+    float a = 0.0f;
+    if (s < splits) {
+      const float ms = w[s * (kD + 2) + kD];
+      a = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+      lloc += w[s * (kD + 2) + kD + 1] * a;
+    }
+    __syncthreads();  // the previous chunk's weights are consumed
+    wgt[tid] = a;
+    __syncthreads();
+    const int n = min(128, splits - base);
+    const float* col = w + (size_t)base * (kD + 2) + tid;
+#pragma unroll 8
+    for (int i = 0; i < n; ++i) O = fmaf(wgt[i], col[(size_t)i * (kD + 2)], O);
+  }
+  __syncthreads();
+  red[tid] = lloc;
+  __syncthreads();
+  for (int o = 64; o >= 1; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  out[(size_t)bh * kD + tid] = half_bits(O / red[0]);
 }
 
 }  // namespace
@@ -376,11 +617,20 @@ hipError_t launch_kv_pack(const uint16_t* K, const uint16_t* V, int B, int T, in
   return hipGetLastError();
 }
 
-// Query heads per workgroup: the whole group if it has at most 8 heads, else
-// its largest divisor up to 8.
+// Grouped queries (at least TKQ_KV_MFMA_MIN heads per KV head) take the
+// matrix-core kernel.
+#ifndef TKQ_KV_MFMA_MIN
+#define TKQ_KV_MFMA_MIN 3
+#endif
+bool kv_use_mfma(int H, int Hk) { return H / Hk >= TKQ_KV_MFMA_MIN; }
+
+// Query heads per workgroup: the whole group if it fits (8 heads for the
+// vector-ALU kernel, 16 for the matrix-core one), else its largest divisor
+// that does.
 int kv_heads_per_wg(int H, int Hk) {
   const int G = H / Hk;
-  for (int gb = G < kKvMaxGroup ? G : kKvMaxGroup; gb > 1; --gb)
+  const int cap = kv_use_mfma(H, Hk) ? 16 : kKvMaxGroup;
+  for (int gb = G < cap ? G : cap; gb > 1; --gb)
     if (G % gb == 0) return gb;
   return 1;
 }
@@ -407,6 +657,15 @@ hipError_t launch_kv_decode(const uint16_t* q, const uint32_t* cache, int B, int
                             uint16_t* out, float* ws, int splits, int pages_per_split, hipStream_t stream) {
   const int P = T / kPage;
   const int gb = kv_heads_per_wg(H, Hk);
+  if (kv_use_mfma(H, Hk)) {
+    const dim3 grid((uint32_t)splits, (uint32_t)(H / gb), (uint32_t)B);
+    hipLaunchKernelGGL(kv_decode_mfma_kernel, grid, dim3(256), 0, stream, q, cache, H, Hk, P, pages_per_split,
+                       sm_scale * kLog2e, ws, splits, gb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kv_merge_kernel, dim3((uint32_t)(B * H)), dim3(128), 0, stream, ws, splits * kWaves, out);
+    return hipGetLastError();
+  }
   const dim3 grid((uint32_t)splits, (uint32_t)(H / gb), (uint32_t)B);
   const float sl2 = sm_scale * kLog2e;
   switch (gb) {

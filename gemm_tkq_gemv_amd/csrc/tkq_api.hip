@@ -325,8 +325,9 @@ int64_t tkq_kv_cache_bytes(int32_t B, int32_t Hk, int32_t T) {
 
 int64_t tkq_kv_decode_workspace_bytes(int32_t B, int32_t H, int32_t Hk, int32_t T) {
   if (check_kv(B, H, Hk, T, tkq::kKvDim)) return -1;
-  const int64_t max_splits = (T / tkq::kKvPage + tkq::kKvWaves - 1) / tkq::kKvWaves;
-  return int64_t(B) * H * max_splits * (tkq::kKvDim + 2) * 4;
+  // one (m, l, o[128]) partial per wave of every split, at most one split per kKvWaves pages
+  const int64_t max_parts = (T / tkq::kKvPage + tkq::kKvWaves - 1) / tkq::kKvWaves * tkq::kKvWaves;
+  return int64_t(B) * H * max_parts * (tkq::kKvDim + 2) * 4;
 }
 
 int tkq_kv_pack(const uint16_t* K, const uint16_t* V, int32_t B, int32_t T, int32_t Hk, int32_t D, uint32_t* cache,

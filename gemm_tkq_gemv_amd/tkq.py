@@ -359,3 +359,32 @@ def kv_decode(q, cache, T, sm_scale, out=None, workspace=None, stream=None):
     _call("tkq_kv_decode", _ptr(q), _ptr(cache), B, H, Hk, T, D, float(sm_scale), _ptr(out), _ptr(workspace),
           workspace.numel() * 4, _stream(stream))
     return out
+
+
+class KvDecoder:
+    """A prepared tkq_kv_decode call (arguments marshalled once; run() is one
+    C call), for decode loops where the per-call Python cost matters."""
+
+    def __init__(self, q, cache, T, sm_scale, out=None, workspace=None, stream=None):
+        _need(q, torch.float16, "q")
+        B, H, D = q.shape
+        Hk = cache.shape[1]
+        self.out = out if out is not None else torch.empty_like(q)
+        _need(self.out, torch.float16, "out", q.shape)
+        nws = lib().tkq_kv_decode_workspace_bytes(B, H, Hk, T)
+        if nws < 0:
+            raise TkqError(ESHAPE, "tkq_kv_decode_workspace_bytes")
+        self.workspace = workspace if workspace is not None else torch.empty(
+            (nws + 3) // 4, dtype=torch.float32, device=q.device)
+        _need(self.workspace, torch.float32, "workspace")
+        self._keep = (q, cache)
+        self._args = (_ptr(q), _ptr(cache), B, H, Hk, T, D, ctypes.c_float(sm_scale), _ptr(self.out),
+                      _ptr(self.workspace), self.workspace.numel() * 4)
+        self._stream = _stream(stream)
+        self._fn = lib().tkq_kv_decode
+
+    def run(self):
+        st = self._fn(*self._args, self._stream)
+        if st != OK:
+            raise TkqError(st, "tkq_kv_decode")
+        return self.out

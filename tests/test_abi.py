@@ -263,8 +263,8 @@ def test_kv_validation():
     L = tkq.lib()
     assert L.tkq_kv_cache_bytes(1, 32, 4096) == 32 * 32 * 17408
     assert L.tkq_kv_cache_bytes(1, 32, 100) == -1
-    assert L.tkq_kv_decode_workspace_bytes(1, 32, 32, 4096) == 32 * 8 * 130 * 4
-    assert L.tkq_kv_decode_workspace_bytes(1, 28, 4, 128) == 28 * 1 * 130 * 4   # 7 per KV head
+    assert L.tkq_kv_decode_workspace_bytes(1, 32, 32, 4096) == 32 * 32 * 130 * 4
+    assert L.tkq_kv_decode_workspace_bytes(1, 28, 4, 128) == 28 * 4 * 130 * 4   # 7 per KV head
     assert L.tkq_kv_decode_workspace_bytes(1, 8, 3, 128) == -1      # H % Hk != 0
     pk = L.tkq_kv_pack
     assert pk(None, A, 1, 128, 1, 128, A, None) == tkq.EINVAL

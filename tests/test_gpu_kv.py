@@ -65,7 +65,9 @@ def test_kv_pack_bit_exact(B, T, Hk):
     (2, 8, 2, 640),         # 4 per KV head, batch 2, 5 pages
     (1, 16, 2, 2048),       # 8 per KV head
     (1, 28, 4, 1024),       # 7 per KV head (Qwen2.5-7B's attention shape)
-    (1, 48, 2, 512),        # 24 per KV head: three workgroups of 8 per KV head
+    (1, 48, 2, 512),        # 24 per KV head: two workgroups of 12 per KV head
+    (1, 32, 2, 1024),       # 16 per KV head: one full matrix-core tile of heads
+    (2, 6, 2, 256),         # 3 per KV head (the smallest group on the matrix-core path)
     (1, 1, 1, 128),         # one page
 ])
 def test_kv_decode_matches_oracle(B, H, Hk, T):
