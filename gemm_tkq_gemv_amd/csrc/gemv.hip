@@ -323,7 +323,19 @@ struct Tile {
   int Cs, C, K;             // chunks per slice, chunks per row, columns
   int row0, nrows;          // first matrix row of the tile, rows in the tile
   bool track;               // greedy selection over this matrix
+  // wave-uniform bases of the tile's codes and metadata: each row step gets a
+  // buffer resource that starts at its first row (scalar arithmetic), so the
+  // per-lane offsets stay loop-invariant and the range check stays exact
+  const char* codes_ptr;
+  const char* meta_ptr;
+  uint32_t codes_bytes, meta_bytes;
 };
+
+// Codings (bit fmt) whose loads use per-step scalar bases (measured per
+// coding: faster for int4 and hier-g32, slower for ternary and K5).
+#ifndef TKQ_GEMV_SBASE_MASK
+#define TKQ_GEMV_SBASE_MASK ((1 << 1) | (1 << 5))
+#endif
 
 // Order-preserving key of an output: larger value -> larger key, and among
 // equal values the smaller row -> larger key.  fp16: -0 counts as +0 (NaN
@@ -366,6 +378,7 @@ struct Runner {
   const Tile& t;
   typename Cd::Regs R;
   uint32_t cof[J], mof[J];
+  uint32_t vc[J], vm[J];  // cof / mof plus this lane's row within a step
   uint32_t xr[J][Cd::XR];
   float bias[J], xsum[J];
   mutable uint64_t best = 0;  // greedy variant: best key of this lane's rows
@@ -380,6 +393,8 @@ struct Runner {
       const bool ok = local < t.Cs && c < t.C;
       cof[j] = ok ? (uint32_t)c * 16u : kFar;
       mof[j] = ok ? (uint32_t)(c / Cd::CPG) * Cd::MB : kFar;
+      vc[j] = ok ? (uint32_t)t.prow * t.row_bytes + cof[j] : kFar;
+      vm[j] = ok ? (uint32_t)t.prow * t.meta_row_bytes + mof[j] : kFar;
     }
   }
 
@@ -419,7 +434,32 @@ struct Runner {
     return (uint32_t)(t.rbase + (st + u) * t.P + t.prow);
   }
 
+  static constexpr bool kSbase = ((TKQ_GEMV_SBASE_MASK) >> FMT) & 1;
+
   __device__ __forceinline__ void issue(int st, Buf& b) const {
+    if constexpr (kSbase) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t s = (uint32_t)(t.rbase + (st + u) * t.P);  // first row of the step (uniform)
+      const uint32_t oc = s * t.row_bytes, om = s * t.meta_row_bytes;
+      const __amdgpu_buffer_rsrc_t rc = make_rsrc(t.codes_ptr + oc, t.codes_bytes > oc ? t.codes_bytes - oc : 0u);
+      const __amdgpu_buffer_rsrc_t rm = make_rsrc(t.meta_ptr + om, t.meta_bytes > om ? t.meta_bytes - om : 0u);
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        if constexpr (Cd::PLANES == 3) {
+#pragma unroll
+          for (int p = 0; p < 3; ++p) b.c[u][j].p[p] = load16_nt(rc, (uint32_t)p * t.plane_bytes + vc[j]);
+        } else {
+          b.c[u][j] = load16_nt(rc, vc[j]);
+        }
+        if constexpr (Cd::MB == 4) b.m[u][j] = load4(rm, vm[j]);
+        else if constexpr (Cd::MB == 2) b.m[u][j] = load2(rm, vm[j]);
+        else if constexpr (Cd::MB == 1) b.m[u][j] = load1(rm, vm[j]);
+        else b.m[u][j] = 0;
+      }
+      if constexpr (FMT == kFmtHier) b.rp[u] = load4(t.rmeta, row(st, u) * 4u);
+    }
+    } else {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t r = row(st, u);
@@ -438,6 +478,7 @@ struct Runner {
         else b.m[u][j] = 0;
       }
       if constexpr (FMT == kFmtHier) b.rp[u] = load4(t.rmeta, r * 4u);
+    }
     }
   }
 
@@ -566,7 +607,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WP
   const GemvShape sh = unpack_shape(d->shape);
 
   Tile t;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   t.lg = sh.lanes_log2;
   t.P = 64 >> t.lg;
   t.sub = lane & ((1 << t.lg) - 1);
@@ -588,11 +629,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WP
   t.track = GREEDY && lo == g.target;
   const char* codes = (const char*)d->codes + (size_t)row0 * t.row_bytes;
   t.codes = make_rsrc(codes, (uint32_t)nrows * t.row_bytes);
+  t.codes_ptr = codes;
+  t.codes_bytes = (uint32_t)nrows * t.row_bytes;
   if constexpr (Cd::MB > 0) {
     const char* meta = (const char*)d->meta + (size_t)row0 * t.meta_row_bytes;
     t.meta = make_rsrc(meta, (uint32_t)nrows * t.meta_row_bytes);
+    t.meta_ptr = meta;
+    t.meta_bytes = (uint32_t)nrows * t.meta_row_bytes;
   } else {
     t.meta = make_rsrc(d->codes, 0u);
+    t.meta_ptr = (const char*)d->codes;
+    t.meta_bytes = 0u;
   }
   if constexpr (FMT == kFmtHier) {
     const char* rm = (const char*)d->meta + hier_row_offset(N, K) + (size_t)row0 * 4u;

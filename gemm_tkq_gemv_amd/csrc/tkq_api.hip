@@ -34,8 +34,22 @@ struct PlanParams {
   int prefer_passes, max_passes;
   int64_t tile, small, tail;
 };
+#ifndef TKQ_INT4_PREFER
+#define TKQ_INT4_PREFER 2
+#endif
+#ifndef TKQ_INT4_TILE_KB
+#define TKQ_INT4_TILE_KB 48
+#endif
+#ifndef TKQ_SMALL_TILE_KB
+#define TKQ_SMALL_TILE_KB 4
+#endif
+#ifndef TKQ_TAIL_MB
+#define TKQ_TAIL_MB 40
+#endif
 PlanParams plan_params(int fmt) {
-  if (fmt == TKQ_FMT_INT4_G128 || fmt == TKQ_FMT_INT4_HIER_G32) return {2, 4, 48 << 10, 4 << 10, 40 << 20};
+  if (fmt == TKQ_FMT_INT4_G128 || fmt == TKQ_FMT_INT4_HIER_G32)
+    return {TKQ_INT4_PREFER, 4, int64_t(TKQ_INT4_TILE_KB) << 10, int64_t(TKQ_SMALL_TILE_KB) << 10,
+            int64_t(TKQ_TAIL_MB) << 20};
   if (fmt == TKQ_FMT_TERN_G128 || fmt == TKQ_FMT_INT2_G128) return {1, TKQ_TERN_JMAX, 24 << 10, 4 << 10, 40 << 20};
   if (fmt == TKQ_FMT_INT3_G128) return {1, 1, 24 << 10, 4 << 10, 40 << 20};
   return {1, 8, 24 << 10, 4 << 10, 40 << 20};
