@@ -37,6 +37,10 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 64;
+constexpr int kXcds = 8;  // accelerator complexes of the part (L2 domains)
+#ifndef TKQ_PREFILL_XCD
+#define TKQ_PREFILL_XCD 1
+#endif
 constexpr int LDSW = BK + 8;  // halfs per LDS row (16 bytes of padding)
 constexpr uint32_t kMagic = 0x64006400u;
 
@@ -169,11 +173,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint16_t* __restrict
   __shared__ __attribute__((aligned(16))) _Float16 xs[2][BM * LDSW];
   __shared__ __attribute__((aligned(16))) _Float16 ws[2][BN * LDSW];
 
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  // Work item -> (split, N tile, M tile), M fastest: the M tiles that share
+  // one weight tile are consecutive.  With XCD-aware order the work items
+  // of one XCD (workgroup b runs on XCD b % 8) are a contiguous range, so
+  // those M tiles also share that XCD's L2.
+  const int MT = (M + BM - 1) / BM, NT = (N + BN - 1) / BN;
+  const int total = (int)gridDim.x;
+#if TKQ_PREFILL_XCD
+  const int xcd = (int)blockIdx.x % kXcds, per = total / kXcds, rem = total % kXcds;
+  const int work = xcd * per + min(xcd, rem) + (int)blockIdx.x / kXcds;
+#else
+  const int work = (int)blockIdx.x;
+#endif
+  const int split = work / (MT * NT), tile = work - split * (MT * NT);
+  const int m0 = (tile % MT) * BM, n0 = (tile / MT) * BN;
+  (void)NT;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (BN / 2);
   const int mrows = min(BM, M - m0), nrows = min(BN, N - n0);
-  const int kbeg = blockIdx.z * ksteps_per_split * BK;
+  const int kbeg = split * ksteps_per_split * BK;
   const int kend = min(K, kbeg + ksteps_per_split * BK);
   const uint32_t xrow = (uint32_t)K * 2u, crow = (uint32_t)K / 2u, mrow = (uint32_t)(K / 128) * 4u;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + (size_t)m0 * K, (uint32_t)mrows * xrow);
@@ -238,7 +256,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint16_t* __restrict
 
   // D layout of a 32x32 fp32 accumulator: register r of lane l holds row
   // 8*(r/4) + 4*(l/32) + r%4, column l%32.
-  float* pz = part ? part + (size_t)blockIdx.z * M * N : nullptr;
+  float* pz = part ? part + (size_t)split * M * N : nullptr;
 #pragma unroll
   for (int a = 0; a < A; ++a)
 #pragma unroll
@@ -313,7 +331,7 @@ void launch_tile(int64_t M, int64_t N, int64_t K, int splits, const uint32_t* co
                  const uint16_t* X, uint16_t* Y, float* part, hipStream_t stream) {
   const int64_t ksteps = (K + BK - 1) / BK;
   const int per_split = (int)((ksteps + splits - 1) / splits);
-  const dim3 grid((uint32_t)((N + BN - 1) / BN), (uint32_t)((M + BM - 1) / BM), (uint32_t)splits);
+  const dim3 grid((uint32_t)(((N + BN - 1) / BN) * ((M + BM - 1) / BM) * splits));
   hipLaunchKernelGGL((prefill_kernel<BM, BN>), grid, dim3(256), 0, stream, X, codes, meta, Y, part, (int)M,
                      (int)N, (int)K, per_split);
 }

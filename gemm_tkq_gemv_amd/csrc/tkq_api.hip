@@ -381,8 +381,8 @@ int tkq_gemm_prefill(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint32_
       (workspace && workspace_bytes == 0))
     return TKQ_EINVAL;
   if (K % 128 || K > TKQ_MAX_K || M > INT32_MAX || N > INT32_MAX || N * K > kMaxWeights ||
-      M * K > kMaxWeights || M * N > kMaxWeights || (N + 63) / 64 > INT32_MAX ||
-      (M + 63) / 64 > 65535 || 128 * K * 2 > INT32_MAX)
+      M * K > kMaxWeights || M * N > kMaxWeights || (M + 63) / 64 * ((N + 63) / 64) * 8 > INT32_MAX ||
+      128 * K * 2 > INT32_MAX)
     return TKQ_ESHAPE;
   if (!aligned16(codes) || !aligned16(meta) || !aligned16(X) || !aligned16(Y) ||
       (workspace && !aligned16(workspace)))
