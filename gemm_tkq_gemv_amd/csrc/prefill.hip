@@ -167,7 +167,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint16_t* __restrict
                                                       const uint32_t* __restrict__ codes,
                                                       const uint32_t* __restrict__ meta,
                                                       uint16_t* __restrict__ Y, float* __restrict__ part,
-                                                      int M, int N, int K, int ksteps_per_split) {
+                                                      int M, int N, int K, int ksteps_per_split, int tsplit,
+                                                      int full_x) {
   constexpr int A = BM / 64, B = BN / 64;  // 32x32 MFMA tiles per wave in M and N
   static_assert(A >= 1 && B >= 1, "tile too small");
   __shared__ __attribute__((aligned(16))) _Float16 xs[2][BM * LDSW];
@@ -185,14 +186,34 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint16_t* __restrict
 #else
   const int work = (int)blockIdx.x;
 #endif
-  const int split = work / (MT * NT), tile = work - split * (MT * NT);
+  int split = work / (MT * NT), tile = work - split * (MT * NT);
+  if (tsplit > 1) {
+    // Tail split: in each XCD's range, the tiles of its last, partial round
+    // are cut into tsplit K pieces (fp32 partials, summed by
+    // tail_reduce_kernel), so that round fills the XCD's slots.
+    // full_x: tiles of the full rounds (the same for every XCD); the XCD's
+    // remaining tiles (at most one round) are the split ones.
+    const int xcd = (int)blockIdx.x % kXcds, k = (int)blockIdx.x / kXcds;
+    const int T = MT * NT, per = T / kXcds, rem = T % kXcds;
+    const int tiles_x = per + (xcd < rem ? 1 : 0), start_x = xcd * per + min(xcd, rem);
+    const int last = tiles_x - full_x;
+    if (k < full_x) {
+      tile = start_x + k;
+      split = -1;
+    } else {
+      const int j = k - full_x;
+      if (j >= last * tsplit) return;  // padding of the grid (uniform: the whole workgroup leaves)
+      tile = start_x + full_x + j / tsplit;
+      split = j % tsplit;
+    }
+  }
   const int m0 = (tile % MT) * BM, n0 = (tile / MT) * BN;
   (void)NT;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (BN / 2);
   const int mrows = min(BM, M - m0), nrows = min(BN, N - n0);
-  const int kbeg = split * ksteps_per_split * BK;
-  const int kend = min(K, kbeg + ksteps_per_split * BK);
+  const int kbeg = split > 0 ? split * ksteps_per_split * BK : 0;
+  const int kend = split < 0 ? K : min(K, kbeg + ksteps_per_split * BK);  // split < 0: a whole tile
   const uint32_t xrow = (uint32_t)K * 2u, crow = (uint32_t)K / 2u, mrow = (uint32_t)(K / 128) * 4u;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + (size_t)m0 * K, (uint32_t)mrows * xrow);
   const __amdgpu_buffer_rsrc_t cr = make_rsrc((const char*)codes + (size_t)n0 * crow, (uint32_t)nrows * crow);
@@ -256,7 +277,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint16_t* __restrict
 
   // D layout of a 32x32 fp32 accumulator: register r of lane l holds row
   // 8*(r/4) + 4*(l/32) + r%4, column l%32.
-  float* pz = part ? part + (size_t)split * M * N : nullptr;
+  float* pz = (part && split >= 0) ? part + (size_t)split * M * N : nullptr;
 #pragma unroll
   for (int a = 0; a < A; ++a)
 #pragma unroll
@@ -283,8 +304,32 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
+// Y of the tail tiles = fp16(sum over the tsplit partials), in piece order.
+// Grid: (XCD, tail tile of that XCD, 16 element chunks).
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restrict__ part, uint16_t* __restrict__ Y,
+                                                          int M, int N, int BM, int BN, int tsplit, int full_x) {
+  const int MT = (M + BM - 1) / BM, NT = (N + BN - 1) / BN, T = MT * NT;
+  const int xcd = blockIdx.x, i = blockIdx.y;
+  const int per = T / kXcds, rem = T % kXcds;
+  const int tiles_x = per + (xcd < rem ? 1 : 0), start_x = xcd * per + min(xcd, rem);
+  if (i >= tiles_x - full_x) return;
+  const int tile = start_x + full_x + i;
+  const int m0 = (tile % MT) * BM, n0 = (tile / MT) * BN;
+  const size_t MN = (size_t)M * N;
+  for (int e = blockIdx.z * 256 + threadIdx.x; e < BM * BN; e += 256 * gridDim.z) {
+    const int r = e / BN, c = e - r * BN;
+    if (m0 + r < M && n0 + c < N) {
+      const size_t o = (size_t)(m0 + r) * N + n0 + c;
+      float v = part[o];
+      for (int z = 1; z < tsplit; ++z) v += part[(size_t)z * MN + o];
+      Y[o] = half_bits(v);
+    }
+  }
+}
+
 struct Config {
   int bm, bn, splits;
+  int tsplit, full_x;  // tail split (1: none); tiles per XCD in its full rounds
 };
 
 // Pick the tile shape that keeps the most of the GPU's workgroup slots busy
@@ -301,7 +346,7 @@ Config choose(int64_t M, int64_t N, int64_t K, int cus, int64_t ws_floats) {
 #endif
   const Cand cands[] = {{128, 256, 1, TKQ_PREFILL_BIG}, {256, 128, 1, TKQ_PREFILL_BIG}, {128, 128, 2, 1.0},
                         {128, 64, 2, 0.8},           {64, 128, 2, 0.8},           {64, 64, 4, 0.55}};
-  Config best = {128, 128, 1};
+  Config best = {128, 128, 1, 1, 0};
   double best_score = -1.0;
   for (const Cand& c : cands) {
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
@@ -310,7 +355,7 @@ Config choose(int64_t M, int64_t N, int64_t K, int cus, int64_t ws_floats) {
     const double score = double(tiles) / double(rounds * slots) * c.eff;
     if (score > best_score + 1e-9) {
       best_score = score;
-      best = {c.bm, c.bn, 1};
+      best = {c.bm, c.bn, 1, 1, 0};
     }
   }
   const int64_t tiles = ((M + best.bm - 1) / best.bm) * ((N + best.bn - 1) / best.bn);
@@ -322,18 +367,46 @@ Config choose(int64_t M, int64_t N, int64_t K, int cus, int64_t ws_floats) {
       best.splits = s;
       if (tiles * s * 5 >= slots * 4) break;
     }
+  } else if (cus % kXcds == 0) {
+    // Tail split: the rounds are those of the largest XCD range; every XCD
+    // cuts the tiles after its full rounds (at most `last`) into s pieces,
+    // the largest s with s * last within one round of slots.
+    const int64_t sx = slots / kXcds, tiles_x = tiles / kXcds + (tiles % kXcds ? 1 : 0);
+    const int64_t rounds = (tiles_x + sx - 1) / sx;
+    const int64_t last = tiles_x - (rounds - 1) * sx;
+#ifndef TKQ_PREFILL_TAIL
+#define TKQ_PREFILL_TAIL 1
+#endif
+    for (int s = 4; s >= 2 && TKQ_PREFILL_TAIL; --s) {
+      if (last * s <= sx && (int64_t)s * M * N <= ws_floats && s <= ksteps / 4) {
+        best.tsplit = s;
+        best.full_x = (int)((rounds - 1) * sx);
+        break;
+      }
+    }
   }
   return best;
 }
 
 template <int BM, int BN>
-void launch_tile(int64_t M, int64_t N, int64_t K, int splits, const uint32_t* codes, const uint32_t* meta,
+void launch_tile(int64_t M, int64_t N, int64_t K, const Config& c, const uint32_t* codes, const uint32_t* meta,
                  const uint16_t* X, uint16_t* Y, float* part, hipStream_t stream) {
   const int64_t ksteps = (K + BK - 1) / BK;
-  const int per_split = (int)((ksteps + splits - 1) / splits);
-  const dim3 grid((uint32_t)(((N + BN - 1) / BN) * ((M + BM - 1) / BM) * splits));
+  const int64_t T = ((N + BN - 1) / BN) * ((M + BM - 1) / BM);
+  if (c.tsplit > 1) {
+    // per XCD: the full-round tiles, then tsplit pieces of each remaining
+    // tile; grid = 8 x the largest XCD's item count
+    const int64_t tiles_x = T / kXcds + (T % kXcds ? 1 : 0);
+    const int64_t items = c.full_x + (tiles_x - c.full_x) * c.tsplit;
+    const int per_piece = (int)((ksteps + c.tsplit - 1) / c.tsplit);
+    hipLaunchKernelGGL((prefill_kernel<BM, BN>), dim3((uint32_t)(items * kXcds)), dim3(256), 0, stream, X, codes,
+                       meta, Y, part, (int)M, (int)N, (int)K, per_piece, c.tsplit, c.full_x);
+    return;
+  }
+  const int per_split = (int)((ksteps + c.splits - 1) / c.splits);
+  const dim3 grid((uint32_t)(T * c.splits));
   hipLaunchKernelGGL((prefill_kernel<BM, BN>), grid, dim3(256), 0, stream, X, codes, meta, Y, part, (int)M,
-                     (int)N, (int)K, per_split);
+                     (int)N, (int)K, per_split, 1, 0);
 }
 
 }  // namespace
@@ -348,15 +421,23 @@ hipError_t launch_prefill(int64_t M, int64_t N, int64_t K, const uint32_t* codes
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
   if (e != hipSuccess) return e;
   const Config c = choose(M, N, K, cus > 0 ? cus : 1, workspace ? workspace_bytes / 4 : 0);
-  float* part = c.splits > 1 ? workspace : nullptr;
-  if (c.bm == 128 && c.bn == 256) launch_tile<128, 256>(M, N, K, c.splits, codes, meta, X, Y, part, stream);
-  else if (c.bm == 256) launch_tile<256, 128>(M, N, K, c.splits, codes, meta, X, Y, part, stream);
-  else if (c.bm == 128 && c.bn == 128) launch_tile<128, 128>(M, N, K, c.splits, codes, meta, X, Y, part, stream);
-  else if (c.bm == 128) launch_tile<128, 64>(M, N, K, c.splits, codes, meta, X, Y, part, stream);
-  else if (c.bn == 128) launch_tile<64, 128>(M, N, K, c.splits, codes, meta, X, Y, part, stream);
-  else launch_tile<64, 64>(M, N, K, c.splits, codes, meta, X, Y, part, stream);
+  float* part = (c.splits > 1 || c.tsplit > 1) ? workspace : nullptr;
+  if (c.bm == 128 && c.bn == 256) launch_tile<128, 256>(M, N, K, c, codes, meta, X, Y, part, stream);
+  else if (c.bm == 256) launch_tile<256, 128>(M, N, K, c, codes, meta, X, Y, part, stream);
+  else if (c.bm == 128 && c.bn == 128) launch_tile<128, 128>(M, N, K, c, codes, meta, X, Y, part, stream);
+  else if (c.bm == 128) launch_tile<128, 64>(M, N, K, c, codes, meta, X, Y, part, stream);
+  else if (c.bn == 128) launch_tile<64, 128>(M, N, K, c, codes, meta, X, Y, part, stream);
+  else launch_tile<64, 64>(M, N, K, c, codes, meta, X, Y, part, stream);
   e = hipGetLastError();
-  if (e != hipSuccess || c.splits == 1) return e;
+  if (e != hipSuccess) return e;
+  if (c.tsplit > 1) {
+    const int64_t T = ((N + c.bn - 1) / c.bn) * ((M + c.bm - 1) / c.bm);
+    const int64_t last = T / kXcds + (T % kXcds ? 1 : 0) - c.full_x;
+    hipLaunchKernelGGL(tail_reduce_kernel, dim3(kXcds, (uint32_t)last, 16), dim3(256), 0, stream, workspace, Y,
+                       (int)M, (int)N, c.bm, c.bn, c.tsplit, c.full_x);
+    return hipGetLastError();
+  }
+  if (c.splits == 1) return e;
   const int64_t MN = M * N;
   int64_t blocks = (MN + 255) / 256;
   if (blocks > 65536) blocks = 65536;

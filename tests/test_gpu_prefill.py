@@ -32,7 +32,8 @@ def _check(Y, X, w_deq, what):
 @pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (64, 128, 256), (65, 200, 384),
                                    (130, 333, 896), (512, 256, 1024), (257, 129, 4864),
-                                   (512, 96, 8192), (33, 1000, 640)])
+                                   (512, 96, 8192), (33, 1000, 640),
+                                   (200, 33000, 256)])   # > one round of tiles: tail split with a workspace
 def test_prefill_ragged(M, N, K, split):
     torch = gpu_or_skip()
     from gemm_tkq_gemv_amd import tkq
@@ -43,14 +44,16 @@ def test_prefill_ragged(M, N, K, split):
     _check(Y, X, oracle_wdeq("int4", oc, om, K), "%dx%dx%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("name", ["gate", "up", "down"])
-def test_prefill_7b_mlp_full(name):
+@pytest.mark.parametrize("name,split", [("gate", False), ("gate", True), ("up", True), ("down", True)])
+def test_prefill_7b_mlp_full(name, split):
+    """With a workspace, gate/up (592 tiles: two rounds per XCD, the second
+    partial) take the tail split, down (224 tiles) the split-K path."""
     torch = gpu_or_skip()
     from gemm_tkq_gemv_amd import tkq
     W = inputs.prefill_W(name)
     N, K = W.shape
     X = inputs.prefill_X(K)
-    codes, meta, Y = _run(torch, tkq, W, X, split=(name == "down"))
+    codes, meta, Y = _run(torch, tkq, W, X, split=split)
     oc, om = oracle_pack("int4", W)
     worst = _check(Y, X, oracle_wdeq("int4", oc, om, K), name)
     print("prefill %s worst |err|/bound %.3g" % (name, worst))
