@@ -40,25 +40,55 @@ ROTATE_BYTES = 1 << 30
 # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE passes (each
 # scaled by what the counter reads for a 256 MiB device copy); see the
 # summaries under profiles/.  Valid only for the kernel sources they were
-# measured on: reported while the sources hash to TRAFFIC_HASH, else null.
-TRAFFIC_SOURCES = ["gemm_tkq_gemv_amd/csrc/gemv.hip", "gemm_tkq_gemv_amd/csrc/tkq_api.hip",
-                   "gemm_tkq_gemv_amd/csrc/prefill.hip", "gemm_tkq_gemv_amd/csrc/device_common.h",
-                   "gemm_tkq_gemv_amd/csrc/kernels.h", "gemm_tkq_gemv_amd/csrc/small_m.hip",
-                   "gemm_tkq_gemv_amd/csrc/kv.hip"]
-TRAFFIC_HASH = "23ea0f8fb056439d"
-TRAFFIC_BYTES = {"0.5b-int4": 268831687, "0.5b-k5": 506979171, "0.5b-tern": 135443486, "bin": 128936040,
-                 "7b-int4": 3790845678, "7b-prefill": 572156335, "0.5b-hier": 268507113,
-                 "0.5b-int2": 143178110, "0.5b-int3": 214389520, "0.5b-int4-greedy": 266668711,
-                 "0.5b-int4-m16": 366618905, "kv-32k": 143389716}
+# measured on: a workload's figure is reported while the sources of its
+# kernel family hash to the value stored with it, else null.
+_COMMON = ["gemm_tkq_gemv_amd/csrc/tkq_api.hip", "gemm_tkq_gemv_amd/csrc/device_common.h",
+           "gemm_tkq_gemv_amd/csrc/kernels.h"]
+TRAFFIC_SOURCES = {"gemv": ["gemm_tkq_gemv_amd/csrc/gemv.hip"] + _COMMON,
+                   "small_m": ["gemm_tkq_gemv_amd/csrc/small_m.hip"] + _COMMON,
+                   "prefill": ["gemm_tkq_gemv_amd/csrc/prefill.hip"] + _COMMON,
+                   "kv": ["gemm_tkq_gemv_amd/csrc/kv.hip"] + _COMMON}
+# workload -> (kernel family, bytes per launch, sha256[:16] of that family's sources)
+TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 277317932, "ee50ac43d9a84272"),
+                 "0.5b-k5": ("gemv", 506989469, "ee50ac43d9a84272"),
+                 "0.5b-tern": ("gemv", 135443283, "ee50ac43d9a84272"),
+                 "bin": ("gemv", 130834588, "ee50ac43d9a84272"),
+                 "7b-int4": ("gemv", 3801701729, "ee50ac43d9a84272"),
+                 "7b-prefill": ("prefill", 317402112, "73bbf72f750c4a2b"),
+                 "0.5b-hier": ("gemv", 279142307, "ee50ac43d9a84272"),
+                 "0.5b-int2": ("gemv", 143167441, "ee50ac43d9a84272"),
+                 "0.5b-int3": ("gemv", 231178228, "ee50ac43d9a84272"),
+                 "0.5b-int4-greedy": ("gemv", 277013610, "ee50ac43d9a84272"),
+                 "0.5b-int4-m16": ("small_m", 366697069, "2898a5db74d0d427"),
+                 "kv-32k": ("kv", 143375413, "70dcd9e591d4a31f"),
+                 "kv-32k-gqa": ("kv", 40152435, "70dcd9e591d4a31f"),
+                 "kv-128k-gqa": ("kv", 151350132, "70dcd9e591d4a31f")}
+
+
+def traffic_family(workload):
+    if workload.startswith("kv-"):
+        return "kv"
+    if workload == "7b-prefill":
+        return "prefill"
+    if "-m" in workload and workload.split("-m")[-1].isdigit():
+        return "small_m"
+    return "gemv"
+
+
+def source_hash(family):
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES[family]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload):
-    import hashlib
-    h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return TRAFFIC_BYTES.get(workload) if h.hexdigest()[:16] == TRAFFIC_HASH else None
+    e = TRAFFIC_BYTES.get(workload)
+    if e is None or source_hash(e[0]) != e[2]:
+        return None
+    return e[1]
 
 
 def log(*a):
