@@ -365,8 +365,8 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
 //    block, tokens 32 (l / 16) .. +31), B = p' (lane l: head l % 16);
 //    D[channel][head] - sum_t p'_t (1024 + zV_t) is the page's output, and
 //    each lane keeps its head's 32 output values in registers.
-//  * each wave writes its own partial (m, l, o) per head; the merge kernel
-//    combines them with the other waves' and splits'.
+//  * the four waves' partials (m, l, o) are combined in LDS and the
+//    workgroup writes one partial per head and split for the merge kernel.
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -381,21 +381,35 @@ __device__ __forceinline__ half8 as_half8(const uint32_t* p) {
   return __builtin_bit_cast(half8, v);
 }
 
+#ifndef TKQ_KV_UPFRONT
+#define TKQ_KV_UPFRONT 0  // issue every load of a page before its scores (more registers: measured slower)
+#endif
 #ifndef TKQ_KV_MFMA_WPE
-#define TKQ_KV_MFMA_WPE 3  // minimum waves per SIMD the register budget must allow
+#define TKQ_KV_MFMA_WPE (TKQ_KV_UPFRONT ? 2 : 3)  // minimum waves per SIMD the register budget must allow
 #endif
 #ifndef TKQ_KV_VPREFETCH
 #define TKQ_KV_VPREFETCH 1  // load the first V codes before the softmax (more registers)
 #endif
+
+// LDS of the matrix-core kernel: the page loop's buffers, reused after it
+// for the combination of the four waves' partials.
+struct MfmaLoop {
+  uint32_t qv[16][kD / 2];                               // query heads, fp16 pairs (zero past NG)
+  uint32_t metas[kWaves][256];                           // K meta then V meta of the wave's page
+  __attribute__((aligned(16))) _Float16 pvs[kWaves][16][kPage];  // p' per head
+};
+union MfmaLds {
+  MfmaLoop loop;
+  float part[kWaves][16][kD + 2];  // per wave and head: o[128], m, l
+};
 
 // NG: query heads of this workgroup (1..16, padded to 16 MFMA columns).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA_WPE, 8))) void kv_decode_mfma_kernel(const uint16_t* __restrict__ q,
                                                              const uint32_t* __restrict__ cache, int H, int Hk,
                                                              int P, int pages_per_split, float scale_log2,
                                                              float* __restrict__ ws, int splits, int NG) {
-  __shared__ uint32_t qv[16][kD / 2];               // query heads, fp16 pairs (zero past NG)
-  __shared__ uint32_t metas[kWaves][256];           // K meta then V meta of the wave's page
-  __shared__ __attribute__((aligned(16))) _Float16 pvs[kWaves][16][kPage];  // p' per head
+  __shared__ MfmaLds lds;
+  auto& qv = lds.loop.qv;
   const int split = blockIdx.x, hsub = blockIdx.y, b = blockIdx.z;
   const int gq = H / Hk;
   const int h0 = hsub * NG, hk = h0 / gq;
@@ -407,8 +421,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA
     qv[g][w] = g < NG ? reinterpret_cast<const uint32_t*>(q + ((size_t)b * H + h0 + g) * kD)[w] : 0u;
   }
   __syncthreads();
-  uint32_t* meta = metas[wave];
-  _Float16* pv = pvs[wave][col];
+  uint32_t* meta = lds.loop.metas[wave];
+  _Float16* pv = lds.loop.pvs[wave][col];
 
   float m = -INFINITY, l = 0.0f;  // this lane's head (col)
   f32x4 o[8];                      // channels 16 cb + 4 blk + r of head col
@@ -419,10 +433,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA
   const uint32_t* base = cache + ((size_t)b * Hk + hk) * (size_t)P * kPageWords;
   for (int p = p0 + wave; p < p1; p += kWaves) {
     const __amdgpu_buffer_rsrc_t pg = make_rsrc(base + (size_t)p * kPageWords, kPageWords * 4u);
+#if TKQ_KV_UPFRONT
+    u32x4 kc[8], vc[8];
+    const u32x4 mt = load16(pg, (uint32_t)(kKM + 4 * lane) * 4u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kc[i] = load16_nt(pg, (uint32_t)(kKC + 16 * (16 * i + col) + 4 * blk) * 4u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vc[i] = load16_nt(pg, (uint32_t)(kVC + 16 * (16 * i + col) + 4 * blk) * 4u);
+    *reinterpret_cast<u32x4*>(&meta[4 * lane]) = mt;
+#else
     *reinterpret_cast<u32x4*>(&meta[4 * lane]) = load16(pg, (uint32_t)(kKM + 4 * lane) * 4u);
     u32x4 kc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) kc[i] = load16_nt(pg, (uint32_t)(kKC + 16 * (16 * i + col) + 4 * blk) * 4u);
+#endif
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
@@ -458,22 +482,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA
     float sc[8][4];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
+#if !TKQ_KV_UPFRONT
       if (half == 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) kc[i] = load16_nt(pg, (uint32_t)(kKC + 16 * (16 * (4 + i) + col) + 4 * blk) * 4u);
       }
+#endif
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+        const u32x4 kw = kc[TKQ_KV_UPFRONT ? 4 * half + i : i];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_plain(kc[i][j], M4, magic), as_half8(qb + 4 * j), d, 0,
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_plain(kw[j], M4, magic), as_half8(qb + 4 * j), d, 0,
                                                      0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[4 * half + i][r] = (d[r] - cst) * scale_log2;
       }
     }
-#if TKQ_KV_VPREFETCH
+#if TKQ_KV_VPREFETCH && !TKQ_KV_UPFRONT
     u32x4 vc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) vc[i] = load16_nt(pg, (uint32_t)(kVC + 16 * (16 * i + col) + 4 * blk) * 4u);
@@ -522,22 +549,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA
       for (int i = 0; i < 16; ++i) praw[i] = src[i];
       pair_order(praw, pb);
     }
-#if !TKQ_KV_VPREFETCH
+#if !TKQ_KV_VPREFETCH && !TKQ_KV_UPFRONT
     u32x4 vc[4];
 #endif
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
+#if !TKQ_KV_UPFRONT
       if (half == 1 || !TKQ_KV_VPREFETCH) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           vc[i] = load16_nt(pg, (uint32_t)(kVC + 16 * (16 * (4 * half + i) + col) + 4 * blk) * 4u);
       }
+#endif
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+        const u32x4 vw = vc[TKQ_KV_UPFRONT ? 4 * half + i : i];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_plain(vc[i][j], M4, magic), as_half8(pb + 4 * j), d, 0,
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_plain(vw[j], M4, magic), as_half8(pb + 4 * j), d, 0,
                                                      0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[4 * half + i][r] = fmaf(o[4 * half + i][r], alpha, d[r] - vcst);
@@ -547,42 +577,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
 
-  // ---- this wave's partial result for its heads: part = split * kWaves + wave
+  // ---- combine the four waves' partials, then write this split's partial per head
+  __syncthreads();  // every wave is done with the loop's LDS
   if (col < NG) {
-    float* out = ws + (((size_t)b * H + h0 + col) * ((size_t)splits * kWaves) + (size_t)split * kWaves + wave) *
-                          (kD + 2);
+    float* pw = lds.part[wave][col];
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) out[16 * cb + 4 * blk + r] = o[cb][r];
+      for (int r = 0; r < 4; ++r) pw[16 * cb + 4 * blk + r] = o[cb][r];
     }
     if (blk == 0) {
-      out[kD] = m;
-      out[kD + 1] = l;
+      pw[kD] = m;
+      pw[kD + 1] = l;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < NG * kD; i += 256) {
+    const int g = i / kD, c = i - g * kD;
+    float M = -INFINITY;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds.part[w][g][kD]);
+    float Lsum = 0.0f, O = 0.0f;
+    for (int w = 0; w < kWaves; ++w) {
+      const float a = lds.part[w][g][kD] == -INFINITY ? 0.0f : exp2f(lds.part[w][g][kD] - M);
+      Lsum += lds.part[w][g][kD + 1] * a;
+      O += lds.part[w][g][c] * a;
+    }
+    float* out = ws + (((size_t)b * H + h0 + g) * splits + split) * (kD + 2);
+    out[c] = O;
+    if (c == 0) {
+      out[kD] = M;
+      out[kD + 1] = Lsum;
     }
   }
 }
 
 // One workgroup per (b, head): merge the splits, normalise, store fp16.
-// Threads take the splits 128 at a time (weights exp2(m_s - M) in LDS), and
-// each channel's sum over them keeps several independent loads in flight.
-__global__ __launch_bounds__(128) void kv_merge_kernel(const float* __restrict__ ws, int splits,
-                                                       uint16_t* __restrict__ out) {
-  __shared__ float red[128];
-  __shared__ float wgt[128];
+// 512 threads = 4 groups of 128 channels; the splits are taken 512 at a time
+// (weights exp2(m_s - M) in LDS) and dealt round-robin to the groups, whose
+// sums meet in LDS at the end.  Maxima and sums over threads: within each
+// wave by shuffles, then over the 8 waves in LDS.
+constexpr int kMergeThreads = 512, kMergeGroups = kMergeThreads / kD, kMergeWaves = kMergeThreads / 64;
+__global__ __launch_bounds__(kMergeThreads) void kv_merge_kernel(const float* __restrict__ ws, int splits,
+                                                                 uint16_t* __restrict__ out) {
+  __shared__ float wgt[kMergeThreads];
+  __shared__ float osum[kMergeGroups][kD];
+  __shared__ float wmax[kMergeWaves], wsum[kMergeWaves];
   const int bh = blockIdx.x, tid = threadIdx.x;
+  const int c = tid % kD, grp = tid / kD, wv = tid >> 6;
   const float* w = ws + (size_t)bh * splits * (kD + 2);
   float mloc = -INFINITY;
-  for (int s = tid; s < splits; s += 128) mloc = fmaxf(mloc, w[s * (kD + 2) + kD]);
-  red[tid] = mloc;
+  for (int s = tid; s < splits; s += kMergeThreads) mloc = fmaxf(mloc, w[s * (kD + 2) + kD]);
+  mloc = wave_max_f(mloc);
+  if ((tid & 63) == 0) wmax[wv] = mloc;
   __syncthreads();
-  for (int o = 64; o >= 1; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
-  }
-  const float M = red[0];
+  float M = wmax[0];
+#pragma unroll
+  for (int i = 1; i < kMergeWaves; ++i) M = fmaxf(M, wmax[i]);
   float O = 0.0f, lloc = 0.0f;
-  for (int base = 0; base < splits; base += 128) {
+  for (int base = 0; base < splits; base += kMergeThreads) {
     const int s = base + tid;
     float a = 0.0f;
     if (s < splits) {
@@ -590,22 +642,26 @@ __global__ __launch_bounds__(128) void kv_merge_kernel(const float* __restrict__
       a = ms == -INFINITY ? 0.0f : exp2f(ms - M);
       lloc += w[s * (kD + 2) + kD + 1] * a;
     }
-    __syncthreads();  // the previous chunk's weights are consumed
+    if (base > 0) __syncthreads();  // the previous chunk's weights are consumed
     wgt[tid] = a;
     __syncthreads();
-    const int n = min(128, splits - base);
-    const float* col = w + (size_t)base * (kD + 2) + tid;
+    const int n = min(kMergeThreads, splits - base);
+    const float* col = w + (size_t)base * (kD + 2) + c;
 #pragma unroll 8
-    for (int i = 0; i < n; ++i) O = fmaf(wgt[i], col[(size_t)i * (kD + 2)], O);
+    for (int i = grp; i < n; i += kMergeGroups) O = fmaf(wgt[i], col[(size_t)i * (kD + 2)], O);
   }
+  osum[grp][c] = O;
+  lloc = wave_sum_f(lloc);
+  if ((tid & 63) == 0) wsum[wv] = lloc;
   __syncthreads();
-  red[tid] = lloc;
-  __syncthreads();
-  for (int o = 64; o >= 1; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
+  if (grp == 0) {
+    float L = 0.0f, t = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMergeWaves; ++i) L += wsum[i];
+#pragma unroll
+    for (int j = 0; j < kMergeGroups; ++j) t += osum[j][c];
+    out[(size_t)bh * kD + c] = half_bits(t / L);
   }
-  out[(size_t)bh * kD + tid] = half_bits(O / red[0]);
 }
 
 }  // namespace
@@ -639,12 +695,16 @@ int kv_splits(int B, int H, int Hk, int T, int cus, int* pages_per_split) {
   const int P = T / kPage;
   const int gb = kv_heads_per_wg(H, Hk);
   const int64_t groups = (int64_t)B * (H / gb);
-  // enough workgroups for TKQ_KV_WG_PER_CU per CU (every wave streams its
-  // own pages; the merge of more splits costs little), at least one page per wave
+  // enough workgroups for a few per CU (every wave streams its own pages;
+  // the merge of more splits costs little), at least one page per wave
 #ifndef TKQ_KV_WG_PER_CU
 #define TKQ_KV_WG_PER_CU 4
 #endif
-  int64_t want = ((int64_t)TKQ_KV_WG_PER_CU * cus + groups - 1) / groups;
+#ifndef TKQ_KV_MFMA_WG_PER_CU
+#define TKQ_KV_MFMA_WG_PER_CU 4
+#endif
+  const int per_cu = kv_use_mfma(H, Hk) ? TKQ_KV_MFMA_WG_PER_CU : TKQ_KV_WG_PER_CU;
+  int64_t want = ((int64_t)per_cu * cus + groups - 1) / groups;
   int64_t max_splits = (P + kWaves - 1) / kWaves;
   if (want > max_splits) want = max_splits;
   if (want < 1) want = 1;
@@ -663,7 +723,7 @@ hipError_t launch_kv_decode(const uint16_t* q, const uint32_t* cache, int B, int
                        sm_scale * kLog2e, ws, splits, gb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kv_merge_kernel, dim3((uint32_t)(B * H)), dim3(128), 0, stream, ws, splits * kWaves, out);
+    hipLaunchKernelGGL(kv_merge_kernel, dim3((uint32_t)(B * H)), dim3(kMergeThreads), 0, stream, ws, splits, out);
     return hipGetLastError();
   }
   const dim3 grid((uint32_t)splits, (uint32_t)(H / gb), (uint32_t)B);
@@ -688,7 +748,7 @@ hipError_t launch_kv_decode(const uint16_t* q, const uint32_t* cache, int B, int
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kv_merge_kernel, dim3((uint32_t)(B * H)), dim3(128), 0, stream, ws, splits, out);
+  hipLaunchKernelGGL(kv_merge_kernel, dim3((uint32_t)(B * H)), dim3(kMergeThreads), 0, stream, ws, splits, out);
   return hipGetLastError();
 }
 
