@@ -336,6 +336,9 @@ struct Config {
 // over whole rounds, weighted by how efficiently the shape uses LDS bandwidth
 // per MFMA.  K is split (needs the workspace) only when the tiles cannot
 // fill every slot once: then the smallest split reaching ~80 % of the slots.
+#ifndef TKQ_PREFILL_SPLIT_SCORE
+#define TKQ_PREFILL_SPLIT_SCORE 1
+#endif
 Config choose(int64_t M, int64_t N, int64_t K, int cus, int64_t ws_floats) {
   struct Cand {
     int bm, bn, per_cu;
@@ -346,13 +349,29 @@ Config choose(int64_t M, int64_t N, int64_t K, int cus, int64_t ws_floats) {
 #endif
   const Cand cands[] = {{128, 256, 1, TKQ_PREFILL_BIG}, {256, 128, 1, TKQ_PREFILL_BIG}, {128, 128, 2, 1.0},
                         {128, 64, 2, 0.8},           {64, 128, 2, 0.8},           {64, 64, 4, 0.55}};
+  const int64_t ksteps = (K + BK - 1) / BK;
   Config best = {128, 128, 1, 1, 0};
   double best_score = -1.0;
   for (const Cand& c : cands) {
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
     const int64_t slots = (int64_t)cus * c.per_cu;
-    const int64_t rounds = (tiles + slots - 1) / slots;
-    const double score = double(tiles) / double(rounds * slots) * c.eff;
+#if TKQ_PREFILL_SPLIT_SCORE
+    // with a workspace, a shape that leaves slots idle may split K: score the
+    // pieces (s the smallest split that fills 80 % of the slots, as below)
+    int s = 1;
+    if (tiles < slots) {
+      for (int t = 2; t <= 8; ++t) {
+        if ((int64_t)t * M * N > ws_floats || t > ksteps / 4) break;
+        s = t;
+        if (tiles * t * 5 >= slots * 4) break;
+      }
+    }
+    const int64_t items = tiles * s;
+#else
+    const int64_t items = tiles;
+#endif
+    const int64_t rounds = (items + slots - 1) / slots;
+    const double score = double(items) / double(rounds * slots) * c.eff;
     if (score > best_score + 1e-9) {
       best_score = score;
       best = {c.bm, c.bn, 1, 1, 0};
@@ -360,7 +379,6 @@ Config choose(int64_t M, int64_t N, int64_t K, int cus, int64_t ws_floats) {
   }
   const int64_t tiles = ((M + best.bm - 1) / best.bm) * ((N + best.bn - 1) / best.bn);
   const int64_t slots = (int64_t)cus * (best.bm * best.bn > 128 * 128 ? 1 : best.bm * best.bn >= 128 * 64 ? 2 : 4);
-  const int64_t ksteps = (K + BK - 1) / BK;
   if (tiles < slots) {
     for (int s = 2; s <= 8; ++s) {
       if ((int64_t)s * M * N > ws_floats || s > ksteps / 4) break;
