@@ -54,15 +54,15 @@ TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 277317932, "ee50ac43d9a84272"),
                  "0.5b-tern": ("gemv", 135443283, "ee50ac43d9a84272"),
                  "bin": ("gemv", 130834588, "ee50ac43d9a84272"),
                  "7b-int4": ("gemv", 3801701729, "ee50ac43d9a84272"),
-                 "7b-prefill": ("prefill", 317402112, "73bbf72f750c4a2b"),
+                 "7b-prefill": ("prefill", 315186624, "b8cf25ab9ef698e9"),
                  "0.5b-hier": ("gemv", 279142307, "ee50ac43d9a84272"),
                  "0.5b-int2": ("gemv", 143167441, "ee50ac43d9a84272"),
                  "0.5b-int3": ("gemv", 231178228, "ee50ac43d9a84272"),
                  "0.5b-int4-greedy": ("gemv", 277013610, "ee50ac43d9a84272"),
                  "0.5b-int4-m16": ("small_m", 366697069, "2898a5db74d0d427"),
-                 "kv-32k": ("kv", 143375413, "70dcd9e591d4a31f"),
-                 "kv-32k-gqa": ("kv", 40152435, "70dcd9e591d4a31f"),
-                 "kv-128k-gqa": ("kv", 151350132, "70dcd9e591d4a31f")}
+                 "kv-32k": ("kv", 143389799, "e3bdce06252d1be7"),
+                 "kv-32k-gqa": ("kv", 37031590, "e3bdce06252d1be7"),
+                 "kv-128k-gqa": ("kv", 145082622, "e3bdce06252d1be7")}
 
 
 def traffic_family(workload):
