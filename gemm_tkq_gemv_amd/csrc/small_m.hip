@@ -88,14 +88,17 @@ struct SmallTile {
   int K, M, c, r;
 };
 
+// Groups at or past K load from an offset beyond the buffer (zeros, no
+// memory access): the loads stay unconditional, so the compiler can count
+// them and wait for exactly the ones a round consumes, not for the next
+// round's prefetch too.
+constexpr uint32_t kFar = 0x80000000u;
 __device__ __forceinline__ void load_round(const SmallTile& t, int kc, CodeBuf& b) {
-  const int ng = min(KC, t.K - kc) / 128;
 #pragma unroll
   for (int g = 0; g < GR; ++g) {
-    if (g < ng) {
-      b.q[g] = load16_nt(t.codes, t.lrow * t.row_bytes + (uint32_t)(kc + 128 * g) / 2u + 16u * t.c);
-      b.m[g] = load4(t.meta, t.lrow * t.meta_row + (uint32_t)((kc / 128 + g) * 4));
-    }
+    const bool ok = kc + 128 * g < t.K;  // uniform
+    b.q[g] = load16_nt(t.codes, ok ? t.lrow * t.row_bytes + (uint32_t)(kc + 128 * g) / 2u + 16u * t.c : kFar);
+    b.m[g] = load4(t.meta, ok ? t.lrow * t.meta_row + (uint32_t)((kc / 128 + g) * 4) : kFar);
   }
 }
 
@@ -173,13 +176,13 @@ __global__ __launch_bounds__(256) void small_m_kernel(const tkq_gemv_desc* __res
     __syncthreads();  // the previous round's reads of xs are done
     stage_x(t, kc, xs);
     __syncthreads();
-    if (kc + KC < K) load_round(t, kc + KC, b);
+    load_round(t, kc + KC, b);  // past K: no memory access
     compute_round(t, kc, a, xs, m0, m1, magic, acc);
     if (kc + KC >= K) break;
     __syncthreads();
     stage_x(t, kc + KC, xs);
     __syncthreads();
-    if (kc + 2 * KC < K) load_round(t, kc + 2 * KC, a);
+    load_round(t, kc + 2 * KC, a);
     compute_round(t, kc + KC, b, xs, m0, m1, magic, acc);
   }
 
