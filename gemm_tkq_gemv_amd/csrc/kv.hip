@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
   const int gq = H / Hk;                        // query heads per KV head
   const int hk = (hsub * G) / gq;               // this workgroup's KV head
   const int h0 = hsub * G;                      // first query head
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int quad = lane >> 2, sub = lane & 3;
   WaveLds& L = lds[wave];
   const Regs R = {in_sgpr(0x000F000Fu), in_sgpr(0x00F000F0u), in_vgpr(kMagic)};
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA
   const int split = blockIdx.x, hsub = blockIdx.y, b = blockIdx.z;
   const int gq = H / Hk;
   const int h0 = hsub * NG, hk = h0 / gq;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col = lane & 15, blk = lane >> 4;
   const uint32_t M4 = in_sgpr(0x000F000Fu), magic = in_vgpr(kMagic);
   for (int i = threadIdx.x; i < 16 * (kD / 2); i += 256) {
