@@ -23,6 +23,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// make_rsrc for [base + off, base + total) (empty past the end) from values
+// the caller knows to be wave-uniform but the compiler may not: they are
+// moved to scalar registers explicitly, so a load through the resource needs
+// no per-lane loop over distinct descriptors.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const char* base, uint32_t off,
+                                                                    uint32_t total) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base) + off;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(total > off ? total - off : 0u);
+  return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), n);
+}
+
 __device__ __forceinline__ u32x4 load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxNT);
 }

@@ -441,9 +441,8 @@ struct Runner {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t s = (uint32_t)(t.rbase + (st + u) * t.P);  // first row of the step (uniform)
-      const uint32_t oc = s * t.row_bytes, om = s * t.meta_row_bytes;
-      const __amdgpu_buffer_rsrc_t rc = make_rsrc(t.codes_ptr + oc, t.codes_bytes > oc ? t.codes_bytes - oc : 0u);
-      const __amdgpu_buffer_rsrc_t rm = make_rsrc(t.meta_ptr + om, t.meta_bytes > om ? t.meta_bytes - om : 0u);
+      const __amdgpu_buffer_rsrc_t rc = make_rsrc_uniform(t.codes_ptr, s * t.row_bytes, t.codes_bytes);
+      const __amdgpu_buffer_rsrc_t rm = make_rsrc_uniform(t.meta_ptr, s * t.meta_row_bytes, t.meta_bytes);
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         if constexpr (Cd::PLANES == 3) {
