@@ -49,20 +49,20 @@ TRAFFIC_SOURCES = {"gemv": ["gemm_tkq_gemv_amd/csrc/gemv.hip"] + _COMMON,
                    "prefill": ["gemm_tkq_gemv_amd/csrc/prefill.hip"] + _COMMON,
                    "kv": ["gemm_tkq_gemv_amd/csrc/kv.hip"] + _COMMON}
 # workload -> (kernel family, bytes per launch, sha256[:16] of that family's sources)
-TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 277317932, "ee50ac43d9a84272"),
-                 "0.5b-k5": ("gemv", 506989469, "ee50ac43d9a84272"),
-                 "0.5b-tern": ("gemv", 135443283, "ee50ac43d9a84272"),
-                 "bin": ("gemv", 130834588, "ee50ac43d9a84272"),
-                 "7b-int4": ("gemv", 3801701729, "ee50ac43d9a84272"),
-                 "7b-prefill": ("prefill", 315186624, "b8cf25ab9ef698e9"),
-                 "0.5b-hier": ("gemv", 279142307, "ee50ac43d9a84272"),
-                 "0.5b-int2": ("gemv", 143167441, "ee50ac43d9a84272"),
-                 "0.5b-int3": ("gemv", 231178228, "ee50ac43d9a84272"),
-                 "0.5b-int4-greedy": ("gemv", 277013610, "ee50ac43d9a84272"),
-                 "0.5b-int4-m16": ("small_m", 366697069, "2898a5db74d0d427"),
-                 "kv-32k": ("kv", 143389799, "e3bdce06252d1be7"),
-                 "kv-32k-gqa": ("kv", 37031590, "e3bdce06252d1be7"),
-                 "kv-128k-gqa": ("kv", 145082622, "e3bdce06252d1be7")}
+TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266603308, "e659fee0c64a130c"),
+                 "0.5b-k5": ("gemv", 506989133, "e659fee0c64a130c"),
+                 "0.5b-tern": ("gemv", 135443816, "e659fee0c64a130c"),
+                 "bin": ("gemv", 130534183, "e659fee0c64a130c"),
+                 "7b-int4": ("gemv", 3803123805, "e659fee0c64a130c"),
+                 "7b-prefill": ("prefill", 312961362, "2bfd4b5df2f5ff56"),
+                 "0.5b-hier": ("gemv", 268489133, "e659fee0c64a130c"),
+                 "0.5b-int2": ("gemv", 143168337, "e659fee0c64a130c"),
+                 "0.5b-int3": ("gemv", 231175257, "e659fee0c64a130c"),
+                 "0.5b-int4-greedy": ("gemv", 266674849, "e659fee0c64a130c"),
+                 "0.5b-int4-m16": ("small_m", 361945585, "805afb4e9f6907e5"),
+                 "kv-32k": ("kv", 143372410, "6db5e9bec22d91b3"),
+                 "kv-32k-gqa": ("kv", 37008110, "6db5e9bec22d91b3"),
+                 "kv-128k-gqa": ("kv", 145058724, "6db5e9bec22d91b3")}
 
 
 def traffic_family(workload):
