@@ -158,3 +158,26 @@ def test_gemv_bin_all_plus_x():
     xb = torch.zeros(K // 32, dtype=torch.int32, device="cuda")       # all +1
     y = tkq.gemv("bin", bits, None, xb, N, K).cpu().numpy()
     assert np.array_equal(y, K - 2 * (W < 0).sum(axis=1))
+
+
+# largest K each coding's GEMV accepts (the header's limits), and one past it
+MAX_GEMV_K = {"int4": 32768, "hier": 32768, "tern": 32768, "int2": 32768, "int3": 32768, "k5": 16384,
+              "bin": 262144}
+
+
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "bin", "hier", "int2", "int3"])
+def test_gemv_max_k(fmt):
+    """The longest rows a GEMV takes: 70 rows (ragged tiles) at the maximum K,
+    checked against the oracle; K one unit further is refused."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    K = MAX_GEMV_K[fmt]
+    W, x = _inputs(fmt, 70, K, 300)
+    (it,) = _items(torch, tkq, fmt, [(W, x)])
+    tkq.GemvBatch(fmt, [it]).run()
+    torch.cuda.synchronize()
+    _check(fmt, W, x, it["y"], it["codes"], it["meta"], "%s 70x%d" % (fmt, K))
+    unit = 32 if fmt in ("hier", "bin") else 128
+    big = dict(it, K=K + unit)
+    with pytest.raises(tkq.TkqError):
+        tkq.GemvBatch(fmt, [big])

@@ -64,3 +64,17 @@ def test_prefill_7b_mlp_full(name, split):
     diff = np.abs(y.float().cpu().numpy().astype(np.float64) - Y[7].float().cpu().numpy())
     w_deq = oracle_wdeq("int4", oc, om, K)
     assert np.all(diff <= 2 * oref.gemv_bound(w_deq, X[7].astype(np.float64)))
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_prefill_max_k(split):
+    """K = 2^20 (the header's limit): 16,384 K steps per tile without a
+    workspace, split over K with one."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    M, N, K = 65, 9, 1 << 20
+    W = inputs.normal_matrix((510, N, K), N, K)
+    X = np.random.default_rng((511, M, K)).standard_normal((M, K), dtype=np.float32).astype(np.float16)
+    _, _, Y = _run(torch, tkq, W, X, split)
+    oc, om = oracle_pack("int4", W)
+    _check(Y, X, oracle_wdeq("int4", oc, om, K), "%dx%dx%d" % (M, N, K))

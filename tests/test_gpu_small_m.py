@@ -112,3 +112,20 @@ def test_small_m_zero_tokens_are_zero_and_finite():
     assert np.all(np.isfinite(Y))
     assert np.all(Y[4] == 0) and np.all(Y[:, 3] == 0)
     _check(W, X, items[0]["y"], "zeros")
+
+
+def test_small_m_max_k():
+    """The longest rows the multi-token path takes (K = 2^20, the header's
+    limit): 9 rows, 16 tokens, 1024 staging rounds; K one group further is
+    refused."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    N, K, M = 9, 1 << 20, 16
+    W = inputs.normal_matrix((740, N, K), N, K)
+    X = _X(741, M, K)
+    items = _items(torch, tkq, [(W, X)], M)
+    tkq.GemvBatch("int4", items, tokens=M).run()
+    torch.cuda.synchronize()
+    _check(W, X, items[0]["y"], "M=16 9x2^20")
+    with pytest.raises(tkq.TkqError):
+        tkq.GemvBatch("int4", [dict(items[0], K=K + 128)], tokens=M)
