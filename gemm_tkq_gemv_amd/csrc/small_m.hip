@@ -102,18 +102,38 @@ __device__ __forceinline__ void load_round(const SmallTile& t, int kc, CodeBuf& 
   }
 }
 
-// Stage X[0..M)[kc, kc + KC) into LDS in the unpack's k order.
+// Stage X[0..M)[kc, kc + KC) into LDS in the unpack's k order.  Each
+// thread issues the loads of SB units before writing any of them, so a
+// round's staging costs ceil(units / (256 SB)) memory round trips rather
+// than one per unit (units past the end read beyond the buffer: zeros).
+#ifndef TKQ_SMALL_SB
+#define TKQ_SMALL_SB 4
+#endif
+constexpr int SB = TKQ_SMALL_SB;
 __device__ __forceinline__ void stage_x(const SmallTile& t, int kc, _Float16* xs) {
   const int units = min(KC, t.K - kc) / 8;  // 8-column units per token row
-  for (int u = threadIdx.x; u < t.M * units; u += 64 * kWaves) {
-    const int m = u / units, e = u - m * units;
-    const u32x4 v = load16(t.x, (uint32_t)(m * t.K + kc + 8 * e) * 2u);
-    u32x4 p;
-    p[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);  // (x0, x4)
-    p[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);  // (x1, x5)
-    p[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);  // (x2, x6)
-    p[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);  // (x3, x7)
-    *reinterpret_cast<u32x4*>(&xs[m * kLdsRow + 8 * e]) = p;
+  const int total = t.M * units;
+  for (int base = 0; base < total; base += 64 * kWaves * SB) {  // uniform trip count
+    u32x4 v[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const int u = base + 64 * kWaves * j + (int)threadIdx.x;
+      const int m = u / units, e = u - m * units;
+      v[j] = load16(t.x, u < total ? (uint32_t)(m * t.K + kc + 8 * e) * 2u : kFar);
+    }
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const int u = base + 64 * kWaves * j + (int)threadIdx.x;
+      if (u < total) {
+        const int m = u / units, e = u - m * units;
+        u32x4 p;
+        p[0] = __builtin_amdgcn_perm(v[j][2], v[j][0], 0x05040100u);  // (x0, x4)
+        p[1] = __builtin_amdgcn_perm(v[j][2], v[j][0], 0x07060302u);  // (x1, x5)
+        p[2] = __builtin_amdgcn_perm(v[j][3], v[j][1], 0x05040100u);  // (x2, x6)
+        p[3] = __builtin_amdgcn_perm(v[j][3], v[j][1], 0x07060302u);  // (x3, x7)
+        *reinterpret_cast<u32x4*>(&xs[m * kLdsRow + 8 * e]) = p;
+      }
+    }
   }
 }
 
