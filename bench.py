@@ -59,7 +59,7 @@ TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266603308, "e659fee0c64a130c"),
                  "0.5b-int2": ("gemv", 143168337, "e659fee0c64a130c"),
                  "0.5b-int3": ("gemv", 231175257, "e659fee0c64a130c"),
                  "0.5b-int4-greedy": ("gemv", 266674849, "e659fee0c64a130c"),
-                 "0.5b-int4-m16": ("small_m", 361945585, "805afb4e9f6907e5"),
+                 "0.5b-int4-m16": ("small_m", 363003491, "6ee15677617400bc"),
                  "kv-32k": ("kv", 143372410, "6db5e9bec22d91b3"),
                  "kv-32k-gqa": ("kv", 37008110, "6db5e9bec22d91b3"),
                  "kv-128k-gqa": ("kv", 145058724, "6db5e9bec22d91b3")}
