@@ -526,7 +526,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the batch-1 GEMV needs no collectives, and "
-              "this build runs on a single MI355X.  Use --gpus 1.", file=sys.stderr)
+              "the library runs each launch on a single MI355X.  Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
