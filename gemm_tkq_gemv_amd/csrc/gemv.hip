@@ -51,8 +51,13 @@ namespace tkq {
 
 namespace {
 
-#ifndef TKQ_GEMV_PINGPONG
-#define TKQ_GEMV_PINGPONG 0
+// Codings (bit fmt) whose runner keeps two load buffers, the next row steps'
+// loads in flight while the current ones are computed (measured per coding:
+// 1-2 % faster for int4, K5 and binary; slower for ternary, int2, int3 and
+// the greedy variant and equal for hier-g32, which keep one buffer and more
+// waves).
+#ifndef TKQ_GEMV_PINGPONG_MASK
+#define TKQ_GEMV_PINGPONG_MASK ((1 << 1) | (1 << 2) | (1 << 4))
 #endif
 #ifndef TKQ_GEMV_WPE
 #define TKQ_GEMV_WPE 1  // minimum waves per SIMD the register budget must allow
@@ -526,31 +531,33 @@ struct Runner {
     }
   }
 
+  static constexpr bool kPingpong = (((TKQ_GEMV_PINGPONG_MASK) >> FMT) & 1) && !GREEDY;
+
   __device__ __forceinline__ void run(uint32_t* part) {
-#if TKQ_GEMV_PINGPONG
-    // Two buffers used alternately: the loads of step st + U are in flight
-    // while step st is computed.
-    Buf a, b;
-    issue(0, a);  // the first codes stream in while x is prepared
-    load_x();
-    for (int st = 0; st < t.steps; st += 2 * U) {
-      if (st + U < t.steps) issue(st + U, b);
-      compute(st, a, part);
-      if (st + U >= t.steps) break;
-      if (st + 2 * U < t.steps) issue(st + 2 * U, a);
-      compute(st + U, b, part);
+    if constexpr (kPingpong) {
+      // Two buffers used alternately: the loads of step st + U are in flight
+      // while step st is computed.
+      Buf a, b;
+      issue(0, a);  // the first codes stream in while x is prepared
+      load_x();
+      for (int st = 0; st < t.steps; st += 2 * U) {
+        if (st + U < t.steps) issue(st + U, b);
+        compute(st, a, part);
+        if (st + U >= t.steps) break;
+        if (st + 2 * U < t.steps) issue(st + 2 * U, a);
+        compute(st + U, b, part);
+      }
+    } else {
+      // One buffer: U row steps are loaded, then computed; the other waves of
+      // the CU keep the memory system busy meanwhile.
+      Buf a;
+      issue(0, a);  // the first codes stream in while x is prepared
+      load_x();
+      for (int st = 0; st < t.steps; st += U) {
+        if (st > 0) issue(st, a);
+        compute(st, a, part);
+      }
     }
-#else
-    // One buffer: U row steps are loaded, then computed; the other waves of
-    // the CU keep the memory system busy meanwhile.
-    Buf a;
-    issue(0, a);  // the first codes stream in while x is prepared
-    load_x();
-    for (int st = 0; st < t.steps; st += U) {
-      if (st > 0) issue(st, a);
-      compute(st, a, part);
-    }
-#endif
   }
 };
 
