@@ -44,7 +44,7 @@ struct PlanParams {
 #define TKQ_SMALL_TILE_KB 4
 #endif
 #ifndef TKQ_TAIL_MB
-#define TKQ_TAIL_MB 40
+#define TKQ_TAIL_MB 60
 #endif
 PlanParams plan_params(int fmt) {
   if (fmt == TKQ_FMT_INT4_G128 || fmt == TKQ_FMT_INT4_HIER_G32)
