@@ -49,20 +49,20 @@ TRAFFIC_SOURCES = {"gemv": ["gemm_tkq_gemv_amd/csrc/gemv.hip"] + _COMMON,
                    "prefill": ["gemm_tkq_gemv_amd/csrc/prefill.hip"] + _COMMON,
                    "kv": ["gemm_tkq_gemv_amd/csrc/kv.hip"] + _COMMON}
 # workload -> (kernel family, bytes per launch, sha256[:16] of that family's sources)
-TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266603308, "e659fee0c64a130c"),
-                 "0.5b-k5": ("gemv", 506989133, "e659fee0c64a130c"),
-                 "0.5b-tern": ("gemv", 135443816, "e659fee0c64a130c"),
-                 "bin": ("gemv", 130534183, "e659fee0c64a130c"),
-                 "7b-int4": ("gemv", 3803123805, "e659fee0c64a130c"),
-                 "7b-prefill": ("prefill", 312961362, "2bfd4b5df2f5ff56"),
-                 "0.5b-hier": ("gemv", 268489133, "e659fee0c64a130c"),
-                 "0.5b-int2": ("gemv", 143168337, "e659fee0c64a130c"),
-                 "0.5b-int3": ("gemv", 231175257, "e659fee0c64a130c"),
-                 "0.5b-int4-greedy": ("gemv", 266674849, "e659fee0c64a130c"),
-                 "0.5b-int4-m16": ("small_m", 363003491, "6ee15677617400bc"),
-                 "kv-32k": ("kv", 143372410, "6db5e9bec22d91b3"),
-                 "kv-32k-gqa": ("kv", 37008110, "6db5e9bec22d91b3"),
-                 "kv-128k-gqa": ("kv", 145058724, "6db5e9bec22d91b3")}
+TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266568800, "81df76e0b6b1049d"),
+                 "0.5b-k5": ("gemv", 506969695, "81df76e0b6b1049d"),
+                 "0.5b-tern": ("gemv", 135443764, "81df76e0b6b1049d"),
+                 "bin": ("gemv", 123783433, "81df76e0b6b1049d"),
+                 "7b-int4": ("gemv", 3787502246, "81df76e0b6b1049d"),
+                 "7b-prefill": ("prefill", 313632554, "2d7378f14da2d78f"),
+                 "0.5b-hier": ("gemv", 268450016, "81df76e0b6b1049d"),
+                 "0.5b-int2": ("gemv", 143168522, "81df76e0b6b1049d"),
+                 "0.5b-int3": ("gemv", 231213059, "81df76e0b6b1049d"),
+                 "0.5b-int4-greedy": ("gemv", 266670593, "81df76e0b6b1049d"),
+                 "0.5b-int4-m16": ("small_m", 362982917, "a64711cba57dfea2"),
+                 "kv-32k": ("kv", 143372582, "8c9804f2d6da7d5d"),
+                 "kv-32k-gqa": ("kv", 37008058, "8c9804f2d6da7d5d"),
+                 "kv-128k-gqa": ("kv", 145058718, "8c9804f2d6da7d5d")}
 
 
 def traffic_family(workload):
