@@ -442,10 +442,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA
     for (int i = 0; i < 8; ++i) vc[i] = load16_nt(pg, (uint32_t)(kVC + 16 * (16 * i + col) + 4 * blk) * 4u);
     *reinterpret_cast<u32x4*>(&meta[4 * lane]) = mt;
 #else
-    *reinterpret_cast<u32x4*>(&meta[4 * lane]) = load16(pg, (uint32_t)(kKM + 4 * lane) * 4u);
+    // the K codes are requested before the metadata is stored to LDS, so
+    // both arrive in one round trip
+    const u32x4 mt = load16(pg, (uint32_t)(kKM + 4 * lane) * 4u);
     u32x4 kc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) kc[i] = load16_nt(pg, (uint32_t)(kKC + 16 * (16 * i + col) + 4 * blk) * 4u);
+    *reinterpret_cast<u32x4*>(&meta[4 * lane]) = mt;
 #endif
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
