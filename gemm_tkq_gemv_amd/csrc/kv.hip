@@ -171,15 +171,18 @@ struct WaveLds {
                                 // independent of the number of heads)
 };
 
-// G: query heads per workgroup (1..8, all reading the same KV head).  Workspace per (b, head, split):
-// {m, l, o[128]} with o unnormalised relative to m (base-2 exponent).
-template <int G>
+// KUP (one query head only): the page's K codes are requested in the same
+// round trip as its metadata.  The registers they take cost a wave per SIMD
+// (134 VGPRs): measured +7 % when every wave has one page, -11 % with two,
+// so the host picks it by pages per wave.
+template <int G, bool KUP = false>
 __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restrict__ q,
                                                         const uint32_t* __restrict__ cache, int H, int Hk, int P,
                                                         int pages_per_split, float scale_log2,
                                                         float* __restrict__ ws, int splits) {
   __shared__ WaveLds lds[kWaves];
   __shared__ float merge[kWaves][G][kD + 2];
+  constexpr bool kKUp = KUP && G == 1;
   const int split = blockIdx.x, hsub = blockIdx.y, b = blockIdx.z;
   const int gq = H / Hk;                        // query heads per KV head
   const int hk = (hsub * G) / gq;               // this workgroup's KV head
@@ -210,7 +213,13 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
   for (int p = p0 + wave; p < p1; p += kWaves) {
     const __amdgpu_buffer_rsrc_t pg = make_rsrc(base + (size_t)p * kPageWords, kPageWords * 4u);
     // page metadata -> LDS (one 16-byte load per lane covers all 256 words)
-    *reinterpret_cast<u32x4*>(&L.meta[4 * lane]) = load16(pg, (uint32_t)(kKM + 4 * lane) * 4u);
+    const u32x4 mt = load16(pg, (uint32_t)(kKM + 4 * lane) * 4u);
+    u32x4 kall[kKUp ? 8 : 1];
+    if constexpr (kKUp) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kall[i] = load16_nt(pg, (uint32_t)(kKC + 16 * (16 * i + quad) + 4 * sub) * 4u);
+    }
+    *reinterpret_cast<u32x4*>(&L.meta[4 * lane]) = mt;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     // The query heads one after another: the page comes from HBM for the
@@ -250,8 +259,10 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
         for (int half = 0; half < 2; ++half) {
           u32x4 kc[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            kc[i] = load16_nt(pg, (uint32_t)(kKC + 16 * (16 * (4 * half + i) + quad) + 4 * sub) * 4u);
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (kKUp) kc[i] = kall[kKUp ? 4 * half + i : 0];
+            else kc[i] = load16_nt(pg, (uint32_t)(kKC + 16 * (16 * (4 * half + i) + quad) + 4 * sub) * 4u);
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) sc[4 * half + i] = quad_sum(chunk_dot(kc[i], qp, R) - cst) * scale_log2;
         }
@@ -737,7 +748,14 @@ hipError_t launch_kv_decode(const uint16_t* q, const uint32_t* cache, int B, int
     hipLaunchKernelGGL(kv_decode_kernel<G>, grid, dim3(256), 0, stream, q, cache, H, Hk, P, pages_per_split, sl2, \
                        ws, splits);                                                                            \
     break;
-    TKQ_KV_CASE(1)
+    case 1:
+      if (pages_per_split <= kWaves)  // one page per wave: K codes with the metadata
+        hipLaunchKernelGGL((kv_decode_kernel<1, true>), grid, dim3(256), 0, stream, q, cache, H, Hk, P,
+                           pages_per_split, sl2, ws, splits);
+      else
+        hipLaunchKernelGGL((kv_decode_kernel<1, false>), grid, dim3(256), 0, stream, q, cache, H, Hk, P,
+                           pages_per_split, sl2, ws, splits);
+      break;
     TKQ_KV_CASE(2)
     TKQ_KV_CASE(3)
     TKQ_KV_CASE(4)

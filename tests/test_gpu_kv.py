@@ -69,6 +69,7 @@ def test_kv_pack_bit_exact(B, T, Hk):
     (1, 32, 2, 1024),       # 16 per KV head: one full matrix-core tile of heads
     (2, 6, 2, 256),         # 3 per KV head (the smallest group on the matrix-core path)
     (1, 1, 1, 128),         # one page
+    (1, 32, 32, 32768),     # MHA, 32k tokens: several pages per wave (the other one-head kernel variant)
 ])
 def test_kv_decode_matches_oracle(B, H, Hk, T):
     torch = gpu_or_skip()
