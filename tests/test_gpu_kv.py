@@ -70,6 +70,7 @@ def test_kv_pack_bit_exact(B, T, Hk):
     (2, 6, 2, 256),         # 3 per KV head (the smallest group on the matrix-core path)
     (1, 1, 1, 128),         # one page
     (1, 32, 32, 32768),     # MHA, 32k tokens: several pages per wave (the other one-head kernel variant)
+    (1, 32, 8, 131072),     # GQA, 128k tokens: several pages per wave on the matrix-core path
 ])
 def test_kv_decode_matches_oracle(B, H, Hk, T):
     torch = gpu_or_skip()
