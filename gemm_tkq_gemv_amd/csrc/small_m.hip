@@ -17,7 +17,9 @@
 //    through registers only.  The chunk is unpacked with the fp16 magic
 //    number (1024 + m * code), shifted by the zero point (exact small
 //    integers) and scaled (one fp16 rounding of s * (q - z)).
-//  * The tokens' x slices are staged through LDS, KC columns per round, in
+//  * The tokens' x slices are staged through LDS, KC columns per round (512
+//    for M > 8: fewer registers and more waves, +3-5 % at M = 16; 1024 for
+//    M <= 8, where longer rounds measured equal or better), in
 //    the k order the unpack produces (0, 4, 1, 5, 2, 6, 3, 7 within each 8),
 //    and read as the B operands (lane l: token l % 16, k-block l / 16).
 //    Lanes of tokens >= M contribute zeros.
@@ -38,12 +40,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kTileRows = kSmallTileRows;  // 16 rows per wave
-#ifndef TKQ_SMALL_KC
-#define TKQ_SMALL_KC 1024
+#ifndef TKQ_SMALL_KC_BIG_M
+#define TKQ_SMALL_KC_BIG_M 512  // columns of X staged per round for M > TKQ_SMALL_KC_SPLIT
 #endif
-constexpr int KC = TKQ_SMALL_KC;  // columns of X staged per round
-constexpr int GR = KC / 128;      // quantization groups per round
-constexpr int kLdsRow = KC + 8;   // halves per staged token row (16 bytes of padding)
+#ifndef TKQ_SMALL_KC_SMALL_M
+#define TKQ_SMALL_KC_SMALL_M 1024
+#endif
+#ifndef TKQ_SMALL_KC_SPLIT
+#define TKQ_SMALL_KC_SPLIT 8
+#endif
+template <int KC>
+constexpr int lds_row() { return KC + 8; }  // halves per staged token row (16 bytes of padding)
 #ifndef TKQ_SMALL_ACC
 #define TKQ_SMALL_ACC 1
 #endif
@@ -77,7 +84,9 @@ __device__ __forceinline__ half8 dequant_word(uint32_t w, uint32_t m0, uint32_t 
   return __builtin_bit_cast(half8, v);
 }
 
+template <int KC>
 struct CodeBuf {
+  static constexpr int GR = KC / 128;  // quantization groups per round
   u32x4 q[GR];
   uint32_t m[GR];
 };
@@ -93,9 +102,10 @@ struct SmallTile {
 // them and wait for exactly the ones a round consumes, not for the next
 // round's prefetch too.
 constexpr uint32_t kFar = 0x80000000u;
-__device__ __forceinline__ void load_round(const SmallTile& t, int kc, CodeBuf& b) {
+template <int KC>
+__device__ __forceinline__ void load_round(const SmallTile& t, int kc, CodeBuf<KC>& b) {
 #pragma unroll
-  for (int g = 0; g < GR; ++g) {
+  for (int g = 0; g < KC / 128; ++g) {
     const bool ok = kc + 128 * g < t.K;  // uniform
     b.q[g] = load16_nt(t.codes, ok ? t.lrow * t.row_bytes + (uint32_t)(kc + 128 * g) / 2u + 16u * t.c : kFar);
     b.m[g] = load4(t.meta, ok ? t.lrow * t.meta_row + (uint32_t)((kc / 128 + g) * 4) : kFar);
@@ -110,7 +120,9 @@ __device__ __forceinline__ void load_round(const SmallTile& t, int kc, CodeBuf& 
 #define TKQ_SMALL_SB 4
 #endif
 constexpr int SB = TKQ_SMALL_SB;
+template <int KC>
 __device__ __forceinline__ void stage_x(const SmallTile& t, int kc, _Float16* xs) {
+  constexpr int kLdsRow = lds_row<KC>();
   const int units = min(KC, t.K - kc) / 8;  // 8-column units per token row
   const int total = t.M * units;
   for (int base = 0; base < total; base += 64 * kWaves * SB) {  // uniform trip count
@@ -137,12 +149,14 @@ __device__ __forceinline__ void stage_x(const SmallTile& t, int kc, _Float16* xs
   }
 }
 
-__device__ __forceinline__ void compute_round(const SmallTile& t, int kc, const CodeBuf& b, const _Float16* xs,
+template <int KC>
+__device__ __forceinline__ void compute_round(const SmallTile& t, int kc, const CodeBuf<KC>& b, const _Float16* xs,
                                               uint32_t m0, uint32_t m1, uint32_t magic, f32x4 (&acc)[NACC]) {
+  constexpr int kLdsRow = lds_row<KC>();
   const int ng = min(KC, t.K - kc) / 128;
   const bool live_token = t.r < t.M;
 #pragma unroll
-  for (int g = 0; g < GR; ++g) {
+  for (int g = 0; g < KC / 128; ++g) {
     if (g < ng) {
       const hv2 s = {h2(b.m[g])[0], h2(b.m[g])[0]};
       const _Float16 z = h2(b.m[g])[1];
@@ -159,8 +173,9 @@ __device__ __forceinline__ void compute_round(const SmallTile& t, int kc, const 
   }
 }
 
+template <int KC>
 __global__ __launch_bounds__(256) void small_m_kernel(const tkq_gemv_desc* __restrict__ descs, int count, int M) {
-  __shared__ __attribute__((aligned(16))) _Float16 xs[16 * kLdsRow];
+  __shared__ __attribute__((aligned(16))) _Float16 xs[16 * lds_row<KC>()];
 
   const int tile = blockIdx.x;
   int lo = 0, hi = count - 1;
@@ -190,17 +205,17 @@ __global__ __launch_bounds__(256) void small_m_kernel(const tkq_gemv_desc* __res
   f32x4 acc[NACC];
 #pragma unroll
   for (int i = 0; i < NACC; ++i) acc[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  CodeBuf a, b;
+  CodeBuf<KC> a, b;
   load_round(t, 0, a);
   for (int kc = 0; kc < K; kc += 2 * KC) {
     __syncthreads();  // the previous round's reads of xs are done
-    stage_x(t, kc, xs);
+    stage_x<KC>(t, kc, xs);
     __syncthreads();
     load_round(t, kc + KC, b);  // past K: no memory access
     compute_round(t, kc, a, xs, m0, m1, magic, acc);
     if (kc + KC >= K) break;
     __syncthreads();
-    stage_x(t, kc + KC, xs);
+    stage_x<KC>(t, kc + KC, xs);
     __syncthreads();
     load_round(t, kc + 2 * KC, a);
     compute_round(t, kc + KC, b, xs, m0, m1, magic, acc);
@@ -222,7 +237,12 @@ __global__ __launch_bounds__(256) void small_m_kernel(const tkq_gemv_desc* __res
 }  // namespace
 
 hipError_t launch_small_m(const tkq_gemv_desc* dev_descs, int count, int64_t tiles, int M, hipStream_t stream) {
-  hipLaunchKernelGGL(small_m_kernel, dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream, dev_descs, count, M);
+  if (M > TKQ_SMALL_KC_SPLIT)
+    hipLaunchKernelGGL(small_m_kernel<TKQ_SMALL_KC_BIG_M>, dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream,
+                       dev_descs, count, M);
+  else
+    hipLaunchKernelGGL(small_m_kernel<TKQ_SMALL_KC_SMALL_M>, dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream,
+                       dev_descs, count, M);
   return hipGetLastError();
 }
 
