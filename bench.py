@@ -59,7 +59,7 @@ TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266568800, "81df76e0b6b1049d"),
                  "0.5b-int2": ("gemv", 143168522, "81df76e0b6b1049d"),
                  "0.5b-int3": ("gemv", 231213059, "81df76e0b6b1049d"),
                  "0.5b-int4-greedy": ("gemv", 266670593, "81df76e0b6b1049d"),
-                 "0.5b-int4-m16": ("small_m", 362982917, "a64711cba57dfea2"),
+                 "0.5b-int4-m16": ("small_m", 389523703, "4ad0080035152d2f"),
                  "kv-32k": ("kv", 143371933, "df773ea2078ca49e"),
                  "kv-4k": ("kv", 18194357, "df773ea2078ca49e"),
                  "kv-32k-gqa": ("kv", 37018468, "df773ea2078ca49e"),
