@@ -135,36 +135,65 @@ def build_sweep(torch, tkq, inputs, model, fmt):
     return items, shapes
 
 
-def rotated_batches(torch, tkq, fmt, items, footprint):
-    """Distinct copies of the packed weights (>= 1 GiB total), one batch each."""
-    copies = max(1, math.ceil(ROTATE_BYTES / footprint))
-    batches = [tkq.GemvBatch(fmt, items)]
-    for _ in range(copies - 1):
-        clone = [dict(it, codes=it["codes"].clone(),
-                      meta=None if it["meta"] is None else it["meta"].clone()) for it in items]
-        batches.append(tkq.GemvBatch(fmt, clone))
+def launch_groups(shapes, launch):
+    """Index groups of the sweep, one GEMV launch per group: "grouped" = the
+    whole sweep in one launch; "staged" = per layer q,k,v | o | gate,up |
+    down, then the output projection (4 * layers + 1 launches); "per-matrix"
+    = one launch per matrix."""
+    n = len(shapes)
+    if launch == "grouped":
+        return [list(range(n))]
+    if launch == "per-matrix":
+        return [[i] for i in range(n)]
+    groups = []
+    for i0 in range(0, n - 1, 7):    # q k v o gate up down of one layer
+        groups += [[i0, i0 + 1, i0 + 2], [i0 + 3], [i0 + 4, i0 + 5], [i0 + 6]]
+    return groups + [[n - 1]]
+
+
+def rotated_batches(torch, tkq, fmt, items, footprint, copies=None, launch="grouped", shapes=None):
+    """Distinct copies of the packed weights (>= 1 GiB total unless `copies`
+    is given; 1 = cache-resident), each a list of prepared launches."""
+    if copies is None:
+        copies = max(1, math.ceil(ROTATE_BYTES / footprint))
+    groups = launch_groups(shapes, launch) if shapes is not None else [list(range(len(items)))]
+    out = []
+    for c in range(copies):
+        its = items if c == 0 else [dict(it, codes=it["codes"].clone(),
+                                         meta=None if it["meta"] is None else it["meta"].clone()) for it in items]
+        out.append([tkq.GemvBatch(fmt, [its[i] for i in g]) for g in groups])
     torch.cuda.synchronize()
-    return batches
+    return out
 
 
-def time_steps(torch, run_step, steps, warmup, graph="none", period=1):
+SWEEP_STATS = {}
+
+
+def time_steps(torch, run_step, steps, warmup, graph="none", period=1, group=10):
     """Warm up, then time exactly `steps` steps between synchronisations with
     HIP events recorded on the stream the kernels are launched on.
 
     graph="step": each of the `period` distinct steps (rotation copies) is
     captured once as a HIP graph and step s replays graph s % period;
     graph="all": the `steps` timed steps are captured as one graph that is
-    replayed once inside the timed region (warm-up steps run eagerly)."""
+    replayed once inside the timed region (warm-up steps run eagerly).
+    Without "all", an event every `group` steps also gives the per-step
+    median, p10 and p90 over the groups (SWEEP_STATS)."""
     for s in range(warmup):
         run_step(s)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    marks = []
     if graph == "none":
         start.record(stream)
         for s in range(steps):
             run_step(s)
+            if (s + 1) % group == 0 and s + 1 < steps:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                marks.append(e)
         end.record(stream)
     elif graph == "step":
         graphs = []
@@ -177,6 +206,10 @@ def time_steps(torch, run_step, steps, warmup, graph="none", period=1):
         start.record(stream)
         for s in range(steps):
             graphs[s % period].replay()
+            if (s + 1) % group == 0 and s + 1 < steps:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                marks.append(e)
         end.record(stream)
     else:
         g = torch.cuda.CUDAGraph()
@@ -188,6 +221,13 @@ def time_steps(torch, run_step, steps, warmup, graph="none", period=1):
         g.replay()
         end.record(stream)
     torch.cuda.synchronize()
+    SWEEP_STATS.clear()
+    if marks:
+        pts = [start] + marks
+        per = sorted(a.elapsed_time(b) / group for a, b in zip(pts, pts[1:]))
+        q = lambda f: per[min(len(per) - 1, int(f * len(per)))]  # noqa: E731
+        SWEEP_STATS.update(median_us=round(q(0.5) * 1e3, 3), p10_us=round(q(0.1) * 1e3, 3),
+                           p90_us=round(q(0.9) * 1e3, 3), groups=len(per), steps_per_group=group)
     return start.elapsed_time(end) / steps  # ms per step
 
 
@@ -283,14 +323,17 @@ def run_sweep(args, torch, tkq, inputs, model, fmt, greedy=False):
     footprint = sum(it["codes"].numel() * it["codes"].element_size()
                     + (0 if it["meta"] is None else it["meta"].numel() * it["meta"].element_size())
                     for it in items)
-    batches = rotated_batches(torch, tkq, fmt, items, footprint)
+    launch = "grouped" if greedy else args.launch
+    batches = rotated_batches(torch, tkq, fmt, items, footprint, args.copies, launch, shapes)
     if greedy:
         token = torch.zeros(1, dtype=torch.int32, device="cuda")
-        scratch = batches[0].greedy_scratch()
+        scratch = batches[0][0].greedy_scratch()
         last = len(items) - 1
-        step = lambda s: batches[s % len(batches)].run_argmax(last, token, scratch)  # noqa: E731
+        step = lambda s: batches[s % len(batches)][0].run_argmax(last, token, scratch)  # noqa: E731
     else:
-        step = lambda s: batches[s % len(batches)].run()  # noqa: E731
+        def step(s):
+            for b in batches[s % len(batches)]:
+                b.run()
     ms = time_steps(torch, step, args.steps, args.warmup, args.graph, len(batches))
     gbs = step_bytes / (ms * 1e-3) / 1e9
     ceiling_tok_s = HBM_PEAK_GBS * 1e9 / step_bytes
@@ -300,18 +343,25 @@ def run_sweep(args, torch, tkq, inputs, model, fmt, greedy=False):
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic: seeded N(0,0.02) weights at the model's shapes, N(0,1) fp16 x",
-        "config": {"workload": "%s decode weight sweep, %s, %d GEMVs in one launch, batch 1%s"
+        "config": {"workload": "%s decode weight sweep, %s, %d GEMVs %s, batch 1%s"
                                % (model, _fmt_name(fmt), len(shapes),
+                                  {"grouped": "in one launch",
+                                   "staged": "in %d launches (per layer q,k,v | o | gate,up | down, then the "
+                                             "output projection)" % len(batches[0]),
+                                   "per-matrix": "in one launch each"}[launch],
                                   ", greedy token selected on the GPU in the same launch" if greedy else ""),
                    "bytes_per_step": step_bytes, "copies_rotated": len(batches),
+                   "cache_resident": len(batches) == 1 and args.copies == 1,
                    "weights": _fmt_name(fmt), "x": "fp16", "accumulate": "fp32", "y": "fp16",
-                   "launch": "hip graph replay" if args.graph != "none" else "stream launch"},
+                   "launch": launch + (", hip graph replay" if args.graph != "none" else ", stream launch")},
+        "sweep_us": dict(SWEEP_STATS),
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tok_s": round(1000.0 / ms, 1), "ceiling_tok_s": round(ceiling_tok_s, 1),
         "frac_of_ceiling": round((1000.0 / ms) / ceiling_tok_s, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": args.traffic if args.traffic is not None else measured_traffic(args.workload)},
+                     "traffic": args.traffic if args.traffic is not None else
+                     (measured_traffic(args.workload) if launch == "grouped" and args.copies is None else None)},
         "kernel": "gemv_kernel<%d>" % tkq.FORMATS[fmt],
     }
     del items, batches
@@ -421,7 +471,7 @@ def run_binary(args, torch, tkq, inputs):
                           N=N, K=K))
     step_bytes = sum(_fmt_bytes("bin")(n, k) for n, k in inputs.BINARY_SHAPES)
     footprint = sum(it["codes"].numel() * 4 for it in items)
-    batches = rotated_batches(torch, tkq, "bin", items, footprint)
+    batches = [b[0] for b in rotated_batches(torch, tkq, "bin", items, footprint)]
     ms = time_steps(torch, lambda s: batches[s % len(batches)].run(), args.steps, args.warmup,
                     args.graph, len(batches))
     gbs = step_bytes / (ms * 1e-3) / 1e9
@@ -516,6 +566,11 @@ def main():
                              "7b-int4", "7b-hier", "7b-prefill", "probe"])
     ap.add_argument("--graph", default="none", choices=["none", "step", "all"],
                     help="launch steps as HIP graph replays (see time_steps)")
+    ap.add_argument("--launch", default="grouped", choices=["grouped", "staged", "per-matrix"],
+                    help="weight sweeps: one grouped launch (the measured path), per-layer stages, or one "
+                         "launch per matrix (shows the launch cost; combine with --graph step)")
+    ap.add_argument("--copies", type=int, default=None,
+                    help="weight copies rotated (default: enough for >= 1 GiB; 1 = cache-resident)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
