@@ -49,16 +49,16 @@ TRAFFIC_SOURCES = {"gemv": ["gemm_tkq_gemv_amd/csrc/gemv.hip"] + _COMMON,
                    "prefill": ["gemm_tkq_gemv_amd/csrc/prefill.hip"] + _COMMON,
                    "kv": ["gemm_tkq_gemv_amd/csrc/kv.hip"] + _COMMON}
 # workload -> (kernel family, bytes per launch, sha256[:16] of that family's sources)
-TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266568800, "81df76e0b6b1049d"),
-                 "0.5b-k5": ("gemv", 506969695, "81df76e0b6b1049d"),
-                 "0.5b-tern": ("gemv", 135443764, "81df76e0b6b1049d"),
-                 "bin": ("gemv", 123783433, "81df76e0b6b1049d"),
-                 "7b-int4": ("gemv", 3787502246, "81df76e0b6b1049d"),
+TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266566507, "44ff53c74243f8be"),
+                 "0.5b-k5": ("gemv", 506962458, "44ff53c74243f8be"),
+                 "0.5b-tern": ("gemv", 135437195, "44ff53c74243f8be"),
+                 "bin": ("gemv", 123977381, "44ff53c74243f8be"),
+                 "7b-int4": ("gemv", 3787523130, "44ff53c74243f8be"),
                  "7b-prefill": ("prefill", 313632554, "2d7378f14da2d78f"),
-                 "0.5b-hier": ("gemv", 268450016, "81df76e0b6b1049d"),
-                 "0.5b-int2": ("gemv", 143168522, "81df76e0b6b1049d"),
-                 "0.5b-int3": ("gemv", 231213059, "81df76e0b6b1049d"),
-                 "0.5b-int4-greedy": ("gemv", 266670593, "81df76e0b6b1049d"),
+                 "0.5b-hier": ("gemv", 268449205, "44ff53c74243f8be"),
+                 "0.5b-int2": ("gemv", 143168273, "44ff53c74243f8be"),
+                 "0.5b-int3": ("gemv", 206196548, "44ff53c74243f8be"),
+                 "0.5b-int4-greedy": ("gemv", 266665778, "44ff53c74243f8be"),
                  "0.5b-int4-m16": ("small_m", 389523703, "4ad0080035152d2f"),
                  "kv-32k": ("kv", 143371933, "df773ea2078ca49e"),
                  "kv-4k": ("kv", 18194357, "df773ea2078ca49e"),

@@ -16,7 +16,7 @@
 //   ternary   : s = fp16(sequential-sum|w| / 128), code = clamp(rint(w/s),-1,1)+1
 //   int2 g128 : as int4 with 4 levels: s = fp16((hi-lo)/3), z, q in 0..3
 //   int3 g128 : as int4 with 8 levels: s = fp16((hi-lo)/7), z, q in 0..7,
-//               stored in the GEMV's plane layout (see tkq.h)
+//               stored plane-major for the GEMV's loads (see tkq.h)
 //   int4 hier-g32 (Whetstone README, quantizer table "group 32 with
 //               hierarchical scale metadata"; "Prior art", the Q4_K
 //               comparison): per 32-group s_g = (hi-lo)/15, m_g = -lo; per
@@ -124,9 +124,10 @@ __global__ __launch_bounds__(256) void pack_int3_kernel(const float* __restrict_
     for (int f = 0; f < 5; ++f) word |= ((uint32_t)c[10 * j + f] << (3 * f)) | ((uint32_t)c[10 * j + 5 + f] << (16 + 3 * f));
     word |= ((uint32_t)(c[30] >> j) & 1u) << 15;
     word |= ((uint32_t)(c[31] >> j) & 1u) << 31;
-    // plane lane / 4, word lane % 4 of this group's 16 bytes in that plane
-    const int64_t plane_words = K / 32;  // K/8 bytes per plane
-    codes[row * (3 * K / 32) + (lane >> 2) * plane_words + 4 * grp + (lane & 3)] = word;
+    // plane lane / 4 (planes of N rows of K/8 bytes), word lane % 4 of this
+    // group's 16 bytes in that plane's row
+    const int64_t row_words = K / 32, rows = groups / gpr;
+    codes[((lane >> 2) * rows + row) * row_words + 4 * grp + (lane & 3)] = word;
   }
   if (lane == 0) meta[g] = (uint32_t)sbits | ((uint32_t)half_bits(zf) << 16);
 }

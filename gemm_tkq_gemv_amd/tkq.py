@@ -189,10 +189,10 @@ def pack_int2_g128(W, stream=None):
 
 
 def pack_int3_g128(W, stream=None):
-    """W fp32 [N,K] -> (codes int32 [N,3K/32] (plane layout), meta int32 [N,K/128])."""
+    """W fp32 [N,K] -> (codes int32 [3,N,K/32] (plane-major layout), meta int32 [N,K/128])."""
     _need(W, torch.float32, "W")
     N, K = W.shape
-    codes = torch.empty((N, 3 * K // 32), dtype=torch.int32, device=W.device)
+    codes = torch.empty((3, N, K // 32), dtype=torch.int32, device=W.device)
     meta = torch.empty((N, K // 128), dtype=torch.int32, device=W.device)
     _call("tkq_pack_int3_g128", _ptr(W), N, K, _ptr(codes), _ptr(meta), _stream(stream))
     return codes, meta

@@ -58,13 +58,13 @@
  *     meta  uint32 [N][K/128]: as TKQ_FMT_INT4_G128;  w = scale * (q - zero)
  * TKQ_FMT_INT3_G128 (Whetstone README, bytes/token and quality tables, "int3
  *   g128" at 3.25 bits/weight):
- *     codes uint32 [N][3K/32]: per 128-group g, block b (codes 32b..32b+31)
+ *     codes uint32 [3][N][K/32]: per 128-group g, block b (codes 32b..32b+31)
  *           is three words W0..W2; Wj holds code 10j+f in bits [3f,3f+3) and
  *           code 10j+5+f in bits [16+3f,16+3f+3) (f = 0..4), bit j of code 30
  *           in bit 15 and bit j of code 31 in bit 31.  The group's 12 words
  *           (b0W0, b0W1, b0W2, b1W0, ...) form three 16-byte planes (words
- *           0-3, 4-7, 8-11); plane p of group g is at byte p*K/8 + 16g of the
- *           row (rows are 3K/8 bytes).
+ *           0-3, 4-7, 8-11).  The matrix is stored plane-major: plane p of
+ *           group g of row n is at byte p*N*K/8 + n*K/8 + 16g.
  *     meta  uint32 [N][K/128]: as TKQ_FMT_INT4_G128;  w = scale * (q - zero)
  * TKQ_FMT_INT4_HIER_G32 (Whetstone README, bytes/token table "int4 hier-g32"
  *   at 4.28 bits/weight, quantizer table "group 32 with hierarchical scale
@@ -165,8 +165,8 @@ int tkq_pack_int2_g128(const float* W, int64_t N, int64_t K, uint32_t* codes,
 
 /* int3 g128, asymmetric RTN (Whetstone README, "int3 g128"): the int4 g128
  * quantizer with eight levels: s = fp16((hi - lo) / 7), z = clamp(rint(-lo /
- * s), 0, 7), q = clamp(rint(w / s) + z, 0, 7).  codes: uint32 [N][3K/32] in
- * the plane layout above; meta: uint32 [N][K/128] = half2 {s, z}.
+ * s), 0, 7), q = clamp(rint(w / s) + z, 0, 7).  codes: uint32 [3][N][K/32]
+ * in the plane-major layout above; meta: uint32 [N][K/128] = half2 {s, z}.
  * K % 128 == 0. */
 int tkq_pack_int3_g128(const float* W, int64_t N, int64_t K, uint32_t* codes,
                        uint32_t* meta, void* stream);

@@ -15,7 +15,7 @@ of a row reads front to back):
 * binary       uint32 [N][K/32]: element 32j+i in bit i of word j.
 * int2         uint32 [N][K/16]: element 16j+i in bits [2i, 2i+2) of word j
                 (the ternary field layout), meta as int4 (half2 {scale, zero}).
-* int3         3 bits per weight, K*3/8 bytes per row, meta as int4.  The
+* int3         3 bits per weight, 3*N*K/8 bytes, meta as int4.  The
                 pages fix only the density (3.25 bits/weight with the g128
                 metadata); the layout is chosen for the GEMV's 16-byte loads:
                 within a 128-group, block b (codes 32b..32b+31) is three
@@ -23,8 +23,10 @@ of a row reads front to back):
                 [3f, 3f+3) and code 10j+5+f in bits [16+3f, 16+3f+3) for
                 f = 0..4, and bit j of code 30 in bit 15, bit j of code 31 in
                 bit 31.  The group's 12 words (b0W0, b0W1, b0W2, b1W0, ...)
-                form three 16-byte planes (words 0-3, 4-7, 8-11); plane p of
-                group g sits at byte p*K/8 + 16*g of the row.
+                form three 16-byte planes (words 0-3, 4-7, 8-11).  The matrix
+                is stored plane-major, uint32 [3][N][K/32]: plane p of group g
+                of row n sits at byte p*N*K/8 + n*K/8 + 16*g, so each plane of
+                consecutive rows is one contiguous run.
 * int4-hier-g32 codes as int4; one metadata block per matrix:
                 bytes [0, N*K/32): byte n*(K/32)+g = sc | (mi << 4) of group g
                 of row n; zero padding up to a multiple of 16 bytes (offset
@@ -113,7 +115,7 @@ def _int3_block_words(c):
 
 
 def pack_int3(q):
-    """int3 codes [N,K] (0..7) -> uint32 [N, 3K/32] in the plane layout."""
+    """int3 codes [N,K] (0..7) -> uint32 [3, N, K/32] in the plane-major layout."""
     q = np.asarray(q)
     N, K = q.shape
     if K % 128:
@@ -124,16 +126,16 @@ def pack_int3(q):
     ng = K // 128
     blocks = c.reshape(N, ng, 4, 32)
     words = _int3_block_words(blocks).reshape(N, ng, 12)          # b0W0 b0W1 b0W2 b1W0 ...
-    planes = words.reshape(N, ng, 3, 4).transpose(0, 2, 1, 3)      # [N][plane][group][4]
-    return planes.reshape(N, 3 * ng * 4).astype(np.uint32)
+    planes = words.reshape(N, ng, 3, 4).transpose(2, 0, 1, 3)      # [plane][N][group][4]
+    return planes.reshape(3, N, ng * 4).astype(np.uint32)
 
 
 def unpack_int3(words, K):
-    """uint32 [N, 3K/32] -> int3 codes uint8 [N,K] (shift-and-mask reads)."""
+    """uint32 [3, N, K/32] -> int3 codes uint8 [N,K] (shift-and-mask reads)."""
     words = np.asarray(words, dtype=np.uint32).astype(np.uint64)
-    N = words.shape[0]
     ng = K // 128
-    w = words.reshape(N, 3, ng, 4).transpose(0, 2, 1, 3).reshape(N, ng, 4, 3)
+    N = words.size // (3 * ng * 4)
+    w = words.reshape(3, N, ng, 4).transpose(1, 2, 0, 3).reshape(N, ng, 4, 3)
     out = np.zeros((N, ng, 4, 32), dtype=np.uint8)
     for j in range(3):
         wj = w[..., j]

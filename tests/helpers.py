@@ -101,9 +101,16 @@ def device_rows_np(fmt, codes, meta, N, K, rows):
     """Packed codes and metadata of selected rows, as device_codes_np would
     give for a matrix of just those rows."""
     import torch
-    rt = torch.from_numpy(np.asarray(rows)).to(codes.device)
+    rows = np.asarray(rows)
+    # int3 codes are plane-major [3][N][K/32]: rows are the second index
+    row_dim = 1 if fmt == "int3" else 0
+    # checked on the host: an index past the end would fail on the device
+    assert codes.shape[row_dim] == N and rows.min() >= 0 and rows.max() < N
+    rt = torch.from_numpy(rows).to(codes.device)
     if fmt == "hier":
         return u32(codes[rt]), hier_meta_rows(meta.cpu().numpy(), N, K, rows)
+    if fmt == "int3":
+        return device_codes_np(fmt, codes[:, rt], meta[rt])
     return device_codes_np(fmt, codes[rt], None if meta is None else meta[rt])
 
 

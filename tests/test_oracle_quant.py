@@ -239,32 +239,36 @@ def test_int3_codes_are_nearest_level():
 
 
 def test_int3_layout_one_hot():
-    """Each code position lands where the layout text puts it."""
-    K = 256
+    """Each code position lands where the layout text puts it (row 1 of a
+    3-row matrix, so a row-major plane order would put it elsewhere)."""
+    K, N, n = 256, 3, 1
     for pos, val in [(0, 7), (4, 5), (5, 3), (9, 7), (10, 1), (27, 6), (29, 7), (30, 5), (31, 6),
                      (128 + 32 * 3 + 31, 7), (128 + 64 + 17, 2)]:
-        q = np.zeros((1, K), np.uint8)
-        q[0, pos] = val
+        q = np.zeros((N, K), np.uint8)
+        q[n, pos] = val
         words = pack.pack_int3(q)
-        assert words.shape == (1, 3 * K // 32)
+        assert words.shape == (3, N, K // 32)
+        flat = words.reshape(-1)
         g, e = divmod(pos, 128)
         b, t = divmod(e, 32)
         widx = 3 * b                           # index of W0 of the block in the group's 12 words
-        nz = np.flatnonzero(words[0])
+        nz = np.flatnonzero(flat)
+
+        def word_index(i):                     # word i of the group: plane i // 4, word i % 4
+            return ((i // 4) * N + n) * (K // 32) + 4 * g + i % 4
+
         expect = {}
         if t < 30:
             j, f = divmod(t, 10)
             shift = 3 * f if f < 5 else 16 + 3 * (f - 5)
-            i = widx + j
-            expect[(i // 4) * (K // 128) * 4 + 4 * g + i % 4] = val << shift
+            expect[word_index(widx + j)] = val << shift
         else:
             for j in range(3):
                 if (val >> j) & 1:
-                    i = widx + j
-                    expect[(i // 4) * (K // 128) * 4 + 4 * g + i % 4] = 1 << (15 if t == 30 else 31)
+                    expect[word_index(widx + j)] = 1 << (15 if t == 30 else 31)
         assert sorted(nz.tolist()) == sorted(expect), pos
         for idx, v in expect.items():
-            assert int(words[0, idx]) == v, pos
+            assert int(flat[idx]) == v, pos
         assert np.array_equal(pack.unpack_int3(words, K), q)
 
 
