@@ -59,6 +59,15 @@ namespace {
 #ifndef TKQ_GEMV_PINGPONG_MASK
 #define TKQ_GEMV_PINGPONG_MASK ((1 << 1) | (1 << 2) | (1 << 4))
 #endif
+// Codings (bit fmt) whose code loads are plain rather than non-temporal.
+// Binary rows (K/8 bytes) start at 32 bytes past a 64-byte boundary on odd
+// rows, and a row's passes end mid-block: blocks touched by two load
+// instructions were fetched from HBM twice under the non-temporal hint
+// (traffic 1.080x against 1.002x plain; plain loads measured 3.89 -> 4.63
+// TB/s on the binary shapes).  Ternary and int2 measured 5 % slower plain.
+#ifndef TKQ_GEMV_PLAIN_MASK
+#define TKQ_GEMV_PLAIN_MASK (1 << 4)
+#endif
 #ifndef TKQ_GEMV_WPE
 #define TKQ_GEMV_WPE 1  // minimum waves per SIMD the register budget must allow
 #endif
@@ -446,6 +455,10 @@ struct Runner {
   }
 
   static constexpr bool kSbase = ((TKQ_GEMV_SBASE_MASK) >> FMT) & 1;
+  static constexpr bool kPlain = ((TKQ_GEMV_PLAIN_MASK) >> FMT) & 1;
+  __device__ static __forceinline__ u32x4 code16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return kPlain ? load16(r, off) : load16_nt(r, off);
+  }
 
   __device__ __forceinline__ void issue(int st, Buf& b) const {
     if constexpr (kSbase) {
@@ -459,10 +472,10 @@ struct Runner {
         if constexpr (Cd::PLANES == 3) {
 #pragma unroll
           for (int p = 0; p < 3; ++p)
-            b.c[u][j].p[p] = load16_nt(
+            b.c[u][j].p[p] = code16(
                 make_rsrc_uniform(t.codes_ptr + p * t.plane_stride, s * t.row_bytes, t.codes_bytes), vc[j]);
         } else {
-          b.c[u][j] = load16_nt(rc, vc[j]);
+          b.c[u][j] = code16(rc, vc[j]);
         }
         if constexpr (Cd::MB == 4) b.m[u][j] = load4(rm, vm[j]);
         else if constexpr (Cd::MB == 2) b.m[u][j] = load2(rm, vm[j]);
@@ -479,11 +492,11 @@ struct Runner {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         if constexpr (Cd::PLANES == 3) {
-          b.c[u][j].p[0] = load16_nt(t.codes, rb + cof[j]);
-          b.c[u][j].p[1] = load16_nt(t.codes_p1, rb + cof[j]);
-          b.c[u][j].p[2] = load16_nt(t.codes_p2, rb + cof[j]);
+          b.c[u][j].p[0] = code16(t.codes, rb + cof[j]);
+          b.c[u][j].p[1] = code16(t.codes_p1, rb + cof[j]);
+          b.c[u][j].p[2] = code16(t.codes_p2, rb + cof[j]);
         } else {
-          b.c[u][j] = load16_nt(t.codes, rb + cof[j]);
+          b.c[u][j] = code16(t.codes, rb + cof[j]);
         }
         if constexpr (Cd::MB == 4) b.m[u][j] = load4(t.meta, mb + mof[j]);
         else if constexpr (Cd::MB == 2) b.m[u][j] = load2(t.meta, mb + mof[j]);
