@@ -68,6 +68,12 @@ namespace {
 #ifndef TKQ_GEMV_PLAIN_MASK
 #define TKQ_GEMV_PLAIN_MASK (1 << 4)
 #endif
+// Codings (bit fmt) whose waves raise their priority while issuing a row
+// step's loads, so that a CU's loads are not held behind other waves' unpack
+// work: int4 only (0.5B sweep +1.5 %, 7B -0.3 %; ternary -4 %).
+#ifndef TKQ_GEMV_SETPRIO_MASK
+#define TKQ_GEMV_SETPRIO_MASK (1 << 1)
+#endif
 #ifndef TKQ_GEMV_WPE
 #define TKQ_GEMV_WPE 1  // minimum waves per SIMD the register budget must allow
 #endif
@@ -460,7 +466,13 @@ struct Runner {
     return kPlain ? load16(r, off) : load16_nt(r, off);
   }
 
+  static constexpr bool kSetprio = ((TKQ_GEMV_SETPRIO_MASK) >> FMT) & 1;
   __device__ __forceinline__ void issue(int st, Buf& b) const {
+    if constexpr (kSetprio) __builtin_amdgcn_s_setprio(1);
+    issue_loads(st, b);
+    if constexpr (kSetprio) __builtin_amdgcn_s_setprio(0);
+  }
+  __device__ __forceinline__ void issue_loads(int st, Buf& b) const {
     if constexpr (kSbase) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
