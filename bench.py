@@ -49,16 +49,16 @@ TRAFFIC_SOURCES = {"gemv": ["gemm_tkq_gemv_amd/csrc/gemv.hip"] + _COMMON,
                    "prefill": ["gemm_tkq_gemv_amd/csrc/prefill.hip"] + _COMMON,
                    "kv": ["gemm_tkq_gemv_amd/csrc/kv.hip"] + _COMMON}
 # workload -> (kernel family, bytes per launch, sha256[:16] of that family's sources)
-TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266577634, "bb72b6e87afaa570"),
-                 "0.5b-k5": ("gemv", 506970608, "bb72b6e87afaa570"),
-                 "0.5b-tern": ("gemv", 135443726, "bb72b6e87afaa570"),
-                 "bin": ("gemv", 115154956, "bb72b6e87afaa570"),
-                 "7b-int4": ("gemv", 3786807517, "bb72b6e87afaa570"),
+TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266576807, "f0da369e2b61fbd3"),
+                 "0.5b-k5": ("gemv", 506954837, "f0da369e2b61fbd3"),
+                 "0.5b-tern": ("gemv", 135433325, "f0da369e2b61fbd3"),
+                 "bin": ("gemv", 115067440, "f0da369e2b61fbd3"),
+                 "7b-int4": ("gemv", 3786812282, "f0da369e2b61fbd3"),
                  "7b-prefill": ("prefill", 313632554, "2d7378f14da2d78f"),
-                 "0.5b-hier": ("gemv", 268446138, "bb72b6e87afaa570"),
-                 "0.5b-int2": ("gemv", 143168466, "bb72b6e87afaa570"),
-                 "0.5b-int3": ("gemv", 206201792, "bb72b6e87afaa570"),
-                 "0.5b-int4-greedy": ("gemv", 266674066, "bb72b6e87afaa570"),
+                 "0.5b-hier": ("gemv", 268490094, "f0da369e2b61fbd3"),
+                 "0.5b-int2": ("gemv", 143167991, "f0da369e2b61fbd3"),
+                 "0.5b-int3": ("gemv", 206200448, "f0da369e2b61fbd3"),
+                 "0.5b-int4-greedy": ("gemv", 266682033, "f0da369e2b61fbd3"),
                  "0.5b-int4-m16": ("small_m", 389523703, "4ad0080035152d2f"),
                  "kv-32k": ("kv", 143371933, "df773ea2078ca49e"),
                  "kv-4k": ("kv", 18194357, "df773ea2078ca49e"),

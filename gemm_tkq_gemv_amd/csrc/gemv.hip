@@ -70,9 +70,10 @@ namespace {
 #endif
 // Codings (bit fmt) whose waves raise their priority while issuing a row
 // step's loads, so that a CU's loads are not held behind other waves' unpack
-// work: int4 only (0.5B sweep +1.5 %, 7B -0.3 %; ternary -4 %).
+// work: int4 (0.5B sweep +1.5 %, 7B -0.3 %) and int4-hier-g32 (+1.9 %);
+// K5 -2 %, ternary -4 %, int3 -3 %, binary +0.5 %.
 #ifndef TKQ_GEMV_SETPRIO_MASK
-#define TKQ_GEMV_SETPRIO_MASK (1 << 1)
+#define TKQ_GEMV_SETPRIO_MASK ((1 << 1) | (1 << 5))
 #endif
 #ifndef TKQ_GEMV_WPE
 #define TKQ_GEMV_WPE 1  // minimum waves per SIMD the register budget must allow
