@@ -60,10 +60,10 @@ TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266576807, "f0da369e2b61fbd3"),
                  "0.5b-int3": ("gemv", 206200448, "f0da369e2b61fbd3"),
                  "0.5b-int4-greedy": ("gemv", 266682033, "f0da369e2b61fbd3"),
                  "0.5b-int4-m16": ("small_m", 382385898, "8ae7d60609f3ddb1"),
-                 "kv-32k": ("kv", 143371933, "df773ea2078ca49e"),
-                 "kv-4k": ("kv", 18194357, "df773ea2078ca49e"),
-                 "kv-32k-gqa": ("kv", 37018468, "df773ea2078ca49e"),
-                 "kv-128k-gqa": ("kv", 145069485, "df773ea2078ca49e")}
+                 "kv-32k": ("kv", 143371671, "7402b7b1004bcc79"),
+                 "kv-4k": ("kv", 18194319, "7402b7b1004bcc79"),
+                 "kv-32k-gqa": ("kv", 37017256, "7402b7b1004bcc79"),
+                 "kv-128k-gqa": ("kv", 145068431, "7402b7b1004bcc79")}
 
 
 def traffic_family(workload):
