@@ -81,10 +81,12 @@ def k5_value(c):
 
 
 def dequant_k5(codes, scale16):
-    """w = s * value(c) with value(c) from the five balanced trits of c."""
+    """w = s * value(c) with value(c) from the five balanced trits of c (the
+    value of each of the 256 byte values is tabulated once from k5_value)."""
     codes = np.asarray(codes, dtype=np.uint8)
     K = codes.shape[1]
-    return _expand_groups(scale16, K) * k5_value(codes).astype(np.float64)
+    table = k5_value(np.arange(256)).astype(np.float64)
+    return _expand_groups(scale16, K) * table[codes]
 
 
 def dequant_tern(codes, scale16, K):
@@ -151,12 +153,18 @@ def greedy_token(y):
     status list: greedy selection stays on the GPU): the index of the largest
     value, the first such index on ties, with -0 and +0 equal.  A plain scan.
     The comparison is on the values as given (the stored fp16 logits of the
-    GEMV, or the int32 outputs of the binary coding)."""
+    GEMV, or the int32 outputs of the binary coding).
+
+    NaN (the pages are silent; a logit is NaN only when an input is): every
+    NaN counts as larger than any number, +inf included, so the first NaN
+    wins -- the convention of numpy's argmax."""
     vals = np.asarray(y).astype(np.float64).ravel()
     if vals.size == 0:
         raise ValueError("empty vector")
     best = 0
     for i in range(1, vals.size):
-        if vals[i] > vals[best]:
+        if np.isnan(vals[best]):
+            break
+        if np.isnan(vals[i]) or vals[i] > vals[best]:
             best = i
     return best
