@@ -23,6 +23,24 @@ float32):
   N(0, 0.02) float32 of the 7B MLP shapes.
 * prefill activations: X = default_rng((5, 10000)) standard normal [512, 3584]
   float16 for gate/up and default_rng((5, 10001)) [512, 18944] for down.
+* large-activation GEMV case (seed s, N, K): heavy-tailed weights
+  0.02 * standard_t(3) with one outlier weight of magnitude 0.5..2 per
+  group of 128 (position and sign drawn) and two activation channels per
+  group set to +-A, A drawn from {1e3, 2e3, 4e3, 8e3, 3e4}, on which every
+  row's weight is exactly 0 (so it quantizes to the zero point); the other
+  activations are N(0, 1).  Decode activations have such outlier channels.
+* KV cache, random: K, V, q standard normal fp16 ([B][T][Hk][128] and
+  [B][H][128]), default_rng((9, B, H, Hk, T)) for the benchmark workloads.
+* KV cache, page markers (B, H, Hk, T): K = 0, so every score ties and the
+  attention is the plain mean over the cache; V[b, t, hk, c] = 15 on the
+  marker channel c = (t // 128 + 37 hk + 11 b) % 128 of the token's page and
+  1 elsewhere (exact on the 4-bit grid); q standard normal from
+  default_rng((10, B, H, Hk, T)).  A page dropped, repeated, or read from
+  another head or sequence moves its marker channel by about 14 / pages.
+* KV cache, one peaked token (B, H, Hk, T, t): K and V standard normal fp16
+  from default_rng((11, B, H, Hk, T)) with K scaled by 0.05, except that
+  token t's K row is +4 in every channel of every KV head; q = +1, so token t
+  dominates every head's softmax and the answer is its V row.
 
 Shapes follow the Qwen2.5-0.5B (hidden 896, intermediate 4864, 24 layers,
 2 KV heads x 64 = 128, vocab 151936, tied head) and Qwen2.5-7B (hidden 3584,
@@ -154,3 +172,52 @@ def normal_matrix(seed, N, K, std=0.02):
 def normal_vector(seed, K):
     """Small seeded fp16 activation vector ~ N(0, 1)."""
     return np.random.default_rng(seed).standard_normal(K, dtype=np.float32).astype(np.float16)
+
+
+def outlier_case(seed, N, K, group=128):
+    """(W fp32 [N,K], x fp16 [K]): heavy-tailed weights with one outlier per
+    group, and large activation channels on all-zero weight columns (the
+    recipe above)."""
+    r = np.random.default_rng(seed)
+    W = (r.standard_t(3, (N, K)) * 0.02).astype(np.float32)
+    x = r.standard_normal(K, dtype=np.float32)
+    G = K // group
+    out_pos = r.integers(0, group, (N, G))
+    out_val = (r.uniform(0.5, 2.0, (N, G)) * r.choice([-1.0, 1.0], (N, G))).astype(np.float32)
+    for g in range(G):
+        W[np.arange(N), g * group + out_pos[:, g]] = out_val[:, g]
+        chans = g * group + r.choice(group, 2, replace=False)
+        W[:, chans] = 0.0
+        x[chans] = r.choice([1e3, 2e3, 4e3, 8e3, 3e4], 2) * r.choice([-1.0, 1.0], 2)
+    return W, x.astype(np.float16)
+
+
+def kv_random_case(B, H, Hk, T, seed=9):
+    """(K, V fp16 [B][T][Hk][128], q fp16 [B][H][128]), standard normal."""
+    r = np.random.default_rng((seed, B, H, Hk, T))
+    K = r.standard_normal((B, T, Hk, 128), dtype=np.float32).astype(np.float16)
+    V = r.standard_normal((B, T, Hk, 128), dtype=np.float32).astype(np.float16)
+    q = r.standard_normal((B, H, 128), dtype=np.float32).astype(np.float16)
+    return K, V, q
+
+
+def kv_marker_case(B, H, Hk, T):
+    """(K, V, q) of the page-marker recipe above."""
+    K = np.zeros((B, T, Hk, 128), np.float16)
+    V = np.ones((B, T, Hk, 128), np.float16)
+    page = np.arange(T) // 128
+    for b in range(B):
+        for hk in range(Hk):
+            V[b, np.arange(T), hk, (page + 37 * hk + 11 * b) % 128] = 15
+    q = np.random.default_rng((10, B, H, Hk, T)).standard_normal((B, H, 128), dtype=np.float32)
+    return K, V, q.astype(np.float16)
+
+
+def kv_peaked_case(B, H, Hk, T, t):
+    """(K, V, q) of the one-peaked-token recipe above."""
+    r = np.random.default_rng((11, B, H, Hk, T))
+    K = (r.standard_normal((B, T, Hk, 128), dtype=np.float32) * np.float32(0.05)).astype(np.float16)
+    V = r.standard_normal((B, T, Hk, 128), dtype=np.float32).astype(np.float16)
+    K[:, t] = 4.0
+    q = np.ones((B, H, 128), np.float16)
+    return K, V, q

@@ -28,15 +28,17 @@ Readings taken where the page is silent:
 * The cache length is a multiple of 128 (whole pages).
 
 The attention itself is the plain definition in fp64 from the dequantized
-cache.  Its tolerance (attention_bound) is derived from the fp16 roundings a
-kernel makes when it folds the scales into the query and the probabilities;
-see that function.
+cache.  Its tolerance (attention_bound) is not given by the page; it is
+derived from the per-row bound the weight GEMV is held to (the scores and
+the output are both GEMVs over the dequantized cache), carried exactly
+through the softmax; see that function.
 """
 
 import numpy as np
 
 from . import pack as _pack
 from . import quant as _quant
+from .ref import TOL
 
 D = 128            # head dimension
 PAGE = 128         # tokens per page
@@ -133,26 +135,35 @@ def attention_decode(q, K, V, sm_scale):
     return out, probs
 
 
-def attention_bound(q, K, V, sm_scale):
-    """Per output element tolerance of a kernel that (a) rounds q_c * s_c (the
-    K channel scale) to fp16, (b) rounds p_t * s_t (the V token scale) to
-    fp16, (c) accumulates in fp32 and (d) stores fp16:
-      score error  |ds_t| <= u * A_t,  A_t = sm_scale * sum_c |q_c K_tc|
-      (u = 2^-11, the fp16 unit roundoff, from (a));
-      probabilities then move by a relative 2 max_t |ds_t| at most (to first
-      order), (b) and (d) add u each, (c) is far below;
-    so |out_c - ref_c| <= (4 u max_t A_t + 3 u) * sum_t p_t |V_tc| + 1e-6,
-    with the factor 2 of the first term doubled for the second-order terms
-    of the exponential.  Returns an array [B][H][128]."""
-    u = 2.0 ** -11
+def attention_bound(q, K, V, sm_scale, eps=TOL, probs=None):
+    """Per output element tolerance [B][H][128] of a decode step.
+
+    Reading (the BitDecoding page states none): single-query attention is
+    two GEMVs over the dequantized cache, the scores s = sm_scale K q and the
+    output o = V^T p, and each is held to the per-row bound of the weight
+    GEMV, |err| <= eps * sum |w x| with eps = 2e-3.  So
+      score error   |ds_t| <= eps * A_t,  A_t = sm_scale * sum_c |q_c K_tc|;
+      softmax       with d = max_t |ds_t|, every p_t moves by a factor in
+                    [exp(-2d), exp(2d)] (numerator and denominator each by
+                    exp(+-d) at most);
+      output        the value GEMV over the perturbed p adds eps * sum_t
+                    p'_t |V_tc| <= eps * exp(2d) * sum_t p_t |V_tc|;
+    hence, exactly (no first-order step),
+      |out_c - ref_c| <= ((1 + eps) * exp(2 eps max_t A_t) - 1)
+                         * sum_t p_t |V_tc|.
+    A kernel's own roundings (fp16 query and probability scaling, fp32 sums,
+    the fp16 store) have to fit inside these two per-GEMV budgets.
+    `probs` (from attention_decode) may be passed to skip recomputing them."""
     q = np.asarray(q, dtype=np.float64)
     B, H, _ = q.shape
     Hk = K.shape[1]
     G = H // Hk
-    out, probs = attention_decode(q, K, V, sm_scale)
+    if probs is None:
+        _, probs = attention_decode(q, K, V, sm_scale)
     bound = np.zeros((B, H, D))
     for b in range(B):
         for h in range(H):
             A = sm_scale * (np.abs(K[b, h // G]) @ np.abs(q[b, h]))
-            bound[b, h] = (4 * u * A.max() + 3 * u) * (probs[b, h] @ np.abs(V[b, h // G])) + 1e-6
+            factor = (1.0 + eps) * np.exp(2.0 * eps * A.max()) - 1.0
+            bound[b, h] = factor * (probs[b, h] @ np.abs(V[b, h // G]))
     return bound

@@ -1,14 +1,20 @@
 """GPU low-bit KV cache (tkq_kv_pack, tkq_kv_decode) against oracle.kv: the
 paged cache bit-exact with the oracle's quantization of the same K and V, and
-the decode output within the derived per-element bound of the fp64 attention
-over the dequantized cache.  Shapes: the BitDecoding README's example (batch
+the decode output within the per-element bound of the fp64 attention over the
+dequantized cache (oracle.kv.attention_bound: the weight GEMV's per-row bound
+applied to both products).  Shapes: the BitDecoding README's example (batch
 1, 32 query and 32 KV heads, head dimension 128, 4096 cached tokens), grouped
-queries (2, 4 and 8 query heads per KV head), a single page, batches, and a
-peaked attention whose answer is one token's value row."""
+queries (2, 4, 7, 8, 16 and 24 query heads per KV head), a single page,
+batches; structural caches that the bound checks page by page (every score
+tied and a marker channel per page, so that a page left out, read twice or
+read from another head moves an output far beyond the bound), and one peaked
+token whose value row is the answer, placed in the last page of the last
+split and at page boundaries."""
 
 import numpy as np
 import pytest
 
+from gemm_tkq_gemv_amd import inputs
 from helpers import gpu_or_skip
 from oracle import kv as okv
 
@@ -35,8 +41,8 @@ def _run(torch, tkq, q, K, V):
 
 def _check(q, cache_np, out, what):
     Kd, Vd = okv.dequant_cache(cache_np)
-    ref, _ = okv.attention_decode(q.astype(np.float64), Kd, Vd, 1 / np.sqrt(128))
-    bound = okv.attention_bound(q.astype(np.float64), Kd, Vd, 1 / np.sqrt(128))
+    ref, probs = okv.attention_decode(q.astype(np.float64), Kd, Vd, 1 / np.sqrt(128))
+    bound = okv.attention_bound(q.astype(np.float64), Kd, Vd, 1 / np.sqrt(128), probs=probs)
     got = out.float().cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(got)), what
     ratio = np.abs(got - ref) / bound
@@ -83,23 +89,64 @@ def test_kv_decode_matches_oracle(B, H, Hk, T):
     print("kv decode B=%d H=%d Hk=%d T=%d worst |err|/bound %.3g" % (B, H, Hk, T, worst))
 
 
-def test_kv_decode_peaked():
-    """One key aligned with the query dominates: the output is that token's
-    (dequantized) value row, to fp16 accuracy."""
+def _cache_np(cache, B, Hk, T):
+    return cache.cpu().numpy().view(np.uint32).reshape(B, Hk, T // 128, okv.PAGE_WORDS)
+
+
+@pytest.mark.parametrize("B,H,Hk,T", [
+    (1, 32, 32, 4096),      # one page per wave (the one-head kernel that requests K with the metadata)
+    (1, 32, 32, 32768),     # several pages per wave, one head per KV head
+    (1, 4, 4, 131072),      # 1024 pages per head: many splits, many pages per wave
+    (1, 32, 8, 32768),      # matrix-core path (4 query heads per KV head)
+    (1, 32, 8, 131072),     # matrix-core path, several pages per wave
+    (2, 8, 2, 4096),        # batch 2, 4 query heads per KV head
+    (2, 4, 2, 2048),        # batch 2, 2 query heads per KV head
+])
+def test_kv_decode_page_markers(B, H, Hk, T):
+    """Every score ties, so the answer is the plain mean over the cache, and
+    each page carries a marker channel (value 15 against 1) that depends on
+    the page, the KV head and the sequence.  A decode that leaves out,
+    repeats or mixes up a page fails the bound here at every T (the CPU
+    tests show it for the oracle with one page dropped or read twice)."""
     torch = gpu_or_skip()
     from gemm_tkq_gemv_amd import tkq
-    B, H, Hk, T = 1, 2, 1, 1024
-    K, V = _kv(803, B, T, Hk)
-    K *= np.float16(0.05)
-    q = np.zeros((B, H, 128), np.float16)
-    q[0, 0, :] = 1.0
-    q[0, 1, :] = -1.0
-    K[0, 700, 0, :] = 4.0            # 4 * 128 / sqrt(128) = 45 above the rest for head 0
-    K[0, 33, 0, :] = -4.0            # and for head 1
+    K, V, q = inputs.kv_marker_case(B, H, Hk, T)
     cache, out = _run(torch, tkq, q, K, V)
-    cn = cache.cpu().numpy().view(np.uint32).reshape(B, Hk, T // 128, okv.PAGE_WORDS)
-    _check(q, cn, out, "peaked")
-    Kd, Vd = okv.dequant_cache(cn)
+    cn = _cache_np(cache, B, Hk, T)
+    worst = _check(q, cn, out, "markers B=%d H=%d Hk=%d T=%d" % (B, H, Hk, T))
+    # the closed form: channel c of (b, hk) averages 15 over its marker pages, 1 elsewhere
+    P = T // 128
     got = out.float().cpu().numpy()
-    assert np.allclose(got[0, 0], Vd[0, 0, 700], atol=2e-3 * np.abs(Vd[0, 0, 700]).max())
-    assert np.allclose(got[0, 1], Vd[0, 0, 33], atol=2e-3 * np.abs(Vd[0, 0, 33]).max())
+    for b in range(B):
+        for h in range(H):
+            hk = h // (H // Hk)
+            n = np.bincount((np.arange(P) + 37 * hk + 11 * b) % 128, minlength=128)
+            want = 1.0 + 14.0 * n / P
+            assert np.allclose(got[b, h], want, rtol=4e-3, atol=0), (b, h)
+    print("kv markers B=%d H=%d Hk=%d T=%d worst |err|/bound %.3g" % (B, H, Hk, T, worst))
+
+
+@pytest.mark.parametrize("B,H,Hk,T,t", [
+    (1, 2, 1, 1024, 700),
+    (1, 32, 32, 4096, 4095),           # last token: last page of the last split
+    (1, 32, 32, 32768, 32767),
+    (1, 32, 32, 32768, 16384),         # first token of a page in the middle
+    (1, 32, 8, 32768, 32767),          # matrix-core path
+    (1, 32, 8, 131072, 131071),
+    (1, 32, 8, 131072, 65535),         # last token of the page before the middle
+    (1, 4, 4, 131072, 131071),
+])
+def test_kv_decode_peaked(B, H, Hk, T, t):
+    """One key aligned with the query dominates every head (score ~45 above
+    the rest): the output is that token's dequantized value row."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    K, V, q = inputs.kv_peaked_case(B, H, Hk, T, t)
+    cache, out = _run(torch, tkq, q, K, V)
+    cn = _cache_np(cache, B, Hk, T)
+    _check(q, cn, out, "peaked B=%d H=%d Hk=%d T=%d t=%d" % (B, H, Hk, T, t))
+    got = out.float().cpu().numpy()
+    for hk in range(Hk):
+        page = okv.unpack_page(cn[0, hk, t // 128])[1][t % 128]
+        for h in range(hk * (H // Hk), (hk + 1) * (H // Hk)):
+            assert np.allclose(got[0, h], page, rtol=0, atol=2e-3 * np.abs(page).max()), (h, t)

@@ -1,13 +1,18 @@
 """Pins of oracle.kv (the low-bit KV-cache decode attention oracle; the
 BitDecoding README's usage: 4-bit codes, group 128, K per channel, V per
 token, head dimension 128): closed forms of single-query softmax attention,
-its shift invariance, the GQA head mapping, lossless pages on a grid, and the
-page layout position by position."""
+its shift invariance, the GQA head mapping, lossless pages on a grid, the
+page layout position by position, and the tolerance: its closed form when
+every score ties, worst-case perturbations inside the two per-GEMV budgets
+(which must stay inside it and come close to it), and a dropped or repeated
+page, which it must reject at 4096, 32768 and 131072 cached tokens."""
 
 import numpy as np
 import pytest
 
+from gemm_tkq_gemv_amd import inputs
 from oracle import kv, pack
+from oracle.ref import TOL
 
 
 def _grid_page(rng):
@@ -107,5 +112,86 @@ def test_cache_roundtrip_and_bound_shape():
     q = rng.standard_normal((1, 4, 128))
     b = kv.attention_bound(q, Kd, Vd, 1 / np.sqrt(128))
     assert b.shape == (1, 4, 128) and np.all(b > 0)
+    # bounded below by the value GEMV's own budget, eps * sum_t p_t |V_tc|
+    _, pr = kv.attention_decode(q, Kd, Vd, 1 / np.sqrt(128))
+    assert np.all(b[0, 0] >= TOL * (pr[0, 0] @ np.abs(Vd[0, 0])))
     with pytest.raises(ValueError):
         kv.pack_cache(K[:, :100], V[:, :100])
+
+
+def test_bound_closed_form_when_scores_tie():
+    # K = 0: every A_t is 0, so the bound is eps * sum_t p_t |V_tc| = eps * mean_t |V_tc|
+    rng = np.random.default_rng(46)
+    K = np.zeros((1, 1, 384, 128))
+    V = rng.standard_normal((1, 1, 384, 128))
+    q = rng.standard_normal((1, 2, 128))
+    b = kv.attention_bound(q, K, V, 0.3)
+    assert np.allclose(b[0, 0], TOL * np.abs(V[0, 0]).mean(axis=0), rtol=1e-12, atol=0)
+    assert np.array_equal(b[0, 0], b[0, 1])
+
+
+def _perturbed(q, K, V, sm_scale, c, sign_s, sign_v):
+    """Attention with every score moved by sign_s[t] * eps * A_t and the value
+    product moved by sign_v * eps * sum_t p'_t |V_tc| (channel c)."""
+    s = sm_scale * (K @ q)
+    A = sm_scale * (np.abs(K) @ np.abs(q))
+    s2 = s + sign_s * TOL * A
+    e = np.exp(s2 - s2.max())
+    p2 = e / e.sum()
+    return p2 @ V[:, c] + sign_v * TOL * (p2 @ np.abs(V[:, c]))
+
+
+def test_bound_holds_and_is_tight_under_worst_perturbations():
+    rng = np.random.default_rng(47)
+    sm = 1 / np.sqrt(128)
+    worst = 0.0
+    for trial in range(6):
+        T = 128 * (1 + trial)
+        K = rng.standard_normal((T, 128)) * (0.5 + trial)
+        V = rng.standard_normal((T, 128))
+        q = rng.standard_normal(128)
+        ref, p = kv.attention_decode(q[None, None], K[None, None], V[None, None], sm)
+        bound = kv.attention_bound(q[None, None], K[None, None], V[None, None], sm, probs=p)[0, 0]
+        for c in range(0, 128, 9):
+            for direction in (1.0, -1.0):
+                # push probability towards the tokens that move channel c in `direction`
+                sign_s = np.where((V[:, c] - ref[0, 0, c]) * direction > 0, 1.0, -1.0)
+                got = _perturbed(q, K, V, sm, c, sign_s, direction)
+                err = abs(got - ref[0, 0, c])
+                assert err <= bound[c] * (1 + 1e-9), (trial, c, err / bound[c])
+                worst = max(worst, err / bound[c])
+        # random perturbations inside the budgets stay inside too
+        for _ in range(20):
+            got = _perturbed(q, K, V, sm, 5, rng.uniform(-1, 1, T), rng.uniform(-1, 1))
+            assert abs(got - ref[0, 0, 5]) <= bound[5]
+    # the derivation is not loose by orders of magnitude: the worst case
+    # reaches a large part of it
+    assert worst > 0.3, worst
+
+
+@pytest.mark.parametrize("T", [4096, 32768, 131072])
+def test_bound_rejects_a_dropped_or_repeated_page(T):
+    """Page-marker cache (every score ties; the marker channel of page p is
+    (p + 0) % 128): the exact attention passes its own check; the same
+    attention with one page left out, or with one page's content read twice
+    in place of another's, fails it."""
+    K, V, q = inputs.kv_marker_case(1, 1, 1, T)
+    cache = kv.pack_cache(K, V)
+    Kd, Vd = kv.dequant_cache(cache)
+    assert np.array_equal(Vd[0, 0], V[0, :, 0].astype(np.float64))     # exact on the grid
+    sm = 1 / np.sqrt(128)
+    qd = q.astype(np.float64)
+    ref, p = kv.attention_decode(qd, Kd, Vd, sm)
+    bound = kv.attention_bound(qd, Kd, Vd, sm, probs=p)
+    assert np.all(np.abs(ref - ref) <= bound)
+    P = T // 128
+    for j in sorted({0, 1, P // 2, P - 2, P - 1}):
+        keep = np.ones(T, bool)
+        keep[128 * j:128 * (j + 1)] = False
+        dropped, _ = kv.attention_decode(qd, Kd[:, :, keep], Vd[:, :, keep], sm)
+        assert np.any(np.abs(dropped - ref) > bound), "page %d dropped passes" % j
+        i = (j + 1) % P
+        Vr = Vd.copy()
+        Vr[:, :, 128 * i:128 * (i + 1)] = Vd[:, :, 128 * j:128 * (j + 1)]
+        repeated, _ = kv.attention_decode(qd, Kd, Vr, sm)
+        assert np.any(np.abs(repeated - ref) > bound), "page %d read twice passes" % j
