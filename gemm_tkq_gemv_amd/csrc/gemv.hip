@@ -107,12 +107,27 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
 //   XB   bytes of x the chunk consumes
 //   CPG  chunks per 128-weight group;  MB metadata bytes per group
 //   Regs register-resident constants (make() once per tile)
-//   prep(raw, xr)       permute natural x pairs into the unpack order
-//   dot(codes, xr, R)   sum over the chunk of (1024 + m*code) * x, as fp32
-//   kZero               a code word whose every field is the zero-point code
+//   Sub  the fp16 pairs subtracted from the unpacked codes: 1024 + m * zero
+//        for every multiplier class m of the chunk (sub(meta) per chunk)
+//   prep(raw, xr)          permute natural x pairs into the unpack order
+//   dot(codes, xr, R, S)   sum over the chunk of m * (code - zero) * x, as fp32
+//
+// The unpack ORs a code field into the mantissa of fp16 1024.0, giving
+// 1024 + m * code exactly; subtracting 1024 + m * zero in fp16 is exact too
+// (both are integers below 2048), so each v_dot2_f32_f16 multiplies x by a
+// small exact integer and the fp32 sums carry only the weights' own terms.
+// (Summing (1024 + m code) x and removing 1024 x afterwards leaves a rounding
+// error that grows with 1024 |x| rather than with |w x|: large activation
+// channels on weights at their zero point pushed it past the tolerance.)
 
 template <int FMT>
 struct Codec;
+
+__device__ __forceinline__ h2 bcast_hi(uint32_t m) {  // (hi half, hi half)
+  const _Float16 z = as_h2(m)[1];
+  return (h2){z, z};
+}
+__device__ __forceinline__ h2 h2c(float v) { return (h2){(_Float16)v, (_Float16)v}; }
 
 // int4: word w holds nibbles q0..q7 of elements 8i..8i+7.  (w & 0x000F000F)
 // pairs (q0, q4); (w & 0x00F000F0) pairs (16 q1, 16 q5); the same on w >> 8
@@ -121,11 +136,18 @@ struct Codec;
 template <>
 struct Codec<kFmtInt4> {
   static constexpr int WPC = 32, XR = 16, XB = 64, CPG = 4, MB = 4, PLANES = 1;
-  static constexpr uint32_t kZero = 0u;
   struct Regs {
     uint32_t m0, m1, magic;
   };
+  struct Sub {
+    h2 c1, c16;
+  };
   __device__ static Regs make() { return {in_sgpr(0x000F000Fu), in_sgpr(0x00F000F0u), in_vgpr(kMagic)}; }
+  // (1024 + z, 1024 + 16 z) from the group's half2 {scale, zero}
+  __device__ static Sub sub(uint32_t meta, const Regs& R) {
+    const h2 zz = bcast_hi(meta), mg = as_h2(R.magic);
+    return {zz + mg, zz * h2c(16.0f) + mg};
+  }
   __device__ static void prep(const uint32_t* raw, uint32_t* xr) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -136,30 +158,34 @@ struct Codec<kFmtInt4> {
       xr[4 * w + 3] = __builtin_amdgcn_perm(d, b, 0x07060302u);  // (x3, x7)
     }
   }
-  __device__ static float dot(u32x4 q, const uint32_t* xr, const Regs& R) {
+  __device__ static float dot(u32x4 q, const uint32_t* xr, const Regs& R, const Sub& S) {
     float lo = 0.0f, hi = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t v = q[w], t = v >> 8;
-      lo = __builtin_amdgcn_fdot2(as_h2((v & R.m0) | R.magic), as_h2(xr[4 * w + 0]), lo, false);
-      hi = __builtin_amdgcn_fdot2(as_h2((v & R.m1) | R.magic), as_h2(xr[4 * w + 1]), hi, false);
-      lo = __builtin_amdgcn_fdot2(as_h2((t & R.m0) | R.magic), as_h2(xr[4 * w + 2]), lo, false);
-      hi = __builtin_amdgcn_fdot2(as_h2((t & R.m1) | R.magic), as_h2(xr[4 * w + 3]), hi, false);
+      lo = __builtin_amdgcn_fdot2(as_h2((v & R.m0) | R.magic) - S.c1, as_h2(xr[4 * w + 0]), lo, false);
+      hi = __builtin_amdgcn_fdot2(as_h2((v & R.m1) | R.magic) - S.c16, as_h2(xr[4 * w + 1]), hi, false);
+      lo = __builtin_amdgcn_fdot2(as_h2((t & R.m0) | R.magic) - S.c1, as_h2(xr[4 * w + 2]), lo, false);
+      hi = __builtin_amdgcn_fdot2(as_h2((t & R.m1) | R.magic) - S.c16, as_h2(xr[4 * w + 3]), hi, false);
     }
     return fmaf(hi, 0.0625f, lo);
   }
 };
 
 // K5: one byte per weight.  v_perm builds (1024 + c0, 1024 + c2) and
-// (1024 + c1, 1024 + c3) from a code word and the byte 0x64.
+// (1024 + c1, 1024 + c3) from a code word and the byte 0x64; the pair
+// (1145, 1145) = 1024 + 121 is subtracted (byte 121 = value 0).
 template <>
 struct Codec<kFmtK5> {
   static constexpr int WPC = 16, XR = 8, XB = 32, CPG = 8, MB = 2, PLANES = 1;
-  static constexpr uint32_t kZero = 0x79797979u;  // 121 = value 0
   struct Regs {
-    uint32_t sel_a, sel_b, magic;
+    uint32_t sel_a, sel_b, magic, zero;
   };
-  __device__ static Regs make() { return {in_sgpr(0x04020400u), in_sgpr(0x04030401u), in_vgpr(0x64646464u)}; }
+  struct Sub {};
+  __device__ static Regs make() {
+    return {in_sgpr(0x04020400u), in_sgpr(0x04030401u), in_vgpr(0x64646464u), in_sgpr(0x64796479u)};
+  }
+  __device__ static Sub sub(uint32_t, const Regs&) { return {}; }
   __device__ static void prep(const uint32_t* raw, uint32_t* xr) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -168,81 +194,109 @@ struct Codec<kFmtK5> {
       xr[2 * w + 1] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // (x1, x3)
     }
   }
-  __device__ static float dot(u32x4 q, const uint32_t* xr, const Regs& R) {
+  __device__ static float dot(u32x4 q, const uint32_t* xr, const Regs& R, const Sub&) {
     float acc = 0.0f;
+    const h2 z = as_h2(R.zero);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t v = q[w];
-      acc = __builtin_amdgcn_fdot2(as_h2(__builtin_amdgcn_perm(R.magic, v, R.sel_a)), as_h2(xr[2 * w + 0]),
+      acc = __builtin_amdgcn_fdot2(as_h2(__builtin_amdgcn_perm(R.magic, v, R.sel_a)) - z, as_h2(xr[2 * w + 0]),
                                    acc, false);
-      acc = __builtin_amdgcn_fdot2(as_h2(__builtin_amdgcn_perm(R.magic, v, R.sel_b)), as_h2(xr[2 * w + 1]),
+      acc = __builtin_amdgcn_fdot2(as_h2(__builtin_amdgcn_perm(R.magic, v, R.sel_b)) - z, as_h2(xr[2 * w + 1]),
                                    acc, false);
     }
     return acc;
   }
 };
 
-// Ternary: 2-bit fields, element 16i+s at bits 2s.  Masks 3 << 2s for
-// s = 0..4 (both halves) give (1024 + 4^s c_s, 1024 + 4^s c_{s+8}); the word
-// shifted right by 10 gives s = 5, 6, 7 with multipliers 1, 4, 16.
+// 2-bit fields (ternary and int2), element 16i+s at bits 2s.  Masks 3 << 2s
+// for s = 0..4 (both halves) give (1024 + 4^s c_s, 1024 + 4^s c_{s+8}); the
+// word shifted right by 10 gives s = 5, 6, 7 with multipliers 1, 4, 16.  The
+// five multiplier classes subtract c[0..4] = 1024 + 4^s * zero.
+struct Sub2 {
+  h2 c[5];
+};
+struct Regs2 {
+  uint32_t m[5], magic;
+};
+__device__ __forceinline__ Regs2 make2() {
+  return {{in_sgpr(0x00030003u), in_sgpr(0x000C000Cu), in_sgpr(0x00300030u), in_sgpr(0x00C000C0u),
+           in_sgpr(0x03000300u)},
+          in_vgpr(kMagic)};
+}
+__device__ __forceinline__ void prep2(const uint32_t* raw, uint32_t* xr) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    // raw[8w + p] = (x_{2p}, x_{2p+1}) of word w's 16 elements
+    const uint32_t* r = raw + 8 * w;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t lo = r[s >> 1], hi = r[4 + (s >> 1)];
+      xr[8 * w + s] = (s & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
+                              : __builtin_amdgcn_perm(hi, lo, 0x05040100u);  // (x_s, x_{s+8})
+    }
+  }
+}
+__device__ __forceinline__ float dot2bit(u32x4 q, const uint32_t* xr, const Regs2& R, const Sub2& S) {
+  float a1 = 0.0f, a4 = 0.0f, a16 = 0.0f, a64 = 0.0f, a256 = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t v = q[w], t = v >> 10;
+    const uint32_t* x = xr + 8 * w;
+    a1 = __builtin_amdgcn_fdot2(as_h2((v & R.m[0]) | R.magic) - S.c[0], as_h2(x[0]), a1, false);
+    a4 = __builtin_amdgcn_fdot2(as_h2((v & R.m[1]) | R.magic) - S.c[1], as_h2(x[1]), a4, false);
+    a16 = __builtin_amdgcn_fdot2(as_h2((v & R.m[2]) | R.magic) - S.c[2], as_h2(x[2]), a16, false);
+    a64 = __builtin_amdgcn_fdot2(as_h2((v & R.m[3]) | R.magic) - S.c[3], as_h2(x[3]), a64, false);
+    a256 = __builtin_amdgcn_fdot2(as_h2((v & R.m[4]) | R.magic) - S.c[4], as_h2(x[4]), a256, false);
+    a1 = __builtin_amdgcn_fdot2(as_h2((t & R.m[0]) | R.magic) - S.c[0], as_h2(x[5]), a1, false);
+    a4 = __builtin_amdgcn_fdot2(as_h2((t & R.m[1]) | R.magic) - S.c[1], as_h2(x[6]), a4, false);
+    a16 = __builtin_amdgcn_fdot2(as_h2((t & R.m[2]) | R.magic) - S.c[2], as_h2(x[7]), a16, false);
+  }
+  return fmaf(a256, 0.00390625f, fmaf(a64, 0.015625f, fmaf(a16, 0.0625f, fmaf(a4, 0.25f, a1))));
+}
+
+// Ternary: code = t + 1, so the zero code is 1 in every field.
 template <>
 struct Codec<kFmtTern> {
   static constexpr int WPC = 64, XR = 32, XB = 128, CPG = 2, MB = 2, PLANES = 1;
-  static constexpr uint32_t kZero = 0x55555555u;  // code 1 = value 0
-  struct Regs {
-    uint32_t m[5], magic;
-  };
-  __device__ static Regs make() {
-    return {{in_sgpr(0x00030003u), in_sgpr(0x000C000Cu), in_sgpr(0x00300030u), in_sgpr(0x00C000C0u),
-             in_sgpr(0x03000300u)},
-            in_vgpr(kMagic)};
+  using Regs = Regs2;
+  using Sub = Sub2;
+  __device__ static Regs make() { return make2(); }
+  __device__ static Sub sub(uint32_t, const Regs&) {
+    return {{h2c(1025.0f), h2c(1028.0f), h2c(1040.0f), h2c(1088.0f), h2c(1280.0f)}};
   }
-  __device__ static void prep(const uint32_t* raw, uint32_t* xr) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // raw[8w + p] = (x_{2p}, x_{2p+1}) of word w's 16 elements
-      const uint32_t* r = raw + 8 * w;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const uint32_t lo = r[s >> 1], hi = r[4 + (s >> 1)];
-        xr[8 * w + s] = (s & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
-                                : __builtin_amdgcn_perm(hi, lo, 0x05040100u);  // (x_s, x_{s+8})
-      }
-    }
-  }
-  __device__ static float dot(u32x4 q, const uint32_t* xr, const Regs& R) {
-    float a1 = 0.0f, a4 = 0.0f, a16 = 0.0f, a64 = 0.0f, a256 = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t v = q[w], t = v >> 10;
-      const uint32_t* x = xr + 8 * w;
-      a1 = __builtin_amdgcn_fdot2(as_h2((v & R.m[0]) | R.magic), as_h2(x[0]), a1, false);
-      a4 = __builtin_amdgcn_fdot2(as_h2((v & R.m[1]) | R.magic), as_h2(x[1]), a4, false);
-      a16 = __builtin_amdgcn_fdot2(as_h2((v & R.m[2]) | R.magic), as_h2(x[2]), a16, false);
-      a64 = __builtin_amdgcn_fdot2(as_h2((v & R.m[3]) | R.magic), as_h2(x[3]), a64, false);
-      a256 = __builtin_amdgcn_fdot2(as_h2((v & R.m[4]) | R.magic), as_h2(x[4]), a256, false);
-      a1 = __builtin_amdgcn_fdot2(as_h2((t & R.m[0]) | R.magic), as_h2(x[5]), a1, false);
-      a4 = __builtin_amdgcn_fdot2(as_h2((t & R.m[1]) | R.magic), as_h2(x[6]), a4, false);
-      a16 = __builtin_amdgcn_fdot2(as_h2((t & R.m[2]) | R.magic), as_h2(x[7]), a16, false);
-    }
-    return fmaf(a256, 0.00390625f, fmaf(a64, 0.015625f, fmaf(a16, 0.0625f, fmaf(a4, 0.25f, a1))));
+  __device__ static void prep(const uint32_t* raw, uint32_t* xr) { prep2(raw, xr); }
+  __device__ static float dot(u32x4 q, const uint32_t* xr, const Regs& R, const Sub& S) {
+    return dot2bit(q, xr, R, S);
   }
 };
 
-// int4-hier-g32: the int4 code layout, so the int4 unpack; a chunk is exactly
-// one 32-weight group, whose metadata is one byte (scale index | min index
-// << 4).  The row's fp16 pair (d, dmin) is applied once per row.
+// int4-hier-g32: the int4 code layout, so the int4 unpack with 1024 removed
+// from both fields (the dot is sum q x); a chunk is exactly one 32-weight
+// group, whose metadata is one byte (scale index | min index << 4).  The
+// row's fp16 pair (d, dmin) is applied once per row.
 template <>
 struct Codec<kFmtHier> : Codec<kFmtInt4> {
   static constexpr int CPG = 1, MB = 1;
+  __device__ static Sub sub(uint32_t, const Regs& R) { return {as_h2(R.magic), as_h2(R.magic)}; }
 };
 
-// int2 g128: the ternary field layout (so the ternary unpack, with code 0 as
-// the bias reference) and the int4 metadata (fp16 scale and zero-point).
+// int2 g128: the ternary field layout and the int4 metadata (fp16 scale and
+// zero-point), so c[s] = 1024 + 4^s z per group.
 template <>
-struct Codec<kFmtInt2> : Codec<kFmtTern> {
-  static constexpr uint32_t kZero = 0u;
-  static constexpr int CPG = 2, MB = 4;
+struct Codec<kFmtInt2> {
+  static constexpr int WPC = 64, XR = 32, XB = 128, CPG = 2, MB = 4, PLANES = 1;
+  using Regs = Regs2;
+  using Sub = Sub2;
+  __device__ static Regs make() { return make2(); }
+  __device__ static Sub sub(uint32_t meta, const Regs& R) {
+    const h2 zz = bcast_hi(meta), mg = as_h2(R.magic);
+    return {{zz + mg, zz * h2c(4.0f) + mg, zz * h2c(16.0f) + mg, zz * h2c(64.0f) + mg, zz * h2c(256.0f) + mg}};
+  }
+  __device__ static void prep(const uint32_t* raw, uint32_t* xr) { prep2(raw, xr); }
+  __device__ static float dot(u32x4 q, const uint32_t* xr, const Regs& R, const Sub& S) {
+    return dot2bit(q, xr, R, S);
+  }
 };
 
 // int3 g128: a chunk is one 128-group = three 16-byte planes (12 words, four
@@ -251,7 +305,8 @@ struct Codec<kFmtInt2> : Codec<kFmtTern> {
 // give (1024 + 8^f c, 1024 + 8^f c') for f = 0, 1, 2 and the word shifted
 // right by 9 gives f = 3, 4 with multipliers 1, 8.  Codes 30 and 31 are
 // spread over bits 15 and 31 of the three words (bit j in word j) and are
-// gathered into one pair with three shift + and_or steps.  Metadata as int4.
+// gathered into one pair with three shift + and_or steps.  Metadata as int4;
+// the classes subtract 1024 + z, 1024 + 8 z and 1024 + 64 z.
 // The planes are matrix-wide (plane p of row n at byte p*N*K/8 + n*K/8), so a
 // row step's load of one plane covers consecutive rows without gaps: with
 // planes interleaved per row, the 32-byte sectors at plane boundaries were
@@ -264,13 +319,19 @@ struct Planes3 {
 template <>
 struct Codec<kFmtInt3> {
   static constexpr int WPC = 128, XR = 64, XB = 256, CPG = 1, MB = 4, PLANES = 3;
-  static constexpr uint32_t kZero = 0u;
   struct Regs {
     uint32_t m0, m1, m2, s0, s1, s2, magic;
+  };
+  struct Sub {
+    h2 c1, c8, c64;
   };
   __device__ static Regs make() {
     return {in_sgpr(0x00070007u), in_sgpr(0x00380038u), in_sgpr(0x01C001C0u), in_sgpr(0x00010001u),
             in_sgpr(0x00020002u), in_sgpr(0x00040004u), in_vgpr(kMagic)};
+  }
+  __device__ static Sub sub(uint32_t meta, const Regs& R) {
+    const h2 zz = bcast_hi(meta), mg = as_h2(R.magic);
+    return {zz + mg, zz * h2c(8.0f) + mg, zz * h2c(64.0f) + mg};
   }
   // pair (e1, e2) of a block's x values; raw[i] = (x_2i, x_2i+1)
   __device__ static uint32_t xpair(const uint32_t* raw, int e1, int e2) {
@@ -289,7 +350,7 @@ struct Codec<kFmtInt3> {
       xr[16 * b + 15] = xpair(r, 30, 31);
     }
   }
-  __device__ static float dot(const Planes3& q, const uint32_t* xr, const Regs& R) {
+  __device__ static float dot(const Planes3& q, const uint32_t* xr, const Regs& R, const Sub& S) {
     float a1 = 0.0f, a8 = 0.0f, a64 = 0.0f;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -303,16 +364,16 @@ struct Codec<kFmtInt3> {
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
         const uint32_t v = w[j], t = v >> 9;
-        a1 = __builtin_amdgcn_fdot2(as_h2((v & R.m0) | R.magic), as_h2(x[5 * j + 0]), a1, false);
-        a8 = __builtin_amdgcn_fdot2(as_h2((v & R.m1) | R.magic), as_h2(x[5 * j + 1]), a8, false);
-        a64 = __builtin_amdgcn_fdot2(as_h2((v & R.m2) | R.magic), as_h2(x[5 * j + 2]), a64, false);
-        a1 = __builtin_amdgcn_fdot2(as_h2((t & R.m0) | R.magic), as_h2(x[5 * j + 3]), a1, false);
-        a8 = __builtin_amdgcn_fdot2(as_h2((t & R.m1) | R.magic), as_h2(x[5 * j + 4]), a8, false);
+        a1 = __builtin_amdgcn_fdot2(as_h2((v & R.m0) | R.magic) - S.c1, as_h2(x[5 * j + 0]), a1, false);
+        a8 = __builtin_amdgcn_fdot2(as_h2((v & R.m1) | R.magic) - S.c8, as_h2(x[5 * j + 1]), a8, false);
+        a64 = __builtin_amdgcn_fdot2(as_h2((v & R.m2) | R.magic) - S.c64, as_h2(x[5 * j + 2]), a64, false);
+        a1 = __builtin_amdgcn_fdot2(as_h2((t & R.m0) | R.magic) - S.c1, as_h2(x[5 * j + 3]), a1, false);
+        a8 = __builtin_amdgcn_fdot2(as_h2((t & R.m1) | R.magic) - S.c8, as_h2(x[5 * j + 4]), a8, false);
       }
       uint32_t p = ((w[0] >> 15) & R.s0) | R.magic;
       p = ((w[1] >> 14) & R.s1) | p;
       p = ((w[2] >> 13) & R.s2) | p;
-      a1 = __builtin_amdgcn_fdot2(as_h2(p), as_h2(x[15]), a1, false);
+      a1 = __builtin_amdgcn_fdot2(as_h2(p) - S.c1, as_h2(x[15]), a1, false);
     }
     return fmaf(a64, 0.015625f, fmaf(a8, 0.125f, a1));
   }
@@ -323,12 +384,14 @@ template <>
 struct Codec<kFmtBin> {
   static constexpr int WPC = 128, XR = 4, XB = 16, CPG = 1, MB = 0, PLANES = 1;
   struct Regs {};
+  struct Sub {};
   __device__ static Regs make() { return {}; }
+  __device__ static Sub sub(uint32_t, const Regs&) { return {}; }
   __device__ static void prep(const uint32_t* raw, uint32_t* xr) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) xr[i] = raw[i];
   }
-  __device__ static int dot(u32x4 q, const uint32_t* xr, const Regs&) {
+  __device__ static int dot(u32x4 q, const uint32_t* xr, const Regs&, const Sub&) {
     int acc = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) acc += __builtin_popcount(q[w] ^ xr[w]);
@@ -365,12 +428,15 @@ struct Tile {
 #endif
 
 // Order-preserving key of an output: larger value -> larger key, and among
-// equal values the smaller row -> larger key.  fp16: -0 counts as +0 (NaN
-// patterns order beyond the infinities); int32 (binary): two's complement.
+// equal values the smaller row -> larger key.  fp16: -0 counts as +0, and
+// every NaN (either sign, any payload) counts as larger than +inf, so the
+// first NaN wins (numpy's argmax convention); int32 (binary): two's
+// complement.
 __device__ __forceinline__ uint64_t greedy_key_f16(uint32_t bits, uint32_t row) {
   bits &= 0xFFFFu;
   if (bits == 0x8000u) bits = 0u;
-  const uint32_t ord = (bits & 0x8000u) ? (~bits & 0xFFFFu) : (bits | 0x8000u);
+  uint32_t ord = (bits & 0x8000u) ? (~bits & 0xFFFFu) : (bits | 0x8000u);
+  if ((bits & 0x7FFFu) > 0x7C00u) ord = 0xFFFFu;  // NaN
   return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - row);
 }
 __device__ __forceinline__ uint64_t greedy_key_i32(uint32_t v, uint32_t row) {
@@ -407,7 +473,7 @@ struct Runner {
   uint32_t cof[J], mof[J];
   uint32_t vc[J], vm[J];  // cof / mof plus this lane's row within a step
   uint32_t xr[J][Cd::XR];
-  float bias[J], xsum[J];
+  float xsum[FMT == kFmtHier ? J : 1];  // int4-hier-g32: sum of each chunk's x
   mutable uint64_t best = 0;  // greedy variant: best key of this lane's rows
 
   __device__ __forceinline__ Runner(const Tile& tile) : t(tile), R(Cd::make()) {
@@ -415,7 +481,7 @@ struct Runner {
     const int L = 1 << t.lg;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int local = t.sub + L * j;
+      const int local = t.sub + L * j;  // lane `sub` of the row's L lanes reads chunks sub, sub + L, ...
       const int c = t.slice * t.Cs + local;
       const bool ok = local < t.Cs && c < t.C;
       cof[j] = ok ? (uint32_t)c * 16u : kFar;
@@ -440,15 +506,7 @@ struct Runner {
         raw[4 * i + 3] = v[3];
       }
       Cd::prep(raw, xr[j]);
-      if constexpr (!kBin) {
-        Chunk zc;
-        if constexpr (Cd::PLANES == 3) {
-#pragma unroll
-          for (int p = 0; p < 3; ++p) zc.p[p] = (u32x4){Cd::kZero, Cd::kZero, Cd::kZero, Cd::kZero};
-        } else {
-          zc = (u32x4){Cd::kZero, Cd::kZero, Cd::kZero, Cd::kZero};
-        }
-        bias[j] = Cd::dot(zc, xr[j], R);
+      if constexpr (FMT == kFmtHier) {  // sum of the chunk's x, for the min term
         float sx = 0.0f;
 #pragma unroll
         for (int i = 0; i < Cd::XR; ++i) sx = __builtin_amdgcn_fdot2(as_h2(xr[j][i]), as_h2(0x3C003C00u), sx, false);
@@ -521,6 +579,25 @@ struct Runner {
     }
   }
 
+  // One row step's output value of this lane -> y (or the k-slice partials).
+  __device__ __forceinline__ void finish(int st, int u, float fv, int iv, bool writer, uint32_t* part) const {
+    const uint32_t r = row(st, u);
+    if (!writer) return;
+    if (t.S == 1) {
+      if constexpr (kBin) {
+        const uint32_t o = (uint32_t)(t.K - 2 * iv);
+        store4(t.y, r * 4u, o);
+        if (GREEDY && t.track && r < (uint32_t)t.nrows) best = max_u64(best, greedy_key_i32(o, t.row0 + r));
+      } else {
+        const uint16_t h = half_bits(fv);
+        store2(t.y, r * 2u, h);
+        if (GREEDY && t.track && r < (uint32_t)t.nrows) best = max_u64(best, greedy_key_f16(h, t.row0 + r));
+      }
+    } else if (r < (uint32_t)kMaxTileRows) {
+      part[t.slice * kMaxTileRows + r] = kBin ? (uint32_t)iv : u32(fv);
+    }
+  }
+
   __device__ __forceinline__ void compute(int st, const Buf& b, uint32_t* part) const {
     const int L = 1 << t.lg;
 #pragma unroll
@@ -529,40 +606,22 @@ struct Runner {
       float rs = 0.0f, rm = 0.0f;  // int4-hier-g32: sum of sc*dot, sum of mi*sum(x)
 #pragma unroll
       for (int j = 0; j < J; ++j) {
+        const uint32_t m = b.m[u][j];
         if constexpr (kBin) {
-          res += Cd::dot(b.c[u][j], xr[j], R);
+          res += Cd::dot(b.c[u][j], xr[j], R, typename Cd::Sub{});
         } else if constexpr (FMT == kFmtHier) {
-          const float d = Cd::dot(b.c[u][j], xr[j], R) - bias[j];
-          const uint32_t m = b.m[u][j];
+          const float d = Cd::dot(b.c[u][j], xr[j], R, Cd::sub(m, R));  // sum q x
           rs = fmaf((float)(m & 15u), d, rs);
           rm = fmaf((float)(m >> 4), xsum[j], rm);
-        } else if constexpr (FMT == kFmtInt4 || FMT == kFmtInt2 || FMT == kFmtInt3) {
-          const float d = Cd::dot(b.c[u][j], xr[j], R) - bias[j];
-          res = fmaf(half_lo(b.m[u][j]), fmaf(-half_hi(b.m[u][j]), xsum[j], d), res);
-        } else {
-          const float d = Cd::dot(b.c[u][j], xr[j], R) - bias[j];
-          res = fmaf(half_lo(b.m[u][j]), d, res);
+        } else {  // sum (q - z) x, times the group scale (low half of the metadata)
+          const float d = Cd::dot(b.c[u][j], xr[j], R, Cd::sub(m, R));
+          res = fmaf(half_lo(m), d, res);
         }
       }
       if constexpr (FMT == kFmtHier) res = fmaf(half_lo(b.rp[u]), rs, -half_hi(b.rp[u]) * rm);
       const Acc v = group_sum(res, t.lg);
-      const uint32_t r = row(st, u);
-      if (t.sub == L - 1) {
-        if (t.S == 1) {
-          if constexpr (kBin) {
-            const uint32_t o = (uint32_t)(t.K - 2 * v);
-            store4(t.y, r * 4u, o);
-            if (GREEDY && t.track && r < (uint32_t)t.nrows) best = max_u64(best, greedy_key_i32(o, t.row0 + r));
-          } else {
-            const uint16_t h = half_bits(v);
-            store2(t.y, r * 2u, h);
-            if (GREEDY && t.track && r < (uint32_t)t.nrows) best = max_u64(best, greedy_key_f16(h, t.row0 + r));
-          }
-        } else if (r < (uint32_t)kMaxTileRows) {
-          if constexpr (kBin) part[t.slice * kMaxTileRows + r] = (uint32_t)v;
-          else part[t.slice * kMaxTileRows + r] = u32(v);
-        }
-      }
+      if constexpr (kBin) finish(st, u, 0.0f, v, t.sub == L - 1, part);
+      else finish(st, u, v, 0, t.sub == L - 1, part);
     }
   }
 

@@ -114,8 +114,19 @@ def _call(name, *args):
         raise TkqError(st, name)
 
 
-def _stream(stream=None):
-    s = stream if stream is not None else torch.cuda.current_stream()
+def _stream(stream=None, *owned):
+    """The stream to enqueue on (the current one by default), as a void*.
+
+    Tensors this binding allocated (on the current stream) and hands to a
+    kernel on another stream are marked as used by that stream, so that the
+    caching allocator does not give their memory to a new allocation before
+    that stream's work is done."""
+    cur = torch.cuda.current_stream()
+    s = stream if stream is not None else cur
+    if stream is not None and stream != cur:
+        for t in owned:
+            if t is not None:
+                t.record_stream(stream)
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -143,7 +154,7 @@ def pack_int4_g128(W, stream=None):
     N, K = W.shape
     codes = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
     meta = torch.empty((N, K // 128), dtype=torch.int32, device=W.device)
-    _call("tkq_pack_int4_g128", _ptr(W), N, K, _ptr(codes), _ptr(meta), _stream(stream))
+    _call("tkq_pack_int4_g128", _ptr(W), N, K, _ptr(codes), _ptr(meta), _stream(stream, codes, meta))
     return codes, meta
 
 
@@ -153,7 +164,7 @@ def pack_k5(W, stream=None):
     N, K = W.shape
     codes = torch.empty((N, K), dtype=torch.uint8, device=W.device)
     scale = torch.empty((N, K // 128), dtype=torch.float16, device=W.device)
-    _call("tkq_pack_k5", _ptr(W), N, K, _ptr(codes), _ptr(scale), _stream(stream))
+    _call("tkq_pack_k5", _ptr(W), N, K, _ptr(codes), _ptr(scale), _stream(stream, codes, scale))
     return codes, scale
 
 
@@ -163,7 +174,7 @@ def pack_tern_g128(W, stream=None):
     N, K = W.shape
     codes = torch.empty((N, K // 16), dtype=torch.int32, device=W.device)
     scale = torch.empty((N, K // 128), dtype=torch.float16, device=W.device)
-    _call("tkq_pack_tern_g128", _ptr(W), N, K, _ptr(codes), _ptr(scale), _stream(stream))
+    _call("tkq_pack_tern_g128", _ptr(W), N, K, _ptr(codes), _ptr(scale), _stream(stream, codes, scale))
     return codes, scale
 
 
@@ -174,7 +185,7 @@ def pack_bin(W, stream=None):
     W2 = W.view(1, -1) if vec else W
     N, K = W2.shape
     bits = torch.empty((N, K // 32), dtype=torch.int32, device=W.device)
-    _call("tkq_pack_bin", _ptr(W2), N, K, _ptr(bits), _stream(stream))
+    _call("tkq_pack_bin", _ptr(W2), N, K, _ptr(bits), _stream(stream, bits))
     return bits.view(-1) if vec else bits
 
 
@@ -184,7 +195,7 @@ def pack_int2_g128(W, stream=None):
     N, K = W.shape
     codes = torch.empty((N, K // 16), dtype=torch.int32, device=W.device)
     meta = torch.empty((N, K // 128), dtype=torch.int32, device=W.device)
-    _call("tkq_pack_int2_g128", _ptr(W), N, K, _ptr(codes), _ptr(meta), _stream(stream))
+    _call("tkq_pack_int2_g128", _ptr(W), N, K, _ptr(codes), _ptr(meta), _stream(stream, codes, meta))
     return codes, meta
 
 
@@ -194,7 +205,7 @@ def pack_int3_g128(W, stream=None):
     N, K = W.shape
     codes = torch.empty((3, N, K // 32), dtype=torch.int32, device=W.device)
     meta = torch.empty((N, K // 128), dtype=torch.int32, device=W.device)
-    _call("tkq_pack_int3_g128", _ptr(W), N, K, _ptr(codes), _ptr(meta), _stream(stream))
+    _call("tkq_pack_int3_g128", _ptr(W), N, K, _ptr(codes), _ptr(meta), _stream(stream, codes, meta))
     return codes, meta
 
 
@@ -213,7 +224,7 @@ def pack_int4_hier_g32(W, stream=None):
     N, K = W.shape
     codes = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
     meta = torch.empty(hier_meta_bytes(N, K), dtype=torch.uint8, device=W.device)
-    _call("tkq_pack_int4_hier_g32", _ptr(W), N, K, _ptr(codes), _ptr(meta), _stream(stream))
+    _call("tkq_pack_int4_hier_g32", _ptr(W), N, K, _ptr(codes), _ptr(meta), _stream(stream, codes, meta))
     return codes, meta
 
 
@@ -267,9 +278,10 @@ class GemvBatch:
 
     def run(self, stream=None):
         if self.tokens is None:
-            _call("tkq_gemv", ctypes.byref(self.plan), _ptr(self.dev_descs), _stream(stream))
+            _call("tkq_gemv", ctypes.byref(self.plan), _ptr(self.dev_descs), _stream(stream, self.dev_descs))
         else:
-            _call("tkq_gemm_small", ctypes.byref(self.plan), _ptr(self.dev_descs), _stream(stream))
+            _call("tkq_gemm_small", ctypes.byref(self.plan), _ptr(self.dev_descs),
+                  _stream(stream, self.dev_descs))
 
     def greedy_scratch(self):
         """Scratch for run_argmax: one int64 per tile of the launch."""
@@ -281,15 +293,17 @@ class GemvBatch:
         _need(token, torch.int32, "token")
         _need(scratch, torch.int64, "scratch")
         _call("tkq_gemv_argmax", ctypes.byref(self.plan), _ptr(self.dev_descs), int(target),
-              _ptr(token), _ptr(scratch), scratch.numel() * 8, _stream(stream))
+              _ptr(token), _ptr(scratch), scratch.numel() * 8, _stream(stream, self.dev_descs))
 
 
 def gemv(fmt, codes, meta, x, N, K, y=None, stream=None):
     """Single GEMV y = dequant(W) . x (binary: K - 2 popcount(W ^ x), int32)."""
     fmt = FORMATS.get(fmt, fmt)
+    owned = None
     if y is None:
         dt = torch.int32 if fmt == FMT_BIN else torch.float16
-        y = torch.empty(N, dtype=dt, device=codes.device)
+        y = owned = torch.empty(N, dtype=dt, device=codes.device)
+    _stream(stream, owned)
     GemvBatch(fmt, [dict(codes=codes, meta=meta, x=x, y=y, N=N, K=K)]).run(stream)
     return y
 
@@ -305,24 +319,26 @@ def gemm_prefill(codes, meta, X, N, Y=None, workspace=None, stream=None):
     M, K = X.shape
     _need(codes, torch.int32, "codes", (N, K // 8))
     _need(meta, torch.int32, "meta", (N, K // 128))
+    owned = None
     if Y is None:
-        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+        Y = owned = torch.empty((M, N), dtype=torch.float16, device=X.device)
     _need(Y, torch.float16, "Y", (M, N))
     ws, wsb = None, 0
     if workspace is not None:
         _need(workspace, torch.float32, "workspace")
         ws, wsb = _ptr(workspace), workspace.numel() * 4
     _call("tkq_gemm_prefill", FMT_INT4_G128, M, N, K, _ptr(codes), _ptr(meta), _ptr(X), _ptr(Y),
-          ws, wsb, _stream(stream))
+          ws, wsb, _stream(stream, owned))
     return Y
 
 
 def read_probe(buf, out=None, stream=None):
     """Stream `buf` once with 16-byte non-temporal loads (bandwidth reference)."""
+    owned = None
     if out is None:
-        out = torch.zeros(4, dtype=torch.int32, device=buf.device)
+        out = owned = torch.zeros(4, dtype=torch.int32, device=buf.device)
     nbytes = buf.numel() * buf.element_size()
-    _call("tkq_read_probe", _ptr(buf), nbytes, _ptr(out), _stream(stream))
+    _call("tkq_read_probe", _ptr(buf), nbytes, _ptr(out), _stream(stream, owned))
     return out
 
 
@@ -338,7 +354,7 @@ def kv_pack(K, V, stream=None):
     if n < 0 or D != 128:
         raise TkqError(ESHAPE, "tkq_kv_cache_bytes")
     cache = torch.empty(n, dtype=torch.uint8, device=K.device)
-    _call("tkq_kv_pack", _ptr(K), _ptr(V), B, T, Hk, D, _ptr(cache), _stream(stream))
+    _call("tkq_kv_pack", _ptr(K), _ptr(V), B, T, Hk, D, _ptr(cache), _stream(stream, cache))
     return cache.view(B, Hk, T // 128, 17408)
 
 
@@ -347,17 +363,20 @@ def kv_decode(q, cache, T, sm_scale, out=None, workspace=None, stream=None):
     _need(q, torch.float16, "q")
     B, H, D = q.shape
     Hk = cache.shape[1]
+    owned = []
     if out is None:
         out = torch.empty_like(q)
+        owned.append(out)
     _need(out, torch.float16, "out", q.shape)
     nws = lib().tkq_kv_decode_workspace_bytes(B, H, Hk, T)
     if nws < 0:
         raise TkqError(ESHAPE, "tkq_kv_decode_workspace_bytes")
     if workspace is None:
         workspace = torch.empty((nws + 3) // 4, dtype=torch.float32, device=q.device)
+        owned.append(workspace)
     _need(workspace, torch.float32, "workspace")
     _call("tkq_kv_decode", _ptr(q), _ptr(cache), B, H, Hk, T, D, float(sm_scale), _ptr(out), _ptr(workspace),
-          workspace.numel() * 4, _stream(stream))
+          workspace.numel() * 4, _stream(stream, *owned))
     return out
 
 
@@ -369,18 +388,23 @@ class KvDecoder:
         _need(q, torch.float16, "q")
         B, H, D = q.shape
         Hk = cache.shape[1]
+        owned = []
         self.out = out if out is not None else torch.empty_like(q)
+        if out is None:
+            owned.append(self.out)
         _need(self.out, torch.float16, "out", q.shape)
         nws = lib().tkq_kv_decode_workspace_bytes(B, H, Hk, T)
         if nws < 0:
             raise TkqError(ESHAPE, "tkq_kv_decode_workspace_bytes")
         self.workspace = workspace if workspace is not None else torch.empty(
             (nws + 3) // 4, dtype=torch.float32, device=q.device)
+        if workspace is None:
+            owned.append(self.workspace)
         _need(self.workspace, torch.float32, "workspace")
         self._keep = (q, cache)
         self._args = (_ptr(q), _ptr(cache), B, H, Hk, T, D, ctypes.c_float(sm_scale), _ptr(self.out),
                       _ptr(self.workspace), self.workspace.numel() * 4)
-        self._stream = _stream(stream)
+        self._stream = _stream(stream, *owned)
         self._fn = lib().tkq_kv_decode
 
     def run(self):

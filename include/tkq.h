@@ -198,7 +198,10 @@ int64_t tkq_hier_meta_bytes(int64_t N, int64_t K);
  * share one coding (e.g. every linear layer read for one decoded token).
  *
  * Float codings: y[n] = sum_k w[n,k] x[k], fp32 accumulation, fp16 output
- * rounded to nearest even; |y - y_exact| <= 2e-3 * sum_k |w[n,k] x[k]|.
+ * rounded to nearest even; |y - y_exact| <= 2e-3 * sum_k |w[n,k] x[k]| for
+ * any finite fp16 x (the code offset is removed exactly before each product,
+ * so the rounding error follows |w x|, also on activation channels far
+ * larger than their weights).
  * Binary: y[n] = K - 2 * popcount(W[n] XOR x) (Whetstone README, "Measured
  * hardware facts"), exact int32.
  *
@@ -259,8 +262,8 @@ int tkq_gemv(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs,
  * their outputs in registers as they store them; a second, one-workgroup
  * kernel on the same stream combines the per-tile results.  The comparison
  * is on the stored outputs (fp16 bits for the float codings, -0 equal to +0;
- * int32 for binary); on equal values the smallest index wins; NaN outputs
- * order above +inf.
+ * int32 for binary); on equal values the smallest index wins; every NaN
+ * output (either sign) counts as larger than +inf, so the first NaN wins.
  * scratch: caller-owned device memory of scratch_bytes >= 8 * plan->tiles,
  * 16-byte aligned, any contents (overwritten).  Calls that share a scratch
  * buffer or token must not run concurrently.
@@ -332,10 +335,12 @@ int64_t tkq_kv_decode_workspace_bytes(int32_t B, int32_t H, int32_t Hk,
  * the T cached tokens of KV head h / (H / Hk), with K and V the dequantized
  * cache.  q, out: fp16 bits [B][H][D]; workspace: caller-owned device
  * memory of at least tkq_kv_decode_workspace_bytes (any contents).
- * Accuracy: the query times the K channel scale and the probability times
- * the V token scale are rounded to fp16, accumulation is fp32, out is
- * rounded to fp16; per element |out - exact| <= (4u max_t A_t + 3u) *
- * sum_t p_t |V_t,c| + 1e-6, u = 2^-11, A_t = sm_scale sum_c |q_c K_t,c|.
+ * Accuracy: both products are held to the GEMV's per-row bound (scores:
+ * |ds_t| <= e A_t, A_t = sm_scale sum_c |q_c K_t,c|; output: e sum_t p_t
+ * |V_t,c|, e = 2e-3), so per element |out - exact| <= ((1 + e) exp(2 e max_t
+ * A_t) - 1) sum_t p_t |V_t,c|.  (The kernels round the query times the K
+ * channel scale and the probability times the V token scale to fp16,
+ * accumulate in fp32 and round out to fp16.)
  * Two kernels on `stream` (the split decode, then the merge).  Returns
  * TKQ_OK, TKQ_EINVAL (null pointers, sm_scale not positive and finite,
  * workspace too small), TKQ_ESHAPE, TKQ_EALIGN or TKQ_EHIP. */

@@ -131,3 +131,19 @@ def check_gemv(y_gpu, w_deq, x, what=""):
     ok, worst = oref.check_within(np.asarray(y_gpu, np.float64), y_ref, bound)
     assert ok, "%s: worst |err|/bound = %g" % (what, worst)
     return worst
+
+
+def tile_edge_rows(desc):
+    """First and last row of every row tile of a prepared descriptor (large
+    tiles of rows_per_tile rows at the top, small tiles of small_rows below;
+    the last tile may overhang N)."""
+    N, big, rpt, sr = desc.N, desc.big_tiles, desc.rows_per_tile, desc.small_rows
+    starts = [t * rpt for t in range(big)]
+    r = big * rpt
+    while r < N:
+        starts.append(r)
+        r += sr
+    edges = []
+    for a, b in zip(starts, starts[1:] + [N]):
+        edges += [a, min(b, N) - 1]
+    return np.unique(np.asarray(edges, dtype=np.int64))

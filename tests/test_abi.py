@@ -154,6 +154,21 @@ def test_prepare_tiles_cover_rows(fmt):
     assert last.big_tiles * last.rows_per_tile < last.N
 
 
+def test_tile_edge_rows_match_the_plan():
+    """The GPU sweep test checks the first and last row of every tile through
+    helpers.tile_edge_rows: on the 7B plan it must name exactly the edges of
+    the tiles the planner made."""
+    from helpers import tile_edge_rows
+    shapes = [(n, k) for _, n, k in inputs.sweep_shapes("qwen2.5-7b")]
+    arr = _descs(1, shapes)
+    assert _prepare(arr)[0] == tkq.OK
+    for d in arr:
+        want = set()
+        for r0, h in _tiles(d):
+            want |= {r0, min(d.N, r0 + h) - 1}
+        assert set(tile_edge_rows(d).tolist()) == want
+
+
 def test_prepare_shapes_for_model_matrices():
     arr = _descs(1, [(896, 896), (896, 4864), (3584, 3584), (3584, 18944)])
     assert _prepare(arr)[0] == tkq.OK

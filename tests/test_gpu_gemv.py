@@ -181,3 +181,42 @@ def test_gemv_max_k(fmt):
     big = dict(it, K=K + unit)
     with pytest.raises(tkq.TkqError):
         tkq.GemvBatch(fmt, [big])
+
+
+@pytest.mark.parametrize("fmt", FLOAT_FMTS)
+@pytest.mark.parametrize("N,K", [(300, 896), (129, 4864), (64, 18944)])
+def test_gemv_large_activations(fmt, N, K):
+    """Activation channels of 1e3..3e4 on weights at their zero point (and one
+    outlier weight per group, heavy-tailed weights): the per-row bound holds,
+    i.e. the rounding error follows |w x| and not the activations' size."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    K = min(K, MAXK[fmt])
+    W, x = inputs.outlier_case((31, N, K), N, K)
+    items = _items(torch, tkq, fmt, [(W, x)])
+    tkq.GemvBatch(fmt, items).run()
+    torch.cuda.synchronize()
+    it = items[0]
+    _check(fmt, W, x, it["y"], it["codes"], it["meta"], "%s outliers %dx%d" % (fmt, N, K))
+
+
+def test_gemv_and_pack_on_a_side_stream():
+    """stream= names a stream other than the current one: the packer, the
+    single GEMV (whose output and descriptor table the binding allocates) and
+    a prepared batch run there and give the current-stream results."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    W, x = _inputs("int4", 333, 896, 41)
+    Wd, xd = torch.from_numpy(W).cuda(), torch.from_numpy(x).cuda()
+    codes, meta = tkq.pack_int4_g128(Wd)
+    y0 = tkq.gemv("int4", codes, meta, xd, 333, 896)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    c2, m2 = tkq.pack_int4_g128(Wd, stream=side)
+    ys = [tkq.gemv("int4", c2, m2, xd, 333, 896, stream=side) for _ in range(3)]
+    side.synchronize()
+    assert torch.equal(c2, codes) and torch.equal(m2, meta)
+    for y in ys:
+        assert torch.equal(y, y0)
+    _check("int4", W, x, y0, codes, meta, "side stream")
