@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -142,6 +143,33 @@ int rows_per_tile(int fmt, int N, int K, tkq::GemvShape sh, int64_t kTileTargetB
   return (int)(int64_t(RG) * P * steps);
 }
 
+// Scratch of tkq_gemv_argmax_static: one 64-bit key per row tile of a
+// launch, in device memory that each GPU the library runs on holds until the
+// process ends (TKQ_STATIC_SLOTS * 8 bytes = 512 KB).  Host code never uses
+// the array's name as an address: the address on each device comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) uint64_t scratch[TKQ_STATIC_SLOTS];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+uint64_t* g_scratch_ptr[kMaxDevices] = {};
+
+// This thread's current device's copy of `scratch`.
+int static_scratch(uint64_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return TKQ_EINVAL;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    g_scratch_ptr[dev] = static_cast<uint64_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return TKQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,14 +303,30 @@ int tkq_gemv(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs, void* st
 }
 
 int tkq_gemv_argmax(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs, int32_t target,
-                    int32_t* token, uint64_t* scratch, int64_t scratch_bytes, void* stream) {
+                    int32_t* token, uint64_t* slots, int64_t scratch_bytes, void* stream) {
   const int st = check_plan(plan, dev_descs);
   if (st) return st;
-  if (!token || !scratch || target < 0 || target >= plan->count) return TKQ_EINVAL;
+  if (!token || !slots || target < 0 || target >= plan->count) return TKQ_EINVAL;
   if (scratch_bytes < 8 * plan->tiles) return TKQ_EINVAL;
-  if ((reinterpret_cast<uintptr_t>(token) & 3u) || !aligned16(scratch)) return TKQ_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(token) & 3u) || !aligned16(slots)) return TKQ_EALIGN;
   return hip_status(tkq::launch_gemv(plan->fmt, plan->variant, dev_descs, plan->count, plan->tiles,
-                                     target, token, scratch, (hipStream_t)stream));
+                                     target, token, slots, (hipStream_t)stream));
+}
+
+int tkq_gemv_argmax_static(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs, int32_t target,
+                           int32_t* token, void* stream) {
+  const int st = check_plan(plan, dev_descs);
+  if (st) return st;
+  if (!token || target < 0 || target >= plan->count) return TKQ_EINVAL;
+  if (plan->tiles > TKQ_STATIC_SLOTS) return TKQ_ESHAPE;
+  if (reinterpret_cast<uintptr_t>(token) & 3u) return TKQ_EALIGN;
+  uint64_t* slots = nullptr;
+  const int ss = static_scratch(&slots);
+  if (ss) return ss;
+  // Every slot the selection reads is written by the same launch (one per
+  // tile of the target), so nothing needs clearing between calls.
+  return hip_status(tkq::launch_gemv(plan->fmt, plan->variant, dev_descs, plan->count, plan->tiles,
+                                     target, token, slots, (hipStream_t)stream));
 }
 
 int tkq_gemm_small_prepare(tkq_gemv_desc* descs, int32_t count, int32_t M, tkq_gemv_plan* plan) {

@@ -74,6 +74,7 @@ _SIGNATURES = {
     "tkq_gemv_prepare": ([ctypes.POINTER(GemvDesc), _I32, ctypes.POINTER(GemvPlan)], ctypes.c_int),
     "tkq_gemv": ([ctypes.POINTER(GemvPlan), _P, _P], ctypes.c_int),
     "tkq_gemv_argmax": ([ctypes.POINTER(GemvPlan), _P, _I32, _P, _P, _I64, _P], ctypes.c_int),
+    "tkq_gemv_argmax_static": ([ctypes.POINTER(GemvPlan), _P, _I32, _P, _P], ctypes.c_int),
     "tkq_gemm_small_prepare": ([ctypes.POINTER(GemvDesc), _I32, _I32, ctypes.POINTER(GemvPlan)],
                                ctypes.c_int),
     "tkq_gemm_small": ([ctypes.POINTER(GemvPlan), _P, _P], ctypes.c_int),
@@ -294,6 +295,14 @@ class GemvBatch:
         _need(scratch, torch.int64, "scratch")
         _call("tkq_gemv_argmax", ctypes.byref(self.plan), _ptr(self.dev_descs), int(target),
               _ptr(token), _ptr(scratch), scratch.numel() * 8, _stream(stream, self.dev_descs))
+
+    def run_argmax_static(self, target, token, stream=None):
+        """run_argmax without caller scratch (tkq_gemv_argmax_static: the
+        library's fixed per-device slot array; calls on one GPU must not
+        overlap)."""
+        _need(token, torch.int32, "token")
+        _call("tkq_gemv_argmax_static", ctypes.byref(self.plan), _ptr(self.dev_descs), int(target),
+              _ptr(token), _stream(stream, self.dev_descs))
 
 
 def gemv(fmt, codes, meta, x, N, K, y=None, stream=None):

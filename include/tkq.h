@@ -274,6 +274,25 @@ int tkq_gemv_argmax(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs,
                     int32_t target, int32_t* token, uint64_t* scratch,
                     int64_t scratch_bytes, void* stream);
 
+/* tkq_gemv_argmax without caller scratch, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The per-tile keys go to a fixed array
+ * inside the library: TKQ_STATIC_SLOTS 64-bit slots (512 KB) per GPU, held
+ * by every GPU the library runs on until the process ends; its address is
+ * looked up (hipGetSymbolAddress) on the first call on each device, with the
+ * caller's current device, which must be the device of `stream`.  Nothing in
+ * the array needs clearing: each launch writes every slot it reads.  No
+ * device memory is allocated or freed.  All calls on one GPU share the
+ * array, so calls that may overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.  Otherwise as
+ * tkq_gemv_argmax: returns TKQ_OK, TKQ_EINVAL (target out of range, null
+ * token, no usable device), TKQ_ESHAPE (plan->tiles > TKQ_STATIC_SLOTS),
+ * TKQ_EALIGN (token not 4-byte aligned), TKQ_EPLAN or TKQ_EHIP. */
+#define TKQ_STATIC_SLOTS 65536
+int tkq_gemv_argmax_static(const tkq_gemv_plan* plan,
+                           const tkq_gemv_desc* dev_descs, int32_t target,
+                           int32_t* token, void* stream);
+
 /* ---- multi-token GEMV (M = 1..16) ----------------------------------------
  * Y_i[m, n] = sum_k X_i[m, k] * w_i[n, k] for M tokens at once over many
  * int4 g128 matrices in one launch: the regime between batch-1 decode and

@@ -249,6 +249,28 @@ def test_gemv_argmax_validation():
     assert f(ctypes.byref(plan), A + 8, 1, A, A, sb, None) == tkq.EALIGN
 
 
+def test_gemv_argmax_static_validation():
+    """The allocation-free greedy entry point rejects every bad argument on
+    the host, before any HIP call, including plans with more row tiles than
+    its fixed slot array holds."""
+    f = tkq.lib().tkq_gemv_argmax_static
+    plan = tkq.GemvPlan()
+    plan.fmt, plan.count, plan.tiles = 1, 1, 1
+    assert f(ctypes.byref(plan), A, 0, A, None) == tkq.EPLAN
+    arr = _descs(1, [(8, 128), (16, 256)])
+    st, plan = _prepare(arr)
+    assert st == tkq.OK
+    assert f(ctypes.byref(plan), A, -1, A, None) == tkq.EINVAL
+    assert f(ctypes.byref(plan), A, 2, A, None) == tkq.EINVAL
+    assert f(ctypes.byref(plan), A, 1, None, None) == tkq.EINVAL
+    assert f(ctypes.byref(plan), A, 1, A + 2, None) == tkq.EALIGN
+    assert f(ctypes.byref(plan), A + 8, 1, A, None) == tkq.EALIGN
+    big = _descs(1, [(1, 128)] * 70000)             # one row tile each
+    st, bplan = _prepare(big)
+    assert st == tkq.OK and bplan.tiles > 65536
+    assert f(ctypes.byref(bplan), A, 0, A, None) == tkq.ESHAPE
+
+
 def test_gemm_small_prepare():
     f = tkq.lib().tkq_gemm_small_prepare
     arr = _descs(1, [(1, 128), (64, 896), (65, 896), (151936, 896)])
