@@ -51,18 +51,7 @@ constexpr int kGemvMaxTileRows = 1024;
 // Row steps a wave keeps in flight per loop iteration for J passes: deep
 // enough that every CU has ~100 KB of loads outstanding.  Used by the kernel
 // and by the planner (tile heights are multiples of it).
-#ifndef TKQ_GEMV_U1
-#define TKQ_GEMV_U1 4
-#endif
-#ifndef TKQ_GEMV_U2
-#define TKQ_GEMV_U2 2
-#endif
-#ifndef TKQ_GEMV_U3
-#define TKQ_GEMV_U3 1
-#endif
-__host__ __device__ constexpr int gemv_unroll(int passes) {
-  return passes == 1 ? TKQ_GEMV_U1 : (passes == 2 ? TKQ_GEMV_U2 : TKQ_GEMV_U3);
-}
+__host__ __device__ constexpr int gemv_unroll(int passes) { return passes == 1 ? 4 : (passes == 2 ? 2 : 1); }
 
 // Largest `passes` value each kernel variant supports (x stays in registers).
 int gemv_max_passes(int fmt);
@@ -80,11 +69,16 @@ hipError_t launch_small_m(const tkq_gemv_desc* dev_descs, int count, int64_t til
 
 // Low-bit KV cache (pages of 128 tokens, head dimension 128) and decode.
 constexpr int kKvPage = 128, kKvDim = 128, kKvPageBytes = 17408, kKvWaves = 4, kKvMaxGroup = 8;
-hipError_t launch_kv_pack(const uint16_t* K, const uint16_t* V, int B, int T, int Hk, uint32_t* cache,
-                          hipStream_t stream);
+// lens: device int32 [B] of valid tokens per sequence (clamped to [0, T]), or
+// nullptr for all T.
+hipError_t launch_kv_pack(const uint16_t* K, const uint16_t* V, const int32_t* lens, int B, int T, int Hk,
+                          uint32_t* cache, hipStream_t stream);
 int kv_splits(int B, int H, int Hk, int T, int cus, int* pages_per_split);
-hipError_t launch_kv_decode(const uint16_t* q, const uint32_t* cache, int B, int H, int Hk, int T, float sm_scale,
-                            uint16_t* out, float* ws, int splits, int pages_per_split, hipStream_t stream);
+// ws: the splits' partials; counters: one zero-initialised uint32 per
+// (sequence, head group), left at zero by every completed call.
+hipError_t launch_kv_decode(const uint16_t* q, const uint32_t* cache, const int32_t* lens, int B, int H, int Hk,
+                            int T, float sm_scale, uint16_t* out, float* ws, uint32_t* counters, int splits,
+                            int pages_per_split, hipStream_t stream);
 
 hipError_t launch_pack(int fmt, const float* W, int64_t N, int64_t K, void* codes, void* meta,
                        hipStream_t stream);

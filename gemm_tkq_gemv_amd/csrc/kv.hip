@@ -27,8 +27,13 @@
 //    order); 4 lanes per channel (32 tokens each).
 //  * The constant parts of the magic-number products (1024 or 64 per code
 //    position) and the zero points are removed per lane chunk in fp32.
-//  * Each workgroup writes (m, l, o[128]) per query head to a workspace; a
-//    second kernel merges the splits (log-sum-exp) and stores fp16.
+//  * Each workgroup writes (m, l, o[128]) per query head to a workspace.
+//    With few splits (short contexts) it counts its arrival and the last
+//    split of each (sequence, head group) to arrive merges the splits
+//    (log-sum-exp) and stores fp16, so a decode step is one launch; with
+//    more, a second kernel merges them.
+//  * Per-sequence lengths: pages past a sequence's length are skipped and
+//    the tokens past it in its last page get score -inf.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -72,20 +77,30 @@ __device__ __forceinline__ uint32_t quant_group(const float* v, int stride, uint
   return (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)half_bits(z) << 16);
 }
 
+// Valid tokens of sequence b: lens[b] clamped to [0, T] (all T without lens).
+__device__ __forceinline__ int seq_len(const int32_t* lens, int b, int T) {
+  return lens ? min(max(lens[b], 0), T) : T;
+}
+
 // One workgroup (256 threads) per page; K and V are fp16 [B][T][Hk][128].
+// Tokens at or past the sequence's length are quantized as zeros: K groups
+// (a channel over the page) already span 0, so their scale and zero-point
+// are those of the valid tokens alone; such a V token is an all-zero group.
 __global__ __launch_bounds__(256) void kv_pack_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                                                      int T, int Hk, uint32_t* __restrict__ cache) {
+                                                      const int32_t* __restrict__ lens, int T, int Hk,
+                                                      uint32_t* __restrict__ cache) {
   __shared__ float tile[kPage * (kD + 1)];
   __shared__ uint8_t codes[kPage * kD];
   const int p = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int P = T / kPage;
   uint32_t* page = cache + (((size_t)b * Hk + hk) * P + p) * kPageWords;
+  const int valid = seq_len(lens, b, T) - kPage * p;  // valid tokens of this page (may be <= 0 or > 128)
   for (int part = 0; part < 2; ++part) {
     const uint16_t* src = part == 0 ? K : V;
     // tile[t][c] = value of token 128p + t, channel c
     for (int i = threadIdx.x; i < kPage * kD; i += 256) {
       const int t = i / kD, c = i - t * kD;
-      const uint16_t bits = src[(((size_t)b * T + (size_t)kPage * p + t) * Hk + hk) * kD + c];
+      const uint16_t bits = t < valid ? src[(((size_t)b * T + (size_t)kPage * p + t) * Hk + hk) * kD + c] : 0;
       tile[t * (kD + 1) + c] = (float)__builtin_bit_cast(_Float16, bits);
     }
     __syncthreads();
@@ -169,6 +184,66 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return v;
 }
 
+// Partial results cross workgroups on different XCDs, whose L2 caches are
+// not coherent with each other: they are written and read with device-scope
+// (sc1) accesses, which go to the device-coherent level, so no cache
+// write-back or invalidation (a release/acquire fence) is needed.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Splits up to which the decode merges its partials in the kernel itself
+// (the last split of a head group to finish does it); with more, one more
+// launch (kv_merge_kernel) spreads the merge over every (sequence, head).
+constexpr int kFuseMaxSplits = 16;
+
+// The arrival of one split of a (sequence, head group): its partial
+// (o[128], m, l per head) is in ws.  Every wave waits until its partial
+// stores are performed, then one thread counts the workgroup's arrival; the
+// last of the `splits` (<= kFuseMaxSplits) workgroups to arrive merges the
+// partials (log-sum-exp; a thread's loads are all issued before any is
+// used), stores fp16 out and resets the counter to 0 for the next call.  No
+// workgroup waits for another.
+__device__ __forceinline__ void arrive_and_merge(const float* ws, uint32_t* counter, int splits, int bh0, int ng,
+                                                 uint16_t* __restrict__ out) {
+  __shared__ int is_last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    is_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (uint32_t)(splits - 1);
+  __syncthreads();
+  if (!is_last) return;
+  for (int i = threadIdx.x; i < ng * kD; i += 256) {
+    const int g = i / kD, c = i - g * kD;
+    const float* w = ws + (size_t)(bh0 + g) * splits * (kD + 2);
+    float ms[kFuseMaxSplits], ls[kFuseMaxSplits], os[kFuseMaxSplits];
+#pragma unroll
+    for (int sp = 0; sp < kFuseMaxSplits; ++sp) {
+      const float* ws_sp = w + (size_t)(sp < splits ? sp : 0) * (kD + 2);  // always in range
+      ms[sp] = ld_dev(ws_sp + kD);
+      ls[sp] = ld_dev(ws_sp + kD + 1);
+      os[sp] = ld_dev(ws_sp + c);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < kFuseMaxSplits; ++sp)
+      if (sp < splits) M = fmaxf(M, ms[sp]);
+    float O = 0.0f, L = 0.0f;
+#pragma unroll
+    for (int sp = 0; sp < kFuseMaxSplits; ++sp) {
+      const float a = sp >= splits || ms[sp] == -INFINITY ? 0.0f : exp2f(ms[sp] - M);
+      L = fmaf(ls[sp], a, L);
+      O = fmaf(os[sp], a, O);
+    }
+    out[(size_t)(bh0 + g) * kD + c] = half_bits(L > 0.0f ? O / L : 0.0f);  // no valid token: 0
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 struct WaveLds {
   uint32_t meta[256];           // K meta [128 channels] then V meta [128 tokens]
   uint32_t qv[kKvMaxGroup][kD / 2];  // query heads, fp16 pairs in natural order
@@ -183,9 +258,11 @@ struct WaveLds {
 // so the host picks it by pages per wave.
 template <int G, bool KUP = false>
 __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restrict__ q,
-                                                        const uint32_t* __restrict__ cache, int H, int Hk, int P,
+                                                        const uint32_t* __restrict__ cache,
+                                                        const int32_t* __restrict__ lens, int H, int Hk, int P,
                                                         int pages_per_split, float scale_log2,
-                                                        float* __restrict__ ws, int splits) {
+                                                        float* __restrict__ ws, int splits,
+                                                        uint32_t* __restrict__ counters, uint16_t* __restrict__ out) {
   __shared__ WaveLds lds[kWaves];
   __shared__ float merge[kWaves][G][kD + 2];
   constexpr bool kKUp = KUP && G == 1;
@@ -214,10 +291,12 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
   }
   for (int i = lane; i < G * kD; i += 64) L.o[i / kD][i % kD] = 0.0f;
 
-  const int p0 = split * pages_per_split, p1 = min(P, p0 + pages_per_split);
+  const int len = seq_len(lens, b, P * kPage);
+  const int p0 = split * pages_per_split, p1 = min((len + kPage - 1) / kPage, p0 + pages_per_split);
   const uint32_t* base = cache + ((size_t)b * Hk + hk) * (size_t)P * kPageWords;
   for (int p = p0 + wave; p < p1; p += kWaves) {
     const __amdgpu_buffer_rsrc_t pg = make_rsrc(base + (size_t)p * kPageWords, kPageWords * 4u);
+    const int valid = len - kPage * p;  // tokens t >= valid are past the sequence (last page only)
     // page metadata -> LDS (one 16-byte load per lane covers all 256 words)
     const u32x4 mt = load16(pg, (uint32_t)(kKM + 4 * lane) * 4u);
     u32x4 kall[kKUp ? 8 : 1];
@@ -270,7 +349,10 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
             else kc[i] = load16_nt(pg, (uint32_t)(kKC + 16 * (16 * (4 * half + i) + quad) + 4 * sub) * 4u);
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[4 * half + i] = quad_sum(chunk_dot(kc[i], qp, R) - cst) * scale_log2;
+          for (int i = 0; i < 4; ++i) {
+            const float v = quad_sum(chunk_dot(kc[i], qp, R) - cst) * scale_log2;
+            sc[4 * half + i] = 16 * (4 * half + i) + quad < valid ? v : -INFINITY;
+          }
         }
       }
 
@@ -358,13 +440,14 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
       Lsum += merge[w][g][kD + 1] * a;
       O += merge[w][g][c] * a;
     }
-    float* out = ws + (((size_t)b * H + h0 + g) * splits + split) * (kD + 2);
-    out[c] = O;
+    float* dst = ws + (((size_t)b * H + h0 + g) * splits + split) * (kD + 2);
+    st_dev(dst + c, O);
     if (c == 0) {
-      out[kD] = M;
-      out[kD + 1] = Lsum;
+      st_dev(dst + kD, M);
+      st_dev(dst + kD + 1, Lsum);
     }
   }
+  if (counters) arrive_and_merge(ws, counters + (size_t)b * gridDim.y + hsub, splits, b * H + h0, G, out);
 }
 
 // ------------------------------------------------- decode, grouped queries --
@@ -383,7 +466,7 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
 //    D[channel][head] - sum_t p'_t (1024 + zV_t) is the page's output, and
 //    each lane keeps its head's 32 output values in registers.
 //  * the four waves' partials (m, l, o) are combined in LDS and the
-//    workgroup writes one partial per head and split for the merge kernel.
+//    workgroup writes one partial per head and split; the last to arrive merges.
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -398,15 +481,6 @@ __device__ __forceinline__ half8 as_half8(const uint32_t* p) {
   return __builtin_bit_cast(half8, v);
 }
 
-#ifndef TKQ_KV_UPFRONT
-#define TKQ_KV_UPFRONT 0  // issue every load of a page before its scores (more registers: measured slower)
-#endif
-#ifndef TKQ_KV_MFMA_WPE
-#define TKQ_KV_MFMA_WPE (TKQ_KV_UPFRONT ? 2 : 3)  // minimum waves per SIMD the register budget must allow
-#endif
-#ifndef TKQ_KV_VPREFETCH
-#define TKQ_KV_VPREFETCH 1  // load the first V codes before the softmax (more registers)
-#endif
 
 // LDS of the matrix-core kernel: the page loop's buffers, reused after it
 // for the combination of the four waves' partials.
@@ -421,10 +495,10 @@ union MfmaLds {
 };
 
 // NG: query heads of this workgroup (1..16, padded to 16 MFMA columns).
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA_WPE, 8))) void kv_decode_mfma_kernel(const uint16_t* __restrict__ q,
-                                                             const uint32_t* __restrict__ cache, int H, int Hk,
-                                                             int P, int pages_per_split, float scale_log2,
-                                                             float* __restrict__ ws, int splits, int NG) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void kv_decode_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint32_t* __restrict__ cache, const int32_t* __restrict__ lens, int H,
+    int Hk, int P, int pages_per_split, float scale_log2, float* __restrict__ ws, int splits, int NG,
+    uint32_t* __restrict__ counters, uint16_t* __restrict__ out) {
   __shared__ MfmaLds lds;
   auto& qv = lds.loop.qv;
   const int split = blockIdx.x, hsub = blockIdx.y, b = blockIdx.z;
@@ -446,19 +520,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int p0 = split * pages_per_split, p1 = min(P, p0 + pages_per_split);
+  const int len = seq_len(lens, b, P * kPage);
+  const int p0 = split * pages_per_split, p1 = min((len + kPage - 1) / kPage, p0 + pages_per_split);
   const uint32_t* base = cache + ((size_t)b * Hk + hk) * (size_t)P * kPageWords;
   for (int p = p0 + wave; p < p1; p += kWaves) {
     const __amdgpu_buffer_rsrc_t pg = make_rsrc(base + (size_t)p * kPageWords, kPageWords * 4u);
-#if TKQ_KV_UPFRONT
-    u32x4 kc[8], vc[8];
-    const u32x4 mt = load16(pg, (uint32_t)(kKM + 4 * lane) * 4u);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) kc[i] = load16_nt(pg, (uint32_t)(kKC + 16 * (16 * i + col) + 4 * blk) * 4u);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) vc[i] = load16_nt(pg, (uint32_t)(kVC + 16 * (16 * i + col) + 4 * blk) * 4u);
-    *reinterpret_cast<u32x4*>(&meta[4 * lane]) = mt;
-#else
+    const int valid = len - kPage * p;  // tokens t >= valid are past the sequence (last page only)
     // the K codes are requested before the metadata is stored to LDS, so
     // both arrive in one round trip
     prio_on();
@@ -468,7 +535,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA
     for (int i = 0; i < 4; ++i) kc[i] = load16_nt(pg, (uint32_t)(kKC + 16 * (16 * i + col) + 4 * blk) * 4u);
     prio_off();
     *reinterpret_cast<u32x4*>(&meta[4 * lane]) = mt;
-#endif
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
@@ -504,33 +570,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA
     float sc[8][4];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-#if !TKQ_KV_UPFRONT
       if (half == 1) {
         prio_on();
 #pragma unroll
         for (int i = 0; i < 4; ++i) kc[i] = load16_nt(pg, (uint32_t)(kKC + 16 * (16 * (4 + i) + col) + 4 * blk) * 4u);
         prio_off();
       }
-#endif
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
-        const u32x4 kw = kc[TKQ_KV_UPFRONT ? 4 * half + i : i];
+        const u32x4 kw = kc[i];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           d = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_plain(kw[j], M4, magic), as_half8(qb + 4 * j), d, 0,
                                                      0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[4 * half + i][r] = (d[r] - cst) * scale_log2;
+        for (int r = 0; r < 4; ++r)
+          sc[4 * half + i][r] = 16 * (4 * half + i) + 4 * blk + r < valid ? (d[r] - cst) * scale_log2 : -INFINITY;
       }
     }
-#if TKQ_KV_VPREFETCH && !TKQ_KV_UPFRONT
+    // the first half of the V codes is requested before the softmax
     u32x4 vc[4];
     prio_on();
 #pragma unroll
     for (int i = 0; i < 4; ++i) vc[i] = load16_nt(pg, (uint32_t)(kVC + 16 * (16 * i + col) + 4 * blk) * 4u);
     prio_off();
-#endif
 
     // ---- online softmax for head col
     float pm = sc[0][0];
@@ -575,24 +639,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA
       for (int i = 0; i < 16; ++i) praw[i] = src[i];
       pair_order(praw, pb);
     }
-#if !TKQ_KV_VPREFETCH && !TKQ_KV_UPFRONT
-    u32x4 vc[4];
-#endif
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-#if !TKQ_KV_UPFRONT
-      if (half == 1 || !TKQ_KV_VPREFETCH) {
+      if (half == 1) {
         prio_on();
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vc[i] = load16_nt(pg, (uint32_t)(kVC + 16 * (16 * (4 * half + i) + col) + 4 * blk) * 4u);
+        for (int i = 0; i < 4; ++i) vc[i] = load16_nt(pg, (uint32_t)(kVC + 16 * (16 * (4 + i) + col) + 4 * blk) * 4u);
         prio_off();
       }
-#endif
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
-        const u32x4 vw = vc[TKQ_KV_UPFRONT ? 4 * half + i : i];
+        const u32x4 vw = vc[i];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           d = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_plain(vw[j], M4, magic), as_half8(pb + 4 * j), d, 0,
@@ -630,16 +688,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_KV_MFMA
       Lsum += lds.part[w][g][kD + 1] * a;
       O += lds.part[w][g][c] * a;
     }
-    float* out = ws + (((size_t)b * H + h0 + g) * splits + split) * (kD + 2);
-    out[c] = O;
+    float* dst = ws + (((size_t)b * H + h0 + g) * splits + split) * (kD + 2);
+    st_dev(dst + c, O);
     if (c == 0) {
-      out[kD] = M;
-      out[kD + 1] = Lsum;
+      st_dev(dst + kD, M);
+      st_dev(dst + kD + 1, Lsum);
     }
   }
+  if (counters) arrive_and_merge(ws, counters + (size_t)b * gridDim.y + hsub, splits, b * H + h0, NG, out);
 }
 
-// One workgroup per (b, head): merge the splits, normalise, store fp16.
+// One workgroup per (b, head): merge the splits, normalise, store fp16
+// (decodes with more than kFuseMaxSplits splits).
 // 512 threads = 4 groups of 128 channels; the splits are taken 512 at a time
 // (weights exp2(m_s - M) in LDS) and dealt round-robin to the groups, whose
 // sums meet in LDS at the end.  Maxima and sums over threads: within each
@@ -688,25 +748,22 @@ __global__ __launch_bounds__(kMergeThreads) void kv_merge_kernel(const float* __
     for (int i = 0; i < kMergeWaves; ++i) L += wsum[i];
 #pragma unroll
     for (int j = 0; j < kMergeGroups; ++j) t += osum[j][c];
-    out[(size_t)bh * kD + c] = half_bits(t / L);
+    out[(size_t)bh * kD + c] = half_bits(L > 0.0f ? t / L : 0.0f);  // no valid token: 0
   }
 }
 
 }  // namespace
 
-hipError_t launch_kv_pack(const uint16_t* K, const uint16_t* V, int B, int T, int Hk, uint32_t* cache,
-                          hipStream_t stream) {
+hipError_t launch_kv_pack(const uint16_t* K, const uint16_t* V, const int32_t* lens, int B, int T, int Hk,
+                          uint32_t* cache, hipStream_t stream) {
   hipLaunchKernelGGL(kv_pack_kernel, dim3((uint32_t)(T / kPage), (uint32_t)Hk, (uint32_t)B), dim3(256), 0, stream, K,
-                     V, T, Hk, cache);
+                     V, lens, T, Hk, cache);
   return hipGetLastError();
 }
 
-// Grouped queries (at least TKQ_KV_MFMA_MIN heads per KV head) take the
-// matrix-core kernel.
-#ifndef TKQ_KV_MFMA_MIN
-#define TKQ_KV_MFMA_MIN 3
-#endif
-bool kv_use_mfma(int H, int Hk) { return H / Hk >= TKQ_KV_MFMA_MIN; }
+// Grouped queries (at least 3 query heads per KV head) take the matrix-core
+// kernel.
+bool kv_use_mfma(int H, int Hk) { return H / Hk >= 3; }
 
 // Query heads per workgroup: the whole group if it fits (8 heads for the
 // vector-ALU kernel, 16 for the matrix-core one), else its largest divisor
@@ -723,15 +780,9 @@ int kv_splits(int B, int H, int Hk, int T, int cus, int* pages_per_split) {
   const int P = T / kPage;
   const int gb = kv_heads_per_wg(H, Hk);
   const int64_t groups = (int64_t)B * (H / gb);
-  // enough workgroups for a few per CU (every wave streams its own pages;
+  // enough workgroups for about 4 per CU (every wave streams its own pages;
   // the merge of more splits costs little), at least one page per wave
-#ifndef TKQ_KV_WG_PER_CU
-#define TKQ_KV_WG_PER_CU 4
-#endif
-#ifndef TKQ_KV_MFMA_WG_PER_CU
-#define TKQ_KV_MFMA_WG_PER_CU 4
-#endif
-  const int per_cu = kv_use_mfma(H, Hk) ? TKQ_KV_MFMA_WG_PER_CU : TKQ_KV_WG_PER_CU;
+  const int per_cu = 4;
   int64_t want = ((int64_t)per_cu * cus + groups - 1) / groups;
   int64_t max_splits = (P + kWaves - 1) / kWaves;
   if (want > max_splits) want = max_splits;
@@ -741,48 +792,46 @@ int kv_splits(int B, int H, int Hk, int T, int cus, int* pages_per_split) {
   return (P + pps - 1) / pps;
 }
 
-hipError_t launch_kv_decode(const uint16_t* q, const uint32_t* cache, int B, int H, int Hk, int T, float sm_scale,
-                            uint16_t* out, float* ws, int splits, int pages_per_split, hipStream_t stream) {
+hipError_t launch_kv_decode(const uint16_t* q, const uint32_t* cache, const int32_t* lens, int B, int H, int Hk,
+                            int T, float sm_scale, uint16_t* out, float* ws, uint32_t* counters, int splits,
+                            int pages_per_split, hipStream_t stream) {
   const int P = T / kPage;
   const int gb = kv_heads_per_wg(H, Hk);
-  if (kv_use_mfma(H, Hk)) {
-    const dim3 grid((uint32_t)splits, (uint32_t)(H / gb), (uint32_t)B);
-    hipLaunchKernelGGL(kv_decode_mfma_kernel, grid, dim3(256), 0, stream, q, cache, H, Hk, P, pages_per_split,
-                       sm_scale * kLog2e, ws, splits, gb);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kv_merge_kernel, dim3((uint32_t)(B * H)), dim3(kMergeThreads), 0, stream, ws, splits, out);
-    return hipGetLastError();
-  }
   const dim3 grid((uint32_t)splits, (uint32_t)(H / gb), (uint32_t)B);
   const float sl2 = sm_scale * kLog2e;
-  switch (gb) {
-#define TKQ_KV_CASE(G)                                                                                          \
-  case G:                                                                                                      \
-    hipLaunchKernelGGL(kv_decode_kernel<G>, grid, dim3(256), 0, stream, q, cache, H, Hk, P, pages_per_split, sl2, \
-                       ws, splits);                                                                            \
+  uint32_t* cnt = splits <= kFuseMaxSplits ? counters : nullptr;  // fused merge, else a merge launch
+  if (kv_use_mfma(H, Hk)) {
+    hipLaunchKernelGGL(kv_decode_mfma_kernel, grid, dim3(256), 0, stream, q, cache, lens, H, Hk, P, pages_per_split,
+                       sl2, ws, splits, gb, cnt, out);
+  } else {
+    switch (gb) {
+#define TKQ_KV_CASE(G)                                                                                           \
+  case G:                                                                                                       \
+    hipLaunchKernelGGL(kv_decode_kernel<G>, grid, dim3(256), 0, stream, q, cache, lens, H, Hk, P, pages_per_split, \
+                       sl2, ws, splits, cnt, out);                                                              \
     break;
-    case 1:
-      if (pages_per_split <= kWaves)  // one page per wave: K codes with the metadata
-        hipLaunchKernelGGL((kv_decode_kernel<1, true>), grid, dim3(256), 0, stream, q, cache, H, Hk, P,
-                           pages_per_split, sl2, ws, splits);
-      else
-        hipLaunchKernelGGL((kv_decode_kernel<1, false>), grid, dim3(256), 0, stream, q, cache, H, Hk, P,
-                           pages_per_split, sl2, ws, splits);
-      break;
-    TKQ_KV_CASE(2)
-    TKQ_KV_CASE(3)
-    TKQ_KV_CASE(4)
-    TKQ_KV_CASE(5)
-    TKQ_KV_CASE(6)
-    TKQ_KV_CASE(7)
-    TKQ_KV_CASE(8)
+      case 1:
+        if (pages_per_split <= kWaves)  // one page per wave: K codes with the metadata
+          hipLaunchKernelGGL((kv_decode_kernel<1, true>), grid, dim3(256), 0, stream, q, cache, lens, H, Hk, P,
+                             pages_per_split, sl2, ws, splits, cnt, out);
+        else
+          hipLaunchKernelGGL((kv_decode_kernel<1, false>), grid, dim3(256), 0, stream, q, cache, lens, H, Hk, P,
+                             pages_per_split, sl2, ws, splits, cnt, out);
+        break;
+      TKQ_KV_CASE(2)
+      TKQ_KV_CASE(3)
+      TKQ_KV_CASE(4)
+      TKQ_KV_CASE(5)
+      TKQ_KV_CASE(6)
+      TKQ_KV_CASE(7)
+      TKQ_KV_CASE(8)
 #undef TKQ_KV_CASE
-    default:
-      return hipErrorInvalidValue;
+      default:
+        return hipErrorInvalidValue;
+    }
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || cnt) return e;
   hipLaunchKernelGGL(kv_merge_kernel, dim3((uint32_t)(B * H)), dim3(kMergeThreads), 0, stream, ws, splits, out);
   return hipGetLastError();
 }

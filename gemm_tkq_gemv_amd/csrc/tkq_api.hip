@@ -28,30 +28,13 @@ constexpr int64_t kMaxWeights = int64_t(1) << 39;
 //  max_passes  cap on passes: the launch's kernel variant is sized for the
 //         largest pass count of its matrices, so one long-K matrix would set
 //         the register budget (and occupancy) of the whole sweep.
-#ifndef TKQ_TERN_JMAX
-#define TKQ_TERN_JMAX 2
-#endif
 struct PlanParams {
   int prefer_passes, max_passes;
   int64_t tile, small, tail;
 };
-#ifndef TKQ_INT4_PREFER
-#define TKQ_INT4_PREFER 2
-#endif
-#ifndef TKQ_INT4_TILE_KB
-#define TKQ_INT4_TILE_KB 48
-#endif
-#ifndef TKQ_SMALL_TILE_KB
-#define TKQ_SMALL_TILE_KB 4
-#endif
-#ifndef TKQ_TAIL_MB
-#define TKQ_TAIL_MB 60
-#endif
 PlanParams plan_params(int fmt) {
-  if (fmt == TKQ_FMT_INT4_G128 || fmt == TKQ_FMT_INT4_HIER_G32)
-    return {TKQ_INT4_PREFER, 4, int64_t(TKQ_INT4_TILE_KB) << 10, int64_t(TKQ_SMALL_TILE_KB) << 10,
-            int64_t(TKQ_TAIL_MB) << 20};
-  if (fmt == TKQ_FMT_TERN_G128 || fmt == TKQ_FMT_INT2_G128) return {1, TKQ_TERN_JMAX, 24 << 10, 4 << 10, 40 << 20};
+  if (fmt == TKQ_FMT_INT4_G128 || fmt == TKQ_FMT_INT4_HIER_G32) return {2, 4, 48 << 10, 4 << 10, 60 << 20};
+  if (fmt == TKQ_FMT_TERN_G128 || fmt == TKQ_FMT_INT2_G128) return {1, 2, 24 << 10, 4 << 10, 40 << 20};
   if (fmt == TKQ_FMT_INT3_G128) return {1, 1, 24 << 10, 4 << 10, 40 << 20};
   return {1, 8, 24 << 10, 4 << 10, 40 << 20};
 }
@@ -381,30 +364,30 @@ int64_t tkq_kv_cache_bytes(int32_t B, int32_t Hk, int32_t T) {
   return int64_t(B) * Hk * (T / tkq::kKvPage) * tkq::kKvPageBytes;
 }
 
-int64_t tkq_kv_decode_workspace_bytes(int32_t B, int32_t H, int32_t Hk, int32_t T) {
-  if (check_kv(B, H, Hk, T, tkq::kKvDim)) return -1;
-  // one (m, l, o[128]) partial per wave of every split, at most one split per kKvWaves pages
+}  // extern "C"
+
+namespace {
+// Workspace of a decode: one arrival counter per (sequence, query head)
+// first (so that a workspace zeroed once serves every later call with no
+// more sequences x heads), then the splits' partials at a 16-byte boundary
+// (one (m, l, o[128]) per head and split, at most one split per kKvWaves
+// pages).
+int64_t kv_counter_bytes(int32_t B, int32_t H) { return (int64_t(B) * H * 4 + 15) / 16 * 16; }
+int64_t kv_partial_bytes(int32_t B, int32_t H, int32_t T) {
   const int64_t max_parts = (T / tkq::kKvPage + tkq::kKvWaves - 1) / tkq::kKvWaves * tkq::kKvWaves;
   return int64_t(B) * H * max_parts * (tkq::kKvDim + 2) * 4;
 }
 
-int tkq_kv_pack(const uint16_t* K, const uint16_t* V, int32_t B, int32_t T, int32_t Hk, int32_t D, uint32_t* cache,
-                void* stream) {
-  if (!K || !V || !cache) return TKQ_EINVAL;
-  const int st = check_kv(B, Hk, Hk, T, D);
-  if (st) return st;
-  if (!aligned16(K) || !aligned16(V) || !aligned16(cache)) return TKQ_EALIGN;
-  return hip_status(tkq::launch_kv_pack(K, V, B, T, Hk, cache, (hipStream_t)stream));
-}
-
-int tkq_kv_decode(const uint16_t* q, const uint32_t* cache, int32_t B, int32_t H, int32_t Hk, int32_t T, int32_t D,
-                  float sm_scale, uint16_t* out, float* workspace, int64_t workspace_bytes, void* stream) {
+int kv_decode_common(const uint16_t* q, const uint32_t* cache, const int32_t* lens, int32_t B, int32_t H,
+                     int32_t Hk, int32_t T, int32_t D, float sm_scale, uint16_t* out, float* workspace,
+                     int64_t workspace_bytes, void* stream) {
   if (!q || !cache || !out || !workspace) return TKQ_EINVAL;
   const int st = check_kv(B, H, Hk, T, D);
   if (st) return st;
   if (!(sm_scale > 0.0f) || !(sm_scale < 1e30f)) return TKQ_EINVAL;
   if (workspace_bytes < tkq_kv_decode_workspace_bytes(B, H, Hk, T)) return TKQ_EINVAL;
   if (!aligned16(q) || !aligned16(cache) || !aligned16(out) || !aligned16(workspace)) return TKQ_EALIGN;
+  if (lens && (reinterpret_cast<uintptr_t>(lens) & 3u)) return TKQ_EALIGN;
   int device = 0;
   hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &device) : hipGetDevice(&device);
   if (e != hipSuccess) return hip_status(e);
@@ -413,8 +396,51 @@ int tkq_kv_decode(const uint16_t* q, const uint32_t* cache, int32_t B, int32_t H
   if (e != hipSuccess) return hip_status(e);
   int pps = 1;
   const int splits = tkq::kv_splits(B, H, Hk, T, cus, &pps);
-  return hip_status(tkq::launch_kv_decode(q, cache, B, H, Hk, T, sm_scale, out, workspace, splits, pps,
+  uint32_t* counters = reinterpret_cast<uint32_t*>(workspace);
+  float* parts = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kv_counter_bytes(B, H));
+  return hip_status(tkq::launch_kv_decode(q, cache, lens, B, H, Hk, T, sm_scale, out, parts, counters, splits, pps,
                                           (hipStream_t)stream));
+}
+
+int kv_pack_common(const uint16_t* K, const uint16_t* V, const int32_t* lens, int32_t B, int32_t T, int32_t Hk,
+                   int32_t D, uint32_t* cache, void* stream) {
+  if (!K || !V || !cache) return TKQ_EINVAL;
+  const int st = check_kv(B, Hk, Hk, T, D);
+  if (st) return st;
+  if (!aligned16(K) || !aligned16(V) || !aligned16(cache)) return TKQ_EALIGN;
+  if (lens && (reinterpret_cast<uintptr_t>(lens) & 3u)) return TKQ_EALIGN;
+  return hip_status(tkq::launch_kv_pack(K, V, lens, B, T, Hk, cache, (hipStream_t)stream));
+}
+}  // namespace
+
+extern "C" {
+
+int64_t tkq_kv_decode_workspace_bytes(int32_t B, int32_t H, int32_t Hk, int32_t T) {
+  if (check_kv(B, H, Hk, T, tkq::kKvDim)) return -1;
+  return kv_counter_bytes(B, H) + kv_partial_bytes(B, H, T);
+}
+
+int tkq_kv_pack(const uint16_t* K, const uint16_t* V, int32_t B, int32_t T, int32_t Hk, int32_t D, uint32_t* cache,
+                void* stream) {
+  return kv_pack_common(K, V, nullptr, B, T, Hk, D, cache, stream);
+}
+
+int tkq_kv_pack_varlen(const uint16_t* K, const uint16_t* V, const int32_t* seqlens, int32_t B, int32_t T,
+                       int32_t Hk, int32_t D, uint32_t* cache, void* stream) {
+  if (!seqlens) return TKQ_EINVAL;
+  return kv_pack_common(K, V, seqlens, B, T, Hk, D, cache, stream);
+}
+
+int tkq_kv_decode(const uint16_t* q, const uint32_t* cache, int32_t B, int32_t H, int32_t Hk, int32_t T, int32_t D,
+                  float sm_scale, uint16_t* out, float* workspace, int64_t workspace_bytes, void* stream) {
+  return kv_decode_common(q, cache, nullptr, B, H, Hk, T, D, sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+int tkq_kv_decode_varlen(const uint16_t* q, const uint32_t* cache, const int32_t* seqlens, int32_t B, int32_t H,
+                         int32_t Hk, int32_t T, int32_t D, float sm_scale, uint16_t* out, float* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  if (!seqlens) return TKQ_EINVAL;
+  return kv_decode_common(q, cache, seqlens, B, H, Hk, T, D, sm_scale, out, workspace, workspace_bytes, stream);
 }
 
 int tkq_gemm_prefill(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint32_t* codes,

@@ -81,7 +81,10 @@ _SIGNATURES = {
     "tkq_kv_cache_bytes": ([_I32, _I32, _I32], ctypes.c_int64),
     "tkq_kv_decode_workspace_bytes": ([_I32, _I32, _I32, _I32], ctypes.c_int64),
     "tkq_kv_pack": ([_P, _P, _I32, _I32, _I32, _I32, _P, _P], ctypes.c_int),
+    "tkq_kv_pack_varlen": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], ctypes.c_int),
     "tkq_kv_decode": ([_P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, _I64, _P], ctypes.c_int),
+    "tkq_kv_decode_varlen": ([_P, _P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, _I64, _P],
+                             ctypes.c_int),
     "tkq_gemm_prefill": ([_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
     "tkq_read_probe": ([_P, _I64, _P, _P], ctypes.c_int),
 }
@@ -353,9 +356,20 @@ def read_probe(buf, out=None, stream=None):
 
 # ---- low-bit KV cache decode attention ------------------------------------------
 
-def kv_pack(K, V, stream=None):
+def _seqlens(seqlens, B, device):
+    if seqlens is None:
+        return None
+    _need(seqlens, torch.int32, "seqlens", (B,))
+    if seqlens.device != device:
+        raise ValueError("seqlens must be on the cache's device")
+    return seqlens
+
+
+def kv_pack(K, V, seqlens=None, stream=None):
     """K, V fp16 [B, T, Hk, 128] -> paged 4-bit cache (uint8 tensor of
-    tkq_kv_cache_bytes bytes, viewed as [B, Hk, T/128, 17408])."""
+    tkq_kv_cache_bytes bytes, viewed as [B, Hk, T/128, 17408]).  seqlens:
+    optional int32 [B] device tensor of valid tokens per sequence
+    (tkq_kv_pack_varlen: tokens past a length are packed as zeros)."""
     _need(K, torch.float16, "K")
     _need(V, torch.float16, "V", K.shape)
     B, T, Hk, D = K.shape
@@ -363,12 +377,26 @@ def kv_pack(K, V, stream=None):
     if n < 0 or D != 128:
         raise TkqError(ESHAPE, "tkq_kv_cache_bytes")
     cache = torch.empty(n, dtype=torch.uint8, device=K.device)
-    _call("tkq_kv_pack", _ptr(K), _ptr(V), B, T, Hk, D, _ptr(cache), _stream(stream, cache))
+    lens = _seqlens(seqlens, B, K.device)
+    if lens is None:
+        _call("tkq_kv_pack", _ptr(K), _ptr(V), B, T, Hk, D, _ptr(cache), _stream(stream, cache))
+    else:
+        _call("tkq_kv_pack_varlen", _ptr(K), _ptr(V), _ptr(lens), B, T, Hk, D, _ptr(cache), _stream(stream, cache))
     return cache.view(B, Hk, T // 128, 17408)
 
 
-def kv_decode(q, cache, T, sm_scale, out=None, workspace=None, stream=None):
-    """q fp16 [B, H, 128] -> out fp16 [B, H, 128] over a cache from kv_pack."""
+def kv_workspace(B, H, Hk, T, device):
+    """A zero-filled decode workspace (tkq_kv_decode_workspace_bytes)."""
+    nws = lib().tkq_kv_decode_workspace_bytes(B, H, Hk, T)
+    if nws < 0:
+        raise TkqError(ESHAPE, "tkq_kv_decode_workspace_bytes")
+    return torch.zeros((nws + 3) // 4, dtype=torch.float32, device=device)
+
+
+def kv_decode(q, cache, T, sm_scale, seqlens=None, out=None, workspace=None, stream=None):
+    """q fp16 [B, H, 128] -> out fp16 [B, H, 128] over a cache from kv_pack
+    (seqlens: optional int32 [B] device tensor, tkq_kv_decode_varlen).
+    workspace: from kv_workspace (zero-filled before its first use)."""
     _need(q, torch.float16, "q")
     B, H, D = q.shape
     Hk = cache.shape[1]
@@ -377,15 +405,17 @@ def kv_decode(q, cache, T, sm_scale, out=None, workspace=None, stream=None):
         out = torch.empty_like(q)
         owned.append(out)
     _need(out, torch.float16, "out", q.shape)
-    nws = lib().tkq_kv_decode_workspace_bytes(B, H, Hk, T)
-    if nws < 0:
-        raise TkqError(ESHAPE, "tkq_kv_decode_workspace_bytes")
     if workspace is None:
-        workspace = torch.empty((nws + 3) // 4, dtype=torch.float32, device=q.device)
+        workspace = kv_workspace(B, H, Hk, T, q.device)
         owned.append(workspace)
     _need(workspace, torch.float32, "workspace")
-    _call("tkq_kv_decode", _ptr(q), _ptr(cache), B, H, Hk, T, D, float(sm_scale), _ptr(out), _ptr(workspace),
-          workspace.numel() * 4, _stream(stream, *owned))
+    lens = _seqlens(seqlens, B, q.device)
+    if lens is None:
+        _call("tkq_kv_decode", _ptr(q), _ptr(cache), B, H, Hk, T, D, float(sm_scale), _ptr(out), _ptr(workspace),
+              workspace.numel() * 4, _stream(stream, *owned))
+    else:
+        _call("tkq_kv_decode_varlen", _ptr(q), _ptr(cache), _ptr(lens), B, H, Hk, T, D, float(sm_scale), _ptr(out),
+              _ptr(workspace), workspace.numel() * 4, _stream(stream, *owned))
     return out
 
 
@@ -393,7 +423,7 @@ class KvDecoder:
     """A prepared tkq_kv_decode call (arguments marshalled once; run() is one
     C call), for decode loops where the per-call Python cost matters."""
 
-    def __init__(self, q, cache, T, sm_scale, out=None, workspace=None, stream=None):
+    def __init__(self, q, cache, T, sm_scale, out=None, workspace=None, seqlens=None, stream=None):
         _need(q, torch.float16, "q")
         B, H, D = q.shape
         Hk = cache.shape[1]
@@ -402,22 +432,22 @@ class KvDecoder:
         if out is None:
             owned.append(self.out)
         _need(self.out, torch.float16, "out", q.shape)
-        nws = lib().tkq_kv_decode_workspace_bytes(B, H, Hk, T)
-        if nws < 0:
-            raise TkqError(ESHAPE, "tkq_kv_decode_workspace_bytes")
-        self.workspace = workspace if workspace is not None else torch.empty(
-            (nws + 3) // 4, dtype=torch.float32, device=q.device)
+        self.workspace = workspace if workspace is not None else kv_workspace(B, H, Hk, T, q.device)
         if workspace is None:
             owned.append(self.workspace)
         _need(self.workspace, torch.float32, "workspace")
-        self._keep = (q, cache)
-        self._args = (_ptr(q), _ptr(cache), B, H, Hk, T, D, ctypes.c_float(sm_scale), _ptr(self.out),
-                      _ptr(self.workspace), self.workspace.numel() * 4)
+        lens = _seqlens(seqlens, B, q.device)
+        self._keep = (q, cache, lens)
+        args = (_ptr(q), _ptr(cache)) + ((_ptr(lens),) if lens is not None else ()) + (
+            B, H, Hk, T, D, ctypes.c_float(sm_scale), _ptr(self.out), _ptr(self.workspace),
+            self.workspace.numel() * 4)
+        self._args = args
         self._stream = _stream(stream, *owned)
-        self._fn = lib().tkq_kv_decode
+        self._name = "tkq_kv_decode" if lens is None else "tkq_kv_decode_varlen"
+        self._fn = getattr(lib(), self._name)
 
     def run(self):
         st = self._fn(*self._args, self._stream)
         if st != OK:
-            raise TkqError(st, "tkq_kv_decode")
+            raise TkqError(st, self._name)
         return self.out

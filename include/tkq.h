@@ -334,7 +334,10 @@ int tkq_gemm_small(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs,
  * (lo = min(min, 0), hi = max(max, 0), s = fp16((hi - lo) / 15), integer z).
  * The cache tensor is [B][Hk][T/128][17408 bytes].
  * Shapes: head dimension D = 128, T % 128 == 0, H % Hk == 0; query head h
- * reads KV head h / (H / Hk). */
+ * reads KV head h / (H / Hk).  T is the cache's capacity in tokens; the
+ * _varlen entry points take per-sequence lengths (BitDecoding README, usage
+ * example: every sequence of a batch has its own cached length), so the
+ * last page of a sequence may be partly filled. */
 
 /* Bytes of a cache for B x Hk x T tokens (host only; -1 if invalid). */
 int64_t tkq_kv_cache_bytes(int32_t B, int32_t Hk, int32_t T);
@@ -346,27 +349,57 @@ int64_t tkq_kv_cache_bytes(int32_t B, int32_t Hk, int32_t T);
 int tkq_kv_pack(const uint16_t* K, const uint16_t* V, int32_t B, int32_t T,
                 int32_t Hk, int32_t D, uint32_t* cache, void* stream);
 
+/* tkq_kv_pack for sequences of their own lengths: seqlens is a device int32
+ * [B] (4-byte aligned), each value clamped to [0, T].  Tokens t >= seqlens[b]
+ * are quantized as zeros (a K group, one channel over a page, spans 0
+ * anyway, so its scale and zero-point are those of the valid tokens; such a
+ * V token is an all-zero group).  Returns as tkq_kv_pack, plus TKQ_EINVAL
+ * for a null seqlens. */
+int tkq_kv_pack_varlen(const uint16_t* K, const uint16_t* V,
+                       const int32_t* seqlens, int32_t B, int32_t T,
+                       int32_t Hk, int32_t D, uint32_t* cache, void* stream);
+
 /* Workspace bytes tkq_kv_decode needs (host only; -1 if invalid). */
 int64_t tkq_kv_decode_workspace_bytes(int32_t B, int32_t H, int32_t Hk,
                                       int32_t T);
 
 /* One decode step: out[b,h,:] = softmax(sm_scale * q[b,h,:] . K^T) . V over
  * the T cached tokens of KV head h / (H / Hk), with K and V the dequantized
- * cache.  q, out: fp16 bits [B][H][D]; workspace: caller-owned device
- * memory of at least tkq_kv_decode_workspace_bytes (any contents).
+ * cache.  q, out: fp16 bits [B][H][D].
+ * workspace: caller-owned device memory of at least
+ * tkq_kv_decode_workspace_bytes.  Its first 4*B*H bytes (rounded up to 16)
+ * are arrival counters that must be zero when a call starts, followed by
+ * per-split partial results; every completed call leaves its own counters
+ * at zero again (and partial results after them).  So: zero-fill the
+ * workspace before its first use, and again after a failed call or before a
+ * call with a larger B*H than the previous call on it.  Calls that share a
+ * workspace must be ordered (one stream).
+ * One kernel on `stream`: the workgroups of each (sequence, query-head
+ * group) split its pages, and the last of them to finish merges the splits
+ * (log-sum-exp) and writes out.
  * Accuracy: both products are held to the GEMV's per-row bound (scores:
  * |ds_t| <= e A_t, A_t = sm_scale sum_c |q_c K_t,c|; output: e sum_t p_t
  * |V_t,c|, e = 2e-3), so per element |out - exact| <= ((1 + e) exp(2 e max_t
  * A_t) - 1) sum_t p_t |V_t,c|.  (The kernels round the query times the K
  * channel scale and the probability times the V token scale to fp16,
  * accumulate in fp32 and round out to fp16.)
- * Two kernels on `stream` (the split decode, then the merge).  Returns
- * TKQ_OK, TKQ_EINVAL (null pointers, sm_scale not positive and finite,
- * workspace too small), TKQ_ESHAPE, TKQ_EALIGN or TKQ_EHIP. */
+ * Returns TKQ_OK, TKQ_EINVAL (null pointers, sm_scale not positive and
+ * finite, workspace too small), TKQ_ESHAPE, TKQ_EALIGN or TKQ_EHIP. */
 int tkq_kv_decode(const uint16_t* q, const uint32_t* cache, int32_t B,
                   int32_t H, int32_t Hk, int32_t T, int32_t D, float sm_scale,
                   uint16_t* out, float* workspace, int64_t workspace_bytes,
                   void* stream);
+
+/* tkq_kv_decode over the first seqlens[b] tokens of sequence b (device int32
+ * [B], 4-byte aligned, each clamped to [0, T]): pages past the length are not
+ * read and the tokens past it in the last page take no part; a sequence of
+ * length 0 gets out = 0.  Returns as tkq_kv_decode, plus TKQ_EINVAL for a
+ * null seqlens. */
+int tkq_kv_decode_varlen(const uint16_t* q, const uint32_t* cache,
+                         const int32_t* seqlens, int32_t B, int32_t H,
+                         int32_t Hk, int32_t T, int32_t D, float sm_scale,
+                         uint16_t* out, float* workspace,
+                         int64_t workspace_bytes, void* stream);
 
 /* ---- prefill GEMM -------------------------------------------------------
  * Y[m,n] = sum_k X[m,k] * w[n,k] with w the int4 g128 dequantized weights

@@ -25,7 +25,13 @@ Readings taken where the page is silent:
   and the cache tensor is [B][H_k][pages][PAGE_BYTES].  V codes are stored
   channel-major so that the value product, like the scores, reads whole
   rows front to back.
-* The cache length is a multiple of 128 (whole pages).
+* The cache's capacity T is a multiple of 128 (whole pages).  Sequences of
+  a batch may have their own lengths len[b] <= T (the README's usage passes
+  per-sequence cached lengths): tokens t >= len[b] are packed as zeros and
+  take no part in the attention.  A K group (one channel over a page)
+  spans 0 anyway, so zeros in place of the missing tokens leave its scale
+  and zero-point those of the valid tokens.  A sequence of length 0 has
+  output 0.
 
 The attention itself is the plain definition in fp64 from the dequantized
 cache.  Its tolerance (attention_bound) is not given by the page; it is
@@ -83,14 +89,22 @@ def unpack_page(words):
     return K, V
 
 
-def pack_cache(K, V):
+def pack_cache(K, V, lens=None):
     """K, V [B][T][H_k][128] (token-major, as a decoder writes them) ->
-    cache uint32 [B][H_k][T/128][PAGE_WORDS]."""
+    cache uint32 [B][H_k][T/128][PAGE_WORDS].  lens [B] (optional): tokens at
+    or past lens[b] are packed as zeros."""
     K = np.asarray(K)
     V = np.asarray(V)
     B, T, Hk, d = K.shape
     if d != D or T % PAGE:
         raise ValueError("head dimension 128 and whole pages of 128 tokens")
+    if lens is not None:
+        K = K.copy()
+        V = V.copy()
+        for b in range(B):
+            n = int(np.clip(lens[b], 0, T))
+            K[b, n:] = 0
+            V[b, n:] = 0
     out = np.zeros((B, Hk, T // PAGE, PAGE_WORDS), dtype=np.uint32)
     for b in range(B):
         for h in range(Hk):
@@ -113,29 +127,33 @@ def dequant_cache(cache):
     return K, V
 
 
-def attention_decode(q, K, V, sm_scale):
+def attention_decode(q, K, V, sm_scale, lens=None):
     """One decode step: q [B][H][128], K, V [B][H_k][T][128] (fp64 values)
     -> (out [B][H][128], p [B][H][T]) in fp64: softmax(sm_scale q.K^T) V,
-    query head h reading KV head h // (H / H_k)."""
+    query head h reading KV head h // (H / H_k), over the first lens[b]
+    tokens of sequence b (all T without lens; none: out 0, p 0)."""
     q = np.asarray(q, dtype=np.float64)
     B, H, _ = q.shape
-    Hk = K.shape[1]
+    Hk, T = K.shape[1], K.shape[2]
     if H % Hk:
         raise ValueError("query heads must be a multiple of KV heads")
     G = H // Hk
     out = np.zeros((B, H, D))
-    probs = np.zeros((B, H, K.shape[2]))
+    probs = np.zeros((B, H, T))
     for b in range(B):
+        n = T if lens is None else int(np.clip(lens[b], 0, T))
+        if n == 0:
+            continue
         for h in range(H):
-            s = sm_scale * (K[b, h // G] @ q[b, h])
+            s = sm_scale * (K[b, h // G, :n] @ q[b, h])
             e = np.exp(s - s.max())
             p = e / e.sum()
-            probs[b, h] = p
-            out[b, h] = p @ V[b, h // G]
+            probs[b, h, :n] = p
+            out[b, h] = p @ V[b, h // G, :n]
     return out, probs
 
 
-def attention_bound(q, K, V, sm_scale, eps=TOL, probs=None):
+def attention_bound(q, K, V, sm_scale, eps=TOL, probs=None, lens=None):
     """Per output element tolerance [B][H][128] of a decode step.
 
     Reading (the BitDecoding page states none): single-query attention is
@@ -153,17 +171,22 @@ def attention_bound(q, K, V, sm_scale, eps=TOL, probs=None):
                          * sum_t p_t |V_tc|.
     A kernel's own roundings (fp16 query and probability scaling, fp32 sums,
     the fp16 store) have to fit inside these two per-GEMV budgets.
-    `probs` (from attention_decode) may be passed to skip recomputing them."""
+    `probs` (from attention_decode) may be passed to skip recomputing them;
+    lens as in attention_decode (A_t over the valid tokens only)."""
     q = np.asarray(q, dtype=np.float64)
     B, H, _ = q.shape
     Hk = K.shape[1]
     G = H // Hk
+    T = K.shape[2]
     if probs is None:
-        _, probs = attention_decode(q, K, V, sm_scale)
+        _, probs = attention_decode(q, K, V, sm_scale, lens)
     bound = np.zeros((B, H, D))
     for b in range(B):
+        n = T if lens is None else int(np.clip(lens[b], 0, T))
+        if n == 0:
+            continue
         for h in range(H):
-            A = sm_scale * (np.abs(K[b, h // G]) @ np.abs(q[b, h]))
+            A = sm_scale * (np.abs(K[b, h // G, :n]) @ np.abs(q[b, h]))
             factor = (1.0 + eps) * np.exp(2.0 * eps * A.max()) - 1.0
-            bound[b, h] = factor * (probs[b, h] @ np.abs(V[b, h // G]))
+            bound[b, h] = factor * (probs[b, h, :n] @ np.abs(V[b, h // G, :n]))
     return bound

@@ -300,8 +300,10 @@ def test_kv_validation():
     L = tkq.lib()
     assert L.tkq_kv_cache_bytes(1, 32, 4096) == 32 * 32 * 17408
     assert L.tkq_kv_cache_bytes(1, 32, 100) == -1
-    assert L.tkq_kv_decode_workspace_bytes(1, 32, 32, 4096) == 32 * 32 * 130 * 4
-    assert L.tkq_kv_decode_workspace_bytes(1, 28, 4, 128) == 28 * 4 * 130 * 4   # 7 per KV head
+    # arrival counters (4 bytes per sequence and head, to 16 bytes) + partials
+    assert L.tkq_kv_decode_workspace_bytes(1, 32, 32, 4096) == 128 + 32 * 32 * 130 * 4
+    assert L.tkq_kv_decode_workspace_bytes(1, 28, 4, 128) == 112 + 28 * 4 * 130 * 4   # 7 per KV head
+    assert L.tkq_kv_decode_workspace_bytes(3, 1, 1, 128) == 16 + 3 * 4 * 130 * 4
     assert L.tkq_kv_decode_workspace_bytes(1, 8, 3, 128) == -1      # H % Hk != 0
     pk = L.tkq_kv_pack
     assert pk(None, A, 1, 128, 1, 128, A, None) == tkq.EINVAL
@@ -316,6 +318,14 @@ def test_kv_validation():
     assert dec(A, A, 1, 4, 3, 256, 128, 0.1, A, A, ws, None) == tkq.ESHAPE
     assert dec(A, None, 1, 4, 2, 256, 128, 0.1, A, A, ws, None) == tkq.EINVAL
     assert dec(A + 2, A, 1, 4, 2, 256, 128, 0.1, A, A, ws, None) == tkq.EALIGN
+    # per-sequence lengths: a null or misaligned length array is refused
+    pv, dv = L.tkq_kv_pack_varlen, L.tkq_kv_decode_varlen
+    assert pv(A, A, None, 1, 128, 1, 128, A, None) == tkq.EINVAL
+    assert pv(A, A, A + 2, 1, 128, 1, 128, A, None) == tkq.EALIGN
+    assert pv(A, A, A, 1, 200, 1, 128, A, None) == tkq.ESHAPE
+    assert dv(A, A, None, 1, 4, 2, 256, 128, 0.1, A, A, ws, None) == tkq.EINVAL
+    assert dv(A, A, A + 2, 1, 4, 2, 256, 128, 0.1, A, A, ws, None) == tkq.EALIGN
+    assert dv(A, A, A, 1, 4, 2, 256, 128, 0.1, A, A, ws - 4, None) == tkq.EINVAL
 
 
 def test_prefill_validation():

@@ -150,3 +150,103 @@ def test_kv_decode_peaked(B, H, Hk, T, t):
         page = okv.unpack_page(cn[0, hk, t // 128])[1][t % 128]
         for h in range(hk * (H // Hk), (hk + 1) * (H // Hk)):
             assert np.allclose(got[0, h], page, rtol=0, atol=2e-3 * np.abs(page).max()), (h, t)
+
+
+def _run_varlen(torch, tkq, q, K, V, lens, workspace=None):
+    lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    cache = tkq.kv_pack(torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(), seqlens=lt)
+    out = tkq.kv_decode(torch.from_numpy(q).cuda(), cache, K.shape[1], 1 / np.sqrt(128), seqlens=lt,
+                        workspace=workspace)
+    torch.cuda.synchronize()
+    return cache, out
+
+
+def _check_varlen(q, cn, out, lens, what):
+    Kd, Vd = okv.dequant_cache(cn)
+    sm = 1 / np.sqrt(128)
+    ref, probs = okv.attention_decode(q.astype(np.float64), Kd, Vd, sm, lens)
+    bound = okv.attention_bound(q.astype(np.float64), Kd, Vd, sm, probs=probs, lens=lens)
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got)), what
+    err = np.abs(got - ref)
+    bad = err > bound
+    assert not bad.any(), "%s: %d elements outside the bound, first at %s" % (
+        what, int(bad.sum()), np.argwhere(bad)[0])
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return float(np.nanmax(np.where(bound > 0, err / bound, 0.0)))
+
+
+def test_kv_pack_varlen_bit_exact():
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    B, T, Hk, lens = 4, 512, 2, [1, 200, 512, 0]
+    K, V = _kv((805, B, T, Hk), B, T, Hk)
+    lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    cache = tkq.kv_pack(torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(), seqlens=lt)
+    torch.cuda.synchronize()
+    got = _cache_np(cache, B, Hk, T)
+    want = okv.pack_cache(K, V, lens)
+    assert np.array_equal(got, want), "pages differ at %s" % (np.argwhere(got != want)[:5],)
+
+
+@pytest.mark.parametrize("B,H,Hk,T,lens", [
+    (4, 32, 32, 4096, [4096, 1000, 129, 1]),      # MHA, partial pages, a single token
+    (3, 32, 8, 32768, [32768 - 77, 5000, 0]),     # matrix-core path; an empty sequence
+    (2, 4, 4, 131072, [131071, 70001]),           # many splits, lengths inside a split
+    (2, 16, 2, 2048, [2047, 640]),                # 8 query heads per KV head
+    (2, 6, 2, 384, [383, 2]),                     # 3 per KV head (smallest matrix-core group)
+])
+def test_kv_decode_varlen_matches_oracle(B, H, Hk, T, lens):
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    K, V = _kv((806, B, H, Hk, T), B, T, Hk)
+    q = _q((807, B, H, T), B, H)
+    cache, out = _run_varlen(torch, tkq, q, K, V, lens)
+    cn = _cache_np(cache, B, Hk, T)
+    worst = _check_varlen(q, cn, out, lens, "varlen B=%d H=%d Hk=%d T=%d lens=%s" % (B, H, Hk, T, lens))
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert not out[b].float().abs().sum().item(), "empty sequence must give 0"
+    print("kv varlen B=%d H=%d Hk=%d T=%d worst |err|/bound %.3g" % (B, H, Hk, T, worst))
+
+
+@pytest.mark.parametrize("B,H,Hk,T,lens", [
+    (2, 8, 8, 4096, [4000, 333]),
+    (1, 32, 8, 32768, [32768 - 100]),
+])
+def test_kv_decode_varlen_page_markers(B, H, Hk, T, lens):
+    """Page markers with lengths that end inside a page: the answer is the
+    mean over each sequence's valid tokens only."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    K, V, q = inputs.kv_marker_case(B, H, Hk, T)
+    cache, out = _run_varlen(torch, tkq, q, K, V, lens)
+    _check_varlen(q, _cache_np(cache, B, Hk, T), out, lens, "varlen markers %s" % (lens,))
+    got = out.float().cpu().numpy()
+    for b, n in enumerate(lens):
+        for h in range(H):
+            hk = h // (H // Hk)
+            pages = np.arange(n) // 128
+            cnt = np.bincount((pages + 37 * hk + 11 * b) % 128, minlength=128)
+            assert np.allclose(got[b, h], 1.0 + 14.0 * cnt / n, rtol=4e-3, atol=0), (b, h)
+
+
+def test_kv_decode_reuses_its_workspace():
+    """Consecutive decodes on one workspace zeroed once (each call leaves its
+    arrival counters at zero), a smaller configuration after a larger one,
+    and a larger one again after re-zeroing: every result matches the
+    oracle."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    ws = tkq.kv_workspace(2, 32, 8, 8192, "cuda")
+    runs = [(2, 32, 8, 8192, [8192, 3000]), (2, 32, 8, 8192, [100, 8000]), (1, 8, 8, 2048, [2048]),
+            "zero", (2, 32, 8, 8192, [5000, 1])]
+    for i, r in enumerate(runs):
+        if r == "zero":
+            ws.zero_()
+            continue
+        B, H, Hk, T, lens = r
+        K, V = _kv((808, i), B, T, Hk)
+        q = _q((809, i), B, H)
+        cache, out = _run_varlen(torch, tkq, q, K, V, lens, workspace=ws)
+        _check_varlen(q, _cache_np(cache, B, Hk, T), out, lens, "reuse %d" % i)

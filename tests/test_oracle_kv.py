@@ -195,3 +195,67 @@ def test_bound_rejects_a_dropped_or_repeated_page(T):
         Vr[:, :, 128 * i:128 * (i + 1)] = Vd[:, :, 128 * j:128 * (j + 1)]
         repeated, _ = kv.attention_decode(qd, Kd, Vr, sm)
         assert np.any(np.abs(repeated - ref) > bound), "page %d read twice passes" % j
+
+
+def test_lengths_equal_truncation():
+    """Attention over the first lens[b] tokens is attention over the cache cut
+    to those tokens; probabilities past the length are 0; full lengths are
+    the plain case; a sequence of length 0 has output 0."""
+    rng = np.random.default_rng(48)
+    K = rng.standard_normal((3, 2, 384, 128))
+    V = rng.standard_normal((3, 2, 384, 128))
+    q = rng.standard_normal((3, 4, 128))
+    lens = [300, 129, 0]
+    out, p = kv.attention_decode(q, K, V, 0.1, lens)
+    for b, n in enumerate(lens[:2]):
+        ref, pr = kv.attention_decode(q[b:b + 1], K[b:b + 1, :, :n], V[b:b + 1, :, :n], 0.1)
+        assert np.allclose(out[b], ref[0], rtol=0, atol=1e-12)
+        assert np.allclose(p[b, :, :n], pr[0], rtol=0, atol=1e-15) and not p[b, :, n:].any()
+    assert not out[2].any() and not p[2].any()
+    full, _ = kv.attention_decode(q, K, V, 0.1)
+    assert np.array_equal(kv.attention_decode(q, K, V, 0.1, [384] * 3)[0], full)
+    b = kv.attention_bound(q, K, V, 0.1, lens=lens)
+    assert not b[2].any() and np.all(b[:2] > 0)
+
+
+def test_partial_page_quantizes_its_valid_tokens_only():
+    """Sequence of 200 tokens in a 256-token cache: in page 1 (72 valid
+    tokens) every K channel's scale and zero-point are those of the valid
+    tokens alone (the group range spans 0 either way), the tokens past the
+    length are zero V groups (scale 1, zero 0, codes 0), and page 0 is the
+    same as without lengths."""
+    rng = np.random.default_rng(49)
+    K = rng.standard_normal((1, 256, 1, 128)).astype(np.float16)
+    V = rng.standard_normal((1, 256, 1, 128)).astype(np.float16)
+    cache = kv.pack_cache(K, V, [200])
+    assert np.array_equal(cache[0, 0, 0], kv.pack_cache(K, V)[0, 0, 0])
+    page = cache[0, 0, 1]
+    ks, kz = pack.unpack_int4_meta(page[4096:4224])
+    v = K[0, 128:200, 0].astype(np.float32)
+    lo = np.minimum(v.min(axis=0), 0)
+    hi = np.maximum(v.max(axis=0), 0)
+    s = ((hi - lo) / np.float32(15)).astype(np.float16)
+    assert np.array_equal(ks, s) and np.array_equal(kz, np.clip(np.rint(-lo / s.astype(np.float32)), 0, 15))
+    vs, vz = pack.unpack_int4_meta(page[4224:4352])
+    assert np.all(vs[72:] == 1) and np.all(vz[72:] == 0)
+    Kd, Vd = kv.unpack_page(page)
+    assert not Vd[72:].any() and not Kd[72:].any()
+
+
+def test_bound_rejects_a_dropped_partial_page():
+    """Page markers with a sequence of 1000 tokens in a 1024-token cache: the
+    exact attention passes; leaving out the last, partial page (104 valid
+    tokens) or reading the page before it in its place fails."""
+    K, V, q = inputs.kv_marker_case(1, 1, 1, 1024)
+    cache = kv.pack_cache(K, V, [1000])
+    Kd, Vd = kv.dequant_cache(cache)
+    sm = 1 / np.sqrt(128)
+    qd = q.astype(np.float64)
+    ref, p = kv.attention_decode(qd, Kd, Vd, sm, [1000])
+    bound = kv.attention_bound(qd, Kd, Vd, sm, probs=p, lens=[1000])
+    dropped, _ = kv.attention_decode(qd, Kd, Vd, sm, [896])
+    assert np.any(np.abs(dropped - ref) > bound)
+    Vr = Vd.copy()
+    Vr[:, :, 896:1024] = Vd[:, :, 768:896]
+    repeated, _ = kv.attention_decode(qd, Kd, Vr, sm, [1000])
+    assert np.any(np.abs(repeated - ref) > bound)
