@@ -56,28 +56,19 @@ namespace {
 // 1-2 % faster for int4, K5 and binary; slower for ternary, int2, int3 and
 // the greedy variant and equal for hier-g32, which keep one buffer and more
 // waves).
-#ifndef TKQ_GEMV_PINGPONG_MASK
-#define TKQ_GEMV_PINGPONG_MASK ((1 << 1) | (1 << 2) | (1 << 4))
-#endif
+constexpr int kPingpongMask = (1 << kFmtInt4) | (1 << kFmtK5) | (1 << kFmtBin);
 // Codings (bit fmt) whose code loads are plain rather than non-temporal.
 // Binary rows (K/8 bytes) start at 32 bytes past a 64-byte boundary on odd
 // rows, and a row's passes end mid-block: blocks touched by two load
 // instructions were fetched from HBM twice under the non-temporal hint
 // (traffic 1.080x against 1.002x plain; plain loads measured 3.89 -> 4.63
 // TB/s on the binary shapes).  Ternary and int2 measured 5 % slower plain.
-#ifndef TKQ_GEMV_PLAIN_MASK
-#define TKQ_GEMV_PLAIN_MASK (1 << 4)
-#endif
+constexpr int kPlainMask = 1 << kFmtBin;
 // Codings (bit fmt) whose waves raise their priority while issuing a row
 // step's loads, so that a CU's loads are not held behind other waves' unpack
 // work: int4 (0.5B sweep +1.5 %, 7B -0.3 %) and int4-hier-g32 (+1.9 %);
 // K5 -2 %, ternary -4 %, int3 -3 %, binary +0.5 %.
-#ifndef TKQ_GEMV_SETPRIO_MASK
-#define TKQ_GEMV_SETPRIO_MASK ((1 << 1) | (1 << 5))
-#endif
-#ifndef TKQ_GEMV_WPE
-#define TKQ_GEMV_WPE 1  // minimum waves per SIMD the register budget must allow
-#endif
+constexpr int kSetprioMask = (1 << kFmtInt4) | (1 << kFmtHier);
 
 constexpr int kWaves = 4;
 constexpr int kMaxTileRows = kGemvMaxTileRows;
@@ -423,9 +414,7 @@ struct Tile {
 
 // Codings (bit fmt) whose loads use per-step scalar bases (measured per
 // coding: faster for int4 and hier-g32, slower for ternary and K5).
-#ifndef TKQ_GEMV_SBASE_MASK
-#define TKQ_GEMV_SBASE_MASK ((1 << 1) | (1 << 5))
-#endif
+constexpr int kSbaseMask = (1 << kFmtInt4) | (1 << kFmtHier);
 
 // Order-preserving key of an output: larger value -> larger key, and among
 // equal values the smaller row -> larger key.  fp16: -0 counts as +0, and
@@ -519,13 +508,13 @@ struct Runner {
     return (uint32_t)(t.rbase + (st + u) * t.P + t.prow);
   }
 
-  static constexpr bool kSbase = ((TKQ_GEMV_SBASE_MASK) >> FMT) & 1;
-  static constexpr bool kPlain = ((TKQ_GEMV_PLAIN_MASK) >> FMT) & 1;
+  static constexpr bool kSbase = (kSbaseMask >> FMT) & 1;
+  static constexpr bool kPlain = (kPlainMask >> FMT) & 1;
   __device__ static __forceinline__ u32x4 code16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return kPlain ? load16(r, off) : load16_nt(r, off);
   }
 
-  static constexpr bool kSetprio = ((TKQ_GEMV_SETPRIO_MASK) >> FMT) & 1;
+  static constexpr bool kSetprio = (kSetprioMask >> FMT) & 1;
   __device__ __forceinline__ void issue(int st, Buf& b) const {
     if constexpr (kSetprio) __builtin_amdgcn_s_setprio(1);
     issue_loads(st, b);
@@ -625,7 +614,7 @@ struct Runner {
     }
   }
 
-  static constexpr bool kPingpong = (((TKQ_GEMV_PINGPONG_MASK) >> FMT) & 1) && !GREEDY;
+  static constexpr bool kPingpong = ((kPingpongMask >> FMT) & 1) && !GREEDY;
 
   __device__ __forceinline__ void run(uint32_t* part) {
     if constexpr (kPingpong) {
@@ -657,12 +646,10 @@ struct Runner {
 
 // Row steps per loop iteration: the planner's unroll, or for the 48-byte
 // int3 chunks a divisor of it (tile heights stay multiples).
-#ifndef TKQ_INT3_U
-#define TKQ_INT3_U 2
-#endif
+constexpr int kInt3Unroll = 2;
 template <int FMT, int J>
 constexpr int runner_unroll() {
-  return Codec<FMT>::PLANES == 3 ? (gemv_unroll(J) % TKQ_INT3_U == 0 ? TKQ_INT3_U : 1) : gemv_unroll(J);
+  return Codec<FMT>::PLANES == 3 ? (gemv_unroll(J) % kInt3Unroll == 0 ? kInt3Unroll : 1) : gemv_unroll(J);
 }
 
 template <int FMT, int J, bool GREEDY>
@@ -683,7 +670,8 @@ struct Greedy {
 };
 
 template <int FMT, int JMAX, bool GREEDY>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TKQ_GEMV_WPE, 8))) void gemv_kernel(const tkq_gemv_desc* __restrict__ descs, int count, Greedy g) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 8))) void gemv_kernel(
+    const tkq_gemv_desc* __restrict__ descs, int count, Greedy g) {
   using Cd = Codec<FMT>;
   constexpr bool kBin = FMT == kFmtBin;
   __shared__ uint32_t part[kWaves * kMaxTileRows];

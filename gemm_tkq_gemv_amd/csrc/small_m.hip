@@ -40,21 +40,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kTileRows = kSmallTileRows;  // 16 rows per wave
-#ifndef TKQ_SMALL_KC_BIG_M
-#define TKQ_SMALL_KC_BIG_M 512  // columns of X staged per round for M > TKQ_SMALL_KC_SPLIT
-#endif
-#ifndef TKQ_SMALL_KC_SMALL_M
-#define TKQ_SMALL_KC_SMALL_M 1024
-#endif
-#ifndef TKQ_SMALL_KC_SPLIT
-#define TKQ_SMALL_KC_SPLIT 8
-#endif
+// Columns of X staged per round: 512 for M > kKcSplit, 1024 otherwise.
+constexpr int kKcBigM = 512, kKcSmallM = 1024, kKcSplit = 8;
 template <int KC>
 constexpr int lds_row() { return KC + 8; }  // halves per staged token row (16 bytes of padding)
-#ifndef TKQ_SMALL_ACC
-#define TKQ_SMALL_ACC 1
-#endif
-constexpr int NACC = TKQ_SMALL_ACC;  // independent accumulators (MFMA dependency chains)
+constexpr int NACC = 1;  // accumulators (MFMA dependency chains; 2-4 measured slower)
 constexpr uint32_t kMagic = 0x64006400u;
 
 __device__ __forceinline__ uint32_t in_sgpr(uint32_t c) {
@@ -121,10 +111,7 @@ __device__ __forceinline__ void load_round(const SmallTile& t, int kc, CodeBuf<K
 // thread issues the loads of SB units before writing any of them, so a
 // round's staging costs ceil(units / (256 SB)) memory round trips rather
 // than one per unit (units past the end read beyond the buffer: zeros).
-#ifndef TKQ_SMALL_SB
-#define TKQ_SMALL_SB 4
-#endif
-constexpr int SB = TKQ_SMALL_SB;
+constexpr int SB = 4;
 template <int KC>
 __device__ __forceinline__ void stage_x(const SmallTile& t, int kc, _Float16* xs) {
   constexpr int kLdsRow = lds_row<KC>();
@@ -242,11 +229,11 @@ __global__ __launch_bounds__(256) void small_m_kernel(const tkq_gemv_desc* __res
 }  // namespace
 
 hipError_t launch_small_m(const tkq_gemv_desc* dev_descs, int count, int64_t tiles, int M, hipStream_t stream) {
-  if (M > TKQ_SMALL_KC_SPLIT)
-    hipLaunchKernelGGL((small_m_kernel<TKQ_SMALL_KC_BIG_M, true>), dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream,
+  if (M > kKcSplit)
+    hipLaunchKernelGGL((small_m_kernel<kKcBigM, true>), dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream,
                        dev_descs, count, M);
   else
-    hipLaunchKernelGGL((small_m_kernel<TKQ_SMALL_KC_SMALL_M, false>), dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream,
+    hipLaunchKernelGGL((small_m_kernel<kKcSmallM, false>), dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream,
                        dev_descs, count, M);
   return hipGetLastError();
 }
