@@ -177,8 +177,9 @@ def time_steps(torch, run_step, steps, warmup, graph="none", period=1, group=10)
     captured once as a HIP graph and step s replays graph s % period;
     graph="all": the `steps` timed steps are captured as one graph that is
     replayed once inside the timed region (warm-up steps run eagerly).
-    Without "all", an event every `group` steps also gives the per-step
-    median, p10 and p90 over the groups (SWEEP_STATS)."""
+    Without "all", an event every `group` steps (and the end event for the
+    last group) also gives the per-step median, p10 and p90 over the groups
+    (SWEEP_STATS)."""
     for s in range(warmup):
         run_step(s)
     torch.cuda.synchronize()
@@ -223,8 +224,11 @@ def time_steps(torch, run_step, steps, warmup, graph="none", period=1, group=10)
     torch.cuda.synchronize()
     SWEEP_STATS.clear()
     if marks:
-        pts = [start] + marks
-        per = sorted(a.elapsed_time(b) / group for a, b in zip(pts, pts[1:]))
+        # every group enters the statistics, the last one (up to `group`
+        # steps, closed by the end event) included
+        pts = [start] + marks + [end]
+        sizes = [group] * len(marks) + [steps - group * len(marks)]
+        per = sorted(a.elapsed_time(b) / n for (a, b), n in zip(zip(pts, pts[1:]), sizes))
         q = lambda f: per[min(len(per) - 1, int(f * len(per)))]  # noqa: E731
         SWEEP_STATS.update(median_us=round(q(0.5) * 1e3, 3), p10_us=round(q(0.1) * 1e3, 3),
                            p90_us=round(q(0.9) * 1e3, 3), groups=len(per), steps_per_group=group)
@@ -233,13 +237,14 @@ def time_steps(torch, run_step, steps, warmup, graph="none", period=1, group=10)
 
 # ------------------------------------------------------------- cpu baseline --
 
-def cpu_baseline_gemv(inputs, model, fmt, budget_s=10.0):
+def cpu_baseline_gemv(inputs, model, fmt, budget_s=10.0, M=None):
     """Oracle (numpy, fp64) timed on the host: dequantize the stored codes and
-    run the fp64 matvec.  The sample is the sweep's matrices in order (the
-    7B head truncated to its first 32768 rows, its other matrices as they
-    come) until ~20 s of preparation; then passes over the prepared sample
-    are timed until `budget_s` seconds of oracle work.  Quantization and
-    packing are not timed.  Rate = algorithmic bytes / time."""
+    run the fp64 matvec (M tokens: the fp64 product X . W^T).  The sample is
+    the sweep's matrices in order (the 7B head truncated to its first 32768
+    rows, its other matrices as they come) until ~20 s of preparation; then
+    passes over the prepared sample are timed until `budget_s` seconds of
+    oracle work.  Quantization and packing are not timed.  Rate =
+    algorithmic bytes (weights once, x and y per token) / time."""
     import numpy as np
 
     from oracle import accounting, pack, quant, ref
@@ -256,6 +261,8 @@ def cpu_baseline_gemv(inputs, model, fmt, budget_s=10.0):
             x = inputs.sweep_x(model, i, K)
         else:
             W, x = inputs.sweep_matrix(model, i, N, K)
+        if M is not None:
+            x = np.stack([inputs.normal_vector((6, i, m), K) for m in range(M)])
         if fmt == "int4":
             q, s, z = quant.quantize_int4_g128(W)
             prepared.append((fmt, (pack.pack_int4(q), pack.pack_int4_meta(s, z)), x, N, K))
@@ -279,29 +286,128 @@ def cpu_baseline_gemv(inputs, model, fmt, budget_s=10.0):
     def one(item):
         f, (c, m), x, N, K = item
         if f == "int4":
-            y = ref.gemv(ref.dequant_int4(c, m, K), x)
+            w = ref.dequant_int4(c, m, K)
         elif f == "k5":
-            y = ref.gemv(ref.dequant_k5(c, m), x)
+            w = ref.dequant_k5(c, m)
         elif f == "hier":
-            y = ref.gemv(ref.dequant_int4_hier(c, m, N, K), x)
+            w = ref.dequant_int4_hier(c, m, N, K)
         elif f == "int2":
-            y = ref.gemv(ref.dequant_int2(c, m, K), x)
+            w = ref.dequant_int2(c, m, K)
         elif f == "int3":
-            y = ref.gemv(ref.dequant_int3(c, m, K), x)
+            w = ref.dequant_int3(c, m, K)
         else:
-            y = ref.gemv(ref.dequant_tern(c, m, K), x)
+            w = ref.dequant_tern(c, m, K)
+        y = ref.gemv(w, x) if x.ndim == 1 else ref.gemm(x, w)
         assert np.all(np.isfinite(y))
-        return accounting.gemv_bytes(f, N, K)
+        weights = accounting.gemv_bytes(f, N, K) - 2 * K - 2 * N
+        return weights + (1 if x.ndim == 1 else x.shape[0]) * (2 * K + 2 * N)
 
-    done_bytes, passes, t0 = 0, 0, time.perf_counter()
+    done_bytes, spent, passes = _cpu_loop(lambda: sum(one(it) for it in prepared), budget_s)
+    return done_bytes / spent, spent, names, passes
+
+
+def gemv_cpu_entry(inputs, model, fmt, budget_s, M=None):
+    rate, spent, done, passes = cpu_baseline_gemv(inputs, model, fmt, budget_s, M)
+    return _cpu_entry(round(rate / 1e12, 8), "TB/s",
+                      "numpy oracle dequantize + fp64 %s, %d passes over the first %d matrices of the sweep "
+                      "(%s), %.1f s of CPU work; quantization not timed"
+                      % ("matvec" if M is None else "product with %d tokens" % M, passes, len(done),
+                         ", ".join(done[:3] + (["..."] if len(done) > 3 else []) + done[-1:]), spent))
+
+
+def _cpu_loop(work, budget_s):
+    """Call work() (which returns the units it did) until budget_s seconds
+    have passed, at least once: (units, seconds, passes)."""
+    done, passes, t0 = 0, 0, time.perf_counter()
     while True:
-        for item in prepared:
-            done_bytes += one(item)
+        done += work()
         passes += 1
         spent = time.perf_counter() - t0
         if spent >= budget_s:
-            break
-    return done_bytes / spent, spent, names, passes
+            return done, spent, passes
+
+
+def _cpu_entry(value, unit, sample):
+    return {"value": value, "unit": unit, "cores": blas_threads(),
+            "host_cores_available": len(os.sched_getaffinity(0)), "kind": "oracle", "sample": sample}
+
+
+def cpu_baseline_binary(inputs, budget_s):
+    """Oracle XOR-popcount GEMV (numpy bitwise_count on uint32 words) over the
+    six binary shapes; packing not timed.  Rate = algorithmic bytes / time."""
+    from oracle import pack, quant, ref
+    prepared = []
+    for N, K in inputs.BINARY_SHAPES:
+        W, x = inputs.binary_case(N, K)
+        prepared.append((pack.pack_bits(quant.sign_bits(W)), pack.pack_bits(quant.sign_bits(x[None, :]))[0], N, K))
+    fb = _fmt_bytes("bin")
+
+    def work():
+        n = 0
+        for wb, xb, N, K in prepared:
+            ref.bin_gemv(wb, xb, K)
+            n += fb(N, K)
+        return n
+    done, spent, passes = _cpu_loop(work, budget_s)
+    return _cpu_entry(round(done / spent / 1e12, 8), "TB/s",
+                      "numpy oracle XOR-popcount over all six binary shapes, %d passes, %.1f s of CPU work; "
+                      "packing not timed" % (passes, spent))
+
+
+def cpu_baseline_prefill(inputs, budget_s):
+    """Oracle prefill: dequantize the int4 gate, up and down weights to fp64
+    and multiply by X in fp64 (the whole step, M = 512); quantization not
+    timed.  Rate = step FLOP / time."""
+    from oracle import pack, quant, ref
+    M = inputs.PREFILL_M
+    prepared = []
+    for name, N, K in inputs.prefill_shapes():
+        q, s_, z = quant.quantize_int4_g128(inputs.prefill_W(name))
+        prepared.append((pack.pack_int4(q), pack.pack_int4_meta(s_, z), inputs.prefill_X(K).astype(np.float64), N, K))
+
+    def work():
+        f = 0
+        for c, m, X, N, K in prepared:
+            ref.gemm(X, ref.dequant_int4(c, m, K))
+            f += 2 * M * N * K
+        return f
+    done, spent, passes = _cpu_loop(work, budget_s)
+    return _cpu_entry(round(done / spent / 1e12, 6), "TFLOP/s",
+                      "numpy oracle fp64 dequantize + fp64 matmul of the whole step (gate, up, down at M = 512), "
+                      "%d passes, %.1f s of CPU work; quantization not timed" % (passes, spent))
+
+
+def cpu_baseline_kv(inputs, B, H, Hk, T, budget_s):
+    """Oracle decode attention (dequantize the cache pages to fp64, fp64
+    softmax attention) on one KV head of the workload and its query heads;
+    packing not timed.  Rate = bytes of that head's cache (+ q, out) / time."""
+    from oracle import kv
+    K, V, q = inputs.kv_random_case(B, H, Hk, T)
+    G = H // Hk
+    cache = kv.pack_cache(K[:1, :, :1], V[:1, :, :1])
+    qs = q[:1, :G].astype(np.float64)
+    nbytes = cache.nbytes + 2 * 2 * G * 128
+
+    def work():
+        Kd, Vd = kv.dequant_cache(cache)
+        kv.attention_decode(qs, Kd, Vd, 1 / math.sqrt(128))
+        return nbytes
+    done, spent, passes = _cpu_loop(work, budget_s)
+    return _cpu_entry(round(done / spent / 1e12, 8), "TB/s",
+                      "numpy oracle page dequantization + fp64 attention for KV head 0 of sequence 0 (%d query "
+                      "heads, %d tokens), %d passes, %.1f s of CPU work; packing not timed" % (G, T, passes, spent))
+
+
+def cpu_baseline_single(inputs, budget_s):
+    """Oracle 896 x 896 int4 GEMV: dequantize + fp64 matvec, per call."""
+    from oracle import pack, quant, ref
+    W, x = inputs.single_gemv_896()
+    q, s_, z = quant.quantize_int4_g128(W)
+    c, m = pack.pack_int4(q), pack.pack_int4_meta(s_, z)
+    done, spent, passes = _cpu_loop(lambda: (ref.gemv(ref.dequant_int4(c, m, 896), x), 1)[1], budget_s)
+    return _cpu_entry(round(spent / done * 1e6, 3), "us",
+                      "numpy oracle dequantize + fp64 matvec of the 896x896 GEMV, %d calls, %.1f s of CPU work"
+                      % (done, spent))
 
 
 def blas_threads():
@@ -362,7 +468,7 @@ def run_sweep(args, torch, tkq, inputs, model, fmt, greedy=False):
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": args.traffic if args.traffic is not None else
                      (measured_traffic(args.workload) if launch == "grouped" and args.copies is None else None)},
-        "kernel": "gemv_kernel<%d>" % tkq.FORMATS[fmt],
+        "kernel": gemv_kernel_name(fmt, max(b.plan.variant for b in batches[0]), greedy),
     }
     del items, batches
     return out
@@ -409,21 +515,17 @@ def run_small(args, torch, tkq, inputs, model, M):
 def run_kv(args, torch, tkq, B, H, Hk, T):
     """Single-query decode attention over a 4-bit paged KV cache (BitDecoding's
     shape: head dimension 128, group 128, K per channel, V per token)."""
-    r = np.random.default_rng((9, B, H, Hk, T))
-    caches = []
-    for i in range(1):
-        K = torch.from_numpy(r.standard_normal((B, T, Hk, 128)).astype(np.float16)).cuda()
-        V = torch.from_numpy(r.standard_normal((B, T, Hk, 128)).astype(np.float16)).cuda()
-        caches.append(tkq.kv_pack(K, V))
-        del K, V
+    from gemm_tkq_gemv_amd import inputs
+    Kh, Vh, qh = inputs.kv_random_case(B, H, Hk, T)
+    caches = [tkq.kv_pack(torch.from_numpy(Kh).cuda(), torch.from_numpy(Vh).cuda())]
+    del Kh, Vh
     cache_bytes = caches[0].numel()
     copies = max(1, math.ceil(ROTATE_BYTES / cache_bytes))
     for _ in range(copies - 1):
         caches.append(caches[0].clone())
-    q = torch.from_numpy(r.standard_normal((B, H, 128)).astype(np.float16)).cuda()
+    q = torch.from_numpy(qh).cuda()
     out = torch.empty_like(q)
-    ws = torch.empty((tkq.lib().tkq_kv_decode_workspace_bytes(B, H, Hk, T) + 3) // 4, dtype=torch.float32,
-                     device="cuda")
+    ws = tkq.kv_workspace(B, H, Hk, T, q.device)
     torch.cuda.synchronize()
     scale = 1 / math.sqrt(128)
     decs = [tkq.KvDecoder(q, c, T, scale, out, ws) for c in caches]
@@ -440,7 +542,15 @@ def run_kv(args, torch, tkq, B, H, Hk, T):
             "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload)},
-            "kernel": "kv_decode_kernel + kv_merge_kernel"}
+            "kernel": "kv_decode_mfma_kernel" if H // Hk >= 3 else "kv_decode_kernel<%d>" % min(H // Hk, 8)}
+
+
+def gemv_kernel_name(fmt, jmax, greedy):
+    """The GEMV kernel instance a launch runs: gemv_kernel<coding, largest
+    pass count, greedy variant> (as the profiler names it)."""
+    from gemm_tkq_gemv_amd import tkq
+    return "gemv_kernel<%d, %d, %s>" % (tkq.FORMATS[fmt], jmax, "true" if greedy else "false") + (
+        " + greedy_finish_kernel" if greedy else "")
 
 
 def _fmt_name(fmt):
@@ -608,28 +718,33 @@ def main():
         out = run_sweep(args, torch, tkq, inputs, model, fmt, greedy=w.endswith("greedy"))
         torch.cuda.empty_cache()
         if not args.no_cpu_baseline:
-            rate, spent, done, passes = cpu_baseline_gemv(inputs, model, fmt, args.cpu_budget)
-            cores = len(os.sched_getaffinity(0))
-            out["cpu_baseline"] = {
-                "value": round(rate / 1e12, 8), "unit": "TB/s", "cores": blas_threads(),
-                "host_cores_available": cores, "kind": "oracle",
-                "sample": "numpy oracle dequantize + fp64 matvec, %d passes over the first %d "
-                          "matrices of the sweep (%s), %.1f s of CPU work; quantization not timed"
-                          % (passes, len(done), ", ".join(done[:3] + (["..."] if len(done) > 3 else [])
-                                                          + done[-1:]), spent)}
+            out["cpu_baseline"] = gemv_cpu_entry(inputs, model, fmt, args.cpu_budget)
     elif w.startswith("kv-"):
         T = {"4k": 4096, "32k": 32768, "128k": 131072}[w.split("-")[1]]
         Hk = 8 if w.endswith("gqa") else 32
         out = run_kv(args, torch, tkq, 1, 32, Hk, T)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_kv(inputs, 1, 32, Hk, T, args.cpu_budget)
     elif "-m" in w:
         model = "qwen2.5-7b" if w.startswith("7b") else "qwen2.5-0.5b"
-        out = run_small(args, torch, tkq, inputs, model, int(w.split("-m")[1]))
+        M = int(w.split("-m")[1])
+        out = run_small(args, torch, tkq, inputs, model, M)
+        torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = gemv_cpu_entry(inputs, model, "int4", args.cpu_budget, M)
     elif w == "bin":
         out = run_binary(args, torch, tkq, inputs)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_binary(inputs, args.cpu_budget)
     elif w == "single-896":
         out = run_single(args, torch, tkq, inputs)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_single(inputs, min(args.cpu_budget, 3.0))
     elif w == "7b-prefill":
         out = run_prefill(args, torch, tkq, inputs)
+        torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_prefill(inputs, args.cpu_budget)
     else:
         out = run_probe(args, torch, tkq, inputs)
     print(json.dumps(out), flush=True)
