@@ -7,7 +7,8 @@
 // kernel is therefore organised around the byte stream:
 //
 //  * Work unit.  One workgroup (4 wave64s) owns a tile of consecutive rows of
-//    one matrix; the grid is the concatenation of every matrix's tiles, and a
+//    one matrix (int4 g128 has its own kernel, gemv_int4_kernel, that reads
+//    128-byte lines per 8-lane unit and keeps x in LDS); the grid is the concatenation of every matrix's tiles, and a
 //    workgroup finds its matrix by binary search over the descriptors'
 //    first-tile indices (scalar loads).  Tiles are large (~24 KB per wave,
 //    amortising the per-tile setup) except over the last stretch of the
@@ -53,10 +54,10 @@ namespace {
 
 // Codings (bit fmt) whose runner keeps two load buffers, the next row steps'
 // loads in flight while the current ones are computed (measured per coding:
-// 1-2 % faster for int4, K5 and binary; slower for ternary, int2, int3 and
-// the greedy variant and equal for hier-g32, which keep one buffer and more
-// waves).
-constexpr int kPingpongMask = (1 << kFmtInt4) | (1 << kFmtK5) | (1 << kFmtBin);
+// 1-2 % faster for K5 and binary; slower for ternary, int2, int3 and the
+// greedy variant and equal for hier-g32, which keep one buffer and more
+// waves).  int4 g128 has a kernel of its own (gemv_int4_kernel below).
+constexpr int kPingpongMask = (1 << kFmtK5) | (1 << kFmtBin);
 // Codings (bit fmt) whose code loads are plain rather than non-temporal.
 // Binary rows (K/8 bytes) start at 32 bytes past a 64-byte boundary on odd
 // rows, and a row's passes end mid-block: blocks touched by two load
@@ -66,9 +67,9 @@ constexpr int kPingpongMask = (1 << kFmtInt4) | (1 << kFmtK5) | (1 << kFmtBin);
 constexpr int kPlainMask = 1 << kFmtBin;
 // Codings (bit fmt) whose waves raise their priority while issuing a row
 // step's loads, so that a CU's loads are not held behind other waves' unpack
-// work: int4 (0.5B sweep +1.5 %, 7B -0.3 %) and int4-hier-g32 (+1.9 %);
-// K5 -2 %, ternary -4 %, int3 -3 %, binary +0.5 %.
-constexpr int kSetprioMask = (1 << kFmtInt4) | (1 << kFmtHier);
+// work: int4-hier-g32 (+1.9 %); K5 -2 %, ternary -4 %, int3 -3 %, binary
+// +0.5 %.
+constexpr int kSetprioMask = 1 << kFmtHier;
 
 constexpr int kWaves = 4;
 constexpr int kMaxTileRows = kGemvMaxTileRows;
@@ -413,8 +414,8 @@ struct Tile {
 };
 
 // Codings (bit fmt) whose loads use per-step scalar bases (measured per
-// coding: faster for int4 and hier-g32, slower for ternary and K5).
-constexpr int kSbaseMask = (1 << kFmtInt4) | (1 << kFmtHier);
+// coding: faster for hier-g32, slower for ternary and K5).
+constexpr int kSbaseMask = 1 << kFmtHier;
 
 // Order-preserving key of an output: larger value -> larger key, and among
 // equal values the smaller row -> larger key.  fp16: -0 counts as +0, and
@@ -796,6 +797,216 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 8))) voi
   }
 }
 
+// ------------------------------------------------ int4 g128 stream kernel --
+// The int4 g128 GEMV streams each tile's codes as 128-byte lines.  A tile of
+// 32 R rows is cut into 32 units of R consecutive rows (8 lanes each, 8
+// units per wave).  A unit walks its rows' 128-weight groups in memory order,
+// two groups per pass: the lanes with an even index in the unit (quad 0)
+// take the even group, the odd lanes (quad 1) the odd one, one 16-byte chunk
+// per lane, so a pass reads 128 contiguous bytes of the unit's rows -- one
+// whole cache line when rows start on 128-byte boundaries (K a multiple of
+// 256, or R even) -- and every lane is busy for any K.  Both quads can be on
+// different rows (odd groups per row), so each lane sums its quad's groups
+// of a row on its own and, when the quad's next group starts a new row,
+// writes that sum to the row's LDS slot for its lane (eight per row, written
+// once each); the tile's rows are finished from their eight slots at the
+// end, in a fixed order.
+// Group metadata: every four passes each lane of a unit loads one word, the
+// unit's next eight groups (32 contiguous bytes), and each pass hands its
+// quad's word to the quad with one ds_swizzle.  x (permuted to the unpack
+// order, 64 bytes per chunk; two copies back to back when the group count is
+// odd, so that a pass's pair of groups is always adjacent) is staged in LDS
+// while the first codes are in flight.  Codes and metadata flow through
+// register rings kInt4Depth passes deep; the addresses of a pass are
+// wave-uniform bases plus loop-invariant lane offsets.
+//
+// Unpack: the low nibble field of a half sits at mantissa bits 0-3, where
+// fp16 1024.0 has ulp 1, and the high nibble field at bits 4-7, where fp16
+// 64.0 has ulp 1/16; OR-ing the fields into those two constants gives
+// 1024 + q and 64 + q exactly, and subtracting 1024 + z and 64 + z leaves
+// q - z exactly in both, so one fp32 chain sums a chunk.
+constexpr int kInt4Depth = 8;                 // passes in flight per lane (a multiple of 4)
+constexpr uint32_t kMagic64 = 0x54005400u;   // fp16 pair (64.0, 64.0)
+
+// ds_swizzle bit mode within 32 lanes: source lane = (lane & 0b11001) | 2j,
+// i.e. unit lane 2j + q for every lane of quad q (j = pass within the block).
+template <int J>
+__device__ __forceinline__ uint32_t quad_meta(uint32_t words) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)words, 0x19 | ((2 * J) << 5));
+}
+
+template <bool GREEDY>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 8))) void gemv_int4_kernel(
+    const tkq_gemv_desc* __restrict__ descs, int count, Greedy g) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  __shared__ unsigned long long wave_best[kWaves];
+  static_assert(kInt4Depth % 4 == 0, "metadata blocks of four passes");
+
+  const int tile = blockIdx.x;
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (descs[mid].work0 <= tile) lo = mid;
+    else hi = mid - 1;
+  }
+  const tkq_gemv_desc* d = descs + lo;
+  const int N = d->N, K = d->K;
+  const int local = tile - d->work0, nbig = d->big_tiles;
+  const int rpt = local < nbig ? d->rows_per_tile : d->small_rows;
+  const int row0 = local < nbig ? local * rpt : nbig * d->rows_per_tile + (local - nbig) * rpt;
+  const int nrows = min(rpt, N - row0);
+  const bool track = GREEDY && lo == g.target;
+
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 1, sub = (lane >> 1) & 3, ul = lane & 7;  // quad, lane in quad, lane in unit
+  const int unit = (int)(threadIdx.x >> 3);             // 0..31
+  const int G = K >> 7;                                  // groups per row
+  const int R = rpt >> 5;                                // rows per unit
+  const int RG = R * G, passes = (RG + 1) >> 1;
+  const bool odd = (RG & 1) != 0;                        // quad 1 idle in the last pass
+  const int xper = (G & 1) ? 2 * G : G;                  // groups of x held in LDS
+  const uint32_t row_bytes = (uint32_t)K >> 1;
+  uint32_t* xl = lds;                                    // 64 words per group
+  float* pl = reinterpret_cast<float*>(lds + xper * 64);  // 8 partial slots per row
+
+  // Codes: pass p of a unit reads bytes 128 p .. 128 p + 127 of the unit's
+  // rows; metadata block B (passes 4B .. 4B + 3) is the unit's groups
+  // 8B .. 8B + 7.  Loads past the unit's last pass get an empty range.
+  const char* tcodes = (const char*)d->codes + (size_t)row0 * row_bytes;
+  const char* tmeta = (const char*)d->meta + (size_t)row0 * (size_t)G * 4u;
+  const uint32_t tbytes = (uint32_t)nrows * row_bytes, tmbytes = (uint32_t)nrows * (uint32_t)G * 4u;
+  const uint32_t vco = (uint32_t)unit * (uint32_t)R * row_bytes + (uint32_t)q * 64u + (uint32_t)sub * 16u;
+  const uint32_t vmo = (uint32_t)(unit * RG + ul) * 4u;
+  uint32_t ico = 0, imo = 0;
+  const uint32_t iend = (uint32_t)passes * 128u, mend = (uint32_t)((passes + 3) >> 2) * 32u;
+  u32x4 cb[kInt4Depth];
+  uint32_t mw[kInt4Depth / 4];
+  auto issue = [&](int k) {
+    __builtin_amdgcn_s_setprio(1);
+    const uint32_t n = ico < iend ? (uint32_t)max((int)tbytes - (int)ico, 0) : 0u;
+    cb[k] = load16_nt(make_rsrc(tcodes + ico, n), vco);
+    if ((k & 3) == 3) {  // after the block's last pass has read it
+      const uint32_t nm = imo < mend ? (uint32_t)max((int)tmbytes - (int)imo, 0) : 0u;
+      mw[k >> 2] = load4(make_rsrc(tmeta + imo, nm), vmo);
+      imo += 32u;
+    }
+    __builtin_amdgcn_s_setprio(0);
+    ico += 128u;
+  };
+#pragma unroll
+  for (int k = 0; k < kInt4Depth; ++k) issue(k);
+
+  // LDS staging: x in the unpack order (chunk c's pairs (x0, x4), (x1, x5),
+  // (x2, x6), (x3, x7) of each 8-element word) and zeroed row slots.
+  {
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(d->x, (uint32_t)K * 2u);
+    const int C = K >> 5;
+    for (int i = threadIdx.x; i < xper * 4; i += 64 * kWaves) {
+      const int c = i < C ? i : i - C;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const u32x4 v = load16(xr, (uint32_t)c * 64u + 16u * w);
+        u32x4 pz;
+        pz[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
+        pz[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
+        pz[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
+        pz[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+        *reinterpret_cast<u32x4*>(&xl[16 * i + 4 * w]) = pz;
+      }
+    }
+    for (int i = threadIdx.x; i < 8 * rpt; i += 64 * kWaves) pl[i] = 0.0f;
+  }
+  __syncthreads();
+
+  const uint32_t m0 = in_sgpr(0x000F000Fu), m1 = in_sgpr(0x00F000F0u);
+  const uint32_t g1024 = in_vgpr(kMagic), g64 = in_vgpr(kMagic64);
+  const char* xlane = (const char*)xl + q * 256 + sub * 64;  // plus (2 p mod xper) * 256
+  char* plane = reinterpret_cast<char*>(pl + 8 * unit * R + ul);  // row r's slot: + 32 r bytes
+  const uint32_t q32 = (uint32_t)q * 32u;
+  const uint64_t kQuad0 = 0x5555555555555555ull;        // lanes of quad 0 in every unit
+  // Pass state (wave-uniform): group index within the row of quad 0's group
+  // (c0) and its row within the unit (as roff); x offset of the pass.
+  int c0 = 0;
+  uint32_t roff = 0;  // 32 r0: byte offset of row r0's slots
+  uint32_t xo = 0;
+  const uint32_t xwrap = (uint32_t)xper * 256u;
+  float acc = 0.0f;
+  for (int b = 0; b < passes; b += kInt4Depth) {
+#pragma unroll
+    for (int k = 0; k < kInt4Depth; ++k) {
+      const int p = b + k;
+      if (p < passes) {
+        const u32x4* xp = reinterpret_cast<const u32x4*>(xlane + xo);
+        const u32x4 xv[4] = {xp[0], xp[1], xp[2], xp[3]};
+        uint32_t m;
+        switch (k & 3) {
+          case 0: m = quad_meta<0>(mw[k >> 2]); break;
+          case 1: m = quad_meta<1>(mw[k >> 2]); break;
+          case 2: m = quad_meta<2>(mw[k >> 2]); break;
+          default: m = quad_meta<3>(mw[k >> 2]); break;
+        }
+        const h2 zz = bcast_hi(m);
+        const h2 c1 = zz + as_h2(g1024), c64 = zz + as_h2(g64);
+        float dv = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t v = cb[k][w], t = v >> 8;
+          dv = __builtin_amdgcn_fdot2(as_h2((v & m0) | g1024) - c1, as_h2(xv[w][0]), dv, false);
+          dv = __builtin_amdgcn_fdot2(as_h2((v & m1) | g64) - c64, as_h2(xv[w][1]), dv, false);
+          dv = __builtin_amdgcn_fdot2(as_h2((t & m0) | g1024) - c1, as_h2(xv[w][2]), dv, false);
+          dv = __builtin_amdgcn_fdot2(as_h2((t & m1) | g64) - c64, as_h2(xv[w][3]), dv, false);
+        }
+        const float a = fmaf(half_lo(m), dv, acc);
+        // Quad 1's group of this pass: c0 + 1 within row r0, or the next row.
+        const bool wrap = c0 + 1 == G;
+        const int c1g = wrap ? 0 : c0 + 1;
+        const bool last_odd = odd && p == passes - 1;    // quad 1 has no group
+        if (last_odd) acc = __builtin_amdgcn_inverse_ballot_w64(kQuad0) ? a : acc;
+        else acc = a;
+        // quads whose row ends with this pass
+        const uint64_t fm = (c0 + 2 >= G ? kQuad0 : 0ull) | (c1g + 2 >= G && !last_odd ? ~kQuad0 : 0ull);
+        if (fm) {
+          if (__builtin_amdgcn_inverse_ballot_w64(fm)) {
+            *reinterpret_cast<float*>(plane + roff + (wrap ? q32 : 0u)) = acc;
+            acc = 0.0f;
+          }
+        }
+        c0 += 2;
+        if (c0 >= G) { c0 -= G; roff += 32u; }
+        if (c0 >= G) { c0 -= G; roff += 32u; }
+        xo += 512u;
+        if (xo >= xwrap) xo -= xwrap;
+      }
+      issue(k);
+    }
+  }
+  __syncthreads();
+
+  // Rows of the tile: the sum of their eight slots (pairwise, fixed order).
+  const __amdgpu_buffer_rsrc_t yr = make_rsrc((char*)d->y + (size_t)row0 * 2u, (uint32_t)nrows * 2u);
+  uint64_t best = 0;
+  for (int r = threadIdx.x; r < nrows; r += 64 * kWaves) {
+    const float4 u = reinterpret_cast<const float4*>(pl)[2 * r], v = reinterpret_cast<const float4*>(pl)[2 * r + 1];
+    const uint16_t h = half_bits(((u.x + u.y) + (u.z + u.w)) + ((v.x + v.y) + (v.z + v.w)));
+    store2(yr, (uint32_t)r * 2u, h);
+    if (GREEDY && track) best = max_u64(best, greedy_key_f16(h, (uint32_t)(row0 + r)));
+  }
+
+  if constexpr (GREEDY) {
+    if (track) {  // uniform over the workgroup
+      best = wave_max_u64(best);
+      const int wave = threadIdx.x >> 6;
+      if (lane == 0) wave_best[wave] = best;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        uint64_t bb = wave_best[0];
+        for (int w = 1; w < kWaves; ++w) bb = max_u64(bb, wave_best[w]);
+        g.slots[tile - d->work0] = bb;
+      }
+    }
+  }
+}
+
 // One workgroup: the largest key over the target's tile slots -> its row.
 __global__ __launch_bounds__(256) void greedy_finish_kernel(const tkq_gemv_desc* __restrict__ descs, int count,
                                                             int target, int tiles,
@@ -859,8 +1070,22 @@ hipError_t launch_gemv(int fmt, int jmax, const tkq_gemv_desc* dev_descs, int co
                        int target, int32_t* token, uint64_t* slots, hipStream_t stream) {
   const bool greedy = target >= 0;
   GemvFn fn = nullptr;
+  size_t lds = 0;
   switch (fmt) {
-    case kFmtInt4: fn = pick<kFmtInt4>(jmax, greedy); break;
+    case kFmtInt4:  // jmax: the launch's dynamic LDS bytes
+      if (jmax < 1 || jmax > kInt4MaxLds) return hipErrorInvalidValue;
+      fn = greedy ? gemv_int4_kernel<true> : gemv_int4_kernel<false>;
+      lds = (size_t)jmax;
+      if (lds > 64 * 1024) {  // above the default dynamic-LDS limit (once per kernel; idempotent)
+        static bool raised[2] = {false, false};
+        if (!raised[greedy]) {
+          const hipError_t e =
+              hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, kInt4MaxLds);
+          if (e != hipSuccess) return e;
+          raised[greedy] = true;
+        }
+      }
+      break;
     case kFmtHier: fn = pick<kFmtHier>(jmax, greedy); break;
     case kFmtInt2: fn = pick<kFmtInt2>(jmax, greedy); break;
     case kFmtInt3: fn = pick<kFmtInt3>(jmax, greedy); break;
@@ -870,7 +1095,7 @@ hipError_t launch_gemv(int fmt, int jmax, const tkq_gemv_desc* dev_descs, int co
   }
   if (!fn) return hipErrorInvalidValue;
   const Greedy g = {target, slots};
-  hipLaunchKernelGGL(fn, dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream, dev_descs, count, g);
+  hipLaunchKernelGGL(fn, dim3((uint32_t)tiles), dim3(64 * kWaves), lds, stream, dev_descs, count, g);
   if (greedy) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -24,8 +24,8 @@ struct GemvShape {
   int passes;      // 16-byte chunks each lane reads per row
   int kslices;     // waves that split one row's K range (1, 2 or 4)
 };
-__host__ __device__ inline int pack_shape(GemvShape s) { return s.lanes_log2 | (s.passes << 4) | (s.kslices << 12); }
-__host__ __device__ inline GemvShape unpack_shape(int v) { return {v & 15, (v >> 4) & 255, (v >> 12) & 15}; }
+__host__ __device__ inline int pack_shape(GemvShape s) { return s.lanes_log2 | (s.passes << 4) | (s.kslices << 16); }
+__host__ __device__ inline GemvShape unpack_shape(int v) { return {v & 15, (v >> 4) & 4095, (v >> 16) & 15}; }
 
 // Weights carried by one 16-byte chunk of codes, per coding.
 inline int weights_per_chunk(int fmt) {
@@ -52,6 +52,14 @@ constexpr int kGemvMaxTileRows = 1024;
 // enough that every CU has ~100 KB of loads outstanding.  Used by the kernel
 // and by the planner (tile heights are multiples of it).
 __host__ __device__ constexpr int gemv_unroll(int passes) { return passes == 1 ? 4 : (passes == 2 ? 2 : 1); }
+
+// int4 g128 GEMV: dynamic LDS of a tile of `rows` rows of K columns -- x
+// (two copies when K / 128 is odd) and eight fp32 slots per row -- and the
+// limit it is held to (160 KB per workgroup less the static part).
+constexpr int kInt4MaxLds = 160 * 1024 - 64;
+__host__ __device__ constexpr int64_t int4_lds_bytes(int K, int rows) {
+  return int64_t((K / 128) % 2 ? 2 * (K / 128) : K / 128) * 256 + int64_t(rows) * 32;
+}
 
 // Largest `passes` value each kernel variant supports (x stays in registers).
 int gemv_max_passes(int fmt);

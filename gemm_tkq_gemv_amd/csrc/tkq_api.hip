@@ -57,9 +57,11 @@ bool known_fmt(int fmt) {
 // Column unit of a coding's GEMV (its group size, or one code word).
 int k_unit(int fmt) { return fmt == TKQ_FMT_INT4_HIER_G32 ? 32 : 128; }
 
-// Largest K each GEMV handles with x resident in registers: chunks per row
-// <= 4 k-slices x 64 lanes x the planner's pass cap.
+// Largest K each GEMV handles: int4 keeps x in LDS (64 KB at K = 32768); the
+// other codings keep x in registers, chunks per row <= 4 k-slices x 64 lanes
+// x the planner's pass cap.
 int64_t gemv_max_k(int fmt) {
+  if (fmt == TKQ_FMT_INT4_G128) return 32768;  // x in LDS: two copies of K = 32640 still fit
   return int64_t(4) * 64 * std::min(tkq::gemv_max_passes(fmt), plan_params(fmt).max_passes) *
          tkq::weights_per_chunk(fmt);
 }
@@ -84,6 +86,9 @@ int pack_common(int fmt, const float* W, int64_t N, int64_t K, void* codes, void
 // with the fewest idle lane-chunk slots (16-byte chunks per row over
 // k-slices x lanes x passes).
 tkq::GemvShape choose_shape(int fmt, int K) {
+  // int4: units of eight lanes walk whole rows group by group (the kernel
+  // has no passes or k-slices to choose).
+  if (fmt == TKQ_FMT_INT4_G128) return {3, K / 128, 1};
   const int prefer = plan_params(fmt).prefer_passes;
   const int C = K / tkq::weights_per_chunk(fmt);
   const int jmax = std::min(tkq::gemv_max_passes(fmt), plan_params(fmt).max_passes);
@@ -111,12 +116,27 @@ tkq::GemvShape choose_shape(int fmt, int K) {
   return best;
 }
 
+// int4 g128: a tile is 32 units of R rows, R ~ the target bytes per wave over
+// eight units; R even when a row has an odd number of groups (units then
+// start on 128-byte boundaries), and the tile's LDS (x, metadata, row slots)
+// within the per-workgroup limit.
+int int4_rows_per_tile(int K, int64_t target) {
+  const int G = K / 128;
+  const int64_t row_bytes = int64_t(K) / 2;
+  int R = (int)std::max<int64_t>(1, (target + 8 * row_bytes - 1) / (8 * row_bytes));
+  R = std::min(R, tkq::kGemvMaxTileRows / 32);
+  if ((G & 1) && R > 1) R &= ~1;
+  while (R > 1 && tkq::int4_lds_bytes(K, 32 * R) > tkq::kInt4MaxLds) R -= (G & 1) && R > 2 ? 2 : 1;
+  return 32 * R;
+}
+
 int rows_per_tile(int fmt, int N, int K, tkq::GemvShape sh, int64_t kTileTargetBytes) {
+  if (fmt == TKQ_FMT_INT4_G128) return int4_rows_per_tile(K, kTileTargetBytes);
   const int C = K / tkq::weights_per_chunk(fmt);
   const int Cs = (C + sh.kslices - 1) / sh.kslices;
   const int P = 64 >> sh.lanes_log2;       // rows per wave step
   const int RG = 4 / sh.kslices;           // row groups per workgroup
-  const int U = tkq::gemv_unroll(sh.passes);  // steps per loop iteration
+  const int U = fmt == TKQ_FMT_INT4_G128 ? 1 : tkq::gemv_unroll(sh.passes);  // steps per loop iteration
   const int64_t step_bytes = int64_t(P) * Cs * tkq::chunk_bytes(fmt);
   int64_t steps = (kTileTargetBytes + step_bytes - 1) / step_bytes;
   const int64_t need = ((int64_t(N) + RG - 1) / RG + P - 1) / P;  // steps to cover N
@@ -258,7 +278,12 @@ int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan) {
     d.small_rows = small;
     work += tiles;
     pos += d.N * row_bytes;
-    if (sh.passes > jmax) jmax = sh.passes;
+    if (fmt == TKQ_FMT_INT4_G128) {  // the variant is the launch's LDS bytes
+      const int64_t lds = tkq::int4_lds_bytes(d.K, big);
+      if (lds > jmax) jmax = (int)lds;
+    } else if (sh.passes > jmax) {
+      jmax = sh.passes;
+    }
   }
   plan->fmt = fmt;
   plan->count = count;
@@ -272,7 +297,8 @@ int tkq_gemv_prepare(tkq_gemv_desc* descs, int32_t count, tkq_gemv_plan* plan) {
 static int check_plan(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs) {
   if (!plan || !dev_descs) return TKQ_EINVAL;
   if (plan->magic != kPlanMagic || !known_fmt(plan->fmt) || plan->count < 1 || plan->tiles < 1 ||
-      plan->tiles > INT32_MAX || plan->variant < 1 || plan->variant > tkq::gemv_max_passes(plan->fmt))
+      plan->tiles > INT32_MAX || plan->variant < 1 ||
+      plan->variant > (plan->fmt == TKQ_FMT_INT4_G128 ? tkq::kInt4MaxLds : tkq::gemv_max_passes(plan->fmt)))
     return TKQ_EPLAN;
   if (!aligned16(dev_descs)) return TKQ_EALIGN;
   return TKQ_OK;

@@ -221,7 +221,7 @@ typedef struct tkq_gemv_desc {
                                       rows each) at the top of the matrix   */
   int32_t rows_per_tile; /* [prepare] rows of a large tile                  */
   int32_t shape;         /* [prepare] lanes-per-row log2 | passes<<4 |
-                                      k-slices<<12                          */
+                                      k-slices<<16                          */
   int32_t small_rows;    /* [prepare] rows of a small tile; small tiles
                                       cover the rows below the large ones   */
   const void* codes;     /* packed codes (layout per fmt)                   */
@@ -236,7 +236,8 @@ typedef struct tkq_gemv_plan {
   int32_t fmt;        /* common coding of the descriptors                   */
   int32_t count;      /* number of descriptors                              */
   int64_t tiles;      /* total row tiles = workgroups per launch            */
-  int32_t variant;    /* largest pass count: selects the kernel variant     */
+  int32_t variant;    /* largest pass count: selects the kernel variant
+                         (int4: sizes the LDS copy of x, K / 128)          */
   int32_t magic;      /* set by tkq_gemv_prepare                            */
   int64_t reserved;
 } tkq_gemv_plan;

@@ -107,7 +107,7 @@ def _prepare(arr):
 
 
 def _shape(d):
-    return 1 << (d.shape & 15), (d.shape >> 4) & 255, (d.shape >> 12) & 15
+    return 1 << (d.shape & 15), (d.shape >> 4) & 4095, (d.shape >> 16) & 15
 
 
 def _tiles(d):
@@ -141,6 +141,16 @@ def test_prepare_tiles_cover_rows(fmt):
             assert r1 == r0 + h0
         L, J, S = _shape(d)
         C = k // per_chunk
+        if fmt == 1:
+            # int4: 32 units of R rows per tile, R even when a row has an odd
+            # number of 128-weight groups (unless R = 1)
+            assert (L, J, S) == (8, k // 128, 1)
+            for h in (d.rows_per_tile, d.small_rows):
+                assert h % 32 == 0 and 0 < h <= 1024
+                assert (k // 128) % 2 == 0 or h == 32 or h % 64 == 0
+            assert d.small_rows <= d.rows_per_tile
+            work += len(tiles)
+            continue
         assert S in (1, 2, 4) and 1 <= J <= 8
         assert S * L * J >= C                       # every chunk has a lane
         P = 64 // L
@@ -172,12 +182,23 @@ def test_tile_edge_rows_match_the_plan():
 def test_prepare_shapes_for_model_matrices():
     arr = _descs(1, [(896, 896), (896, 4864), (3584, 3584), (3584, 18944)])
     assert _prepare(arr)[0] == tkq.OK
-    # int4 prefers two passes on ties: 28 chunks -> 16 lanes x 2 passes
-    # (4 rows per wave step) rather than 32 lanes x 1 pass (same utilisation)
-    assert _shape(arr[0]) == (16, 2, 1)
-    assert _shape(arr[1]) == (64, 3, 1)   # 152 chunks: 64 lanes, three passes
-    assert _shape(arr[2]) == (64, 2, 1)   # 112 chunks
-    assert _shape(arr[3]) == (64, 3, 4)   # 592 chunks: four k-slices
+    # int4: units of eight lanes, the pass field holds the row's group count
+    assert [_shape(d) for d in arr] == [(8, 7, 1), (8, 38, 1), (8, 28, 1), (8, 148, 1)]
+    # rows per tile: 32 units of R rows, R from 48 KB per wave (even for 7 groups)
+    assert [d.rows_per_tile for d in arr] == [32 * 14, 32 * 3, 32 * 4, 32 * 1]
+    # the plan's variant is the largest tile's dynamic LDS: x (two copies for an
+    # odd group count) and eight fp32 slots per row
+    lds = [(2 * g if g % 2 else g) * 256 + r * 32
+           for g, r in [(7, 448), (38, 96), (28, 128), (148, 32)]]
+    assert plan_variant(arr) == max(lds)
+    # other codings keep x in registers: K5 (16 weights per chunk), 896 columns
+    # = 56 chunks -> 64 lanes x 1 pass
+    arr = _descs(2, [(896, 896)])
+    assert _prepare(arr)[0] == tkq.OK and _shape(arr[0]) == (64, 1, 1)
+
+
+def plan_variant(arr):
+    return _prepare(arr)[1].variant
 
 
 def test_prepare_sweep_counts():

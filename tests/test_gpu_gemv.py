@@ -220,3 +220,17 @@ def test_gemv_and_pack_on_a_side_stream():
     for y in ys:
         assert torch.equal(y, y0)
     _check("int4", W, x, y0, codes, meta, "side stream")
+
+
+@pytest.mark.parametrize("N,K", [(70, 32640), (97, 16256), (33, 128 * 3)])
+def test_gemv_int4_odd_group_counts(N, K):
+    """int4 rows with an odd number of 128-weight groups: x is held twice in
+    LDS and the tile's units pair groups across row ends; K = 32640 is the
+    largest LDS footprint a tile can have (x twice plus 32 rows of metadata)."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    W, x = _inputs("int4", N, K, 500 + K // 128)
+    (it,) = _items(torch, tkq, "int4", [(W, x)])
+    tkq.GemvBatch("int4", [it]).run()
+    torch.cuda.synchronize()
+    _check("int4", W, x, it["y"], it["codes"], it["meta"], "int4 %dx%d" % (N, K))
