@@ -546,11 +546,14 @@ def run_kv(args, torch, tkq, B, H, Hk, T):
 
 
 def gemv_kernel_name(fmt, jmax, greedy):
-    """The GEMV kernel instance a launch runs: gemv_kernel<coding, largest
-    pass count, greedy variant> (as the profiler names it)."""
+    """The GEMV kernel instance a launch runs, as the profiler names it:
+    int4 g128 has its own kernel, gemv_int4_kernel<greedy variant>; the other
+    codings run gemv_kernel<coding, largest pass count, greedy variant>."""
     from gemm_tkq_gemv_amd import tkq
-    return "gemv_kernel<%d, %d, %s>" % (tkq.FORMATS[fmt], jmax, "true" if greedy else "false") + (
-        " + greedy_finish_kernel" if greedy else "")
+    flag = "true" if greedy else "false"
+    name = ("gemv_int4_kernel<%s>" % flag if fmt == "int4"
+            else "gemv_kernel<%d, %d, %s>" % (tkq.FORMATS[fmt], jmax, flag))
+    return name + (" + greedy_finish_kernel" if greedy else "")
 
 
 def _fmt_name(fmt):
