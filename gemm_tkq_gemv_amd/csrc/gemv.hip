@@ -8,9 +8,10 @@
 //
 //  * Work unit.  One workgroup (4 wave64s) owns a tile of consecutive rows of
 //    one matrix (int4 g128 has its own kernel, gemv_int4_kernel, that reads
-//    128-byte lines per 8-lane unit and keeps x in LDS); the grid is the concatenation of every matrix's tiles, and a
-//    workgroup finds its matrix by binary search over the descriptors'
-//    first-tile indices (scalar loads).  Tiles are large (~24 KB per wave,
+//    128-byte lines per 8-lane unit and keeps x in LDS); the grid is the
+//    concatenation of every matrix's tiles, and a workgroup finds its matrix
+//    by binary search over the descriptors' first-tile indices (scalar
+//    loads).  Tiles are large (~24 KB per wave,
 //    amortising the per-tile setup) except over the last stretch of the
 //    sweep, where small tiles let the final workgroups finish together
 //    instead of trailing one large tile's duration behind each other.
