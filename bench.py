@@ -49,21 +49,21 @@ TRAFFIC_SOURCES = {"gemv": ["gemm_tkq_gemv_amd/csrc/gemv.hip"] + _COMMON,
                    "prefill": ["gemm_tkq_gemv_amd/csrc/prefill.hip"] + _COMMON,
                    "kv": ["gemm_tkq_gemv_amd/csrc/kv.hip"] + _COMMON}
 # workload -> (kernel family, bytes per launch, sha256[:16] of that family's sources)
-TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266576807, "f0da369e2b61fbd3"),
-                 "0.5b-k5": ("gemv", 506954837, "f0da369e2b61fbd3"),
-                 "0.5b-tern": ("gemv", 135433325, "f0da369e2b61fbd3"),
-                 "bin": ("gemv", 115067440, "f0da369e2b61fbd3"),
-                 "7b-int4": ("gemv", 3786812282, "f0da369e2b61fbd3"),
-                 "7b-prefill": ("prefill", 313632554, "2d7378f14da2d78f"),
-                 "0.5b-hier": ("gemv", 268490094, "f0da369e2b61fbd3"),
-                 "0.5b-int2": ("gemv", 143167991, "f0da369e2b61fbd3"),
-                 "0.5b-int3": ("gemv", 206200448, "f0da369e2b61fbd3"),
-                 "0.5b-int4-greedy": ("gemv", 266682033, "f0da369e2b61fbd3"),
-                 "0.5b-int4-m16": ("small_m", 382385898, "8ae7d60609f3ddb1"),
-                 "kv-32k": ("kv", 143371671, "7402b7b1004bcc79"),
-                 "kv-4k": ("kv", 18194319, "7402b7b1004bcc79"),
-                 "kv-32k-gqa": ("kv", 37017256, "7402b7b1004bcc79"),
-                 "kv-128k-gqa": ("kv", 145068431, "7402b7b1004bcc79")}
+TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266549561, "35f714caa64813a4"),
+                 "0.5b-k5": ("gemv", 506970088, "35f714caa64813a4"),
+                 "0.5b-tern": ("gemv", 135446130, "35f714caa64813a4"),
+                 "bin": ("gemv", 115069925, "35f714caa64813a4"),
+                 "7b-int4": ("gemv", 3782045937, "35f714caa64813a4"),
+                 "7b-prefill": ("prefill", 314142403, "c4eec7362ab15d85"),
+                 "0.5b-hier": ("gemv", 268434790, "35f714caa64813a4"),
+                 "0.5b-int2": ("gemv", 143152906, "35f714caa64813a4"),
+                 "0.5b-int3": ("gemv", 206226590, "35f714caa64813a4"),
+                 "0.5b-int4-greedy": ("gemv", 266617012, "35f714caa64813a4"),
+                 "0.5b-int4-m16": ("small_m", 382402161, "b7fba09e0dc1c849"),
+                 "kv-32k": ("kv", 143471786, "f64f67bc468cd055"),
+                 "kv-4k": ("kv", 18406316, "f64f67bc468cd055"),
+                 "kv-32k-gqa": ("kv", 37208579, "f64f67bc468cd055"),
+                 "kv-128k-gqa": ("kv", 145428332, "f64f67bc468cd055")}
 
 
 def traffic_family(workload):
