@@ -817,16 +817,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 8))) voi
 // quad's word to the quad with one ds_swizzle.  x (permuted to the unpack
 // order, 64 bytes per chunk; two copies back to back when the group count is
 // odd, so that a pass's pair of groups is always adjacent) is staged in LDS
-// while the first codes are in flight.  Codes and metadata flow through
-// register rings kInt4Depth passes deep; the addresses of a pass are
-// wave-uniform bases plus loop-invariant lane offsets.
+// while the first codes are in flight.  Codes flow through a register ring
+// kInt4Depth passes deep, metadata two blocks (eight passes) ahead; the
+// addresses of a pass are wave-uniform bases plus loop-invariant lane
+// offsets.
 //
 // Unpack: the low nibble field of a half sits at mantissa bits 0-3, where
 // fp16 1024.0 has ulp 1, and the high nibble field at bits 4-7, where fp16
 // 64.0 has ulp 1/16; OR-ing the fields into those two constants gives
 // 1024 + q and 64 + q exactly, and subtracting 1024 + z and 64 + z leaves
 // q - z exactly in both, so one fp32 chain sums a chunk.
-constexpr int kInt4Depth = 8;                 // passes in flight per lane (a multiple of 4)
+constexpr int kInt4Unroll = 8;                // passes per loop iteration: two metadata blocks
+constexpr int kInt4Depth = 4;                 // passes of codes in flight per lane (divides kInt4Unroll)
 constexpr uint32_t kMagic64 = 0x54005400u;   // fp16 pair (64.0, 64.0)
 
 // ds_swizzle bit mode within 32 lanes: source lane = (lane & 0b11001) | 2j,
@@ -841,7 +843,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 8))) voi
     const tkq_gemv_desc* __restrict__ descs, int count, Greedy g) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   __shared__ unsigned long long wave_best[kWaves];
-  static_assert(kInt4Depth % 4 == 0, "metadata blocks of four passes");
+  static_assert(kInt4Unroll == 8 && kInt4Unroll % kInt4Depth == 0, "two metadata blocks per iteration");
 
   const int tile = blockIdx.x;
   int lo = 0, hi = count - 1;
@@ -881,19 +883,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 8))) voi
   uint32_t ico = 0, imo = 0;
   const uint32_t iend = (uint32_t)passes * 128u, mend = (uint32_t)((passes + 3) >> 2) * 32u;
   u32x4 cb[kInt4Depth];
-  uint32_t mw[kInt4Depth / 4];
-  auto issue = [&](int k) {
+  uint32_t mw[2];
+  auto issue = [&](int slot) {  // the next pass's codes
     __builtin_amdgcn_s_setprio(1);
     const uint32_t n = ico < iend ? (uint32_t)max((int)tbytes - (int)ico, 0) : 0u;
-    cb[k] = load16_nt(make_rsrc(tcodes + ico, n), vco);
-    if ((k & 3) == 3) {  // after the block's last pass has read it
-      const uint32_t nm = imo < mend ? (uint32_t)max((int)tmbytes - (int)imo, 0) : 0u;
-      mw[k >> 2] = load4(make_rsrc(tmeta + imo, nm), vmo);
-      imo += 32u;
-    }
+    cb[slot] = load16_nt(make_rsrc(tcodes + ico, n), vco);
     __builtin_amdgcn_s_setprio(0);
     ico += 128u;
   };
+  auto issue_meta = [&](int slot) {  // the next metadata block
+    const uint32_t nm = imo < mend ? (uint32_t)max((int)tmbytes - (int)imo, 0) : 0u;
+    mw[slot] = load4(make_rsrc(tmeta + imo, nm), vmo);
+    imo += 32u;
+  };
+  issue_meta(0);
+  issue_meta(1);
 #pragma unroll
   for (int k = 0; k < kInt4Depth; ++k) issue(k);
 
@@ -932,9 +936,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 8))) voi
   uint32_t xo = 0;
   const uint32_t xwrap = (uint32_t)xper * 256u;
   float acc = 0.0f;
-  for (int b = 0; b < passes; b += kInt4Depth) {
+  for (int b = 0; b < passes; b += kInt4Unroll) {
 #pragma unroll
-    for (int k = 0; k < kInt4Depth; ++k) {
+    for (int k = 0; k < kInt4Unroll; ++k) {
       const int p = b + k;
       if (p < passes) {
         const u32x4* xp = reinterpret_cast<const u32x4*>(xlane + xo);
@@ -951,7 +955,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 8))) voi
         float dv = 0.0f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint32_t v = cb[k][w], t = v >> 8;
+          const uint32_t v = cb[k % kInt4Depth][w], t = v >> 8;
           dv = __builtin_amdgcn_fdot2(as_h2((v & m0) | g1024) - c1, as_h2(xv[w][0]), dv, false);
           dv = __builtin_amdgcn_fdot2(as_h2((v & m1) | g64) - c64, as_h2(xv[w][1]), dv, false);
           dv = __builtin_amdgcn_fdot2(as_h2((t & m0) | g1024) - c1, as_h2(xv[w][2]), dv, false);
@@ -978,7 +982,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 8))) voi
         xo += 512u;
         if (xo >= xwrap) xo -= xwrap;
       }
-      issue(k);
+      issue(k % kInt4Depth);
+      if ((k & 3) == 3) issue_meta(k >> 2);  // after the block's last pass has read it
     }
   }
   __syncthreads();
