@@ -25,8 +25,13 @@
 //    scales, o_c = sum_t p_t sV_t (v_ct - zV_t) = sum_t p'_t v_ct - sum_t
 //    p'_t zV_t, p' = p * sV rounded to fp16 (in LDS, read back in the unpack
 //    order); 4 lanes per channel (32 tokens each).
-//  * The constant parts of the magic-number products (1024 or 64 per code
-//    position) and the zero points are removed per lane chunk in fp32.
+//  * Exact unpack: a code field OR-ed into fp16 1024.0 (low nibble, ulp 1)
+//    or 64.0 (high nibble, ulp 1/16) gives M + code; subtracting M + zero in
+//    fp16 leaves code - zero exactly, so every product is a small exact
+//    integer times q' or p' and the fp32 sums carry only the dequantized
+//    terms (removing M * sum x after the sum instead left an error that grows
+//    with M |x|: a query channel of ~1e3 on zero-point keys broke the
+//    tolerance).
 //  * Each workgroup writes (m, l, o[128]) per query head to a workspace.
 //    With few splits (short contexts) it counts its arrival and the last
 //    split of each (sequence, head group) to arrive merges the splits
@@ -130,24 +135,43 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const uint16_t* __restrict
 
 // ---------------------------------------------------------------- decode --
 struct Regs {
-  uint32_t m0, m1, magic;
+  uint32_t m0, m1, magic, magic64;
 };
+constexpr uint32_t kMagic64 = 0x54005400u;  // fp16 pair (64.0, 64.0)
 
 // sum over one 16-byte chunk (32 codes, natural nibble order) of
-// (1024 + m code) * x with the GEMV's pairing (0,4),(1,5),(2,6),(3,7) and
-// x16 fields rescaled: = sum_k code_k x_k + sum_k c_k x_k, c_k = 1024 for
-// even k, 64 for odd k.
-__device__ __forceinline__ float chunk_dot(u32x4 q, const uint32_t* xr, const Regs& R) {
-  float lo = 0.0f, hi = 0.0f;
+// (code - zero) * x with the GEMV's pairing (0,4),(1,5),(2,6),(3,7):
+// zs[4w + i] = (M + z, M + z') for the chunk positions (8w + i, 8w + i + 4),
+// M = 1024 for the low nibble fields (i even) and 64 for the high ones.
+__device__ __forceinline__ float chunk_dot(u32x4 q, const uint32_t* xr, const uint32_t* zs, const Regs& R) {
+  float acc = 0.0f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const uint32_t v = q[w], t = v >> 8;
-    lo = __builtin_amdgcn_fdot2(as_h2((v & R.m0) | R.magic), as_h2(xr[4 * w + 0]), lo, false);
-    hi = __builtin_amdgcn_fdot2(as_h2((v & R.m1) | R.magic), as_h2(xr[4 * w + 1]), hi, false);
-    lo = __builtin_amdgcn_fdot2(as_h2((t & R.m0) | R.magic), as_h2(xr[4 * w + 2]), lo, false);
-    hi = __builtin_amdgcn_fdot2(as_h2((t & R.m1) | R.magic), as_h2(xr[4 * w + 3]), hi, false);
+    acc = __builtin_amdgcn_fdot2(as_h2((v & R.m0) | R.magic) - as_h2(zs[4 * w + 0]), as_h2(xr[4 * w + 0]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2((v & R.m1) | R.magic64) - as_h2(zs[4 * w + 1]), as_h2(xr[4 * w + 1]), acc,
+                                 false);
+    acc = __builtin_amdgcn_fdot2(as_h2((t & R.m0) | R.magic) - as_h2(zs[4 * w + 2]), as_h2(xr[4 * w + 2]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2((t & R.m1) | R.magic64) - as_h2(zs[4 * w + 3]), as_h2(xr[4 * w + 3]), acc,
+                                 false);
   }
-  return fmaf(hi, 0.0625f, lo);
+  return acc;
+}
+
+// The subtrahends of chunk_dot for the 32 chunk positions whose zero points
+// are the high halves of meta[0..31] (half2 {scale, zero} words); with
+// `mixed` the high nibble positions take 64 (chunk_dot), else all take 1024
+// (the matrix-core kernel's multiplier-1 unpack).
+__device__ __forceinline__ void chunk_zeros(const uint32_t* meta, bool mixed, const Regs& R, uint32_t* zs) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t zz = __builtin_amdgcn_perm(meta[8 * w + i + 4], meta[8 * w + i], 0x07060302u);
+      const uint32_t mg = (mixed && (i & 1)) ? R.magic64 : R.magic;
+      zs[4 * w + i] = __builtin_bit_cast(uint32_t, as_h2(zz) + as_h2(mg));
+    }
+  }
 }
 
 // 32 natural-order fp16 values (16 words, 2 per word) -> the pairing order.
@@ -257,7 +281,8 @@ struct WaveLds {
 // (134 VGPRs): measured +7 % when every wave has one page, -11 % with two,
 // so the host picks it by pages per wave.
 template <int G, bool KUP = false>
-__global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 1 && !KUP ? 4 : 1, 8))) void kv_decode_kernel(
+    const uint16_t* __restrict__ q,
                                                         const uint32_t* __restrict__ cache,
                                                         const int32_t* __restrict__ lens, int H, int Hk, int P,
                                                         int pages_per_split, float scale_log2,
@@ -273,7 +298,7 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int quad = lane >> 2, sub = lane & 3;
   WaveLds& L = lds[wave];
-  const Regs R = {in_sgpr(0x000F000Fu), in_sgpr(0x00F000F0u), in_vgpr(kMagic)};
+  const Regs R = {in_sgpr(0x000F000Fu), in_sgpr(0x00F000F0u), in_vgpr(kMagic), in_vgpr(kMagic64)};
 
   // query heads -> LDS (fp16 pairs)
   for (int i = lane; i < G * kD / 2; i += 64) {
@@ -327,19 +352,8 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
 #pragma unroll
           for (int i = 0; i < 16; ++i) qp[i] = __builtin_bit_cast(uint32_t, as_h2(qp[i]) * as_h2(sp[i]));
         }
-        // constant part of this lane's chunk: sum_c q'_c (zK_c + (c even ? 1024 : 64))
-        float cst = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const h2 pr = as_h2(qp[4 * w + i]);  // channels (8w + i, 8w + i + 4) of the chunk
-            const int ch = 32 * sub + 8 * w + i;
-            const float k0 = (i & 1) ? 64.0f : 1024.0f;
-            cst = fmaf((float)pr[0], half_hi(L.meta[ch]) + k0, cst);
-            cst = fmaf((float)pr[1], half_hi(L.meta[ch + 4]) + k0, cst);
-          }
-        }
+        uint32_t zk[16];  // M + zK of the chunk's channels
+        chunk_zeros(&L.meta[32 * sub], true, R, zk);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           u32x4 kc[4];
@@ -350,14 +364,14 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float v = quad_sum(chunk_dot(kc[i], qp, R) - cst) * scale_log2;
+            const float v = quad_sum(chunk_dot(kc[i], qp, zk, R)) * scale_log2;
             sc[4 * half + i] = 16 * (4 * half + i) + quad < valid ? v : -INFINITY;
           }
         }
       }
 
-      // ---- online softmax (base 2), p' = p * sV to LDS, constant part of V
-      float vconst, valpha;
+      // ---- online softmax (base 2), p' = p * sV to LDS
+      float valpha;
       {
         float pm = sc[0];
 #pragma unroll
@@ -366,23 +380,19 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
         const float mn = fmaxf(m[g], pm);
         const float alpha = exp2f(m[g] - mn);  // 0 on the first page (m = -inf)
         m[g] = mn;
-        float ps = 0.0f, cs = 0.0f;
+        float ps = 0.0f;
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
           const int t = 16 * st + quad;
           const float pt = exp2f(sc[st] - mn);
           const uint32_t vm = L.meta[128 + t];
           const _Float16 pp = (_Float16)(pt * half_lo(vm));  // p' = p * sV
-          // token t sits at position t % 8 of its word: even -> 1024, odd -> 64
-          const float k0 = (t & 1) ? 64.0f : 1024.0f;
           if (sub == 0) {
             ps += pt;
-            cs = fmaf((float)pp, half_hi(vm) + k0, cs);
             reinterpret_cast<_Float16*>(L.pv[0])[t] = pp;
           }
         }
         l[g] = l[g] * alpha + wave_sum_f(ps);
-        vconst = wave_sum_f(cs);
         valpha = alpha;
       }
       __builtin_amdgcn_wave_barrier();
@@ -390,6 +400,8 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
 
       // ---- value product: lane chunk = tokens 32 sub .. 32 sub + 31 of channel 16 st + quad
       {
+        uint32_t zv[16];  // M + zV of the chunk's tokens
+        chunk_zeros(&L.meta[128 + 32 * sub], true, R, zv);
         uint32_t pp[16];
         {
           uint32_t praw[16];
@@ -403,10 +415,9 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             vc[i] = load16_nt(pg, (uint32_t)(kVC + 16 * (16 * (4 * half + i) + quad) + 4 * sub) * 4u);
-          // the constant part is common to every channel of the page
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float d = quad_sum(chunk_dot(vc[i], pp, R)) - vconst;
+            const float d = quad_sum(chunk_dot(vc[i], pp, zv, R));
             if (sub == 0) {
               float& oc = L.o[g][16 * (4 * half + i) + quad];
               oc = fmaf(oc, valpha, d);
@@ -456,24 +467,26 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint16_t* __restri
 // the matrix cores and the work per page no longer grows with the group:
 //  * scores: A = K codes (lane l: token l % 16 of a 16-token block, channels
 //    32 (l / 16) .. +31 = one 16-byte chunk), unpacked with multiplier 1 only
-//    (four shifts per word) into (1024 + k) fp16 pairs; B = q' = q * sK
-//    (lane l: head l % 16, the same 32 channels), in the unpack's k order.
-//    D[token][head] - sum_c q'_c (1024 + zK_c) is the score.
+//    (four shifts per word) into (1024 + k) fp16 pairs minus (1024 + zK)
+//    (exact: k - zK); B = q' = q * sK (lane l: head l % 16, the same 32
+//    channels), in the unpack's k order.  D[token][head] is the score.
 //  * softmax per head in the lanes of that head's column (l % 16), online
 //    over pages; p' = p * sV goes through LDS, head-major.
 //  * value product: A = V codes (lane l: channel l % 16 of a 16-channel
-//    block, tokens 32 (l / 16) .. +31), B = p' (lane l: head l % 16);
-//    D[channel][head] - sum_t p'_t (1024 + zV_t) is the page's output, and
-//    each lane keeps its head's 32 output values in registers.
+//    block, tokens 32 (l / 16) .. +31, minus 1024 + zV), B = p' (lane l:
+//    head l % 16); D[channel][head] is the page's output, and each lane
+//    keeps its head's 32 output values in registers.
 //  * the four waves' partials (m, l, o) are combined in LDS and the
 //    workgroup writes one partial per head and split; the last to arrive merges.
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// One code word (8 nibbles, natural order) -> (1024 + c) fp16 values in the
-// order (0, 4, 1, 5, 2, 6, 3, 7).
-__device__ __forceinline__ half8 unpack_plain(uint32_t w, uint32_t m, uint32_t magic) {
-  u32x4 v = {(w & m) | magic, ((w >> 4) & m) | magic, ((w >> 8) & m) | magic, ((w >> 12) & m) | magic};
+// One code word (8 nibbles, natural order) -> (c - z) fp16 values in the
+// order (0, 4, 1, 5, 2, 6, 3, 7): OR into 1024.0, minus zs[i] = (1024 + z,
+// 1024 + z') of the pair (i, i + 4), both exact.
+__device__ __forceinline__ half8 unpack_exact(uint32_t w, uint32_t m, uint32_t magic, const uint32_t* zs) {
+  h2 v[4] = {as_h2((w & m) | magic) - as_h2(zs[0]), as_h2(((w >> 4) & m) | magic) - as_h2(zs[1]),
+             as_h2(((w >> 8) & m) | magic) - as_h2(zs[2]), as_h2(((w >> 12) & m) | magic) - as_h2(zs[3])};
   return __builtin_bit_cast(half8, v);
 }
 __device__ __forceinline__ half8 as_half8(const uint32_t* p) {
@@ -507,6 +520,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col = lane & 15, blk = lane >> 4;
   const uint32_t M4 = in_sgpr(0x000F000Fu), magic = in_vgpr(kMagic);
+  const Regs R = {M4, M4, magic, magic};  // chunk_zeros with multiplier 1 only
   for (int i = threadIdx.x; i < 16 * (kD / 2); i += 256) {
     const int g = i / (kD / 2), w = i - g * (kD / 2);
     qv[g][w] = g < NG ? reinterpret_cast<const uint32_t*>(q + ((size_t)b * H + h0 + g) * kD)[w] : 0u;
@@ -538,9 +552,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
-    // ---- q' = q * sK for head col, channels 32 blk .. +31, and the score constant
-    uint32_t qb[16];
-    float cst = 0.0f;
+    // ---- q' = q * sK for head col, channels 32 blk .. +31, and 1024 + zK of those channels
+    uint32_t qb[16], zk[16];
+    chunk_zeros(&meta[32 * blk], false, R, zk);
     {
       uint32_t sraw[16], qraw[16], sp[16];
 #pragma unroll
@@ -552,18 +566,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
       pair_order(qraw, qb);
 #pragma unroll
       for (int i = 0; i < 16; ++i) qb[i] = __builtin_bit_cast(uint32_t, as_h2(qb[i]) * as_h2(sp[i]));
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const h2 pr = as_h2(qb[4 * w + i]);  // channels (8w + i, 8w + i + 4) of the chunk
-          const int ch = 32 * blk + 8 * w + i;
-          cst = fmaf((float)pr[0], half_hi(meta[ch]) + 1024.0f, cst);
-          cst = fmaf((float)pr[1], half_hi(meta[ch + 4]) + 1024.0f, cst);
-        }
-      }
-      cst += __shfl_xor(cst, 16, 64);
-      cst += __shfl_xor(cst, 32, 64);
     }
 
     // ---- scores: 8 blocks of 16 tokens; lane holds tokens 16 tb + 4 blk + r of head col
@@ -582,11 +584,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         const u32x4 kw = kc[i];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_plain(kw[j], M4, magic), as_half8(qb + 4 * j), d, 0,
-                                                     0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_exact(kw[j], M4, magic, zk + 4 * j), as_half8(qb + 4 * j),
+                                                     d, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          sc[4 * half + i][r] = 16 * (4 * half + i) + 4 * blk + r < valid ? (d[r] - cst) * scale_log2 : -INFINITY;
+          sc[4 * half + i][r] = 16 * (4 * half + i) + 4 * blk + r < valid ? d[r] * scale_log2 : -INFINITY;
       }
     }
     // the first half of the V codes is requested before the softmax
@@ -608,7 +610,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     const float mn = fmaxf(m, pm);
     const float alpha = exp2f(m - mn);  // 0 on the first page (m = -inf)
     m = mn;
-    float ps = 0.0f, vcst = 0.0f;
+    float ps = 0.0f;
 #pragma unroll
     for (int tb = 0; tb < 8; ++tb) {
 #pragma unroll
@@ -619,19 +621,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         const _Float16 pp = (_Float16)(pt * half_lo(vm));  // p' = p * sV
         pv[t] = pp;
         ps += pt;
-        vcst = fmaf((float)pp, half_hi(vm) + 1024.0f, vcst);
       }
     }
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
-    vcst += __shfl_xor(vcst, 16, 64);
-    vcst += __shfl_xor(vcst, 32, 64);
     l = l * alpha + ps;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
-    // ---- value product: B = p' of head col, tokens 32 blk .. +31
-    uint32_t pb[16];
+    // ---- value product: B = p' of head col, tokens 32 blk .. +31 (A minus 1024 + zV of those tokens)
+    uint32_t pb[16], zv[16];
+    chunk_zeros(&meta[128 + 32 * blk], false, R, zv);
     {
       uint32_t praw[16];
       const uint32_t* src = reinterpret_cast<const uint32_t*>(pv) + 16 * blk;
@@ -653,10 +653,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         const u32x4 vw = vc[i];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_plain(vw[j], M4, magic), as_half8(pb + 4 * j), d, 0,
-                                                     0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_exact(vw[j], M4, magic, zv + 4 * j), as_half8(pb + 4 * j),
+                                                     d, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[4 * half + i][r] = fmaf(o[4 * half + i][r], alpha, d[r] - vcst);
+        for (int r = 0; r < 4; ++r) o[4 * half + i][r] = fmaf(o[4 * half + i][r], alpha, d[r]);
       }
     }
     __builtin_amdgcn_wave_barrier();

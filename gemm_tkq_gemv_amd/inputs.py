@@ -41,6 +41,11 @@ float32):
   from default_rng((11, B, H, Hk, T)) with K scaled by 0.05, except that
   token t's K row is +4 in every channel of every KV head; q = +1, so token t
   dominates every head's softmax and the answer is its V row.
+* KV cache, query outliers (B, H, Hk, T): K, V, q standard normal fp16 from
+  default_rng((12, B, H, Hk, T)), except that channels 5, 37, 77 and 120 of
+  K are 0 for every token (each such channel quantizes to its zero point)
+  and carry query values of +-1e3, -3e3, +1e4 and -3e4 in every head.
+  Queries have such outlier channels; their keys here dequantize to 0.
 
 Shapes follow the Qwen2.5-0.5B (hidden 896, intermediate 4864, 24 layers,
 2 KV heads x 64 = 128, vocab 151936, tied head) and Qwen2.5-7B (hidden 3584,
@@ -221,3 +226,15 @@ def kv_peaked_case(B, H, Hk, T, t):
     K[:, t] = 4.0
     q = np.ones((B, H, 128), np.float16)
     return K, V, q
+
+
+def kv_outlier_case(B, H, Hk, T):
+    """(K, V, q) of the query-outlier recipe above."""
+    r = np.random.default_rng((12, B, H, Hk, T))
+    K = r.standard_normal((B, T, Hk, 128), dtype=np.float32).astype(np.float16)
+    V = r.standard_normal((B, T, Hk, 128), dtype=np.float32).astype(np.float16)
+    q = r.standard_normal((B, H, 128), dtype=np.float32)
+    for c, a in zip((5, 37, 77, 120), (1e3, -3e3, 1e4, -3e4)):
+        K[:, :, :, c] = 0
+        q[:, :, c] = a
+    return K, V, q.astype(np.float16)

@@ -9,7 +9,8 @@ batches; structural caches that the bound checks page by page (every score
 tied and a marker channel per page, so that a page left out, read twice or
 read from another head moves an output far beyond the bound), and one peaked
 token whose value row is the answer, placed in the last page of the last
-split and at page boundaries."""
+split and at page boundaries; query outlier channels (1e3..3e4) on key
+channels that dequantize to 0."""
 
 import numpy as np
 import pytest
@@ -174,6 +175,24 @@ def _check_varlen(q, cn, out, lens, what):
         what, int(bad.sum()), np.argwhere(bad)[0])
     with np.errstate(divide="ignore", invalid="ignore"):
         return float(np.nanmax(np.where(bound > 0, err / bound, 0.0)))
+
+
+@pytest.mark.parametrize("B,H,Hk,T", [
+    (1, 32, 32, 4096),      # one page per wave, merged in the kernel
+    (1, 32, 32, 32768),     # several pages per wave, merge launch
+    (1, 32, 8, 32768),      # grouped queries on the matrix cores
+    (2, 28, 4, 1024),
+])
+def test_kv_decode_query_outliers(B, H, Hk, T):
+    """Query channels of 1e3..3e4 on key channels that dequantize to 0: the
+    per-element bound holds (the products are exact small integers times q',
+    so the large channels contribute exactly 0 to the scores)."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    K, V, q = inputs.kv_outlier_case(B, H, Hk, T)
+    cache, out = _run(torch, tkq, q, K, V)
+    cn = cache.cpu().numpy().view(np.uint32).reshape(B, Hk, T // 128, okv.PAGE_WORDS)
+    _check(q, cn, out, "outliers B%d H%d Hk%d T%d" % (B, H, Hk, T))
 
 
 def test_kv_pack_varlen_bit_exact():
