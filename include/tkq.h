@@ -198,10 +198,15 @@ int64_t tkq_hier_meta_bytes(int64_t N, int64_t K);
  * share one coding (e.g. every linear layer read for one decoded token).
  *
  * Float codings: y[n] = sum_k w[n,k] x[k], fp32 accumulation, fp16 output
- * rounded to nearest even; |y - y_exact| <= 2e-3 * sum_k |w[n,k] x[k]| for
- * any finite fp16 x (the code offset is removed exactly before each product,
- * so the rounding error follows |w x|, also on activation channels far
- * larger than their weights).
+ * rounded to nearest even; |y - y_exact| <= 2e-3 * sum_k |w[n,k] x[k]|.
+ * int4, K5, ternary, int2 and int3: for any finite fp16 x (the code offset
+ * is removed exactly before each product, so the rounding error follows
+ * |w x|, also on activation channels far larger than their weights).
+ * int4-hier-g32: its weight is the difference d sc q - dmin mi of two terms
+ * that the coding sums separately over each 32-group (sum q x and sum x),
+ * so the error follows (|d sc q| + |dmin mi|) |x|; the bound holds unless
+ * activations far larger than the rest meet weights whose two terms nearly
+ * cancel.
  * Binary: y[n] = K - 2 * popcount(W[n] XOR x) (Whetstone README, "Measured
  * hardware facts"), exact int32.
  *
