@@ -49,21 +49,21 @@ TRAFFIC_SOURCES = {"gemv": ["gemm_tkq_gemv_amd/csrc/gemv.hip"] + _COMMON,
                    "prefill": ["gemm_tkq_gemv_amd/csrc/prefill.hip"] + _COMMON,
                    "kv": ["gemm_tkq_gemv_amd/csrc/kv.hip"] + _COMMON}
 # workload -> (kernel family, bytes per launch, sha256[:16] of that family's sources)
-TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266549561, "35f714caa64813a4"),
-                 "0.5b-k5": ("gemv", 506970088, "35f714caa64813a4"),
-                 "0.5b-tern": ("gemv", 135446130, "35f714caa64813a4"),
-                 "bin": ("gemv", 115069925, "35f714caa64813a4"),
-                 "7b-int4": ("gemv", 3782045937, "35f714caa64813a4"),
-                 "7b-prefill": ("prefill", 314142403, "c4eec7362ab15d85"),
-                 "0.5b-hier": ("gemv", 268434790, "35f714caa64813a4"),
-                 "0.5b-int2": ("gemv", 143152906, "35f714caa64813a4"),
-                 "0.5b-int3": ("gemv", 206226590, "35f714caa64813a4"),
-                 "0.5b-int4-greedy": ("gemv", 266617012, "35f714caa64813a4"),
+TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266616382, "bc880d4caa4f70ed"),
+                 "0.5b-k5": ("gemv", 506971706, "bc880d4caa4f70ed"),
+                 "0.5b-tern": ("gemv", 135444579, "bc880d4caa4f70ed"),
+                 "bin": ("gemv", 115068394, "bc880d4caa4f70ed"),
+                 "7b-int4": ("gemv", 3781892473, "bc880d4caa4f70ed"),
+                 "7b-prefill": ("prefill", 238649904, "51e4b4940c183935"),
+                 "0.5b-hier": ("gemv", 268438052, "bc880d4caa4f70ed"),
+                 "0.5b-int2": ("gemv", 143153278, "bc880d4caa4f70ed"),
+                 "0.5b-int3": ("gemv", 206228152, "bc880d4caa4f70ed"),
+                 "0.5b-int4-greedy": ("gemv", 266671289, "bc880d4caa4f70ed"),
                  "0.5b-int4-m16": ("small_m", 382402161, "b7fba09e0dc1c849"),
-                 "kv-32k": ("kv", 143471786, "f64f67bc468cd055"),
-                 "kv-4k": ("kv", 18406316, "f64f67bc468cd055"),
-                 "kv-32k-gqa": ("kv", 37208579, "f64f67bc468cd055"),
-                 "kv-128k-gqa": ("kv", 145428332, "f64f67bc468cd055")}
+                 "kv-32k": ("kv", 149787535, "a3d88fe57da6444a"),
+                 "kv-4k": ("kv", 18428762, "a3d88fe57da6444a"),
+                 "kv-32k-gqa": ("kv", 37219000, "a3d88fe57da6444a"),
+                 "kv-128k-gqa": ("kv", 145439450, "a3d88fe57da6444a")}
 
 
 def traffic_family(workload):
@@ -594,6 +594,7 @@ def run_binary(args, torch, tkq, inputs):
             "vs_baseline": None, "dtype": "u32", "data": "synthetic Bernoulli(0.5) signs",
             "config": {"workload": "binary sign GEMVs N in {896,4864,151936} x K in {896,4864}, one launch",
                        "bytes_per_step": step_bytes, "copies_rotated": len(batches)},
+            "kernel": gemv_kernel_name("bin", batches[0].plan.variant, False),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("bin")}}
@@ -647,6 +648,7 @@ def run_prefill(args, torch, tkq, inputs):
                                    "GEMM (N=37888, K=3584) then down (N=3584, K=18944)",
                        "flops_per_step": flops},
             "tok_s": round(M * 1000.0 / ms, 1),
+            "kernel": "prefill_kernel<8> (gate+up, then down) + tail_reduce_kernel + splitk_reduce_kernel",
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("7b-prefill")}}

@@ -98,6 +98,8 @@ def _cache_np(cache, B, Hk, T):
     (1, 32, 32, 4096),      # one page per wave (the one-head kernel that requests K with the metadata)
     (1, 32, 32, 32768),     # several pages per wave, one head per KV head
     (1, 4, 4, 131072),      # 1024 pages per head: many splits, many pages per wave
+    (3, 16, 16, 11264),     # 22 splits per head (just past the in-kernel merge), batch 3
+    (1, 1, 1, 262144),      # 512 splits of one head
     (1, 32, 8, 32768),      # matrix-core path (4 query heads per KV head)
     (1, 32, 8, 131072),     # matrix-core path, several pages per wave
     (2, 8, 2, 4096),        # batch 2, 4 query heads per KV head
