@@ -405,8 +405,8 @@ constexpr int per_cu(int mb) { return mb >= 8 ? 1 : 2; }
 
 // Pick the tile height that keeps the most of the GPU's workgroup slots busy
 // over whole rounds, weighted by its unpack work per MFMA (every M tile
-// unpacks its weight tile again; MB = 2, for short M, is bound by that
-// vector work).  With
+// unpacks its weight tile again; MB = 2 is bound by that vector work) and by
+// the share of its tile rows that hold tokens (so short M takes MB = 2).  With
 // a workspace, a shape that leaves slots idle may split K: the smallest split
 // that fills 80 % of the slots.  A shape with more than one round may
 // instead split the tiles of its last, partial round (tail split).
@@ -436,7 +436,9 @@ Config choose(int64_t M, int64_t N, int64_t K, int cus, int64_t ws_floats) {
     const int64_t slots = (int64_t)cus * per_cu(c.mb);
     const int64_t items = tiles * split_for(tiles, slots);
     const int64_t rounds = (items + slots - 1) / slots;
-    const double score = double(items) / double(rounds * slots) * c.eff;
+    // rows of the M tiles that hold tokens (M = 64 in 256-row tiles wastes 3/4 of the MFMAs)
+    const double fill = double(M) / double(((M + bm - 1) / bm) * bm);
+    const double score = double(items) / double(rounds * slots) * c.eff * fill;
     if (score > best_score + 1e-9) {
       best_score = score;
       best = {c.mb, 1, 1, 0};
