@@ -54,7 +54,7 @@ TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266616382, "bc880d4caa4f70ed"),
                  "0.5b-tern": ("gemv", 135444579, "bc880d4caa4f70ed"),
                  "bin": ("gemv", 115068394, "bc880d4caa4f70ed"),
                  "7b-int4": ("gemv", 3781892473, "bc880d4caa4f70ed"),
-                 "7b-prefill": ("prefill", 238649904, "51e4b4940c183935"),
+                 "7b-prefill": ("prefill", 238651956, "ea017520faf44819"),
                  "0.5b-hier": ("gemv", 268438052, "bc880d4caa4f70ed"),
                  "0.5b-int2": ("gemv", 143153278, "bc880d4caa4f70ed"),
                  "0.5b-int3": ("gemv", 206228152, "bc880d4caa4f70ed"),
