@@ -20,6 +20,9 @@ accounting  parameter counts, bits/weight, bytes per token and the
 kv          the paged 4-bit KV cache (K per channel, V per token, pages of
             128 tokens) and single-query decode attention in fp64, with its
             derived tolerance.
+rescore     greedy selection with head rescore: the k largest stored logits
+            as candidates, their logits recomputed exactly from the fp16
+            output projection, the largest recomputed one as the token.
 
 Every function cites the page passage it follows.  Pages are cited by title
 and section: "Whetstone" (the Whetstone README), "TKintegers K5" (the
@@ -33,4 +36,4 @@ reduce to the plain definition ``y = W_deq . x`` in fp64 and are pinned by
 closed-form special cases and brute force on tiny inputs.
 """
 
-from . import accounting, pack, quant, ref  # noqa: F401
+from . import accounting, pack, quant, ref, rescore  # noqa: F401
