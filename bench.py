@@ -49,21 +49,21 @@ TRAFFIC_SOURCES = {"gemv": ["gemm_tkq_gemv_amd/csrc/gemv.hip"] + _COMMON,
                    "prefill": ["gemm_tkq_gemv_amd/csrc/prefill.hip"] + _COMMON,
                    "kv": ["gemm_tkq_gemv_amd/csrc/kv.hip"] + _COMMON}
 # workload -> (kernel family, bytes per launch, sha256[:16] of that family's sources)
-TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266616382, "bc880d4caa4f70ed"),
-                 "0.5b-k5": ("gemv", 506971706, "bc880d4caa4f70ed"),
-                 "0.5b-tern": ("gemv", 135444579, "bc880d4caa4f70ed"),
-                 "bin": ("gemv", 115068394, "bc880d4caa4f70ed"),
-                 "7b-int4": ("gemv", 3781892473, "bc880d4caa4f70ed"),
-                 "7b-prefill": ("prefill", 238651956, "ea017520faf44819"),
-                 "0.5b-hier": ("gemv", 268438052, "bc880d4caa4f70ed"),
-                 "0.5b-int2": ("gemv", 143153278, "bc880d4caa4f70ed"),
-                 "0.5b-int3": ("gemv", 206228152, "bc880d4caa4f70ed"),
-                 "0.5b-int4-greedy": ("gemv", 266671289, "bc880d4caa4f70ed"),
-                 "0.5b-int4-m16": ("small_m", 382402161, "b7fba09e0dc1c849"),
-                 "kv-32k": ("kv", 149787535, "a3d88fe57da6444a"),
-                 "kv-4k": ("kv", 18428762, "a3d88fe57da6444a"),
-                 "kv-32k-gqa": ("kv", 37219000, "a3d88fe57da6444a"),
-                 "kv-128k-gqa": ("kv", 145439450, "a3d88fe57da6444a")}
+TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266616382, "03e66444fcacc795"),
+                 "0.5b-k5": ("gemv", 506971706, "03e66444fcacc795"),
+                 "0.5b-tern": ("gemv", 135444579, "03e66444fcacc795"),
+                 "bin": ("gemv", 115068394, "03e66444fcacc795"),
+                 "7b-int4": ("gemv", 3781892473, "03e66444fcacc795"),
+                 "7b-prefill": ("prefill", 238651956, "61f6f7075c778bf4"),
+                 "0.5b-hier": ("gemv", 268438052, "03e66444fcacc795"),
+                 "0.5b-int2": ("gemv", 143153278, "03e66444fcacc795"),
+                 "0.5b-int3": ("gemv", 206228152, "03e66444fcacc795"),
+                 "0.5b-int4-greedy": ("gemv", 266671289, "03e66444fcacc795"),
+                 "0.5b-int4-m16": ("small_m", 382402161, "69db892dc296ab00"),
+                 "kv-32k": ("kv", 149787535, "ab2d5fbe2f4f612c"),
+                 "kv-4k": ("kv", 18428762, "ab2d5fbe2f4f612c"),
+                 "kv-32k-gqa": ("kv", 37219000, "ab2d5fbe2f4f612c"),
+                 "kv-128k-gqa": ("kv", 145439450, "ab2d5fbe2f4f612c")}
 
 
 def traffic_family(workload):
@@ -332,6 +332,34 @@ def _cpu_entry(value, unit, sample):
             "host_cores_available": len(os.sched_getaffinity(0)), "kind": "oracle", "sample": sample}
 
 
+def cpu_baseline_rescore(inputs, model, k, budget_s):
+    """Oracle output projection with head rescore, per token: dequantize the
+    int4 head and multiply in fp64, then pick the k candidates from the
+    stored (fp16-rounded) logits and recompute them from the fp16 copy
+    (oracle.rescore); quantization not timed.  Rate = algorithmic bytes of
+    the head GEMV and the rescore / time."""
+    from oracle import pack, quant, ref, rescore
+    shapes = inputs.sweep_shapes(model)
+    i = len(shapes) - 1
+    _, N, K = shapes[i]
+    W, x = inputs.sweep_matrix(model, i, N, K)
+    q, s_, z = quant.quantize_int4_g128(W)
+    c, m = pack.pack_int4(q), pack.pack_int4_meta(s_, z)
+    head16 = W.astype(np.float16)
+    del W, q
+    unit = _fmt_bytes("int4")(N, K) + rescore_bytes(N, K, k)
+
+    def work():
+        y = ref.gemv(ref.dequant_int4(c, m, K), x).astype(np.float16)
+        rescore.head_rescore(y, head16, x, k)
+        return unit
+    done, spent, passes = _cpu_loop(work, budget_s)
+    return _cpu_entry(round(done / spent / 1e12, 8), "TB/s",
+                      "numpy oracle: int4 output projection (%d x %d) dequantize + fp64 matvec, then head "
+                      "rescore of the %d largest stored logits, %d tokens, %.1f s of CPU work; quantization "
+                      "not timed" % (N, K, k, passes, spent))
+
+
 def cpu_baseline_binary(inputs, budget_s):
     """Oracle XOR-popcount GEMV (numpy bitwise_count on uint32 words) over the
     six binary shapes; packing not timed.  Rate = algorithmic bytes / time."""
@@ -420,27 +448,53 @@ def blas_threads():
 
 # ------------------------------------------------------------------- runners --
 
-def run_sweep(args, torch, tkq, inputs, model, fmt, greedy=False):
+def rescore_bytes(n, K, k):
+    """Algorithmic bytes of one head rescore: the stored fp16 logits once, the
+    k candidate rows of the fp16 head copy, x, and the token."""
+    return 2 * n + 2 * k * K + 2 * K + 4
+
+
+def run_sweep(args, torch, tkq, inputs, model, fmt, greedy=False, rescore_k=0):
     """greedy: the launch also selects the largest output of the last GEMV
-    (the output projection) into a device token (tkq_gemv_argmax)."""
+    (the output projection) into a device token (tkq_gemv_argmax).
+    rescore_k > 0: after the sweep, tkq_head_rescore recomputes the k largest
+    stored logits of the output projection from an fp16 copy of it."""
     items, shapes = build_sweep(torch, tkq, inputs, model, fmt)
     fmt_bytes = _fmt_bytes(fmt)
     step_bytes = sum(fmt_bytes(n, k) for _, n, k in shapes)
+    last = len(items) - 1
+    if rescore_k:
+        _, Nh, Kh = shapes[last]
+        Wh, _ = inputs.sweep_matrix(model, last, Nh, Kh)
+        head16 = torch.from_numpy(Wh).cuda().half().contiguous()
+        del Wh
+        step_bytes += rescore_bytes(Nh, Kh, rescore_k)
     footprint = sum(it["codes"].numel() * it["codes"].element_size()
                     + (0 if it["meta"] is None else it["meta"].numel() * it["meta"].element_size())
                     for it in items)
-    launch = "grouped" if greedy else args.launch
+    launch = "grouped" if (greedy or rescore_k) else args.launch
     batches = rotated_batches(torch, tkq, fmt, items, footprint, args.copies, launch, shapes)
+    rescore_us = None
     if greedy:
         token = torch.zeros(1, dtype=torch.int32, device="cuda")
         scratch = batches[0][0].greedy_scratch()
-        last = len(items) - 1
         step = lambda s: batches[s % len(batches)][0].run_argmax(last, token, scratch)  # noqa: E731
+    elif rescore_k:
+        token = torch.zeros(1, dtype=torch.int32, device="cuda")
+        yh, xh = items[last]["y"], items[last]["x"]   # shared by every weight copy
+
+        def step(s):
+            batches[s % len(batches)][0].run()
+            tkq.head_rescore(yh, head16, xh, rescore_k, token=token)
     else:
         def step(s):
             for b in batches[s % len(batches)]:
                 b.run()
     ms = time_steps(torch, step, args.steps, args.warmup, args.graph, len(batches))
+    sweep_stats = dict(SWEEP_STATS)
+    if rescore_k:   # the rescore kernel alone, on the last sweep's logits
+        rescore_us = round(1000.0 * time_steps(
+            torch, lambda s: tkq.head_rescore(yh, head16, xh, rescore_k, token=token), 200, 20), 3)
     gbs = step_bytes / (ms * 1e-3) / 1e9
     ceiling_tok_s = HBM_PEAK_GBS * 1e9 / step_bytes
     out = {
@@ -455,12 +509,15 @@ def run_sweep(args, torch, tkq, inputs, model, fmt, greedy=False):
                                    "staged": "in %d launches (per layer q,k,v | o | gate,up | down, then the "
                                              "output projection)" % len(batches[0]),
                                    "per-matrix": "in one launch each"}[launch],
-                                  ", greedy token selected on the GPU in the same launch" if greedy else ""),
+                                  ", greedy token selected on the GPU in the same launch" if greedy else
+                                  (", then greedy selection with head rescore (the %d largest stored logits of "
+                                   "the output projection recomputed from its fp16 copy)" % rescore_k
+                                   if rescore_k else "")),
                    "bytes_per_step": step_bytes, "copies_rotated": len(batches),
                    "cache_resident": len(batches) == 1 and args.copies == 1,
                    "weights": _fmt_name(fmt), "x": "fp16", "accumulate": "fp32", "y": "fp16",
                    "launch": launch + (", hip graph replay" if args.graph != "none" else ", stream launch")},
-        "sweep_us": dict(SWEEP_STATS),
+        "sweep_us": sweep_stats,
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tok_s": round(1000.0 / ms, 1), "ceiling_tok_s": round(ceiling_tok_s, 1),
         "frac_of_ceiling": round((1000.0 / ms) / ceiling_tok_s, 4),
@@ -468,8 +525,13 @@ def run_sweep(args, torch, tkq, inputs, model, fmt, greedy=False):
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": args.traffic if args.traffic is not None else
                      (measured_traffic(args.workload) if launch == "grouped" and args.copies is None else None)},
-        "kernel": gemv_kernel_name(fmt, max(b.plan.variant for b in batches[0]), greedy),
+        "kernel": gemv_kernel_name(fmt, max(b.plan.variant for b in batches[0]), greedy)
+                  + (" + head_rescore_kernel" if rescore_k else ""),
     }
+    if rescore_k:
+        out["rescore"] = {"k": rescore_k, "kernel_us": rescore_us,
+                          "bytes": rescore_bytes(shapes[last][1], shapes[last][2], rescore_k),
+                          "head_copy_bytes": 2 * shapes[last][1] * shapes[last][2]}
     del items, batches
     return out
 
@@ -675,7 +737,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="0.5b-int4",
-                    choices=["0.5b-int4", "0.5b-int4-greedy", "0.5b-k5", "0.5b-tern", "0.5b-hier",
+                    choices=["0.5b-int4", "0.5b-int4-greedy", "0.5b-int4-rescore", "0.5b-k5", "0.5b-tern", "0.5b-hier",
                              "0.5b-int2", "0.5b-int3", "0.5b-int4-m2", "0.5b-int4-m4", "0.5b-int4-m8", "0.5b-int4-m16",
                              "7b-int4-m16", "kv-32k", "kv-32k-gqa", "kv-4k", "kv-128k-gqa", "bin", "single-896",
                              "7b-int4", "7b-hier", "7b-prefill", "probe"])
@@ -686,6 +748,8 @@ def main():
                          "launch per matrix (shows the launch cost; combine with --graph step)")
     ap.add_argument("--copies", type=int, default=None,
                     help="weight copies rotated (default: enough for >= 1 GiB; 1 = cache-resident)")
+    ap.add_argument("--rescore-k", type=int, default=64,
+                    help="candidates recomputed by the 0.5b-int4-rescore workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -716,14 +780,16 @@ def main():
         del src, dst
 
     w = args.workload
-    if w in ("0.5b-int4", "0.5b-int4-greedy", "0.5b-k5", "0.5b-tern", "0.5b-hier", "0.5b-int2",
-             "0.5b-int3", "7b-int4", "7b-hier"):
+    if w in ("0.5b-int4", "0.5b-int4-greedy", "0.5b-int4-rescore", "0.5b-k5", "0.5b-tern", "0.5b-hier",
+             "0.5b-int2", "0.5b-int3", "7b-int4", "7b-hier"):
         model = "qwen2.5-7b" if w.startswith("7b") else "qwen2.5-0.5b"
         fmt = w.split("-")[1]
-        out = run_sweep(args, torch, tkq, inputs, model, fmt, greedy=w.endswith("greedy"))
+        rk = args.rescore_k if w.endswith("rescore") else 0
+        out = run_sweep(args, torch, tkq, inputs, model, fmt, greedy=w.endswith("greedy"), rescore_k=rk)
         torch.cuda.empty_cache()
         if not args.no_cpu_baseline:
-            out["cpu_baseline"] = gemv_cpu_entry(inputs, model, fmt, args.cpu_budget)
+            out["cpu_baseline"] = (cpu_baseline_rescore(inputs, model, rk, args.cpu_budget) if rk else
+                                   gemv_cpu_entry(inputs, model, fmt, args.cpu_budget))
     elif w.startswith("kv-"):
         T = {"4k": 4096, "32k": 32768, "128k": 131072}[w.split("-")[1]]
         Hk = 8 if w.endswith("gqa") else 32

@@ -98,6 +98,13 @@ hipError_t launch_prefill(int64_t M, int64_t N, int64_t K, const uint32_t* codes
                           const uint16_t* X, uint16_t* Y, float* workspace, int64_t workspace_bytes,
                           hipStream_t stream);
 
+// Greedy selection with head rescore: one workgroup of 1024 threads.
+// rescore_capacity: keys the candidate collection may hold (k shares).
+int64_t rescore_capacity(int64_t n, int k);
+hipError_t launch_head_rescore(const uint16_t* logits, int64_t n, const uint16_t* head, const uint16_t* x,
+                               int64_t K, int k, int32_t* token, int32_t* cand, float* cand_logits,
+                               hipStream_t stream);
+
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream);
 
 }  // namespace tkq

@@ -487,6 +487,20 @@ int tkq_gemm_prefill(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint32_
                                         workspace ? workspace_bytes : 0, (hipStream_t)stream));
 }
 
+int tkq_head_rescore(const uint16_t* logits, int64_t n, const uint16_t* head, const uint16_t* x, int64_t K,
+                     int32_t k, int32_t* token, int32_t* cand, float* cand_logits, void* stream) {
+  if (!logits || !head || !x || !token || n < 1 || K < 1 || k < 1 || k > n) return TKQ_EINVAL;
+  if (k > TKQ_RESCORE_MAX_K || n > INT32_MAX || K % 8 || K > TKQ_MAX_K ||
+      tkq::rescore_capacity(n, k) > TKQ_RESCORE_CAP)
+    return TKQ_ESHAPE;
+  if (!aligned16(logits) || !aligned16(head) || !aligned16(x)) return TKQ_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(token) | reinterpret_cast<uintptr_t>(cand) |
+       reinterpret_cast<uintptr_t>(cand_logits)) & 3u)
+    return TKQ_EALIGN;
+  return hip_status(tkq::launch_head_rescore(logits, n, head, x, K, k, token, cand, cand_logits,
+                                             (hipStream_t)stream));
+}
+
 int tkq_read_probe(const void* buf, int64_t bytes, uint32_t* out, void* stream) {
   if (!buf || !out || bytes < 16) return TKQ_EINVAL;
   if (bytes % 16) return TKQ_ESHAPE;

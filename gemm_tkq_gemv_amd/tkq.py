@@ -87,6 +87,7 @@ _SIGNATURES = {
                              ctypes.c_int),
     "tkq_gemm_prefill": ([_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
     "tkq_read_probe": ([_P, _I64, _P, _P], ctypes.c_int),
+    "tkq_head_rescore": ([_P, _I64, _P, _P, _I64, _I32, _P, _P, _P, _P], ctypes.c_int),
 }
 
 _lib = None
@@ -318,6 +319,35 @@ def gemv(fmt, codes, meta, x, N, K, y=None, stream=None):
     _stream(stream, owned)
     GemvBatch(fmt, [dict(codes=codes, meta=meta, x=x, y=y, N=N, K=K)]).run(stream)
     return y
+
+
+# ---- greedy selection with head rescore -------------------------------------
+
+def head_rescore(logits, head, x, k, token=None, cand=None, cand_logits=None, stream=None):
+    """tkq_head_rescore: the k largest stored logits (fp16 [n]) are computed
+    again from the fp16 head copy ([n, K]) and x (fp16 [K]); returns the token
+    (int32 device tensor, 1 element).  cand (int32 [k]) and cand_logits
+    (float32 [k]) receive the candidate rows in greedy order and their
+    recomputed logits when given."""
+    _need(logits, torch.float16, "logits")
+    n = logits.numel()
+    _need(head, torch.float16, "head")
+    if head.dim() != 2 or head.shape[0] != n:
+        raise ValueError("head must be [n, K] with n = logits.numel()")
+    K = head.shape[1]
+    _need(x, torch.float16, "x", (K,))
+    owned = None
+    if token is None:
+        token = owned = torch.empty(1, dtype=torch.int32, device=logits.device)
+    _need(token, torch.int32, "token")
+    if cand is not None:
+        _need(cand, torch.int32, "cand", (k,))
+    if cand_logits is not None:
+        _need(cand_logits, torch.float32, "cand_logits", (k,))
+    _call("tkq_head_rescore", _ptr(logits), n, _ptr(head), _ptr(x), K, int(k), _ptr(token),
+          _ptr(cand) if cand is not None else None,
+          _ptr(cand_logits) if cand_logits is not None else None, _stream(stream, owned))
+    return token
 
 
 # ---- prefill GEMM --------------------------------------------------------------

@@ -299,6 +299,40 @@ int tkq_gemv_argmax_static(const tkq_gemv_plan* plan,
                            const tkq_gemv_desc* dev_descs, int32_t target,
                            int32_t* token, void* stream);
 
+/* Greedy selection with head rescore (Whetstone README, "New in 0.6.0", the
+ * head-rescore item: an fp16 copy of the output projection is kept beside
+ * the quantized one, and only the logits that decide the token are computed
+ * again from that copy).  Run after the quantized output projection has
+ * stored its logits (tkq_gemv), on the same stream.
+ *   candidates: the k largest stored logits in the order of greedy selection
+ *     (the order of tkq_gemv_argmax: -0 equal to +0, every NaN above +inf, on
+ *     equal values the smaller row first);
+ *   recomputed logit of candidate row r: sum_j head[r][j] * x[j], fp16 x fp16
+ *     products (exact in fp32) summed in fp32, so
+ *     |l - l_exact| <= gamma_(K-1) * sum_j |head[r][j] x[j]| with
+ *     gamma_m = m u / (1 - m u), u = 2^-24 (any summation order);
+ *   *token: the candidate whose recomputed logit is largest, in that same
+ *     order (NaN above every number, smaller row on ties).
+ * logits: fp16 bits [n] (the stored outputs of the quantized projection);
+ * head: fp16 bits [n][K], row-major; x: fp16 bits [K] (the projection's
+ * input); token: device int32.  cand (device int32 [k]) and cand_logits
+ * (device float [k]) are optional (NULL to skip): the candidate rows in
+ * greedy order and their recomputed logits.  One workgroup, all
+ * intermediate state in LDS: no scratch memory.
+ * Limits: 1 <= k <= min(n, TKQ_RESCORE_MAX_K); n < 2^31; K % 8 == 0,
+ * K <= TKQ_MAX_K; k * 8 * ceil(ceil(n / 8) / 1024) <= TKQ_RESCORE_CAP (the
+ * candidates are collected from k shares of that many logits each: e.g.
+ * k <= 107 at n = 151,936, k <= 64 up to n = 262,144).
+ * Returns TKQ_OK, TKQ_EINVAL (null logits, head, x or token; n, K or k < 1;
+ * k > n), TKQ_ESHAPE (the limits above), TKQ_EALIGN (logits, head or x not
+ * 16-byte aligned; token, cand or cand_logits not 4-byte aligned) or
+ * TKQ_EHIP. */
+#define TKQ_RESCORE_MAX_K 1024
+#define TKQ_RESCORE_CAP 16384
+int tkq_head_rescore(const uint16_t* logits, int64_t n, const uint16_t* head,
+                     const uint16_t* x, int64_t K, int32_t k, int32_t* token,
+                     int32_t* cand, float* cand_logits, void* stream);
+
 /* ---- multi-token GEMV (M = 1..16) ----------------------------------------
  * Y_i[m, n] = sum_k X_i[m, k] * w_i[n, k] for M tokens at once over many
  * int4 g128 matrices in one launch: the regime between batch-1 decode and

@@ -368,3 +368,31 @@ def test_read_probe_validation():
     assert f(A, 8, A, None) == tkq.EINVAL
     assert f(A, 24, A, None) == tkq.ESHAPE
     assert f(A + 4, 64, A, None) == tkq.EALIGN
+
+
+def test_head_rescore_validation():
+    """Greedy selection with head rescore: every bad argument is refused on the
+    host, including k beyond the candidate collection's capacity."""
+    f = tkq.lib().tkq_head_rescore
+    n, K = 151936, 896
+    assert f(None, n, A, A, K, 64, A, None, None, None) == tkq.EINVAL
+    assert f(A, n, None, A, K, 64, A, None, None, None) == tkq.EINVAL
+    assert f(A, n, A, None, K, 64, A, None, None, None) == tkq.EINVAL
+    assert f(A, n, A, A, K, 64, None, None, None, None) == tkq.EINVAL
+    assert f(A, 0, A, A, K, 1, A, None, None, None) == tkq.EINVAL
+    assert f(A, n, A, A, 0, 1, A, None, None, None) == tkq.EINVAL
+    assert f(A, n, A, A, K, 0, A, None, None, None) == tkq.EINVAL
+    assert f(A, 5, A, A, K, 6, A, None, None, None) == tkq.EINVAL       # k > n
+    assert f(A, n, A, A, 900, 8, A, None, None, None) == tkq.ESHAPE     # K % 8
+    assert f(A, n, A, A, (1 << 20) + 8, 8, A, None, None, None) == tkq.ESHAPE
+    assert f(A, 1 << 31, A, A, K, 8, A, None, None, None) == tkq.ESHAPE
+    assert f(A, 5000, A, A, K, 1025, A, None, None, None) == tkq.ESHAPE  # k > TKQ_RESCORE_MAX_K
+    # capacity: k * 8 * ceil(ceil(n / 8) / 1024) <= 16384
+    assert f(A, n, A, A, K, 108, A, None, None, None) == tkq.ESHAPE     # 108 * 152 > 16384
+    assert f(A, 262145, A, A, K, 64, A, None, None, None) == tkq.ESHAPE
+    assert f(A + 2, n, A, A, K, 8, A, None, None, None) == tkq.EALIGN
+    assert f(A, n, A + 8, A, K, 8, A, None, None, None) == tkq.EALIGN
+    assert f(A, n, A, A + 4, K, 8, A, None, None, None) == tkq.EALIGN
+    assert f(A, n, A, A, K, 8, A + 2, None, None, None) == tkq.EALIGN
+    assert f(A, n, A, A, K, 8, A, A + 1, None, None) == tkq.EALIGN
+    assert f(A, n, A, A, K, 8, A, None, A + 2, None) == tkq.EALIGN
