@@ -15,8 +15,14 @@ once) / measured time per step, in TB/s.  The roofline object reports the
 same kernel against the 8 TB/s HBM peak; cpu_baseline times the numpy oracle
 on a bounded sample of the same workload on the host cores.
 
-Other workloads (for measurement; each prints its own line): single-896,
-0.5b-k5, 0.5b-tern, bin, 7b-int4, 7b-prefill, probe.
+Other workloads (for measurement; each prints its own line): the 0.5B sweep
+in the other codings (0.5b-k5, 0.5b-tern, 0.5b-hier, 0.5b-int2, 0.5b-int3),
+with the greedy token (0.5b-int4-greedy) or the head rescore
+(0.5b-int4-rescore, --rescore-k candidates), for M tokens at once
+(0.5b-int4-mM, M = 2, 4, 8, 16; 7b-int4-m16), the binary shapes (bin), the 7B
+sweep (7b-int4, 7b-hier), the 7B MLP prefill (7b-prefill), KV-cache decode
+(kv-4k, kv-32k, kv-32k-gqa, kv-128k-gqa), one 896 x 896 GEMV (single-896) and
+the read probe (probe).
 """
 
 import argparse
