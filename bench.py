@@ -55,21 +55,21 @@ TRAFFIC_SOURCES = {"gemv": ["gemm_tkq_gemv_amd/csrc/gemv.hip"] + _COMMON,
                    "prefill": ["gemm_tkq_gemv_amd/csrc/prefill.hip"] + _COMMON,
                    "kv": ["gemm_tkq_gemv_amd/csrc/kv.hip"] + _COMMON}
 # workload -> (kernel family, bytes per launch, sha256[:16] of that family's sources)
-TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266616382, "03e66444fcacc795"),
-                 "0.5b-k5": ("gemv", 506971706, "03e66444fcacc795"),
-                 "0.5b-tern": ("gemv", 135444579, "03e66444fcacc795"),
-                 "bin": ("gemv", 115068394, "03e66444fcacc795"),
-                 "7b-int4": ("gemv", 3781892473, "03e66444fcacc795"),
-                 "7b-prefill": ("prefill", 238651956, "61f6f7075c778bf4"),
-                 "0.5b-hier": ("gemv", 268438052, "03e66444fcacc795"),
-                 "0.5b-int2": ("gemv", 143153278, "03e66444fcacc795"),
-                 "0.5b-int3": ("gemv", 206228152, "03e66444fcacc795"),
-                 "0.5b-int4-greedy": ("gemv", 266671289, "03e66444fcacc795"),
-                 "0.5b-int4-m16": ("small_m", 382402161, "69db892dc296ab00"),
-                 "kv-32k": ("kv", 149787535, "ab2d5fbe2f4f612c"),
-                 "kv-4k": ("kv", 18428762, "ab2d5fbe2f4f612c"),
-                 "kv-32k-gqa": ("kv", 37219000, "ab2d5fbe2f4f612c"),
-                 "kv-128k-gqa": ("kv", 145439450, "ab2d5fbe2f4f612c")}
+TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266616382, "2aee3066839fc642"),
+                 "0.5b-k5": ("gemv", 506971706, "2aee3066839fc642"),
+                 "0.5b-tern": ("gemv", 135444579, "2aee3066839fc642"),
+                 "bin": ("gemv", 115068394, "2aee3066839fc642"),
+                 "7b-int4": ("gemv", 3781892473, "2aee3066839fc642"),
+                 "7b-prefill": ("prefill", 238651956, "143dc970ac5e58dd"),
+                 "0.5b-hier": ("gemv", 268438052, "2aee3066839fc642"),
+                 "0.5b-int2": ("gemv", 143153278, "2aee3066839fc642"),
+                 "0.5b-int3": ("gemv", 206228152, "2aee3066839fc642"),
+                 "0.5b-int4-greedy": ("gemv", 266671289, "2aee3066839fc642"),
+                 "0.5b-int4-m16": ("small_m", 382402161, "dcca247aa7644067"),
+                 "kv-32k": ("kv", 149787535, "54f3ec3318d10c46"),
+                 "kv-4k": ("kv", 18428762, "54f3ec3318d10c46"),
+                 "kv-32k-gqa": ("kv", 37219000, "54f3ec3318d10c46"),
+                 "kv-128k-gqa": ("kv", 145439450, "54f3ec3318d10c46")}
 
 
 def traffic_family(workload):
@@ -488,17 +488,21 @@ def run_sweep(args, torch, tkq, inputs, model, fmt, greedy=False, rescore_k=0):
     elif rescore_k:
         token = torch.zeros(1, dtype=torch.int32, device="cuda")
         yh, xh = items[last]["y"], items[last]["x"]   # shared by every weight copy
-
-        def step(s):
-            batches[s % len(batches)][0].run()
-            tkq.head_rescore(yh, head16, xh, rescore_k, token=token)
+        if args.rescore_path == "fused":   # the GEMV stores per-tile keys, the rescore starts from them
+            scratch = batches[0][0].greedy_scratch()
+            step = lambda s: batches[s % len(batches)][0].run_argmax_rescore(  # noqa: E731
+                last, head16, rescore_k, token, scratch)
+        else:
+            def step(s):
+                batches[s % len(batches)][0].run()
+                tkq.head_rescore(yh, head16, xh, rescore_k, token=token)
     else:
         def step(s):
             for b in batches[s % len(batches)]:
                 b.run()
     ms = time_steps(torch, step, args.steps, args.warmup, args.graph, len(batches))
     sweep_stats = dict(SWEEP_STATS)
-    if rescore_k:   # the rescore kernel alone, on the last sweep's logits
+    if rescore_k:   # the standalone rescore kernel alone, on the last sweep's logits
         rescore_us = round(1000.0 * time_steps(
             torch, lambda s: tkq.head_rescore(yh, head16, xh, rescore_k, token=token), 200, 20), 3)
     gbs = step_bytes / (ms * 1e-3) / 1e9
@@ -517,7 +521,9 @@ def run_sweep(args, torch, tkq, inputs, model, fmt, greedy=False, rescore_k=0):
                                    "per-matrix": "in one launch each"}[launch],
                                   ", greedy token selected on the GPU in the same launch" if greedy else
                                   (", then greedy selection with head rescore (the %d largest stored logits of "
-                                   "the output projection recomputed from its fp16 copy)" % rescore_k
+                                   "the output projection recomputed from its fp16 copy; %s)"
+                                   % (rescore_k, "candidates from the GEMV's per-tile keys"
+                                      if args.rescore_path == "fused" else "candidates from the stored logits")
                                    if rescore_k else "")),
                    "bytes_per_step": step_bytes, "copies_rotated": len(batches),
                    "cache_resident": len(batches) == 1 and args.copies == 1,
@@ -531,11 +537,14 @@ def run_sweep(args, torch, tkq, inputs, model, fmt, greedy=False, rescore_k=0):
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": args.traffic if args.traffic is not None else
                      (measured_traffic(args.workload) if launch == "grouped" and args.copies is None else None)},
-        "kernel": gemv_kernel_name(fmt, max(b.plan.variant for b in batches[0]), greedy)
-                  + (" + head_rescore_kernel" if rescore_k else ""),
+        "kernel": (gemv_kernel_name(fmt, max(b.plan.variant for b in batches[0]),
+                                    greedy or (rescore_k and args.rescore_path == "fused")).split(" + ")[0]
+                   + (" + gemv_rescore_kernel" if rescore_k and args.rescore_path == "fused" else
+                      " + head_rescore_kernel" if rescore_k else
+                      " + greedy_finish_kernel" if greedy else "")),
     }
     if rescore_k:
-        out["rescore"] = {"k": rescore_k, "kernel_us": rescore_us,
+        out["rescore"] = {"k": rescore_k, "path": args.rescore_path, "standalone_kernel_us": rescore_us,
                           "bytes": rescore_bytes(shapes[last][1], shapes[last][2], rescore_k),
                           "head_copy_bytes": 2 * shapes[last][1] * shapes[last][2]}
     del items, batches
@@ -756,6 +765,8 @@ def main():
                     help="weight copies rotated (default: enough for >= 1 GiB; 1 = cache-resident)")
     ap.add_argument("--rescore-k", type=int, default=64,
                     help="candidates recomputed by the 0.5b-int4-rescore workload")
+    ap.add_argument("--rescore-path", default="fused", choices=["fused", "standalone"],
+                    help="0.5b-int4-rescore: tkq_gemv_argmax_rescore (fused) or tkq_gemv + tkq_head_rescore")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

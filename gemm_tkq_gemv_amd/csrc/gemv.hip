@@ -1102,7 +1102,7 @@ hipError_t launch_gemv(int fmt, int jmax, const tkq_gemv_desc* dev_descs, int co
   if (!fn) return hipErrorInvalidValue;
   const Greedy g = {target, slots};
   hipLaunchKernelGGL(fn, dim3((uint32_t)tiles), dim3(64 * kWaves), lds, stream, dev_descs, count, g);
-  if (greedy) {
+  if (greedy && token) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(greedy_finish_kernel, dim3(1), dim3(64 * kWaves), 0, stream, dev_descs, count, target,

@@ -64,8 +64,9 @@ __host__ __device__ constexpr int64_t int4_lds_bytes(int K, int rows) {
 // Largest `passes` value each kernel variant supports (x stays in registers).
 int gemv_max_passes(int fmt);
 // jmax: largest `passes` among the descriptors (selects the kernel variant).
-// target >= 0: also select the largest output of descriptor `target` into
-// *token (slots: scratch of one uint64 per tile of the launch).
+// target >= 0: also store the largest output key of each of descriptor
+// `target`'s row tiles into slots (scratch of one uint64 per tile of the
+// launch) and, when token is not null, select the largest into *token.
 hipError_t launch_gemv(int fmt, int jmax, const tkq_gemv_desc* dev_descs, int count, int64_t tiles,
                        int target, int32_t* token, uint64_t* slots, hipStream_t stream);
 
@@ -104,6 +105,12 @@ int64_t rescore_capacity(int64_t n, int k);
 hipError_t launch_head_rescore(const uint16_t* logits, int64_t n, const uint16_t* head, const uint16_t* x,
                                int64_t K, int k, int32_t* token, int32_t* cand, float* cand_logits,
                                hipStream_t stream);
+
+// The same selection over a grouped GEMV's target, from the per-tile keys the
+// greedy variant stored in slots (launch_gemv with token = nullptr first).
+hipError_t launch_gemv_rescore(const tkq_gemv_desc* dev_descs, int count, int target, int64_t tiles,
+                               const uint64_t* slots, const uint16_t* head, int k, int32_t* token, int32_t* cand,
+                               float* cand_logits, hipStream_t stream);
 
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream);
 

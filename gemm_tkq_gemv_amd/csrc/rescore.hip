@@ -32,6 +32,8 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kInFlight = 16;    // 16-byte loads a thread issues before using any
 constexpr int kRankMax = 256;    // collections up to this size are ranked by counting
+constexpr int kBatch = 4;        // chunks (or tile keys) per thread in flight in the collection passes
+constexpr uint32_t kFar = 0x80000000u;  // buffer offset past every range: loads return 0, no access
 
 // 16-bit order key of a stored fp16 logit: larger value -> larger key; -0
 // counts as +0 and every NaN (either sign, any payload) above +inf.  At least
@@ -78,21 +80,27 @@ __device__ __forceinline__ uint64_t key_f32(float v, uint32_t row) {
 }
 __device__ __forceinline__ uint32_t key_row(uint64_t key) { return 0xFFFFFFFFu - (uint32_t)key; }
 
-// Keys of the 8 logits of chunk c (logits 8c .. 8c+7); 0 for those at or
-// past n.  A full chunk is one 16-byte load, the ragged last one 2-byte loads.
-__device__ __forceinline__ void chunk_keys(__amdgpu_buffer_rsrc_t rs, int64_t c, int64_t n, int64_t nfull,
-                                           uint64_t kk[8]) {
-  if (c < nfull) {
-    const u32x4 v = load16(rs, (uint32_t)(c * 16));
+// Keys of the 8 logits of a full chunk v (rows r0 .. r0 + 7).
+__device__ __forceinline__ void full_keys(u32x4 v, uint32_t r0, uint64_t kk[8]) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) kk[e] = key_f16((e & 1) ? (v[e >> 1] >> 16) : v[e >> 1], (uint32_t)(8 * c + e));
-  } else {
+  for (int e = 0; e < 8; ++e) kk[e] = key_f16((e & 1) ? (v[e >> 1] >> 16) : v[e >> 1], r0 + e);
+}
+// Keys of logits r0 .. r1 - 1 (up to 8; 0 for the rest), one 2-byte load each.
+__device__ __forceinline__ void part_keys(__amdgpu_buffer_rsrc_t rs, uint32_t r0, uint32_t r1, uint64_t kk[8]) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int64_t i = 8 * c + e;
-      kk[e] = i < n ? key_f16(load2(rs, (uint32_t)(i * 2)), (uint32_t)i) : 0;
-    }
+  for (int e = 0; e < 8; ++e) kk[e] = r0 + e < r1 ? key_f16(load2(rs, (r0 + e) * 2u), r0 + e) : 0;
+}
+// The largest value key (ord_f16) of a full chunk's 8 logits, two per packed
+// instruction: a chunk below a threshold value needs no 64-bit keys.
+__device__ __forceinline__ uint32_t chunk_value(u32x4 v) {
+  u16x2 vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const u16x2 o = ord2_raw(v[w]);
+    vmax = __builtin_elementwise_max(vmax, o);
+    vmin = __builtin_elementwise_min(vmin, o);
   }
+  return share_value(max((uint32_t)vmax.x, (uint32_t)vmax.y), min((uint32_t)vmin.x, (uint32_t)vmin.y));
 }
 
 // Sorts s[0, P) into descending order (P a power of two, <= every thread's
@@ -116,61 +124,58 @@ __device__ void bitonic_desc(uint64_t* s, int P) {
 }
 
 // Wave 0: the largest bin b of hist[256] whose suffix count S(b) (bins >= b)
-// reaches `need`, and S(b + 1); need >= 1 and S(0) >= need.
+// reaches `need`, and S(b + 1); need >= 1 and S(0) >= need.  Lane l holds
+// bins 255 - 4l .. 252 - 4l (from the top down), so an inclusive prefix sum
+// over the lanes (DPP row shifts, then row broadcasts) gives S at each
+// lane's lowest bin, and the first lane that reaches `need` holds b.
 __device__ __forceinline__ void suffix_select(const uint32_t* hist, uint32_t need, uint32_t* bin,
                                               uint32_t* above) {
   const int lane = threadIdx.x & 63;
-  uint32_t h[4], sum = 0;
+  const u32x4 q = *reinterpret_cast<const u32x4*>(hist + 252 - 4 * lane);
+  const uint32_t h[4] = {q[3], q[2], q[1], q[0]};  // bins 255 - 4l - i
+  const uint32_t sum = h[0] + h[1] + h[2] + h[3];
+  uint32_t p = sum;
+  p += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p, 0x111, 0xF, 0xF, false);  // row_shr:1
+  p += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p, 0x112, 0xF, 0xF, false);  // row_shr:2
+  p += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p, 0x114, 0xF, 0xF, false);  // row_shr:4
+  p += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p, 0x118, 0xF, 0xF, false);  // row_shr:8
+  p += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p, kRowBcast15, 0xA, 0xF, false);
+  p += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p, kRowBcast31, 0xC, 0xF, false);
+  const uint64_t reached = __ballot(p >= need);
+  const int first = __builtin_ctzll(reached);
+  if (lane == first) {
+    uint32_t cum = p - sum;  // S(256 - 4 lane): the bins above this lane's
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[i] = hist[4 * lane + i];
-    sum += h[i];
-  }
-  uint32_t s = sum;  // -> sum over lanes >= lane
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t u = __shfl_down(s, o, 64);
-    if (lane + o < 64) s += u;
-  }
-  int mine = -1;
-  uint32_t suf = s;  // S(4 lane + i) as i goes up
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (suf >= need) mine = 4 * lane + i;
-    suf -= h[i];
-  }
-  int b = mine;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) b = max(b, __shfl_xor(b, o, 64));
-  if (lane == (b >> 2)) {
-    uint32_t sb = s;
-    for (int i = 0; i < (b & 3); ++i) sb -= h[i];
-    *bin = (uint32_t)b;
-    *above = sb - h[b & 3];
+    for (int i = 0; i < 4; ++i) {
+      if (cum + h[i] >= need) {
+        *bin = 255u - 4u * (uint32_t)lane - (uint32_t)i;
+        *above = cum;
+        break;
+      }
+      cum += h[i];
+    }
   }
 }
 
-__global__ __launch_bounds__(kThreads) void head_rescore_kernel(const uint16_t* __restrict__ logits, int64_t n,
-                                                                const uint16_t* __restrict__ head,
-                                                                const uint16_t* __restrict__ x, int64_t K, int k,
-                                                                int32_t* __restrict__ token, int32_t* __restrict__ cand,
-                                                                float* __restrict__ cand_logits) {
-  extern __shared__ uint64_t lds[];
-  uint64_t* cands = lds;             // [kThreads]: the candidates, in greedy order
-  uint64_t* coll = lds + kThreads;   // [collection capacity], power of two
-  __shared__ uint32_t hist1[256], hist2[256];
-  __shared__ uint32_t count, nwin, ntie, bin1, above1, bin2, above2;  // counters zeroed below
-  __shared__ unsigned long long tau_s;
-  __shared__ int32_t winners[kThreads];
-  __shared__ float exact[TKQ_RESCORE_MAX_K];
-  __shared__ unsigned long long wave_best[kThreads / 64];
+// Workgroup state of the selection (besides the two dynamic LDS arrays).
+struct Lds {
+  alignas(16) uint32_t hist1[256], hist2[256];  // read 16 bytes at a time by suffix_select
+  uint32_t count, nwin, ntie, bin1, above1, bin2, above2, over;
+  unsigned long long tau;
+  int32_t winners[kThreads];
+  float exact[TKQ_RESCORE_MAX_K];
+  unsigned long long wave_best[kThreads / 64];
+};
 
+// Steps 1-3 from the stored logits alone: coll[0, S.count) receives every key
+// >= tau (a superset of the k largest), at most k * 8 * R of them.
+__device__ __forceinline__ void collect_shares(Lds& S, uint64_t* cands, uint64_t* coll, const uint16_t* logits, int64_t n, int k) {
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int64_t nchunks = (n + 7) / 8, nfull = n / 8;
   const int64_t R = (nchunks + kThreads - 1) / kThreads;  // chunks per share
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(logits, (uint32_t)(n * 2));
-  if (t < 256) hist1[t] = hist2[t] = 0u;
-  if (t == 0) count = nwin = ntie = 0u;
+  if (t < 256) S.hist1[t] = S.hist2[t] = 0u;
+  if (t == 0) S.count = S.nwin = S.ntie = 0u;
 
   // 1. this thread's share maximum value.  Every round but the last holds a
   // full chunk for every thread; the last one may hold a full, a ragged or no
@@ -179,9 +184,11 @@ __global__ __launch_bounds__(kThreads) void head_rescore_kernel(const uint16_t* 
   const int64_t Rfull = R - 1;
   for (int64_t r0 = 0; r0 < Rfull; r0 += kInFlight) {
     u32x4 v[kInFlight];
+    // all loads in one block (one in a branch of its own each made the
+    // compiler wait for every earlier load first); past Rfull they read zeros
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u)
-      if (r0 + u < Rfull) v[u] = load16(rs, (uint32_t)((t + (r0 + u) * kThreads) * 16));
+      v[u] = load16(rs, r0 + u < Rfull ? (uint32_t)((t + (r0 + u) * kThreads) * 16) : kFar);
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) {
       if (r0 + u < Rfull) {
@@ -210,93 +217,282 @@ __global__ __launch_bounds__(kThreads) void head_rescore_kernel(const uint16_t* 
   __syncthreads();
 
   // 2. tau = the k-th largest share maximum key
-  if (M) atomicAdd(&hist1[M >> 8], 1u);
+  if (M) atomicAdd(&S.hist1[M >> 8], 1u);
   __syncthreads();
-  if (wave == 0) {
-    uint32_t nonempty = 0;
-    for (int i = lane; i < 256; i += 64) nonempty += hist1[i];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) nonempty += __shfl_xor(nonempty, o, 64);
-    if (nonempty <= (uint32_t)k) {  // at most k non-empty shares: take them all
-      if (lane == 0) bin1 = 0xFFFFFFFFu;
-    } else {
-      suffix_select(hist1, (uint32_t)k, &bin1, &above1);
-    }
+  if (min(nchunks, (int64_t)kThreads) <= k) {  // at most k non-empty shares (t < nchunks): take them all
+    if (t == 0) S.bin1 = 0xFFFFFFFFu;
+  } else if (wave == 0) {
+    suffix_select(S.hist1, (uint32_t)k, &S.bin1, &S.above1);
   }
   __syncthreads();
   uint64_t tau = 1;  // every real key is >= 1
   bool winner = M != 0;
-  if (bin1 != 0xFFFFFFFFu) {
-    if (M && (M >> 8) == bin1) atomicAdd(&hist2[M & 0xFFu], 1u);
+  if (S.bin1 != 0xFFFFFFFFu) {
+    if (M && (M >> 8) == S.bin1) atomicAdd(&S.hist2[M & 0xFFu], 1u);
     __syncthreads();
-    if (wave == 0) suffix_select(hist2, (uint32_t)k - above1, &bin2, &above2);
+    if (wave == 0) suffix_select(S.hist2, (uint32_t)k - S.above1, &S.bin2, &S.above2);
     __syncthreads();
-    const uint32_t v16 = (bin1 << 8) | bin2;
-    const uint32_t m = (uint32_t)k - above1 - above2;  // shares of maximum v16 to take (>= 1)
+    const uint32_t v16 = (S.bin1 << 8) | S.bin2;
+    const uint32_t m = (uint32_t)k - S.above1 - S.above2;  // shares of maximum v16 to take (>= 1)
     winner = M > v16;
-    if (hist2[bin2] == m) {
+    if (S.hist2[S.bin2] == m) {
       // exactly m shares have maximum v16: all of them are winners, and the
       // keys of value >= v16 lie in the k winners' shares only
       tau = (uint64_t)v16 << 32;
       winner = M >= v16;
     } else {
       // more: each tied share's first row of value v16 decides.  The tied
-      // shares (listed in `winners`) are read again, their first keys of
+      // shares (listed in `S.winners`) are read again, their first keys of
       // value v16 max-reduced into `cands`; both are free until later steps.
       uint32_t my = 0;
       if (M == v16) {
-        my = atomicAdd(&ntie, 1u);
-        winners[my] = t;
+        my = atomicAdd(&S.ntie, 1u);
+        S.winners[my] = t;
         cands[my] = 0;
       }
       __syncthreads();
-      const int nt = (int)ntie;
-      for (int64_t p = t; p < (int64_t)nt * R; p += kThreads) {
-        const int64_t c = winners[p / R] + (p % R) * kThreads;
-        if (c >= nchunks) continue;
-        uint64_t kk[8];
-        chunk_keys(rs, c, n, nfull, kk);
-        uint64_t f = 0;
+      const int nt = (int)S.ntie;
+      for (int64_t p0 = 0; p0 < (int64_t)nt * R; p0 += kBatch * kThreads) {
+        u32x4 v[kBatch];
+        int64_t c[kBatch];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f = (kk[e] >> 32) == v16 && kk[e] > f ? kk[e] : f;
-        if (f) atomicMax(reinterpret_cast<unsigned long long*>(&cands[p / R]), (unsigned long long)f);
+        for (int u = 0; u < kBatch; ++u) {
+          const int64_t p = p0 + u * kThreads + t, pp = p < (int64_t)nt * R ? p : 0;
+          c[u] = S.winners[pp / R] + (pp % R) * kThreads;
+          if (p >= (int64_t)nt * R) c[u] = nchunks;
+          v[u] = load16(rs, c[u] < nfull ? (uint32_t)(c[u] * 16) : kFar);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (c[u] >= nchunks) continue;
+          uint64_t kk[8];
+          if (c[u] < nfull) {
+            if (chunk_value(v[u]) < v16) continue;
+            full_keys(v[u], (uint32_t)(8 * c[u]), kk);
+          } else {
+            part_keys(rs, (uint32_t)(8 * c[u]), (uint32_t)n, kk);
+          }
+          uint64_t f = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f = (kk[e] >> 32) == v16 && kk[e] > f ? kk[e] : f;
+          const int64_t p = p0 + u * kThreads + t;
+          if (f) atomicMax(reinterpret_cast<unsigned long long*>(&cands[p / R]), (unsigned long long)f);
+        }
       }
       __syncthreads();
       if (M == v16) {
         const uint64_t mine = cands[my];
         uint32_t rank = 0;
         for (int j = 0; j < nt; ++j) rank += cands[j] > mine;
-        if (rank == m - 1) tau_s = mine;
+        if (rank == m - 1) S.tau = mine;
         winner = rank < m;
       }
       __syncthreads();
-      tau = tau_s;
+      tau = S.tau;
     }
   }
-  if (winner) winners[atomicAdd(&nwin, 1u)] = t;
+  if (winner) S.winners[atomicAdd(&S.nwin, 1u)] = t;
   __syncthreads();
-  const int W = (int)nwin;  // k, or every non-empty share when there are at most k
+  const int W = (int)S.nwin;  // k, or every non-empty share when there are at most k
 
-  // 3. collect every key >= tau from the winners' shares
-  for (int64_t p = t; p < (int64_t)W * R; p += kThreads) {
-    const int64_t c = winners[p / R] + (p % R) * kThreads;
-    if (c >= nchunks) continue;
-    uint64_t kk[8];
-    chunk_keys(rs, c, n, nfull, kk);
-    uint32_t mask = 0;
+  // 3. collect every key >= tau from the winners' shares (chunks whose
+  // largest value is below tau's are skipped on their packed value keys)
+  const uint32_t tv = (uint32_t)(tau >> 32);
+  for (int64_t p0 = 0; p0 < (int64_t)W * R; p0 += kBatch * kThreads) {
+    u32x4 v[kBatch];
+    int64_t c[kBatch];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) mask |= (kk[e] >= tau && kk[e] != 0) ? 1u << e : 0u;
-    if (mask) {
-      const uint32_t at = atomicAdd(&count, (uint32_t)__builtin_popcount(mask));
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t p = p0 + u * kThreads + t, pp = p < (int64_t)W * R ? p : 0;
+      c[u] = S.winners[pp / R] + (pp % R) * kThreads;
+      if (p >= (int64_t)W * R) c[u] = nchunks;
+      v[u] = load16(rs, c[u] < nfull ? (uint32_t)(c[u] * 16) : kFar);
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if ((mask >> e) & 1u) coll[at + __builtin_popcount(mask & ((1u << e) - 1u))] = kk[e];
+    for (int u = 0; u < kBatch; ++u) {
+      if (c[u] >= nchunks) continue;
+      uint64_t kk[8];
+      if (c[u] < nfull) {
+        if (chunk_value(v[u]) < tv) continue;
+        full_keys(v[u], (uint32_t)(8 * c[u]), kk);
+      } else {
+        part_keys(rs, (uint32_t)(8 * c[u]), (uint32_t)n, kk);
+      }
+      uint32_t mask = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mask |= (kk[e] >= tau && kk[e] != 0) ? 1u << e : 0u;
+      if (mask) {
+        const uint32_t at = atomicAdd(&S.count, (uint32_t)__builtin_popcount(mask));
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if ((mask >> e) & 1u) coll[at + __builtin_popcount(mask & ((1u << e) - 1u))] = kk[e];
+      }
     }
   }
   __syncthreads();
 
+}
+
+// Steps 1-3 from the per-tile maximum keys that the greedy GEMV variant
+// stored for the output projection's row tiles (tile i: rows row0(i) ..
+// row0(i) + rows(i) - 1, large tiles of rpt rows first, then tiles of srows).
+// The keys are exact and distinct, so tau = the k-th largest tile key (two
+// value histograms, then the tied keys ranked), the k tiles with keys >= tau
+// are the winners, and their rows are read in pieces of up to 8.  Returns
+// false (for the whole workgroup) when the tied keys or the collected keys
+// would not fit in `cap` entries of coll.
+__device__ __forceinline__ bool collect_tiles(Lds& S, uint64_t* coll, int cap, const uint16_t* logits, int64_t n,
+                              const uint64_t* slots, int ntiles, int nbig, int rpt, int srows, int k) {
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  if (t < 256) S.hist1[t] = S.hist2[t] = 0u;
+  if (t == 0) S.count = S.nwin = S.ntie = S.over = 0u;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(slots, (uint32_t)ntiles * 8u);  // past the end: key 0
+  // Up to kBatch * kThreads tiles the keys stay in registers for every pass
+  // below (one memory round trip); more are read again for each pass.
+  const bool resident = ntiles <= kBatch * kThreads;
+  uint64_t res[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u)
+    res[u] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rk, (uint32_t)(u * kThreads + t) * 8u, 0, 0));
+  auto keys = [&](int i0, uint64_t* v) {  // tile keys i0 + u * kThreads + t
+    if (resident) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = res[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        v[u] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                                rk, (uint32_t)(i0 + u * kThreads + t) * 8u, 0, 0));
+    }
+  };
+  __syncthreads();
+
+  uint64_t tau = 1;  // every real key is >= 1
+  if (ntiles > k) {
+    for (int i0 = 0; i0 < ntiles; i0 += kBatch * kThreads) {
+      uint64_t v[kBatch];
+      keys(i0, v);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (v[u]) atomicAdd(&S.hist1[(uint32_t)(v[u] >> 40) & 0xFFu], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) suffix_select(S.hist1, (uint32_t)k, &S.bin1, &S.above1);
+    __syncthreads();
+    const uint32_t b1 = S.bin1;
+    for (int i0 = 0; i0 < ntiles; i0 += kBatch * kThreads) {
+      uint64_t v[kBatch];
+      keys(i0, v);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (v[u] && ((uint32_t)(v[u] >> 40) & 0xFFu) == b1) atomicAdd(&S.hist2[(uint32_t)(v[u] >> 32) & 0xFFu], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) suffix_select(S.hist2, (uint32_t)k - S.above1, &S.bin2, &S.above2);
+    __syncthreads();
+    const uint64_t v16 = ((uint64_t)b1 << 8) | S.bin2;
+    const uint32_t m = (uint32_t)k - S.above1 - S.above2;  // tied keys to take (>= 1)
+    const uint32_t ceq = S.hist2[S.bin2];
+    if (ceq == m) {
+      tau = v16 << 32;  // exactly the k largest tile keys have value >= v16
+    } else {
+      if (ceq > (uint32_t)cap) {  // uniform: ceq is the same for every thread
+        __syncthreads();            // every thread has read the histograms before a fallback resets them
+        return false;
+      }
+      for (int i0 = 0; i0 < ntiles; i0 += kBatch * kThreads) {
+        uint64_t v[kBatch];
+        keys(i0, v);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+          if (v[u] && (v[u] >> 32) == v16) coll[atomicAdd(&S.ntie, 1u)] = v[u];
+      }
+      __syncthreads();
+      if (ceq <= (uint32_t)kRankMax) {
+        if (t < (int)ceq) {
+          const uint64_t key = coll[t];
+          uint32_t rank = 0;
+          for (uint32_t j = 0; j < ceq; ++j) rank += coll[j] > key;
+          if (rank == m - 1) S.tau = key;
+        }
+      } else {
+        int P = 1;
+        while (P < (int)ceq) P <<= 1;
+        for (int i = (int)ceq + t; i < P; i += kThreads) coll[i] = 0;
+        __syncthreads();
+        bitonic_desc(coll, P);
+        if (t == 0) S.tau = coll[m - 1];
+      }
+      __syncthreads();
+      tau = S.tau;
+    }
+  }
+  for (int i0 = 0; i0 < ntiles; i0 += kBatch * kThreads) {
+    uint64_t v[kBatch];
+    keys(i0, v);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (v[u] && v[u] >= tau) S.winners[atomicAdd(&S.nwin, 1u)] = i0 + u * kThreads + t;
+  }
+  __syncthreads();
+  const int W = (int)S.nwin;  // k, or every tile when there are at most k
+
+  // every key >= tau of the winners' rows; piece j of a winner = its rows
+  // 8j .. 8j + 7 (one 16-byte load when they start on a multiple of 8)
+  const int maxp = (max(rpt, srows) + 7) / 8;
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(logits, (uint32_t)(n * 2));
+  for (int p0 = 0; p0 < W * maxp; p0 += kBatch * kThreads) {
+    u32x4 v[kBatch];
+    uint32_t start[kBatch], end[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = p0 + u * kThreads + t, pp = p < W * maxp ? p : 0;  // branch-free: see step 1
+      const int i = S.winners[pp / maxp], j = pp % maxp;
+      const int r0 = i < nbig ? i * rpt : nbig * rpt + (i - nbig) * srows;
+      const int r1 = min(r0 + (i < nbig ? rpt : srows), (int)n);
+      start[u] = p < W * maxp ? (uint32_t)min(r0 + 8 * j, r1) : 0u;
+      end[u] = p < W * maxp ? (uint32_t)min(r0 + 8 * j + 8, r1) : 0u;
+      const bool whole = end[u] == start[u] + 8 && (start[u] & 7u) == 0;
+      v[u] = load16(ry, whole ? start[u] * 2u : kFar);
+    }
+    const uint32_t tv = (uint32_t)(tau >> 32);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (end[u] == start[u]) continue;
+      uint64_t kk[8];
+      if (end[u] == start[u] + 8 && (start[u] & 7u) == 0) {
+        if (chunk_value(v[u]) < tv) continue;  // no key of the piece reaches tau
+        full_keys(v[u], start[u], kk);
+      } else {
+        part_keys(ry, start[u], end[u], kk);
+      }
+      uint32_t mask = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mask |= (kk[e] >= tau && kk[e] != 0) ? 1u << e : 0u;
+      if (mask) {
+        const uint32_t at = atomicAdd(&S.count, (uint32_t)__builtin_popcount(mask));
+        if (at + (uint32_t)__builtin_popcount(mask) > (uint32_t)cap) {
+          S.over = 1u;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if ((mask >> e) & 1u) coll[at + __builtin_popcount(mask & ((1u << e) - 1u))] = kk[e];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const bool ok = S.over == 0u;
+  __syncthreads();  // every thread has read S.over before a fallback resets the state
+  return ok;
+}
+
+// Steps 4-6 on coll[0, S.count): candidates, recomputed logits, token.
+__device__ __forceinline__ void finish(Lds& S, uint64_t* cands, uint64_t* coll, const uint16_t* head, const uint16_t* x, int64_t K,
+                       int k, int32_t* token, int32_t* cand, float* cand_logits) {
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   // 4. the k largest collected keys, in greedy order (keys are distinct)
-  const int total = (int)count;
+  const int total = (int)S.count;
   if (total <= kRankMax) {
     if (t < total) {
       const uint64_t key = coll[t];
@@ -355,7 +551,7 @@ __global__ __launch_bounds__(kThreads) void head_rescore_kernel(const uint16_t* 
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
       const int j = j0 + u * (kThreads / 64);
-      if (lane == 0 && j < k) exact[j] = sum;
+      if (lane == 0 && j < k) S.exact[j] = sum;
     }
   }
   __syncthreads();
@@ -364,10 +560,10 @@ __global__ __launch_bounds__(kThreads) void head_rescore_kernel(const uint16_t* 
   uint64_t b = 0;
   for (int j = t; j < k; j += kThreads) {
     const uint32_t row = key_row(cands[j]);
-    const uint64_t kk = key_f32(exact[j], row);
+    const uint64_t kk = key_f32(S.exact[j], row);
     b = kk > b ? kk : b;
     if (cand) cand[j] = (int32_t)row;
-    if (cand_logits) cand_logits[j] = exact[j];
+    if (cand_logits) cand_logits[j] = S.exact[j];
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -376,13 +572,50 @@ __global__ __launch_bounds__(kThreads) void head_rescore_kernel(const uint16_t* 
     const uint64_t other = ((uint64_t)hi << 32) | lo;
     b = other > b ? other : b;
   }
-  if (lane == 0) wave_best[wave] = b;
+  if (lane == 0) S.wave_best[wave] = b;
   __syncthreads();
   if (t == 0) {
-    uint64_t m = wave_best[0];
-    for (int w = 1; w < kThreads / 64; ++w) m = wave_best[w] > m ? wave_best[w] : m;
+    uint64_t m = S.wave_best[0];
+    for (int w = 1; w < kThreads / 64; ++w) m = S.wave_best[w] > m ? S.wave_best[w] : m;
     *token = (int32_t)key_row(m);
   }
+}
+
+__global__ __launch_bounds__(kThreads) void head_rescore_kernel(const uint16_t* __restrict__ logits, int64_t n,
+                                                                const uint16_t* __restrict__ head,
+                                                                const uint16_t* __restrict__ x, int64_t K, int k,
+                                                                int32_t* __restrict__ token, int32_t* __restrict__ cand,
+                                                                float* __restrict__ cand_logits) {
+  extern __shared__ uint64_t lds[];
+  __shared__ Lds S;
+  uint64_t* cands = lds;            // [kThreads]: the candidates, in greedy order
+  uint64_t* coll = lds + kThreads;  // [collection capacity], power of two
+  collect_shares(S, cands, coll, logits, n, k);
+  finish(S, cands, coll, head, x, K, k, token, cand, cand_logits);
+}
+
+// After the greedy GEMV variant: the target's stored logits, x and tile
+// geometry come from its descriptor, the per-tile keys from `slots`.  When
+// the tile keys leave too many keys to collect (ties, large tiles), the
+// selection starts again from the logits alone.
+__global__ __launch_bounds__(kThreads) void gemv_rescore_kernel(const tkq_gemv_desc* __restrict__ descs, int count,
+                                                                int target, int tiles,
+                                                                const uint64_t* __restrict__ slots,
+                                                                const uint16_t* __restrict__ head, int k,
+                                                                int32_t* __restrict__ token, int32_t* __restrict__ cand,
+                                                                float* __restrict__ cand_logits) {
+  extern __shared__ uint64_t lds[];
+  __shared__ Lds S;
+  uint64_t* cands = lds;
+  uint64_t* coll = lds + kThreads;  // TKQ_RESCORE_CAP entries
+  const tkq_gemv_desc* d = descs + target;
+  const int n = d->N;
+  const int ntiles = (target + 1 < count ? descs[target + 1].work0 : tiles) - d->work0;
+  const uint16_t* y = reinterpret_cast<const uint16_t*>(d->y);
+  if (!collect_tiles(S, coll, TKQ_RESCORE_CAP, y, n, slots, ntiles, d->big_tiles, d->rows_per_tile, d->small_rows,
+                     k))
+    collect_shares(S, cands, coll, y, n, k);
+  finish(S, cands, coll, head, reinterpret_cast<const uint16_t*>(d->x), d->K, k, token, cand, cand_logits);
 }
 
 }  // namespace
@@ -410,6 +643,22 @@ hipError_t launch_head_rescore(const uint16_t* logits, int64_t n, const uint16_t
   }
   hipLaunchKernelGGL(head_rescore_kernel, dim3(1), dim3(kThreads), lds, stream, logits, n, head, x, K, k, token,
                      cand, cand_logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_rescore(const tkq_gemv_desc* dev_descs, int count, int target, int64_t tiles,
+                               const uint64_t* slots, const uint16_t* head, int k, int32_t* token, int32_t* cand,
+                               float* cand_logits, hipStream_t stream) {
+  const size_t lds = (size_t)(kThreads + TKQ_RESCORE_CAP) * 8;
+  static bool raised = false;  // above the default dynamic-LDS limit (once; idempotent)
+  if (!raised) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_rescore_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    raised = true;
+  }
+  hipLaunchKernelGGL(gemv_rescore_kernel, dim3(1), dim3(kThreads), lds, stream, dev_descs, count, target, (int)tiles,
+                     slots, head, k, token, cand, cand_logits);
   return hipGetLastError();
 }
 

@@ -501,6 +501,28 @@ int tkq_head_rescore(const uint16_t* logits, int64_t n, const uint16_t* head, co
                                              (hipStream_t)stream));
 }
 
+int tkq_gemv_argmax_rescore(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs, int32_t target, int64_t N,
+                            int64_t K, const uint16_t* head, int32_t k, int32_t* token, int32_t* cand,
+                            float* cand_logits, uint64_t* slots, int64_t scratch_bytes, void* stream) {
+  const int st = check_plan(plan, dev_descs);
+  if (st) return st;
+  if (plan->fmt == TKQ_FMT_BIN) return TKQ_EFORMAT;
+  if (target < 0 || target >= plan->count || !head || !token || !slots) return TKQ_EINVAL;
+  if (scratch_bytes < 8 * plan->tiles || N < 1 || K < 1 || k < 1 || k > N) return TKQ_EINVAL;
+  if (k > TKQ_RESCORE_MAX_K || N > INT32_MAX || K % 8 || K > TKQ_MAX_K ||
+      tkq::rescore_capacity(N, k) > TKQ_RESCORE_CAP)
+    return TKQ_ESHAPE;
+  if (!aligned16(head) || !aligned16(slots)) return TKQ_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(token) | reinterpret_cast<uintptr_t>(cand) |
+       reinterpret_cast<uintptr_t>(cand_logits)) & 3u)
+    return TKQ_EALIGN;
+  const hipError_t e = tkq::launch_gemv(plan->fmt, plan->variant, dev_descs, plan->count, plan->tiles, target,
+                                        nullptr, slots, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(tkq::launch_gemv_rescore(dev_descs, plan->count, target, plan->tiles, slots, head, k, token,
+                                             cand, cand_logits, (hipStream_t)stream));
+}
+
 int tkq_read_probe(const void* buf, int64_t bytes, uint32_t* out, void* stream) {
   if (!buf || !out || bytes < 16) return TKQ_EINVAL;
   if (bytes % 16) return TKQ_ESHAPE;

@@ -88,6 +88,8 @@ _SIGNATURES = {
     "tkq_gemm_prefill": ([_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
     "tkq_read_probe": ([_P, _I64, _P, _P], ctypes.c_int),
     "tkq_head_rescore": ([_P, _I64, _P, _P, _I64, _I32, _P, _P, _P, _P], ctypes.c_int),
+    "tkq_gemv_argmax_rescore": ([ctypes.POINTER(GemvPlan), _P, _I32, _I64, _I64, _P, _I32, _P, _P, _P, _P, _I64,
+                                 _P], ctypes.c_int),
 }
 
 _lib = None
@@ -307,6 +309,25 @@ class GemvBatch:
         _need(token, torch.int32, "token")
         _call("tkq_gemv_argmax_static", ctypes.byref(self.plan), _ptr(self.dev_descs), int(target),
               _ptr(token), _stream(stream, self.dev_descs))
+
+
+    def run_argmax_rescore(self, target, head, k, token, scratch, cand=None, cand_logits=None, stream=None):
+        """run() plus greedy selection with head rescore over item `target`
+        (tkq_gemv_argmax_rescore): head is the fp16 copy [N, K] of the
+        target's weights; token int32 [1]; scratch: greedy_scratch();
+        cand int32 [k] and cand_logits float32 [k] optional."""
+        d = self.descs[target]
+        _need(head, torch.float16, "head", (d.N, d.K))
+        _need(token, torch.int32, "token")
+        _need(scratch, torch.int64, "scratch")
+        if cand is not None:
+            _need(cand, torch.int32, "cand", (k,))
+        if cand_logits is not None:
+            _need(cand_logits, torch.float32, "cand_logits", (k,))
+        _call("tkq_gemv_argmax_rescore", ctypes.byref(self.plan), _ptr(self.dev_descs), int(target), d.N, d.K,
+              _ptr(head), int(k), _ptr(token), _ptr(cand) if cand is not None else None,
+              _ptr(cand_logits) if cand_logits is not None else None, _ptr(scratch), scratch.numel() * 8,
+              _stream(stream, self.dev_descs))
 
 
 def gemv(fmt, codes, meta, x, N, K, y=None, stream=None):

@@ -333,6 +333,33 @@ int tkq_head_rescore(const uint16_t* logits, int64_t n, const uint16_t* head,
                      const uint16_t* x, int64_t K, int32_t k, int32_t* token,
                      int32_t* cand, float* cand_logits, void* stream);
 
+/* Grouped GEMV plus greedy selection with head rescore over descriptor
+ * `target` (the output projection): computes exactly what tkq_gemv computes,
+ * and then what tkq_head_rescore computes over the target's stored outputs,
+ * with x = the target's x.  The GEMV workgroups of the target store the
+ * largest output key of each of their row tiles in `scratch`, so the
+ * candidates are found from those keys and the rows of at most k tiles
+ * instead of a pass over every output (when ties or large tiles would leave
+ * more keys to collect than TKQ_RESCORE_CAP, the selection falls back to the
+ * pass over every output; the result is the same).
+ * N, K: the target descriptor's N and K (a mismatch is undefined behaviour,
+ * like a descriptor table that does not match its plan); head: fp16 bits
+ * [N][K], row-major; token, cand, cand_logits, k: as tkq_head_rescore.
+ * scratch: caller-owned device memory of scratch_bytes >= 8 * plan->tiles,
+ * 16-byte aligned, any contents (overwritten).  Calls that share a scratch
+ * buffer or outputs must not run concurrently.
+ * Returns as tkq_gemv, plus TKQ_EFORMAT (binary coding: its outputs are
+ * int32), TKQ_EINVAL (target out of range; null head, token or scratch;
+ * scratch too small; N, K or k < 1; k > N), TKQ_ESHAPE (the limits of
+ * tkq_head_rescore for n = N) and TKQ_EALIGN (head or scratch not 16-byte
+ * aligned; token, cand or cand_logits not 4-byte aligned). */
+int tkq_gemv_argmax_rescore(const tkq_gemv_plan* plan,
+                            const tkq_gemv_desc* dev_descs, int32_t target,
+                            int64_t N, int64_t K, const uint16_t* head,
+                            int32_t k, int32_t* token, int32_t* cand,
+                            float* cand_logits, uint64_t* scratch,
+                            int64_t scratch_bytes, void* stream);
+
 /* ---- multi-token GEMV (M = 1..16) ----------------------------------------
  * Y_i[m, n] = sum_k X_i[m, k] * w_i[n, k] for M tokens at once over many
  * int4 g128 matrices in one launch: the regime between batch-1 decode and

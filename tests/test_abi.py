@@ -396,3 +396,46 @@ def test_head_rescore_validation():
     assert f(A, n, A, A, K, 8, A + 2, None, None, None) == tkq.EALIGN
     assert f(A, n, A, A, K, 8, A, A + 1, None, None) == tkq.EALIGN
     assert f(A, n, A, A, K, 8, A, None, A + 2, None) == tkq.EALIGN
+
+
+def test_gemv_argmax_rescore_validation():
+    """The fused GEMV + head rescore entry point refuses every bad argument on
+    the host (plan, target, coding, sizes, capacity, alignment)."""
+    f = tkq.lib().tkq_gemv_argmax_rescore
+    plan = tkq.GemvPlan()
+    plan.fmt, plan.count, plan.tiles = 1, 1, 1
+    assert f(ctypes.byref(plan), A, 0, 128, 128, A, 4, A, None, None, A, 1 << 20, None) == tkq.EPLAN
+    arr = _descs(1, [(8, 128), (400, 256)])
+    st, plan = _prepare(arr)
+    assert st == tkq.OK
+    sb = 8 * plan.tiles
+    ok = (A, 1, 400, 256, A, 4, A, None, None, A, sb, None)
+
+    def call(**kw):
+        names = ["descs", "target", "N", "K", "head", "k", "token", "cand", "cl", "scratch", "sb", "stream"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return f(ctypes.byref(plan), *[args[n] for n in names])
+    assert call(target=-1) == tkq.EINVAL
+    assert call(target=2) == tkq.EINVAL
+    assert call(head=None) == tkq.EINVAL
+    assert call(token=None) == tkq.EINVAL
+    assert call(scratch=None) == tkq.EINVAL
+    assert call(sb=sb - 8) == tkq.EINVAL
+    assert call(N=0) == tkq.EINVAL
+    assert call(K=0) == tkq.EINVAL
+    assert call(k=0) == tkq.EINVAL
+    assert call(k=401) == tkq.EINVAL
+    assert call(K=260) == tkq.ESHAPE
+    assert call(N=151936, k=108) == tkq.ESHAPE
+    assert call(N=5000, k=1025) == tkq.ESHAPE
+    assert call(head=A + 8) == tkq.EALIGN
+    assert call(scratch=A + 8) == tkq.EALIGN
+    assert call(token=A + 2) == tkq.EALIGN
+    assert call(cand=A + 1) == tkq.EALIGN
+    assert call(cl=A + 2) == tkq.EALIGN
+    assert call(descs=A + 8) == tkq.EALIGN
+    bin_arr = _descs(4, [(8, 128)])
+    st, bplan = _prepare(bin_arr)
+    assert st == tkq.OK
+    assert f(ctypes.byref(bplan), A, 0, 8, 128, A, 4, A, None, None, A, 1 << 20, None) == tkq.EFORMAT

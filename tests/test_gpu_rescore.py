@@ -193,3 +193,103 @@ def test_rescore_maximum_sizes():
         x16 = xd.cpu().numpy()
         rows = lambda r: hd[torch.from_numpy(np.asarray(r)).cuda()].cpu().numpy()
         _check(y16, rows, x16, k, tok, cand, cl, "max n=%d K=%d" % (n, K))
+
+
+# ---- fused: grouped GEMV + head rescore (tkq_gemv_argmax_rescore) ----------
+
+_PACK = {"int4": "pack_int4_g128", "k5": "pack_k5", "tern": "pack_tern_g128", "hier": "pack_int4_hier_g32",
+         "int2": "pack_int2_g128", "int3": "pack_int3_g128"}
+
+
+def _fused(torch, tkq, fmt, mats, target, k, calls=2, Wdev=None):
+    """Grouped GEMV of `mats` [(W numpy or None, x numpy)] with the fused
+    rescore over `target`; returns (token, cand, cand_logits, stored y of the
+    target, head fp16 on the device, x of the target on the device)."""
+    items = []
+    for i, (W, x) in enumerate(mats):
+        Wd = Wdev if (W is None) else torch.from_numpy(W).cuda()
+        N, K = Wd.shape
+        codes, meta = getattr(tkq, _PACK[fmt])(Wd)
+        y = torch.full((N,), float("nan"), dtype=torch.float16, device="cuda")
+        items.append(dict(codes=codes, meta=meta, x=torch.from_numpy(x).cuda(), y=y, N=N, K=K))
+        if i == target:
+            head = Wd.half().contiguous()
+    batch = tkq.GemvBatch(fmt, items)
+    scratch = batch.greedy_scratch()
+    outs = []
+    for c in range(calls):
+        token = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+        cand = torch.full((k,), -7, dtype=torch.int32, device="cuda")
+        cl = torch.full((k,), float("nan"), dtype=torch.float32, device="cuda")
+        scratch.random_(0, 2 ** 62, generator=torch.Generator("cuda").manual_seed(c))   # garbage in the scratch
+        batch.run_argmax_rescore(target, head, k, token, scratch, cand=cand, cand_logits=cl)
+        torch.cuda.synchronize()
+        outs.append((int(token.item()), cand.cpu().numpy(), cl.cpu().numpy()))
+    for o in outs[1:]:
+        assert o[0] == outs[0][0] and np.array_equal(o[1], outs[0][1])
+        assert np.array_equal(o[2].view(np.uint32), outs[0][2].view(np.uint32))
+    return outs[0] + (items[target]["y"], head, items[target]["x"])
+
+
+def _fused_check(torch, tkq, res, k, what):
+    """The fused result equals the standalone rescore over the same stored
+    logits bit for bit, and both meet the oracle."""
+    tok, cand, cl, y, head, xd = res
+    t2, c2, l2 = _rescore_dev(torch, tkq, y, head, xd, k)
+    assert tok == t2 and np.array_equal(cand, c2), "%s: fused and standalone rescore differ" % what
+    assert np.array_equal(cl.view(np.uint32), l2.view(np.uint32)), what
+    rows = lambda r: head[torch.from_numpy(np.asarray(r)).cuda()].cpu().numpy()
+    _check(y.cpu().numpy(), rows, xd.cpu().numpy(), k, tok, cand, cl, what)
+
+
+def test_fused_rescore_lm_head():
+    """The 0.5B output projection alone (large tiles, then the small tail
+    tiles): k = 1, 16, 64, 107; the stored logits equal a plain GEMV's."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    W, x = inputs.sweep_matrix("qwen2.5-0.5b", 168, 151936, 896)
+    for k in (1, 16, 64, 107):
+        res = _fused(torch, tkq, "int4", [(W, x)], 0, k)
+        _fused_check(torch, tkq, res, k, "lm_head k=%d" % k)
+        if k == 1:
+            codes, meta = tkq.pack_int4_g128(torch.from_numpy(W).cuda())
+            yp = tkq.gemv("int4", codes, meta, torch.from_numpy(x).cuda(), 151936, 896)
+            torch.cuda.synchronize()
+            assert np.array_equal(res[3].cpu().numpy().view(np.uint16), yp.cpu().numpy().view(np.uint16))
+
+
+@pytest.mark.parametrize("fmt", ["int4", "k5", "tern", "hier", "int2", "int3"])
+def test_fused_rescore_grouped(fmt):
+    """Mixed shapes in one launch, the target first, in the middle and last;
+    the other codings' tiles need not start on multiples of 8 rows."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    shapes = [(896, 896), (128, 896), (4864, 896), (896, 4864), (20000, 896)]
+    mats = [(inputs.normal_matrix((730, i), n, kk), inputs.normal_vector((731, i), kk))
+            for i, (n, kk) in enumerate(shapes)]
+    for target, k in ((0, 64), (2, 33), (4, 100), (1, 128)):
+        res = _fused(torch, tkq, fmt, mats, target, k)
+        _fused_check(torch, tkq, res, k, "%s target %d k=%d" % (fmt, target, k))
+
+
+@pytest.mark.parametrize("distinct", [1, 3])
+def test_fused_rescore_ties_fall_back(distinct):
+    """Rows drawn from one or three distinct rows: the stored logits take that
+    many values and every tile maximum ties.  With three values the winners'
+    rows hold ~8,700 keys at k = 64, which the collection takes; with one,
+    every row of the first k - 1 (large) tiles ties, more than the collection
+    takes, so the selection starts again from the logits.  Equal recomputed
+    logits go to the smallest row."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    N, K = 151936, 896
+    rng = np.random.default_rng(740 + distinct)
+    base = torch.from_numpy((rng.standard_normal((distinct, K)) * 0.02).astype(np.float32)).cuda()
+    pick = torch.from_numpy(rng.integers(0, distinct, N)).cuda()
+    Wd = base[pick].contiguous()
+    x = inputs.normal_vector(741, K)
+    for k in (1, 64, 107):
+        res = _fused(torch, tkq, "int4", [(None, x)], 0, k, Wdev=Wd)
+        _fused_check(torch, tkq, res, k, "%d-row ties k=%d" % (distinct, k))
+        if distinct == 1:
+            assert res[0] == 0 and list(res[1]) == list(range(k))
