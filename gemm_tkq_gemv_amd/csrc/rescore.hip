@@ -34,6 +34,7 @@ constexpr int kInFlight = 16;    // 16-byte loads a thread issues before using a
 constexpr int kRankMax = 256;    // collections up to this size are ranked by counting
 constexpr int kBatch = 4;        // chunks (or tile keys) per thread in flight in the collection passes
 constexpr uint32_t kFar = 0x80000000u;  // buffer offset past every range: loads return 0, no access
+constexpr int kWl = 2 * kThreads;  // worklist entries (uint32, in the candidate array until step 4)
 
 // 16-bit order key of a stored fp16 logit: larger value -> larger key; -0
 // counts as +0 and every NaN (either sign, any payload) above +inf.  At least
@@ -160,7 +161,7 @@ __device__ __forceinline__ void suffix_select(const uint32_t* hist, uint32_t nee
 // Workgroup state of the selection (besides the two dynamic LDS arrays).
 struct Lds {
   alignas(16) uint32_t hist1[256], hist2[256];  // read 16 bytes at a time by suffix_select
-  uint32_t count, nwin, ntie, bin1, above1, bin2, above2, over;
+  uint32_t count, nwin, ntie, bin1, above1, bin2, above2, over, nwl;
   unsigned long long tau;
   int32_t winners[kThreads];
   float exact[TKQ_RESCORE_MAX_K];
@@ -296,7 +297,9 @@ __device__ __forceinline__ void collect_shares(Lds& S, uint64_t* cands, uint64_t
   const int W = (int)S.nwin;  // k, or every non-empty share when there are at most k
 
   // 3. collect every key >= tau from the winners' shares (chunks whose
-  // largest value is below tau's are skipped on their packed value keys)
+  // largest value is below tau's are skipped on their packed value keys; at
+  // about one chunk per thread a worklist, as in collect_tiles, measured
+  // slower here)
   const uint32_t tv = (uint32_t)(tau >> 32);
   for (int64_t p0 = 0; p0 < (int64_t)W * R; p0 += kBatch * kThreads) {
     u32x4 v[kBatch];
@@ -330,7 +333,6 @@ __device__ __forceinline__ void collect_shares(Lds& S, uint64_t* cands, uint64_t
     }
   }
   __syncthreads();
-
 }
 
 // Steps 1-3 from the per-tile maximum keys that the greedy GEMV variant
@@ -341,11 +343,11 @@ __device__ __forceinline__ void collect_shares(Lds& S, uint64_t* cands, uint64_t
 // are the winners, and their rows are read in pieces of up to 8.  Returns
 // false (for the whole workgroup) when the tied keys or the collected keys
 // would not fit in `cap` entries of coll.
-__device__ __forceinline__ bool collect_tiles(Lds& S, uint64_t* coll, int cap, const uint16_t* logits, int64_t n,
+__device__ __forceinline__ bool collect_tiles(Lds& S, uint64_t* cands, uint64_t* coll, int cap, const uint16_t* logits, int64_t n,
                               const uint64_t* slots, int ntiles, int nbig, int rpt, int srows, int k) {
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   if (t < 256) S.hist1[t] = S.hist2[t] = 0u;
-  if (t == 0) S.count = S.nwin = S.ntie = S.over = 0u;
+  if (t == 0) S.count = S.nwin = S.ntie = S.over = S.nwl = 0u;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(slots, (uint32_t)ntiles * 8u);  // past the end: key 0
   // Up to kBatch * kThreads tiles the keys stay in registers for every pass
   // below (one memory round trip); more are read again for each pass.
@@ -438,46 +440,63 @@ __device__ __forceinline__ bool collect_tiles(Lds& S, uint64_t* coll, int cap, c
   const int W = (int)S.nwin;  // k, or every tile when there are at most k
 
   // every key >= tau of the winners' rows; piece j of a winner = its rows
-  // 8j .. 8j + 7 (one 16-byte load when they start on a multiple of 8)
+  // 8j .. 8j + 7 (one 16-byte load when they start on a multiple of 8).
+  // Pieces whose largest value reaches tau's go to a worklist (in `cands`,
+  // free until step 4), then one thread per listed piece forms its keys.
   const int maxp = (max(rpt, srows) + 7) / 8;
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(logits, (uint32_t)(n * 2));
+  const uint32_t tv = (uint32_t)(tau >> 32);
+  uint32_t* wl = reinterpret_cast<uint32_t*>(cands);
+  auto piece = [&](int p, uint32_t& start, uint32_t& end) {  // rows of piece p (empty past the list)
+    const int pp = p < W * maxp ? p : 0;
+    const int i = S.winners[pp / maxp], j = pp % maxp;
+    const int r0 = i < nbig ? i * rpt : nbig * rpt + (i - nbig) * srows;
+    const int r1 = min(r0 + (i < nbig ? rpt : srows), (int)n);
+    start = p < W * maxp ? (uint32_t)min(r0 + 8 * j, r1) : 0u;
+    end = p < W * maxp ? (uint32_t)min(r0 + 8 * j + 8, r1) : 0u;
+  };
   for (int p0 = 0; p0 < W * maxp; p0 += kBatch * kThreads) {
     u32x4 v[kBatch];
     uint32_t start[kBatch], end[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int p = p0 + u * kThreads + t, pp = p < W * maxp ? p : 0;  // branch-free: see step 1
-      const int i = S.winners[pp / maxp], j = pp % maxp;
-      const int r0 = i < nbig ? i * rpt : nbig * rpt + (i - nbig) * srows;
-      const int r1 = min(r0 + (i < nbig ? rpt : srows), (int)n);
-      start[u] = p < W * maxp ? (uint32_t)min(r0 + 8 * j, r1) : 0u;
-      end[u] = p < W * maxp ? (uint32_t)min(r0 + 8 * j + 8, r1) : 0u;
+    for (int u = 0; u < kBatch; ++u) {  // branch-free: see step 1
+      piece(p0 + u * kThreads + t, start[u], end[u]);
       const bool whole = end[u] == start[u] + 8 && (start[u] & 7u) == 0;
       v[u] = load16(ry, whole ? start[u] * 2u : kFar);
     }
-    const uint32_t tv = (uint32_t)(tau >> 32);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      if (end[u] == start[u]) continue;
-      uint64_t kk[8];
-      if (end[u] == start[u] + 8 && (start[u] & 7u) == 0) {
-        if (chunk_value(v[u]) < tv) continue;  // no key of the piece reaches tau
-        full_keys(v[u], start[u], kk);
-      } else {
-        part_keys(ry, start[u], end[u], kk);
+      const bool whole = end[u] == start[u] + 8 && (start[u] & 7u) == 0;
+      if (end[u] > start[u] && (!whole || chunk_value(v[u]) >= tv)) {
+        const uint32_t at = atomicAdd(&S.nwl, 1u);
+        if (at < (uint32_t)kWl) wl[at] = (uint32_t)(p0 + u * kThreads + t);
+        else S.over = 1u;
       }
-      uint32_t mask = 0;
+    }
+  }
+  __syncthreads();
+  if (S.over) {        // uniform
+    __syncthreads();   // every thread has read S.over before a fallback resets it
+    return false;
+  }
+  const int nwl = (int)S.nwl;
+  for (int w = t; w < nwl; w += kThreads) {
+    uint32_t start, end;
+    piece((int)wl[w], start, end);
+    uint64_t kk[8];
+    if (end == start + 8 && (start & 7u) == 0) full_keys(load16(ry, start * 2u), start, kk);
+    else part_keys(ry, start, end, kk);
+    uint32_t mask = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mask |= (kk[e] >= tau && kk[e] != 0) ? 1u << e : 0u;
-      if (mask) {
-        const uint32_t at = atomicAdd(&S.count, (uint32_t)__builtin_popcount(mask));
-        if (at + (uint32_t)__builtin_popcount(mask) > (uint32_t)cap) {
-          S.over = 1u;
-        } else {
+    for (int e = 0; e < 8; ++e) mask |= (kk[e] >= tau && kk[e] != 0) ? 1u << e : 0u;
+    if (mask) {
+      const uint32_t at = atomicAdd(&S.count, (uint32_t)__builtin_popcount(mask));
+      if (at + (uint32_t)__builtin_popcount(mask) > (uint32_t)cap) {
+        S.over = 1u;
+      } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if ((mask >> e) & 1u) coll[at + __builtin_popcount(mask & ((1u << e) - 1u))] = kk[e];
-        }
+        for (int e = 0; e < 8; ++e)
+          if ((mask >> e) & 1u) coll[at + __builtin_popcount(mask & ((1u << e) - 1u))] = kk[e];
       }
     }
   }
@@ -612,7 +631,7 @@ __global__ __launch_bounds__(kThreads) void gemv_rescore_kernel(const tkq_gemv_d
   const int n = d->N;
   const int ntiles = (target + 1 < count ? descs[target + 1].work0 : tiles) - d->work0;
   const uint16_t* y = reinterpret_cast<const uint16_t*>(d->y);
-  if (!collect_tiles(S, coll, TKQ_RESCORE_CAP, y, n, slots, ntiles, d->big_tiles, d->rows_per_tile, d->small_rows,
+  if (!collect_tiles(S, cands, coll, TKQ_RESCORE_CAP, y, n, slots, ntiles, d->big_tiles, d->rows_per_tile, d->small_rows,
                      k))
     collect_shares(S, cands, coll, y, n, k);
   finish(S, cands, coll, head, reinterpret_cast<const uint16_t*>(d->x), d->K, k, token, cand, cand_logits);
