@@ -10,7 +10,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every pointer argument named as a tensor (W, codes, meta, scale, bits, x,
- *   y, X, Y, buf, out, dev_descs) is a DEVICE pointer owned by the caller
+ *   y, X, Y, buf, out, dev_descs, logits, head, token, cand, cand_logits,
+ *   scratch, workspace) is a DEVICE pointer owned by the caller
  *   (e.g. a torch tensor's data_ptr()).  The library never allocates, frees or
  *   retains device memory, and keeps no mutable global state apart from a
  *   per-thread copy of the last HIP error code.  Host pointers are named
