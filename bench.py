@@ -66,10 +66,10 @@ TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266616382, "2aee3066839fc642"),
                  "0.5b-int3": ("gemv", 206228152, "2aee3066839fc642"),
                  "0.5b-int4-greedy": ("gemv", 266671289, "2aee3066839fc642"),
                  "0.5b-int4-m16": ("small_m", 382402161, "dcca247aa7644067"),
-                 "kv-32k": ("kv", 149787535, "54f3ec3318d10c46"),
-                 "kv-4k": ("kv", 18428762, "54f3ec3318d10c46"),
-                 "kv-32k-gqa": ("kv", 37219000, "54f3ec3318d10c46"),
-                 "kv-128k-gqa": ("kv", 145439450, "54f3ec3318d10c46")}
+                 "kv-32k": ("kv", 143489614, "b36e2b1cae6332ba"),
+                 "kv-4k": ("kv", 18430846, "b36e2b1cae6332ba"),
+                 "kv-32k-gqa": ("kv", 37219117, "b36e2b1cae6332ba"),
+                 "kv-128k-gqa": ("kv", 145439373, "b36e2b1cae6332ba")}
 
 
 def traffic_family(workload):

@@ -186,9 +186,32 @@ __device__ __forceinline__ void pair_order(const uint32_t* raw, uint32_t* xr) {
   }
 }
 
-__device__ __forceinline__ float quad_sum(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
+// Cross-lane steps without the LDS pipe: DPP within rows of 16 lanes, and
+// gfx950's permlane swaps across rows (with the value in both operands, the
+// two results hold each lane's own value and that of lane ^ 16 or ^ 32).
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(u32(v), u32(v), false, false);
+  return fmaxf(f32(r[0]), f32(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(u32(v), u32(v), false, false);
+  return fmaxf(f32(r[0]), f32(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(u32(v), u32(v), false, false);
+  return f32(r[0]) + f32(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(u32(v), u32(v), false, false);
+  return f32(r[0]) + f32(r[1]);
+}
+__device__ __forceinline__ float quad_sum(float v) {  // lanes ^ 1, then ^ 2: the total in all four
+  v += dppf<kQuadSwap1>(v);
+  v += dppf<kQuadSwap2>(v);
   return v;
 }
 // The matrix-core kernel's waves raise their priority while they issue a
@@ -197,15 +220,21 @@ __device__ __forceinline__ float quad_sum(float v) {
 // measured 1 % slower with it and does not).
 __device__ __forceinline__ void prio_on() { __builtin_amdgcn_s_setprio(1); }
 __device__ __forceinline__ void prio_off() { __builtin_amdgcn_s_setprio(0); }
+// Whole-wave max / sum in every lane: quads, then the mirrors within 8 and
+// 16 lanes (the halves being uniform by then), then across rows.
 __device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dppf<kQuadSwap1>(v));
+  v = fmaxf(v, dppf<kQuadSwap2>(v));
+  v = fmaxf(v, dppf<kRowHalfMirror>(v));
+  v = fmaxf(v, dppf<kRowMirror>(v));
+  return max_xor32(max_xor16(v));
 }
 __device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dppf<kQuadSwap1>(v);
+  v += dppf<kQuadSwap2>(v);
+  v += dppf<kRowHalfMirror>(v);
+  v += dppf<kRowMirror>(v);
+  return sum_xor32(sum_xor16(v));
 }
 
 // Partial results cross workgroups on different XCDs, whose L2 caches are
@@ -605,8 +634,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
 #pragma unroll
       for (int r = 0; r < 4; ++r) pm = fmaxf(pm, sc[tb][r]);
     }
-    pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
-    pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+    pm = max_xor32(max_xor16(pm));
     const float mn = fmaxf(m, pm);
     const float alpha = exp2f(m - mn);  // 0 on the first page (m = -inf)
     m = mn;
@@ -623,8 +651,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         ps += pt;
       }
     }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
+    ps = sum_xor32(sum_xor16(ps));
     l = l * alpha + ps;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
