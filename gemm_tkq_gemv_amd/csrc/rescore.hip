@@ -124,6 +124,46 @@ __device__ void bitonic_desc(uint64_t* s, int P) {
   }
 }
 
+// Whole-wave reductions without the LDS pipe: DPP quad and mirror steps within
+// rows of 16 lanes, then gfx950's permlane swaps across rows (with the value
+// in both operands the two results hold each lane's own value and that of
+// lane ^ 16 or ^ 32).  The result is in every lane.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += f32(dppu<kQuadSwap1>(u32(v)));
+  v += f32(dppu<kQuadSwap2>(u32(v)));
+  v += f32(dppu<kRowHalfMirror>(u32(v)));
+  v += f32(dppu<kRowMirror>(u32(v)));
+  auto r = __builtin_amdgcn_permlane16_swap(u32(v), u32(v), false, false);
+  v = f32(r[0]) + f32(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(u32(v), u32(v), false, false);
+  return f32(r[0]) + f32(r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_dpp64(uint64_t v) {
+  const uint64_t o = ((uint64_t)dppu<CTRL>((uint32_t)(v >> 32)) << 32) | dppu<CTRL>((uint32_t)v);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint64_t max_swap64(uint64_t v, bool wide) {
+  const uint32_t h = (uint32_t)(v >> 32), l = (uint32_t)v;
+  const auto rh = wide ? __builtin_amdgcn_permlane32_swap(h, h, false, false)
+                       : __builtin_amdgcn_permlane16_swap(h, h, false, false);
+  const auto rl = wide ? __builtin_amdgcn_permlane32_swap(l, l, false, false)
+                       : __builtin_amdgcn_permlane16_swap(l, l, false, false);
+  const uint64_t a = ((uint64_t)rh[0] << 32) | rl[0], b = ((uint64_t)rh[1] << 32) | rl[1];
+  return a > b ? a : b;
+}
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
+  v = max_dpp64<kQuadSwap1>(v);
+  v = max_dpp64<kQuadSwap2>(v);
+  v = max_dpp64<kRowHalfMirror>(v);
+  v = max_dpp64<kRowMirror>(v);
+  return max_swap64(max_swap64(v, false), true);
+}
+
 // Wave 0: the largest bin b of hist[256] whose suffix count S(b) (bins >= b)
 // reaches `need`, and S(b + 1); need >= 1 and S(0) >= need.  Lane l holds
 // bins 255 - 4l .. 252 - 4l (from the top down), so an inclusive prefix sum
@@ -566,9 +606,7 @@ __device__ __forceinline__ void finish(Lds& S, uint64_t* cands, uint64_t* coll, 
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      float sum = acc[u];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      const float sum = wave_sum(acc[u]);
       const int j = j0 + u * (kThreads / 64);
       if (lane == 0 && j < k) S.exact[j] = sum;
     }
@@ -584,13 +622,7 @@ __device__ __forceinline__ void finish(Lds& S, uint64_t* cands, uint64_t* coll, 
     if (cand) cand[j] = (int32_t)row;
     if (cand_logits) cand_logits[j] = S.exact[j];
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t hi = __shfl_xor((uint32_t)(b >> 32), o, 64);
-    const uint32_t lo = __shfl_xor((uint32_t)b, o, 64);
-    const uint64_t other = ((uint64_t)hi << 32) | lo;
-    b = other > b ? other : b;
-  }
+  b = wave_max64(b);
   if (lane == 0) S.wave_best[wave] = b;
   __syncthreads();
   if (t == 0) {

@@ -293,3 +293,19 @@ def test_fused_rescore_ties_fall_back(distinct):
         _fused_check(torch, tkq, res, k, "%d-row ties k=%d" % (distinct, k))
         if distinct == 1:
             assert res[0] == 0 and list(res[1]) == list(range(k))
+
+
+def test_fused_rescore_7b_head():
+    """The 7B output projection (152,064 x 3,584, weights drawn on the
+    device) in int4 and int4-hier-g32, k = 64: longer head rows in the
+    recompute, other tile heights."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    N, K = 152064, 3584
+    Wd = inputs.device_normal_matrix(torch, 5196, N, K)
+    x = inputs.sweep_x("qwen2.5-7b", 196, K)
+    for fmt in ("int4", "hier"):
+        res = _fused(torch, tkq, fmt, [(None, x)], 0, 64, Wdev=Wd)
+        _fused_check(torch, tkq, res, 64, "7B head %s" % fmt)
+    del Wd
+    torch.cuda.empty_cache()
