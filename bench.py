@@ -55,16 +55,16 @@ TRAFFIC_SOURCES = {"gemv": ["gemm_tkq_gemv_amd/csrc/gemv.hip"] + _COMMON,
                    "prefill": ["gemm_tkq_gemv_amd/csrc/prefill.hip"] + _COMMON,
                    "kv": ["gemm_tkq_gemv_amd/csrc/kv.hip"] + _COMMON}
 # workload -> (kernel family, bytes per launch, sha256[:16] of that family's sources)
-TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266616382, "2aee3066839fc642"),
-                 "0.5b-k5": ("gemv", 506971706, "2aee3066839fc642"),
-                 "0.5b-tern": ("gemv", 135444579, "2aee3066839fc642"),
-                 "bin": ("gemv", 115068394, "2aee3066839fc642"),
-                 "7b-int4": ("gemv", 3781892473, "2aee3066839fc642"),
+TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266616382, "20c70ae719d399ba"),
+                 "0.5b-k5": ("gemv", 506971706, "20c70ae719d399ba"),
+                 "0.5b-tern": ("gemv", 135444579, "20c70ae719d399ba"),
+                 "bin": ("gemv", 115068394, "20c70ae719d399ba"),
+                 "7b-int4": ("gemv", 3781892473, "20c70ae719d399ba"),
                  "7b-prefill": ("prefill", 238651956, "143dc970ac5e58dd"),
-                 "0.5b-hier": ("gemv", 268438052, "2aee3066839fc642"),
-                 "0.5b-int2": ("gemv", 143153278, "2aee3066839fc642"),
-                 "0.5b-int3": ("gemv", 206228152, "2aee3066839fc642"),
-                 "0.5b-int4-greedy": ("gemv", 266671289, "2aee3066839fc642"),
+                 "0.5b-hier": ("gemv", 268438052, "20c70ae719d399ba"),
+                 "0.5b-int2": ("gemv", 143153278, "20c70ae719d399ba"),
+                 "0.5b-int3": ("gemv", 206228152, "20c70ae719d399ba"),
+                 "0.5b-int4-greedy": ("gemv", 266693011, "20c70ae719d399ba"),
                  "0.5b-int4-m16": ("small_m", 382402161, "dcca247aa7644067"),
                  "kv-32k": ("kv", 143489614, "b36e2b1cae6332ba"),
                  "kv-4k": ("kv", 18430846, "b36e2b1cae6332ba"),

@@ -434,14 +434,30 @@ __device__ __forceinline__ uint64_t greedy_key_i32(uint32_t v, uint32_t row) {
   return ((uint64_t)(v ^ 0x80000000u) << 32) | (uint64_t)(0xFFFFFFFFu - row);
 }
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+// Whole-wave maximum in every lane without the LDS pipe: DPP quad and mirror
+// steps within rows of 16 lanes, then gfx950's permlane swaps across rows
+// (with the value in both operands the two results hold each lane's own
+// value and that of lane ^ 16 or ^ 32).
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_dpp_u64(uint64_t v) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(v >> 32), CTRL, 0xF, 0xF, false);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  return max_u64(v, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ uint64_t max_swap_u64(uint64_t v, bool wide) {
+  const uint32_t h = (uint32_t)(v >> 32), l = (uint32_t)v;
+  const auto rh = wide ? __builtin_amdgcn_permlane32_swap(h, h, false, false)
+                       : __builtin_amdgcn_permlane16_swap(h, h, false, false);
+  const auto rl = wide ? __builtin_amdgcn_permlane32_swap(l, l, false, false)
+                       : __builtin_amdgcn_permlane16_swap(l, l, false, false);
+  return max_u64(((uint64_t)rh[0] << 32) | rl[0], ((uint64_t)rh[1] << 32) | rl[1]);
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-    v = max_u64(v, ((uint64_t)hi << 32) | lo);
-  }
-  return v;
+  v = max_dpp_u64<kQuadSwap1>(v);
+  v = max_dpp_u64<kQuadSwap2>(v);
+  v = max_dpp_u64<kRowHalfMirror>(v);
+  v = max_dpp_u64<kRowMirror>(v);
+  return max_swap_u64(max_swap_u64(v, false), true);
 }
 
 constexpr uint32_t kFar = 0x80000000u;  // offset past any buffer, no wrap

@@ -22,6 +22,8 @@
 //  5. each candidate's logit is recomputed in fp32 from its fp16 head row and
 //     x: fp16 x fp16 products are exact in fp32, so only the fp32 sums round;
 //  6. the token is the candidate with the largest recomputed logit.
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -671,6 +673,21 @@ __global__ __launch_bounds__(kThreads) void gemv_rescore_kernel(const tkq_gemv_d
 
 }  // namespace
 
+// Raises a kernel's dynamic-LDS limit above the 64 KB default, once per
+// kernel (which = 0, 1) and device: the attribute is set on the current
+// device, so each device the library runs on needs its own call.
+static hipError_t allow_lds(const void* fn, int which, int bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<bool> raised[2][kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && raised[which][dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) raised[which][dev].store(true, std::memory_order_release);
+  return e;
+}
+
 int64_t rescore_capacity(int64_t n, int k) {
   const int64_t R = ((n + 7) / 8 + kThreads - 1) / kThreads;
   return (int64_t)k * R * 8;
@@ -682,15 +699,10 @@ hipError_t launch_head_rescore(const uint16_t* logits, int64_t n, const uint16_t
   int64_t P = 1;
   while (P < rescore_capacity(n, k)) P <<= 1;
   const size_t lds = (size_t)(kThreads + P) * 8;
-  if (lds > 64 * 1024) {  // above the default dynamic-LDS limit (once; idempotent)
-    static bool raised = false;
-    if (!raised) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(head_rescore_kernel),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (kThreads + TKQ_RESCORE_CAP) * 8);
-      if (e != hipSuccess) return e;
-      raised = true;
-    }
+  if (lds > 64 * 1024) {  // above the default dynamic-LDS limit
+    const hipError_t e = allow_lds(reinterpret_cast<const void*>(head_rescore_kernel), 0,
+                                   (kThreads + TKQ_RESCORE_CAP) * 8);
+    if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(head_rescore_kernel, dim3(1), dim3(kThreads), lds, stream, logits, n, head, x, K, k, token,
                      cand, cand_logits);
@@ -701,13 +713,8 @@ hipError_t launch_gemv_rescore(const tkq_gemv_desc* dev_descs, int count, int ta
                                const uint64_t* slots, const uint16_t* head, int k, int32_t* token, int32_t* cand,
                                float* cand_logits, hipStream_t stream) {
   const size_t lds = (size_t)(kThreads + TKQ_RESCORE_CAP) * 8;
-  static bool raised = false;  // above the default dynamic-LDS limit (once; idempotent)
-  if (!raised) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_rescore_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    raised = true;
-  }
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(gemv_rescore_kernel), 1, (int)lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(gemv_rescore_kernel, dim3(1), dim3(kThreads), lds, stream, dev_descs, count, target, (int)tiles,
                      slots, head, k, token, cand, cand_logits);
   return hipGetLastError();
