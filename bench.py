@@ -19,7 +19,8 @@ Other workloads (for measurement; each prints its own line): the 0.5B sweep
 in the other codings (0.5b-k5, 0.5b-tern, 0.5b-hier, 0.5b-int2, 0.5b-int3),
 with the greedy token (0.5b-int4-greedy) or the head rescore
 (0.5b-int4-rescore, --rescore-k candidates), for M tokens at once
-(0.5b-int4-mM, M = 2, 4, 8, 16; 7b-int4-m16), the binary shapes (bin), the 7B
+(0.5b-int4-mM, M = 2, 4, 8, 16; 7b-int4-m16; int4-hier-g32: 0.5b-hier-m16,
+7b-hier-m16), the binary shapes (bin), the 7B
 sweep (7b-int4, 7b-hier), the 7B MLP prefill (7b-prefill), KV-cache decode
 (kv-4k, kv-32k, kv-32k-gqa, kv-128k-gqa), one 896 x 896 GEMV (single-896) and
 the read probe (probe).
@@ -55,21 +56,22 @@ TRAFFIC_SOURCES = {"gemv": ["gemm_tkq_gemv_amd/csrc/gemv.hip"] + _COMMON,
                    "prefill": ["gemm_tkq_gemv_amd/csrc/prefill.hip"] + _COMMON,
                    "kv": ["gemm_tkq_gemv_amd/csrc/kv.hip"] + _COMMON}
 # workload -> (kernel family, bytes per launch, sha256[:16] of that family's sources)
-TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266616382, "20c70ae719d399ba"),
-                 "0.5b-k5": ("gemv", 506971706, "20c70ae719d399ba"),
-                 "0.5b-tern": ("gemv", 135444579, "20c70ae719d399ba"),
-                 "bin": ("gemv", 115068394, "20c70ae719d399ba"),
-                 "7b-int4": ("gemv", 3781892473, "20c70ae719d399ba"),
-                 "7b-prefill": ("prefill", 238651956, "143dc970ac5e58dd"),
-                 "0.5b-hier": ("gemv", 268438052, "20c70ae719d399ba"),
-                 "0.5b-int2": ("gemv", 143153278, "20c70ae719d399ba"),
-                 "0.5b-int3": ("gemv", 206228152, "20c70ae719d399ba"),
-                 "0.5b-int4-greedy": ("gemv", 266693011, "20c70ae719d399ba"),
-                 "0.5b-int4-m16": ("small_m", 382402161, "dcca247aa7644067"),
-                 "kv-32k": ("kv", 143489614, "b36e2b1cae6332ba"),
-                 "kv-4k": ("kv", 18430846, "b36e2b1cae6332ba"),
-                 "kv-32k-gqa": ("kv", 37219117, "b36e2b1cae6332ba"),
-                 "kv-128k-gqa": ("kv", 145439373, "b36e2b1cae6332ba")}
+TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266616382, "b6f6bd5552d3944b"),
+                 "0.5b-k5": ("gemv", 506971706, "b6f6bd5552d3944b"),
+                 "0.5b-tern": ("gemv", 135444579, "b6f6bd5552d3944b"),
+                 "bin": ("gemv", 115068394, "b6f6bd5552d3944b"),
+                 "7b-int4": ("gemv", 3781892473, "b6f6bd5552d3944b"),
+                 "7b-prefill": ("prefill", 238651956, "c2541f1b6ffb18bc"),
+                 "0.5b-hier": ("gemv", 268438052, "b6f6bd5552d3944b"),
+                 "0.5b-int2": ("gemv", 143153278, "b6f6bd5552d3944b"),
+                 "0.5b-int3": ("gemv", 206228152, "b6f6bd5552d3944b"),
+                 "0.5b-int4-greedy": ("gemv", 266693011, "b6f6bd5552d3944b"),
+                 "0.5b-int4-m16": ("small_m", 382402161, "1b6c1ca484e5e02d"),
+                 "0.5b-hier-m16": ("small_m", 383530509, "1b6c1ca484e5e02d"),
+                 "kv-32k": ("kv", 143489614, "96a6fe5bf66eaca8"),
+                 "kv-4k": ("kv", 18430846, "96a6fe5bf66eaca8"),
+                 "kv-32k-gqa": ("kv", 37219117, "96a6fe5bf66eaca8"),
+                 "kv-128k-gqa": ("kv", 145439373, "96a6fe5bf66eaca8")}
 
 
 def traffic_family(workload):
@@ -551,34 +553,40 @@ def run_sweep(args, torch, tkq, inputs, model, fmt, greedy=False, rescore_k=0):
     return out
 
 
-def run_small(args, torch, tkq, inputs, model, M):
+SMALL_FMT_NAMES = {"int4": "int4-g128", "hier": "int4-hier-g32"}
+
+
+def run_small(args, torch, tkq, inputs, model, M, fmt="int4"):
     """Multi-token GEMV: the model's whole sweep for M tokens at once
-    (speculative verification of M draft tokens), int4 g128, one launch."""
-    items, shapes = build_sweep(torch, tkq, inputs, model, "int4")
+    (speculative verification of M draft tokens), int4 g128 or
+    int4-hier-g32, one launch."""
+    items, shapes = build_sweep(torch, tkq, inputs, model, fmt)
     for i, it in enumerate(items):
         K, N = it["K"], it["N"]
         X = np.stack([inputs.normal_vector((6, i, m), K) for m in range(M)])
         it["x"] = torch.from_numpy(X).cuda()
         it["y"] = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    weight_bytes = sum(it["codes"].numel() * 4 + it["meta"].numel() * 4 for it in items)
+    # codes + metadata the kernel reads (the hier block's alignment padding is not read)
+    weight_bytes = sum(n * k // 2 + n * k // 32 + (4 * n if fmt == "hier" else 0) for _, n, k in shapes)
     step_bytes = weight_bytes + sum(M * (2 * k + 2 * n) for _, n, k in shapes)
     flops = sum(2 * M * n * k for _, n, k in shapes)
     copies = max(1, math.ceil(ROTATE_BYTES / weight_bytes))
-    batches = [tkq.GemvBatch("int4", items, tokens=M)]
+    batches = [tkq.GemvBatch(fmt, items, tokens=M)]
     for _ in range(copies - 1):
         clone = [dict(it, codes=it["codes"].clone(), meta=it["meta"].clone()) for it in items]
-        batches.append(tkq.GemvBatch("int4", clone, tokens=M))
+        batches.append(tkq.GemvBatch(fmt, clone, tokens=M))
     torch.cuda.synchronize()
     ms = time_steps(torch, lambda s: batches[s % len(batches)].run(), args.steps, args.warmup, args.graph,
                     len(batches))
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    return {"metric": "int4-g128 multi-token GEMV (M=%d) achieved HBM TB/s" % M,
+    name = SMALL_FMT_NAMES[fmt]
+    return {"metric": "%s multi-token GEMV (M=%d) achieved HBM TB/s" % (name, M),
             "value": round(gbs / 1000.0, 4), "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "f16",
             "data": "synthetic: seeded N(0,0.02) weights at the model's shapes, N(0,1) fp16 tokens",
-            "config": {"workload": "%s weight sweep for %d tokens at once (int4-g128, %d matrices, one launch)"
-                                   % (model, M, len(shapes)),
+            "config": {"workload": "%s weight sweep for %d tokens at once (%s, %d matrices, one launch)"
+                                   % (model, M, name, len(shapes)),
                        "tokens": M, "bytes_per_step": step_bytes, "flops_per_step": flops,
                        "copies_rotated": len(batches)},
             "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
@@ -754,7 +762,7 @@ def main():
     ap.add_argument("--workload", default="0.5b-int4",
                     choices=["0.5b-int4", "0.5b-int4-greedy", "0.5b-int4-rescore", "0.5b-k5", "0.5b-tern", "0.5b-hier",
                              "0.5b-int2", "0.5b-int3", "0.5b-int4-m2", "0.5b-int4-m4", "0.5b-int4-m8", "0.5b-int4-m16",
-                             "7b-int4-m16", "kv-32k", "kv-32k-gqa", "kv-4k", "kv-128k-gqa", "bin", "single-896",
+                             "7b-int4-m16", "0.5b-hier-m16", "7b-hier-m16", "kv-32k", "kv-32k-gqa", "kv-4k", "kv-128k-gqa", "bin", "single-896",
                              "7b-int4", "7b-hier", "7b-prefill", "probe"])
     ap.add_argument("--graph", default="none", choices=["none", "step", "all"],
                     help="launch steps as HIP graph replays (see time_steps)")
@@ -816,10 +824,11 @@ def main():
     elif "-m" in w:
         model = "qwen2.5-7b" if w.startswith("7b") else "qwen2.5-0.5b"
         M = int(w.split("-m")[1])
-        out = run_small(args, torch, tkq, inputs, model, M)
+        fmt = "hier" if "-hier-" in w else "int4"
+        out = run_small(args, torch, tkq, inputs, model, M, fmt)
         torch.cuda.empty_cache()
         if not args.no_cpu_baseline:
-            out["cpu_baseline"] = gemv_cpu_entry(inputs, model, "int4", args.cpu_budget, M)
+            out["cpu_baseline"] = gemv_cpu_entry(inputs, model, fmt, args.cpu_budget, M)
     elif w == "bin":
         out = run_binary(args, torch, tkq, inputs)
         if not args.no_cpu_baseline:

@@ -70,11 +70,13 @@ int gemv_max_passes(int fmt);
 hipError_t launch_gemv(int fmt, int jmax, const tkq_gemv_desc* dev_descs, int count, int64_t tiles,
                        int target, int32_t* token, uint64_t* slots, hipStream_t stream);
 
-// Multi-token GEMV (int4 g128, M = 1..16): one workgroup (4 waves of 16
-// rows) per 64-row tile; descriptors prepared by tkq_gemm_small_prepare.
+// Multi-token GEMV (int4 g128, or int4-hier-g32 when hier, M = 1..16): one
+// workgroup (4 waves of 16 rows) per 64-row tile; descriptors prepared by
+// tkq_gemm_small_prepare.
 constexpr int kSmallTileRows = 64;
 constexpr int kSmallMaxM = 16;
-hipError_t launch_small_m(const tkq_gemv_desc* dev_descs, int count, int64_t tiles, int M, hipStream_t stream);
+hipError_t launch_small_m(const tkq_gemv_desc* dev_descs, int count, int64_t tiles, int M, bool hier,
+                          hipStream_t stream);
 
 // Low-bit KV cache (pages of 128 tokens, head dimension 128) and decode.
 constexpr int kKvPage = 128, kKvDim = 128, kKvPageBytes = 17408, kKvWaves = 4, kKvMaxGroup = 8;

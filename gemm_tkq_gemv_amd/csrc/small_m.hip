@@ -1,7 +1,8 @@
-// Multi-token GEMV over int4 g128 weights for gfx950: Y[m, n] = sum_k X[m, k]
-// * w[n, k] for M = 1..16 tokens at once (speculative verification, short
-// prefill: Whetstone README, "Prior art", where several tokens share every
-// weight read; the timing table's 16-token pass).
+// Multi-token GEMV over int4 g128 or int4-hier-g32 weights for gfx950:
+// Y[m, n] = sum_k X[m, k] * w[n, k] for M = 1..16 tokens at once
+// (speculative verification, short prefill: Whetstone README, "Prior art",
+// where several tokens share every weight read; the timing table's 16-token
+// pass).
 //
 // Every weight is still read from HBM once, but it is used M times, so at
 // M = 16 the arithmetic (~60 flop per byte of int4) is beyond the vector ALUs
@@ -17,6 +18,14 @@
 //    through registers only.  The chunk is unpacked with the fp16 magic
 //    number (1024 + m * code), shifted by the zero point (exact small
 //    integers) and scaled (one fp16 rounding of s * (q - z)).
+//  * int4-hier-g32 (Whetstone README, quantizer table, "group 32 with
+//    hierarchical scale metadata"): the 16-byte chunk is exactly one
+//    32-group, and a group's index byte sits where the g128 coding keeps a
+//    group's half2, 4 bytes per 128 columns (lane c takes byte c).  The
+//    lane forms the group's step S = fp16(d sc) and offset O = fp16(dmin mi)
+//    with one packed fp16 multiply of (sc, mi) by the row's (d, dmin), and
+//    each weight is fma(q, S, -O) in fp16: three roundings, so the error of
+//    a weight is below 2^-10 (|d sc q| + |dmin mi|).
 //  * The tokens' x slices are staged through LDS, KC columns per round (512
 //    for M > 8: fewer registers and more waves, +3-5 % at M = 16; 1024 for
 //    M <= 8, where longer rounds measured equal or better), in
@@ -74,6 +83,23 @@ __device__ __forceinline__ half8 dequant_word(uint32_t w, uint32_t m0, uint32_t 
   return __builtin_bit_cast(half8, v);
 }
 
+// One code word -> 8 fp16 weights fma(q, S, -O) (int4-hier-g32) in the
+// order (0, 4, 1, 5, 2, 6, 3, 7); so = (S, S), no = (-O, -O).  The codes
+// themselves come out exact: 1024 + q - 1024, (1024 + 16 q) / 16 - 64.
+__device__ __forceinline__ half8 dequant_word_hier(uint32_t w, uint32_t m0, uint32_t m1, uint32_t magic, hv2 so,
+                                                   hv2 no) {
+  const hv2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const hv2 n1024 = {(_Float16)(-1024.0f), (_Float16)(-1024.0f)};
+  const hv2 n64 = {(_Float16)(-64.0f), (_Float16)(-64.0f)};
+  const uint32_t t = w >> 8;
+  const hv2 a = __builtin_elementwise_fma(h2((w & m0) | magic) + n1024, so, no);
+  const hv2 b = __builtin_elementwise_fma(__builtin_elementwise_fma(h2((w & m1) | magic), sixteenth, n64), so, no);
+  const hv2 c = __builtin_elementwise_fma(h2((t & m0) | magic) + n1024, so, no);
+  const hv2 d = __builtin_elementwise_fma(__builtin_elementwise_fma(h2((t & m1) | magic), sixteenth, n64), so, no);
+  u32x4 v = {u32h(a), u32h(b), u32h(c), u32h(d)};
+  return __builtin_bit_cast(half8, v);
+}
+
 template <int KC>
 struct CodeBuf {
   static constexpr int GR = KC / 128;  // quantization groups per round
@@ -85,6 +111,7 @@ struct SmallTile {
   __amdgpu_buffer_rsrc_t codes, meta, x;
   uint32_t lrow, row_bytes, meta_row;
   int K, M, c, r;
+  hv2 dd;  // int4-hier-g32: the lane's row pair (d, dmin)
 };
 
 // Groups at or past K load from an offset beyond the buffer (zeros, no
@@ -141,7 +168,7 @@ __device__ __forceinline__ void stage_x(const SmallTile& t, int kc, _Float16* xs
   }
 }
 
-template <int KC>
+template <int KC, bool HIER>
 __device__ __forceinline__ void compute_round(const SmallTile& t, int kc, const CodeBuf<KC>& b, const _Float16* xs,
                                               uint32_t m0, uint32_t m1, uint32_t magic, f32x4 (&acc)[NACC]) {
   constexpr int kLdsRow = lds_row<KC>();
@@ -150,13 +177,25 @@ __device__ __forceinline__ void compute_round(const SmallTile& t, int kc, const 
 #pragma unroll
   for (int g = 0; g < KC / 128; ++g) {
     if (g < ng) {
-      const hv2 s = {h2(b.m[g])[0], h2(b.m[g])[0]};
-      const _Float16 z = h2(b.m[g])[1];
-      const hv2 nz1 = {(_Float16)(-1024.0f) - z, (_Float16)(-1024.0f) - z};
-      const hv2 nz16 = {(_Float16)(-64.0f) - z, (_Float16)(-64.0f) - z};
+      hv2 s, nz1, nz16 = {};
+      if constexpr (HIER) {
+        // (1024 + sc, 1024 + mi) from the lane's index byte, then (sc, mi) exactly
+        const uint32_t ix = b.m[g] >> (8 * t.c);
+        const hv2 scmi = h2((ix & 0xFu) | ((ix & 0xF0u) << 12) | magic) - h2(magic);
+        const hv2 so = scmi * t.dd;  // (S, O), one rounding each
+        s = (hv2){so[0], so[0]};
+        nz1 = (hv2){-so[1], -so[1]};
+      } else {
+        s = (hv2){h2(b.m[g])[0], h2(b.m[g])[0]};
+        const _Float16 z = h2(b.m[g])[1];
+        nz1 = (hv2){(_Float16)(-1024.0f) - z, (_Float16)(-1024.0f) - z};
+        nz16 = (hv2){(_Float16)(-64.0f) - z, (_Float16)(-64.0f) - z};
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const half8 a = dequant_word(b.q[g][j], m0, m1, magic, nz1, nz16, s);
+        half8 a;
+        if constexpr (HIER) a = dequant_word_hier(b.q[g][j], m0, m1, magic, s, nz1);
+        else a = dequant_word(b.q[g][j], m0, m1, magic, nz1, nz16, s);
         half8 xb = {};
         if (live_token) xb = *reinterpret_cast<const half8*>(&xs[t.r * kLdsRow + 128 * g + 32 * t.c + 8 * j]);
         acc[j % NACC] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, xb, acc[j % NACC], 0, 0, 0);
@@ -165,7 +204,7 @@ __device__ __forceinline__ void compute_round(const SmallTile& t, int kc, const 
   }
 }
 
-template <int KC, bool PRIO>
+template <int KC, bool PRIO, bool HIER>
 __global__ __launch_bounds__(256) void small_m_kernel(const tkq_gemv_desc* __restrict__ descs, int count, int M) {
   __shared__ __attribute__((aligned(16))) _Float16 xs[16 * lds_row<KC>()];
 
@@ -193,6 +232,11 @@ __global__ __launch_bounds__(256) void small_m_kernel(const tkq_gemv_desc* __res
   t.meta = make_rsrc((const char*)d->meta + (size_t)row0 * t.meta_row, (uint32_t)nrows * t.meta_row);
   t.x = make_rsrc(d->x, (uint32_t)M * (uint32_t)K * 2u);
   const uint32_t m0 = in_sgpr(0x000F000Fu), m1 = in_sgpr(0x00F000F0u), magic = in_vgpr(kMagic);
+  if constexpr (HIER) {  // rows past N read beyond the buffer: zeros
+    const __amdgpu_buffer_rsrc_t rm =
+        make_rsrc((const char*)d->meta + hier_row_offset(N, K) + (size_t)row0 * 4u, (uint32_t)nrows * 4u);
+    t.dd = h2(load4(rm, t.lrow * 4u));
+  }
 
   f32x4 acc[NACC];
 #pragma unroll
@@ -204,13 +248,13 @@ __global__ __launch_bounds__(256) void small_m_kernel(const tkq_gemv_desc* __res
     stage_x<KC>(t, kc, xs);
     __syncthreads();
     load_round<KC, PRIO>(t, kc + KC, b);  // past K: no memory access
-    compute_round(t, kc, a, xs, m0, m1, magic, acc);
+    compute_round<KC, HIER>(t, kc, a, xs, m0, m1, magic, acc);
     if (kc + KC >= K) break;
     __syncthreads();
     stage_x<KC>(t, kc + KC, xs);
     __syncthreads();
     load_round<KC, PRIO>(t, kc + 2 * KC, a);
-    compute_round(t, kc + KC, b, xs, m0, m1, magic, acc);
+    compute_round<KC, HIER>(t, kc + KC, b, xs, m0, m1, magic, acc);
   }
 
   // lane l holds Y rows 4 (l / 16) + i of the wave's block for token l % 16
@@ -226,15 +270,22 @@ __global__ __launch_bounds__(256) void small_m_kernel(const tkq_gemv_desc* __res
   }
 }
 
-}  // namespace
-
-hipError_t launch_small_m(const tkq_gemv_desc* dev_descs, int count, int64_t tiles, int M, hipStream_t stream) {
+template <bool HIER>
+void launch_small_m_fmt(const tkq_gemv_desc* dev_descs, int count, int64_t tiles, int M, hipStream_t stream) {
   if (M > kKcSplit)
-    hipLaunchKernelGGL((small_m_kernel<kKcBigM, true>), dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream,
+    hipLaunchKernelGGL((small_m_kernel<kKcBigM, true, HIER>), dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream,
                        dev_descs, count, M);
   else
-    hipLaunchKernelGGL((small_m_kernel<kKcSmallM, false>), dim3((uint32_t)tiles), dim3(64 * kWaves), 0, stream,
-                       dev_descs, count, M);
+    hipLaunchKernelGGL((small_m_kernel<kKcSmallM, false, HIER>), dim3((uint32_t)tiles), dim3(64 * kWaves), 0,
+                       stream, dev_descs, count, M);
+}
+
+}  // namespace
+
+hipError_t launch_small_m(const tkq_gemv_desc* dev_descs, int count, int64_t tiles, int M, bool hier,
+                          hipStream_t stream) {
+  if (hier) launch_small_m_fmt<true>(dev_descs, count, tiles, M, stream);
+  else launch_small_m_fmt<false>(dev_descs, count, tiles, M, stream);
   return hipGetLastError();
 }
 

@@ -341,10 +341,12 @@ int tkq_gemv_argmax_static(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_d
 int tkq_gemm_small_prepare(tkq_gemv_desc* descs, int32_t count, int32_t M, tkq_gemv_plan* plan) {
   if (!descs || !plan || count < 1 || M < 1) return TKQ_EINVAL;
   if (M > tkq::kSmallMaxM) return TKQ_ESHAPE;
+  const int32_t fmt = descs[0].fmt;
+  if (fmt != TKQ_FMT_INT4_G128 && fmt != TKQ_FMT_INT4_HIER_G32) return TKQ_EFORMAT;
   int64_t work = 0;
   for (int32_t i = 0; i < count; ++i) {
     tkq_gemv_desc& d = descs[i];
-    if (d.fmt != TKQ_FMT_INT4_G128) return TKQ_EFORMAT;
+    if (d.fmt != fmt) return TKQ_EFORMAT;
     if (d.N < 1 || d.K < 1 || !d.codes || !d.meta || !d.x || !d.y) return TKQ_EINVAL;
     if (d.K % 128 || d.K > TKQ_MAX_K || int64_t(d.N) * d.K > kMaxWeights ||
         int64_t(M) * d.K * 2 > INT32_MAX || int64_t(M) * d.N * 2 > INT32_MAX)
@@ -359,7 +361,7 @@ int tkq_gemm_small_prepare(tkq_gemv_desc* descs, int32_t count, int32_t M, tkq_g
     d.small_rows = tkq::kSmallTileRows;
     work += tiles;
   }
-  plan->fmt = TKQ_FMT_INT4_G128;
+  plan->fmt = fmt;
   plan->count = count;
   plan->tiles = work;
   plan->variant = M;
@@ -370,11 +372,13 @@ int tkq_gemm_small_prepare(tkq_gemv_desc* descs, int32_t count, int32_t M, tkq_g
 
 int tkq_gemm_small(const tkq_gemv_plan* plan, const tkq_gemv_desc* dev_descs, void* stream) {
   if (!plan || !dev_descs) return TKQ_EINVAL;
-  if (plan->magic != kSmallMagic || plan->fmt != TKQ_FMT_INT4_G128 || plan->count < 1 || plan->tiles < 1 ||
+  if (plan->magic != kSmallMagic || (plan->fmt != TKQ_FMT_INT4_G128 && plan->fmt != TKQ_FMT_INT4_HIER_G32) ||
+      plan->count < 1 || plan->tiles < 1 ||
       plan->tiles > INT32_MAX || plan->variant < 1 || plan->variant > tkq::kSmallMaxM)
     return TKQ_EPLAN;
   if (!aligned16(dev_descs)) return TKQ_EALIGN;
-  return hip_status(tkq::launch_small_m(dev_descs, plan->count, plan->tiles, plan->variant, (hipStream_t)stream));
+  return hip_status(tkq::launch_small_m(dev_descs, plan->count, plan->tiles, plan->variant,
+                                        plan->fmt == TKQ_FMT_INT4_HIER_G32, (hipStream_t)stream));
 }
 
 static int check_kv(int64_t B, int64_t H, int64_t Hk, int64_t T, int64_t D) {

@@ -252,7 +252,7 @@ class GemvBatch:
 
     def __init__(self, fmt, items, device=None, tokens=None):
         """tokens: None for the batch-1 GEMV (x [K], y [N]); M in 1..16 for
-        the multi-token GEMV (x [M, K], y [M, N]; int4 g128 only)."""
+        the multi-token GEMV (x [M, K], y [M, N]; int4 g128 or int4-hier-g32)."""
         fmt = FORMATS.get(fmt, fmt)
         items = list(items)
         if not items:

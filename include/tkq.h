@@ -363,21 +363,28 @@ int tkq_gemv_argmax_rescore(const tkq_gemv_plan* plan,
 
 /* ---- multi-token GEMV (M = 1..16) ----------------------------------------
  * Y_i[m, n] = sum_k X_i[m, k] * w_i[n, k] for M tokens at once over many
- * int4 g128 matrices in one launch: the regime between batch-1 decode and
- * prefill (Whetstone README, "Prior art": speculative verification and
- * prefill, where several tokens share each weight read).  Each weight is
- * read from HBM once and used M times; the products run on the matrix cores
- * from fp16 weights s * (q - z) (one rounding) with fp32 accumulation;
- * fp16 output rounded to nearest even;
- * |Y - Y_exact| <= 2e-3 * sum_k |X[m,k] w[n,k]| entry-wise.
+ * int4 g128 or int4-hier-g32 matrices in one launch: the regime between
+ * batch-1 decode and prefill (Whetstone README, "Prior art": speculative
+ * verification and prefill, where several tokens share each weight read).
+ * Each weight is read from HBM once and used M times; the products run on
+ * the matrix cores from fp16 weights with fp32 accumulation; fp16 output
+ * rounded to nearest even.
+ * int4 g128: weights s * (q - z) (one rounding);
+ *   |Y - Y_exact| <= 2e-3 * sum_k |X[m,k] w[n,k]| entry-wise.
+ * int4-hier-g32: weights fma(q, fp16(d sc), -fp16(dmin mi)) in fp16 (three
+ *   roundings); |Y - Y_exact| <= 2e-3 * sum_k |X[m,k]| (|d sc q| + |dmin mi|)
+ *   entry-wise, while d sc and dmin mi are normal fp16 numbers (any weights
+ *   of ordinary magnitude).
  *
- * Descriptors as for tkq_gemv with fmt = TKQ_FMT_INT4_G128, except
+ * Descriptors as for tkq_gemv with fmt = TKQ_FMT_INT4_G128 or
+ * TKQ_FMT_INT4_HIER_G32 (one coding per call), except
  *   x: fp16 [M][K] (token-major), y: fp16 [M][N] (token-major).
- * tkq_gemm_small_prepare (host only) validates them (K % 128 == 0, M*K and
- * M*N below 2^30), fills the [prepare] fields and *plan for this M; a plan
- * from tkq_gemv_prepare is not accepted here, nor the reverse.
+ * tkq_gemm_small_prepare (host only) validates them (K % 128 == 0 for both
+ * codings, M*K and M*N below 2^30), fills the [prepare] fields and *plan for
+ * this M; a plan from tkq_gemv_prepare is not accepted here, nor the reverse.
  * Returns TKQ_OK, TKQ_EINVAL (null pointers, count or M < 1), TKQ_ESHAPE
- * (M > 16 or sizes), TKQ_EFORMAT (not int4 g128) or TKQ_EALIGN. */
+ * (M > 16 or sizes), TKQ_EFORMAT (another coding, or codings mixed) or
+ * TKQ_EALIGN. */
 int tkq_gemm_small_prepare(tkq_gemv_desc* descs, int32_t count, int32_t M,
                            tkq_gemv_plan* plan);
 

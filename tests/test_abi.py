@@ -306,6 +306,11 @@ def test_gemm_small_prepare():
     assert f(arr, 4, 0, ctypes.byref(plan)) == tkq.EINVAL
     bad = _descs(2, [(8, 128)])
     assert f(bad, 1, 4, ctypes.byref(plan)) == tkq.EFORMAT
+    hier = _descs(5, [(8, 128), (65, 896)])       # int4-hier-g32 is taken too, one coding per call
+    assert f(hier, 2, 4, ctypes.byref(plan)) == tkq.OK and plan.fmt == 5
+    hier[1].fmt = 1
+    assert f(hier, 2, 4, ctypes.byref(plan)) == tkq.EFORMAT
+    assert f(_descs(5, [(8, 96)]), 1, 4, ctypes.byref(plan)) == tkq.ESHAPE   # K % 128 for both codings
     bad = _descs(1, [(8, 96)])
     assert f(bad, 1, 4, ctypes.byref(plan)) == tkq.ESHAPE
     # plans are not interchangeable between the batch-1 and multi-token entry points
