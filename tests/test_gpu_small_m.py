@@ -129,3 +129,31 @@ def test_small_m_max_k():
     _check(W, X, items[0]["y"], "M=16 9x2^20")
     with pytest.raises(tkq.TkqError):
         tkq.GemvBatch("int4", [dict(items[0], K=K + 128)], tokens=M)
+
+
+def _outlier_tokens(seed, N, K, M, group):
+    """W and M tokens that share the outlier recipe of the batch-1 tests:
+    heavy-tailed weights, one outlier weight per group, and two channels per
+    group of 1e3..3e4 on all-zero weight columns (signs drawn per token)."""
+    W, x0 = inputs.outlier_case(seed, N, K, group)
+    big = np.abs(x0.astype(np.float32)) >= 1e3
+    r = np.random.default_rng((*seed, 1))
+    X = r.standard_normal((M, K)).astype(np.float32)
+    X[:, big] = x0[big].astype(np.float32) * r.choice([-1.0, 1.0], (M, int(big.sum())))
+    return W, X.astype(np.float16)
+
+
+@pytest.mark.parametrize("M", [3, 16])
+def test_small_m_large_activations(M):
+    """Activations of 1e3..3e4 on weights at their zero point: the entry-wise
+    bound holds (the weights are exact fp16 s (q - z) and the products exact
+    in fp32, so the error follows |x w|, not the activations' size)."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    N, K = 200, 4864
+    W, X = _outlier_tokens((750, M), N, K, M, 128)
+    assert np.abs(X.astype(np.float32)).max() >= 1e3
+    items = _items(torch, tkq, [(W, X)], M)
+    tkq.GemvBatch("int4", items, tokens=M).run()
+    torch.cuda.synchronize()
+    _check(W, X, items[0]["y"], "outliers M=%d" % M)

@@ -181,3 +181,19 @@ def test_small_m_hier_max_k():
     tkq.GemvBatch("hier", items, tokens=M).run()
     torch.cuda.synchronize()
     _check(W, X, items[0], "M=16 9x2^20")
+
+
+@pytest.mark.parametrize("M", [3, 16])
+def test_small_m_hier_large_activations(M):
+    """Activations of 1e3..3e4 on all-zero weight columns, heavy-tailed
+    weights with one outlier per 32-group: the two-term bound holds."""
+    torch = gpu_or_skip()
+    from gemm_tkq_gemv_amd import tkq
+    from test_gpu_small_m import _outlier_tokens
+    N, K = 200, 4864
+    W, X = _outlier_tokens((820, M), N, K, M, 32)
+    assert np.abs(X.astype(np.float32)).max() >= 1e3
+    items = _items(torch, tkq, [(W, X)], M)
+    tkq.GemvBatch("hier", items, tokens=M).run()
+    torch.cuda.synchronize()
+    _check(W, X, items[0], "outliers M=%d" % M)
