@@ -134,36 +134,41 @@ __device__ __forceinline__ void load_round(const SmallTile& t, int kc, CodeBuf<K
   if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
 }
 
-// Stage X[0..M)[kc, kc + KC) into LDS in the unpack's k order.  Each
-// thread issues the loads of SB units before writing any of them, so a
-// round's staging costs ceil(units / (256 SB)) memory round trips rather
-// than one per unit (units past the end read beyond the buffer: zeros).
+// Stage X[0..M)[kc, kc + KC) into LDS in the unpack's k order.  Thread i
+// takes the 8-column unit i % U (U = KC / 8 units per token row) of token
+// rows i / U + P j, j < SB (P = token rows per pass of the workgroup), so
+// one batch covers every row a variant takes (KC = 512: 4 x 4 = 16 rows;
+// KC = 1024: 2 x 4 = 8 rows) with no division.  Each thread issues its SB
+// loads before writing any of them (one memory round trip per round); units
+// past the round's end or rows past M read beyond the buffer (zeros) and
+// are not written.
 constexpr int SB = 4;
 template <int KC>
 __device__ __forceinline__ void stage_x(const SmallTile& t, int kc, _Float16* xs) {
   constexpr int kLdsRow = lds_row<KC>();
-  const int units = min(KC, t.K - kc) / 8;  // 8-column units per token row
-  const int total = t.M * units;
-  for (int base = 0; base < total; base += 64 * kWaves * SB) {  // uniform trip count
-    u32x4 v[SB];
+  constexpr int U = KC / 8;
+  constexpr int P = 64 * kWaves / U;
+  static_assert(P * U == 64 * kWaves, "a pass covers whole token rows");
+  static_assert(P * SB >= (KC == kKcSmallM ? kKcSplit : kSmallMaxM), "one batch covers every token row");
+  const int units = min(KC, t.K - kc) / 8;
+  const int e = (int)threadIdx.x % U, m0 = (int)threadIdx.x / U;
+  u32x4 v[SB];
 #pragma unroll
-    for (int j = 0; j < SB; ++j) {
-      const int u = base + 64 * kWaves * j + (int)threadIdx.x;
-      const int m = u / units, e = u - m * units;
-      v[j] = load16(t.x, u < total ? (uint32_t)(m * t.K + kc + 8 * e) * 2u : kFar);
-    }
+  for (int j = 0; j < SB; ++j) {
+    const int m = m0 + P * j;
+    const bool ok = m < t.M && e < units;
+    v[j] = load16(t.x, ok ? (uint32_t)(m * t.K + kc + 8 * e) * 2u : kFar);
+  }
 #pragma unroll
-    for (int j = 0; j < SB; ++j) {
-      const int u = base + 64 * kWaves * j + (int)threadIdx.x;
-      if (u < total) {
-        const int m = u / units, e = u - m * units;
-        u32x4 p;
-        p[0] = __builtin_amdgcn_perm(v[j][2], v[j][0], 0x05040100u);  // (x0, x4)
-        p[1] = __builtin_amdgcn_perm(v[j][2], v[j][0], 0x07060302u);  // (x1, x5)
-        p[2] = __builtin_amdgcn_perm(v[j][3], v[j][1], 0x05040100u);  // (x2, x6)
-        p[3] = __builtin_amdgcn_perm(v[j][3], v[j][1], 0x07060302u);  // (x3, x7)
-        *reinterpret_cast<u32x4*>(&xs[m * kLdsRow + 8 * e]) = p;
-      }
+  for (int j = 0; j < SB; ++j) {
+    const int m = m0 + P * j;
+    if (m < t.M && e < units) {
+      u32x4 p;
+      p[0] = __builtin_amdgcn_perm(v[j][2], v[j][0], 0x05040100u);  // (x0, x4)
+      p[1] = __builtin_amdgcn_perm(v[j][2], v[j][0], 0x07060302u);  // (x1, x5)
+      p[2] = __builtin_amdgcn_perm(v[j][3], v[j][1], 0x05040100u);  // (x2, x6)
+      p[3] = __builtin_amdgcn_perm(v[j][3], v[j][1], 0x07060302u);  // (x3, x7)
+      *reinterpret_cast<u32x4*>(&xs[m * kLdsRow + 8 * e]) = p;
     }
   }
 }
