@@ -31,7 +31,9 @@
 //    M <= 8, where longer rounds measured equal or better), in
 //    the k order the unpack produces (0, 4, 1, 5, 2, 6, 3, 7 within each 8),
 //    and read as the B operands (lane l: token l % 16, k-block l / 16).
-//    Lanes of tokens >= M contribute zeros.
+//    Lanes of tokens >= M read LDS rows zeroed once per workgroup, so the
+//    B-operand reads need no condition (one without a condition lets the
+//    compiler issue them ahead of their MFMAs).
 //  * The codes of round i + 1 are loaded into a second register buffer
 //    while round i is computed, so every wave keeps its next KC / 2 bytes
 //    per row in flight.
@@ -178,7 +180,6 @@ __device__ __forceinline__ void compute_round(const SmallTile& t, int kc, const 
                                               uint32_t m0, uint32_t m1, uint32_t magic, f32x4 (&acc)[NACC]) {
   constexpr int kLdsRow = lds_row<KC>();
   const int ng = min(KC, t.K - kc) / 128;
-  const bool live_token = t.r < t.M;
 #pragma unroll
   for (int g = 0; g < KC / 128; ++g) {
     if (g < ng) {
@@ -201,8 +202,8 @@ __device__ __forceinline__ void compute_round(const SmallTile& t, int kc, const 
         half8 a;
         if constexpr (HIER) a = dequant_word_hier(b.q[g][j], m0, m1, magic, s, nz1);
         else a = dequant_word(b.q[g][j], m0, m1, magic, nz1, nz16, s);
-        half8 xb = {};
-        if (live_token) xb = *reinterpret_cast<const half8*>(&xs[t.r * kLdsRow + 128 * g + 32 * t.c + 8 * j]);
+        // token rows past M read the zeros written at the start of the kernel
+        const half8 xb = *reinterpret_cast<const half8*>(&xs[t.r * kLdsRow + 128 * g + 32 * t.c + 8 * j]);
         acc[j % NACC] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, xb, acc[j % NACC], 0, 0, 0);
       }
     }
@@ -248,6 +249,11 @@ __global__ __launch_bounds__(256) void small_m_kernel(const tkq_gemv_desc* __res
   for (int i = 0; i < NACC; ++i) acc[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
   CodeBuf<KC> a, b;
   load_round<KC, PRIO>(t, 0, a);
+  // Token rows M..15 of xs are never staged: zero them once, so that the
+  // lanes of tokens past M read zeros unconditionally (the first barrier
+  // below orders these writes before any read).
+  for (int i = threadIdx.x; i < (kSmallMaxM - M) * lds_row<KC>() / 8; i += 64 * kWaves)
+    *reinterpret_cast<u32x4*>(&xs[M * lds_row<KC>() + 8 * i]) = (u32x4){0u, 0u, 0u, 0u};
   for (int kc = 0; kc < K; kc += 2 * KC) {
     __syncthreads();  // the previous round's reads of xs are done
     stage_x<KC>(t, kc, xs);
