@@ -66,8 +66,8 @@ TRAFFIC_BYTES = {"0.5b-int4": ("gemv", 266616382, "b6f6bd5552d3944b"),
                  "0.5b-int2": ("gemv", 143153278, "b6f6bd5552d3944b"),
                  "0.5b-int3": ("gemv", 206228152, "b6f6bd5552d3944b"),
                  "0.5b-int4-greedy": ("gemv", 266693011, "b6f6bd5552d3944b"),
-                 "0.5b-int4-m16": ("small_m", 383034850, "65cc62860199d90f"),
-                 "0.5b-hier-m16": ("small_m", 387569089, "65cc62860199d90f"),
+                 "0.5b-int4-m16": ("small_m", 383039047, "84bc997abcf0d8f2"),
+                 "0.5b-hier-m16": ("small_m", 387133073, "84bc997abcf0d8f2"),
                  "kv-32k": ("kv", 143489614, "96a6fe5bf66eaca8"),
                  "kv-4k": ("kv", 18430846, "96a6fe5bf66eaca8"),
                  "kv-32k-gqa": ("kv", 37219117, "96a6fe5bf66eaca8"),
